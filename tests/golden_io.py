@@ -1,0 +1,65 @@
+"""Reader for the hand-derived cases in tests/golden/hand_cases.txt."""
+
+from __future__ import annotations
+
+import os
+from dataclasses import dataclass
+from typing import List, Optional
+
+import numpy as np
+
+from workloads.synth import f32_to_bits
+
+GOLDEN_DIR = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+NEG_INF_WORD = {"f32": 0xFF800000, "f16": 0xFC00, "bf16": 0xFF80}
+
+
+@dataclass
+class HandCase:
+    name: str
+    dtype: str
+    x: np.ndarray  # bits [B, V]
+    p: Optional[np.ndarray]  # bits [B]
+    k: Optional[np.ndarray]  # int32 [B]
+    expect: np.ndarray  # bits [B, V]
+
+
+def _parse_values(tokens, dtype):
+    vals = []
+    for t in tokens:
+        if t == "-inf":
+            vals.append(-np.inf)
+        elif t == "-0":
+            vals.append(-0.0)
+        else:
+            vals.append(float(t))
+    return f32_to_bits(np.array(vals, dtype=np.float32), dtype)
+
+
+def load_hand_cases(path: Optional[str] = None) -> List[HandCase]:
+    path = path or os.path.join(GOLDEN_DIR, "hand_cases.txt")
+    cases = []
+    cur = None
+    with open(path) as f:
+        for raw in f:
+            line = raw.strip()
+            if not line or line.startswith("#"):
+                continue
+            head, *rest = line.split()
+            if head == "case":
+                cur = dict(name=rest[0], dtype=rest[1], x=[], p=None, k=None, expect=[])
+                cases.append(cur)
+            elif head == "x":
+                cur["x"].append(_parse_values(rest, cur["dtype"]))
+            elif head == "expect":
+                cur["expect"].append(_parse_values(rest, cur["dtype"]))
+            elif head == "p":
+                cur["p"] = None if rest == ["none"] else _parse_values(rest, cur["dtype"])
+            elif head == "k":
+                cur["k"] = None if rest == ["none"] else np.array([int(v) for v in rest], dtype=np.int32)
+            else:
+                raise ValueError(f"bad golden line: {line}")
+    return [
+        HandCase(c["name"], c["dtype"], np.stack(c["x"]), c["p"], c["k"], np.stack(c["expect"]))
+        for c in cases
+    ]

@@ -1,0 +1,223 @@
+"""Checks that pin the CPU oracle to facts other than its own code.
+
+Each check takes ``apply_fn(logits_bits, dtype, p_bits, k) -> out_bits`` and
+raises AssertionError on a mismatch, so the same checks run against the real
+oracle (they must pass) and against deliberately broken copies of it (each
+copy must fail at least one check).
+
+The facts used:
+  * hand-derived cases (tests/golden/hand_cases.txt), including the calling
+    example of the ApplyTopKTopPWithSorted page, §7;
+  * top-k by counting: the threshold T is the value with
+    #(x > T) < k <= #(x >= T), found without sorting;
+  * top-p by the textbook nucleus rule (Holtzman et al., "The Curious Case of
+    Neural Text Degeneration"): walking from the most probable token down, a
+    token is kept while the probability mass strictly above it is below p,
+    here p' = 1 - t with t the fp32 value the filter compares against; the
+    walk visits equal values from the highest index down, which is the
+    reverse of a stable ascending sort;
+  * invariants: at least one survivor, survivors form a suffix of the stable
+    order, kept bits equal the inputs, p = 0 keeps exactly the last sorted
+    position, disabled k values agree, permutation equivariance.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+from tests.golden_io import NEG_INF_WORD, load_hand_cases
+from workloads.synth import bits_to_f32, random_rows
+
+
+def _vals(bits, dtype):
+    return bits_to_f32(np.asarray(bits), dtype).astype(np.float64)
+
+
+def _t32(p_bits_b, dtype):
+    p32 = np.float32(bits_to_f32(np.asarray([p_bits_b]), dtype)[0])
+    return np.float32(np.float32(1.0) - p32)
+
+
+def check_hand_cases(apply_fn):
+    for case in load_hand_cases():
+        got = apply_fn(case.x, case.dtype, case.p, case.k)
+        assert np.array_equal(got, case.expect), (case.name, got, case.expect)
+
+
+def topk_threshold_by_counting(x, k):
+    """Value T with #(x > T) < k <= #(x >= T), by counting (no sort)."""
+    for T in set(float(v) for v in x):
+        gt = sum(1 for v in x if v > T)
+        ge = sum(1 for v in x if v >= T)
+        if gt < k <= ge:
+            return T
+    raise AssertionError("no threshold found")
+
+
+def expected_keep_bruteforce(x, k, t):
+    """Survivor set from counting (top-k) and the nucleus walk (top-p).
+
+    Returns (keep bool array, ambiguous flag). ``ambiguous`` is set when the
+    mass above some token is within 1e-9 of p', where double rounding could
+    legitimately decide either way.
+    """
+    V = len(x)
+    keep_k = np.ones(V, dtype=bool)
+    if k is not None and 1 <= k <= V - 1:
+        T = topk_threshold_by_counting(x, k)
+        keep_k = np.array([v >= T for v in x])
+    if t is None:
+        return keep_k, False
+    order = sorted(range(V), key=lambda i: (x[i], i), reverse=True)
+    alive = [i for i in order if keep_k[i]]
+    m = x[alive[0]]
+    w = [math.exp(x[i] - m) for i in alive]
+    Z = math.fsum(w)
+    p_prime = 1.0 - float(t)
+    keep = np.zeros(V, dtype=bool)
+    ambiguous = False
+    for pos, i in enumerate(alive):
+        above = math.fsum(w[:pos]) / Z
+        if abs(above - p_prime) < 1e-9:
+            ambiguous = True
+        if pos == 0 or above < p_prime:
+            keep[i] = True
+    return keep, ambiguous
+
+
+def check_bruteforce_tiny(apply_fn, dtypes=("f32", "bf16", "f16"), n_rows=6, max_v=8):
+    """Every k in [-1, V+1] and a p grid on tiny rows with ties and both zeros."""
+    p_grid = [0.0, 0.05, 0.2, 0.35, 0.5, 0.65, 0.8, 0.95, 1.0]
+    seed = 0
+    for dtype in dtypes:
+        for V in range(1, max_v + 1):
+            for kind in ("normal", "ties", "zeros", "gumbel"):
+                seed += 1
+                xb = random_rows(seed, n_rows, V, dtype, kind=kind, scale=1.5)
+                for b in range(n_rows):
+                    row = xb[b : b + 1]
+                    x = list(_vals(row[0], dtype))
+                    for kk in [None] + list(range(-1, V + 2)):
+                        for pv in [None] + p_grid:
+                            if kk is None and pv is None:
+                                continue
+                            p_bits = None
+                            t = None
+                            if pv is not None:
+                                from workloads.synth import f32_to_bits
+
+                                p_bits = f32_to_bits(np.array([pv], np.float32), dtype)
+                                t = _t32(p_bits[0], dtype)
+                            k_arr = None if kk is None else np.array([kk], np.int32)
+                            got = apply_fn(row, dtype, p_bits, k_arr)[0]
+                            keep, amb = expected_keep_bruteforce(x, kk, t)
+                            if amb:
+                                continue
+                            exp = np.where(keep, row[0], NEG_INF_WORD[dtype]).astype(row.dtype)
+                            assert np.array_equal(got, exp), (dtype, V, kind, b, kk, pv, x, got, exp)
+
+
+def check_topk_counting_random(apply_fn, dtype="f32", V=257, B=24):
+    """Larger rows, k only: survivors are exactly {x >= T} with T by counting."""
+    for kind in ("normal", "ties", "zeros"):
+        xb = random_rows(1000 + V, B, V, dtype, kind=kind)
+        rng = np.random.default_rng(7)
+        k = rng.integers(1, V - 1, size=B, endpoint=True).astype(np.int32)
+        got = apply_fn(xb, dtype, None, k)
+        for b in range(B):
+            x = _vals(xb[b], dtype)
+            T = topk_threshold_by_counting(list(x), int(k[b]))
+            exp = np.where(x >= T, xb[b], NEG_INF_WORD[dtype]).astype(xb.dtype)
+            assert np.array_equal(got[b], exp), (kind, b)
+
+
+def check_nucleus_random(apply_fn, dtype="f32", V=96, B=32):
+    """Moderate rows, joint and p-only, against the nucleus walk."""
+    for kind in ("normal", "ties", "gumbel"):
+        xb = random_rows(2000 + V, B, V, dtype, kind=kind)
+        rng = np.random.default_rng(11)
+        k = rng.integers(-1, V + 1, size=B, endpoint=True).astype(np.int32)
+        pf = rng.uniform(0.0, 1.0, size=B).astype(np.float32)
+        from workloads.synth import f32_to_bits
+
+        p = f32_to_bits(pf, dtype)
+        for use_k in (True, False):
+            got = apply_fn(xb, dtype, p, k if use_k else None)
+            for b in range(B):
+                x = list(_vals(xb[b], dtype))
+                keep, amb = expected_keep_bruteforce(x, int(k[b]) if use_k else None, _t32(p[b], dtype))
+                if amb:
+                    continue
+                exp = np.where(keep, xb[b], NEG_INF_WORD[dtype]).astype(xb.dtype)
+                assert np.array_equal(got[b], exp), (kind, b, use_k)
+
+
+def check_invariants(apply_fn, dtype="bf16", V=300, B=16):
+    from workloads.synth import f32_to_bits
+
+    rng = np.random.default_rng(5)
+    for kind in ("normal", "ties", "zeros", "spikes", "const"):
+        xb = random_rows(3000 + V, B, V, dtype, kind=kind)
+        vals = _vals(xb, dtype).reshape(B, V)
+        k = rng.integers(1, V - 1, size=B, endpoint=True).astype(np.int32)
+        p = f32_to_bits(rng.uniform(0.0, 1.0, size=B).astype(np.float32), dtype)
+        neg = NEG_INF_WORD[dtype]
+        out = apply_fn(xb, dtype, p, k)
+        for b in range(B):
+            kept = out[b] != neg
+            # at least one survivor; kept bits are the input bits
+            assert kept.any()
+            assert np.array_equal(out[b][kept], xb[b][kept])
+            # survivors form a suffix of the stable ascending order
+            order = sorted(range(V), key=lambda i: (vals[b, i], i))
+            flags = kept[order]
+            first = int(np.argmax(flags))
+            assert flags[first:].all(), (kind, b)
+        # p = 0 keeps exactly the last sorted position (max, highest index)
+        p0 = f32_to_bits(np.zeros(B, np.float32), dtype)
+        out0 = apply_fn(xb, dtype, p0, None)
+        for b in range(B):
+            kept = np.nonzero(out0[b] != neg)[0]
+            mx = vals[b].max()
+            assert list(kept) == [int(np.nonzero(vals[b] == mx)[0].max())], (kind, b)
+        # k = 1 without p keeps the max and all its ties
+        out1 = apply_fn(xb, dtype, None, np.ones(B, np.int32))
+        for b in range(B):
+            assert np.array_equal(out1[b] != neg, vals[b] == vals[b].max()), (kind, b)
+        # disabled k values agree with each other and with k absent
+        outs = [apply_fn(xb, dtype, p, np.full(B, kk, np.int32)) for kk in (0, -3, V, V + 5)]
+        ref = apply_fn(xb, dtype, p, None)
+        for o in outs:
+            assert np.array_equal(o, ref), kind
+        # p = 1 (t = 0) with k equals k alone when no probability underflows
+        p1 = f32_to_bits(np.ones(B, np.float32), dtype)
+        assert np.array_equal(apply_fn(xb, dtype, p1, k), apply_fn(xb, dtype, None, k)), kind
+
+
+def check_permutation_equivariance(apply_fn, dtype="f32", V=200, B=8):
+    from workloads.synth import f32_to_bits
+
+    xb = random_rows(4000, B, V, dtype, kind="normal")
+    rng = np.random.default_rng(9)
+    k = rng.integers(1, V, size=B).astype(np.int32)
+    p = f32_to_bits(rng.uniform(0.2, 0.99, size=B).astype(np.float32), dtype)
+    out = apply_fn(xb, dtype, p, k)
+    for trial in range(3):
+        perm = rng.permutation(V)
+        outp = apply_fn(xb[:, perm], dtype, p, k)
+        for b in range(B):
+            if len(set(xb[b].tolist())) != V:
+                continue  # equivariance holds for distinct values only
+            assert np.array_equal(outp[b], out[b][perm])
+
+
+ALL_CHECKS = [
+    check_hand_cases,
+    check_topk_counting_random,
+    check_nucleus_random,
+    check_invariants,
+    check_permutation_equivariance,
+    check_bruteforce_tiny,
+]

@@ -1,0 +1,107 @@
+"""The CPU oracle against its pins (no GPU needed)."""
+
+import numpy as np
+import pytest
+
+from oracle import apply_top_k_top_p, apply_top_k_top_p_with_sorted
+from tests import oracle_pins as pins
+from workloads.synth import bits_to_f32, make_workload, random_rows, split_modes, stable_ascending_sort
+
+
+def oracle_apply(x, dtype, p, k):
+    return apply_top_k_top_p(x, dtype, p, k, keep_traces=False).out
+
+
+@pytest.mark.parametrize("check", pins.ALL_CHECKS, ids=lambda c: c.__name__)
+def test_oracle_pins(check):
+    check(oracle_apply)
+
+
+def test_with_sorted_matches_apply():
+    """Pre-sorted entry on a stable sort equals the sorting entry (both forms)."""
+    for dtype, kind in (("bf16", "normal"), ("f32", "ties"), ("f16", "zeros")):
+        xb = random_rows(77, 12, 333, dtype, kind=kind)
+        k, p = pins_params(12, 333, dtype)
+        ref = oracle_apply(xb, dtype, p, k)
+        idx, sv = stable_ascending_sort(xb, dtype)
+        a = apply_top_k_top_p_with_sorted(sv, idx, dtype, p, k, logits_bits=xb).out
+        b = apply_top_k_top_p_with_sorted(sv, idx, dtype, p, k, logits_bits=None).out
+        assert np.array_equal(a, ref)
+        assert np.array_equal(b, ref)
+
+
+def pins_params(B, V, dtype):
+    from workloads.synth import random_params
+
+    return random_params(B * 1000 + V, B, V, dtype)
+
+
+def test_cumsum_numerics():
+    """The float64 cumsum ends at 1 and never decreases."""
+    for c in (1, 2, 3):
+        wl = make_workload(c, rows=range(3))
+        res = apply_top_k_top_p(wl.logits, wl.dtype, wl.p, wl.k)
+        for tr in res.traces:
+            if tr.probs_sum32 is None:
+                continue
+            assert np.all(np.diff(tr.probs_sum32.astype(np.float64)) >= 0)
+            assert abs(float(tr.probs_sum32[-1]) - 1.0) <= 1e-6
+
+
+def test_errors():
+    x = np.zeros((1, 4), np.uint32)
+    with pytest.raises(ValueError):
+        apply_top_k_top_p(x, "f32", None, None)
+    with pytest.raises(ValueError):
+        apply_top_k_top_p(x, "f64", None, np.ones(1, np.int32))
+
+
+def test_empty_and_single_column():
+    x = np.zeros((0, 5), np.uint16)
+    assert apply_top_k_top_p(x, "bf16", None, np.ones(0, np.int32)).out.shape == (0, 5)
+    x1 = random_rows(3, 4, 1, "bf16")
+    out = oracle_apply(x1, "bf16", np.zeros(4, np.uint16), np.ones(4, np.int32))
+    assert np.array_equal(out, x1)
+
+
+@pytest.mark.parametrize("c", [1, 2, 3, 4, 5])
+def test_workload_invariants(c):
+    """Invariants on a few real rows of every workload."""
+    wl = make_workload(c, rows=[0, 1, 2, 3])
+    neg = {"f32": 0xFF800000, "f16": 0xFC00, "bf16": 0xFF80}[wl.dtype]
+    if wl.entry == "apply":
+        res = apply_top_k_top_p(wl.logits, wl.dtype, wl.p, wl.k)
+    else:
+        res = apply_top_k_top_p_with_sorted(wl.sorted_value, wl.sorted_indices, wl.dtype, wl.p, wl.k,
+                                            logits_bits=wl.logits)
+        ref = apply_top_k_top_p(wl.logits, wl.dtype, wl.p, wl.k, keep_traces=False).out
+        assert np.array_equal(res.out, ref)
+    vals = bits_to_f32(wl.logits, wl.dtype).reshape(wl.B, wl.V)
+    for b in range(wl.B):
+        kept = res.out[b] != neg
+        assert kept.any()
+        assert np.array_equal(res.out[b][kept], wl.logits[b][kept])
+        assert kept[int(np.argmax(vals[b]))] or vals[b][kept].max() == vals[b].max()
+        if wl.k is not None and 1 <= wl.k[b] <= wl.V - 1:
+            # top-k survivors are at least k and include every value above the threshold
+            assert kept.sum() <= np.count_nonzero(vals[b] >= np.sort(vals[b])[wl.V - wl.k[b]])
+
+
+def test_workload3_modes_match_null_calls():
+    """Workload 3's single call (k=0 / p=1 stand-ins) equals calls with absent p / k."""
+    wl = make_workload(3, rows=range(6))
+    full = oracle_apply(wl.logits, wl.dtype, wl.p, wl.k)
+    for pos, p, k in split_modes(wl):
+        sub = apply_top_k_top_p(wl.logits[pos], wl.dtype, p, k, keep_traces=False).out
+        assert np.array_equal(sub, full[pos])
+
+
+def test_t_readings_report():
+    """The two readings of 1 - p agree for fp32 p >= 0.5 and differ only below (reported)."""
+    from oracle import one_minus_p
+    from workloads.synth import f32_to_bits
+
+    for pv in (0.5, 0.6, 0.75, 0.9, 0.99):
+        for dtype in ("bf16", "f16"):
+            pb = f32_to_bits(np.array([pv], np.float32), dtype)[0]
+            assert one_minus_p(pb, dtype, "fp32") == one_minus_p(pb, dtype, "dtype")

@@ -1,0 +1,68 @@
+"""Plant plausible mistakes in a copy of the CPU oracle; the pins must catch each.
+
+This shows the pins in tests/oracle_pins.py have teeth: every mutant below is
+a one-line slip someone could make while writing the filter, and each one must
+fail at least one pin. The mutants live only in memory, on the CPU.
+"""
+
+import sys
+import types
+
+import pytest
+
+import oracle.topktopp_oracle as O
+from tests import oracle_pins as pins
+
+MUTANTS = {
+    "topk_masks_ties_too": ("top_k_mask = s < top_k_value", "top_k_mask = s <= top_k_value"),
+    "kth_index_off_by_one": ("top_k_value = s[V - int(k_b)]", "top_k_value = s[V - int(k_b) - 1]"),
+    "topp_strict_less": ("top_p_mask = probs_sum32 <= t", "top_p_mask = probs_sum32 < t"),
+    "last_position_not_forced": ("top_p_mask[V - 1] = False", "pass"),
+    "cumsum_from_largest": ("probs_sum = np.cumsum(probs_value)",
+                            "probs_sum = np.cumsum(probs_value[::-1])[::-1]"),
+    "softmax_ignores_topk": ("s[top_k_mask] = -np.inf", "pass"),
+    "t_is_p_not_one_minus_p": ("t = np.float32(np.float32(1.0) - p32)", "t = p32"),
+    "ties_reverse_index_order": ('np.argsort(x, kind="stable")', 'np.argsort(-x, kind="stable")[::-1]'),
+    "gather_instead_of_scatter": ("out[b, sorted_indices] = sorted_bits",
+                                  "out[b] = sorted_bits[sorted_indices]"),
+    "topk_disabled_only_for_k_le_0": ("1 <= int(k_b) <= V - 1", "1 <= int(k_b) <= V + 100"),
+    "kept_values_as_float_not_bits": ("np.where(masked, NEG_INF_BITS[dtype], row_bits[sorted_indices])",
+                                      "np.where(masked, NEG_INF_BITS[dtype], "
+                                      "np.where(row_bits[sorted_indices] == NEG_INF_BITS['f32'] >> 16, 0, "
+                                      "row_bits[sorted_indices] & ~np.asarray(0x8000, row_bits.dtype)))"),
+}
+
+CHEAP_FIRST = [
+    pins.check_hand_cases,
+    pins.check_invariants,
+    pins.check_topk_counting_random,
+    pins.check_nucleus_random,
+    pins.check_permutation_equivariance,
+    pins.check_bruteforce_tiny,
+]
+
+
+def make_mutant(old, new):
+    src = open(O.__file__).read()
+    assert src.count(old) == 1, old
+    name = "oracle_mutant_%x" % (abs(hash((old, new))))
+    mod = types.ModuleType(name)
+    mod.__file__ = O.__file__
+    sys.modules[name] = mod  # dataclasses look their module up here
+    exec(compile(src.replace(old, new), name, "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name):
+    mod = make_mutant(*MUTANTS[name])
+
+    def apply_fn(x, dtype, p, k):
+        return mod.apply_top_k_top_p(x, dtype, p, k, keep_traces=False).out
+
+    for check in CHEAP_FIRST:
+        try:
+            check(apply_fn)
+        except (AssertionError, IndexError, ValueError):
+            return
+    pytest.fail(f"mutant {name} passed every pin")

@@ -1,0 +1,194 @@
+#!/usr/bin/env python3
+"""Throughput of the top-k / top-p logits filter on one MI355X.
+
+A step is one call of the filter over a whole batch of synthetic input; the
+default batch is 256 rows of 151936 bf16 logits (4 * Gumbel(0,1)) with the
+rows cycling through top-k only, top-p only and joint modes. Inputs are
+resident in HBM before timing starts. Four input/output buffer sets are
+rotated so the 256 MB Infinity Cache cannot hold the working set between
+steps.
+
+Prints one JSON line: rows/s (value), the dominant kernel's achieved HBM
+bandwidth against the 8 TB/s peak (roofline), and the CPU oracle timed on a
+bounded sample of the same rows (cpu_baseline).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1..5]
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+METRIC = "rows/s and HBM GB/s (% roofline), top-k/top-p filter B=256 V=151936 bf16"
+HBM_PEAK_GBS = 8000.0
+TORCH_VIEW = {"f32": ("int32", "float32"), "f16": ("int16", "float16"), "bf16": ("int16", "bfloat16")}
+WORKLOAD_TEXT = {
+    1: "apply_top_k_top_p joint, B=4 V=1000 fp32 N(0,2)",
+    2: "apply_top_k_top_p, B=64 V=32000 fp16 N(0,3)+8 spikes, k off w.p. 0.25",
+    3: "apply_top_k_top_p mixed modes (k only / p only / joint by row), B=256 V=151936 bf16 4*Gumbel",
+    4: "apply_top_k_top_p tie stress, B=1024 V=128256 fp32 N(0,2) snapped to 0.25",
+    5: "apply_top_k_top_p_with_sorted with logits, B=128 V=262144 bf16 N(0,3)",
+}
+
+
+def dev(bits, dtype):
+    import torch
+
+    if bits is None:
+        return None
+    iv, fv = TORCH_VIEW[dtype]
+    return torch.from_numpy(np.ascontiguousarray(bits).view(getattr(np, iv))).cuda().view(getattr(torch, fv))
+
+
+def algorithmic_bytes(wl):
+    """Minimal HBM bytes of one call: read every logit once, write every output
+    once, read p and k; the pre-sorted entry also reads at least the k largest
+    sorted values of each row."""
+    s = wl.elem_bytes
+    per_row = 2 * wl.V * s + s + 4
+    total = wl.B * per_row
+    if wl.entry == "with_sorted":
+        total += int(np.clip(wl.k, 0, wl.V).sum()) * s
+    return total
+
+
+def cpu_baseline(wl, budget_s=10.0):
+    """The CPU oracle, as it stands, on the first rows of the same workload."""
+    from oracle import apply_top_k_top_p, apply_top_k_top_p_with_sorted
+
+    done = 0
+    t0 = time.perf_counter()
+    while done < wl.B and (time.perf_counter() - t0) < budget_s:
+        r = slice(done, min(wl.B, done + 8))
+        if wl.entry == "apply":
+            apply_top_k_top_p(wl.logits[r], wl.dtype, wl.p[r], wl.k[r], keep_traces=False)
+        else:
+            apply_top_k_top_p_with_sorted(wl.sorted_value[r], wl.sorted_indices[r], wl.dtype, wl.p[r], wl.k[r],
+                                          logits_bits=wl.logits[r], keep_traces=False)
+        done = r.stop
+    dt = time.perf_counter() - t0
+    return {
+        "value": round(done / dt, 3),
+        "unit": "rows/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"first {done} of {wl.B} rows of the timed workload, numpy float64 oracle, one thread, "
+                  f"{dt:.1f} s",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=3, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--sets", type=int, default=4, help="rotating input/output buffer sets")
+    ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds for the CPU oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--policy", type=int, default=0, help="plan policy: 0 auto, 1 general, 2 registers")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this filter is row-parallel and is built and measured on a "
+              "single MI355X; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import top_logits_filtering_amd as tk
+    from workloads.synth import make_workload
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    tk.load_library()
+    tk.set_plan_policy(args.policy)
+    wl = make_workload(args.workload)
+    dt = wl.dtype
+    p = dev(wl.p, dt)
+    k = torch.from_numpy(wl.k).cuda()
+    sets = []
+    for _ in range(max(1, args.sets)):
+        if wl.entry == "apply":
+            x = dev(wl.logits, dt)
+            sets.append((x, torch.empty_like(x)))
+        else:
+            x = dev(wl.logits, dt)
+            sets.append((x, torch.empty_like(x), dev(wl.sorted_value, dt),
+                         torch.from_numpy(wl.sorted_indices).cuda()))
+
+    def step(i):
+        st = sets[i % len(sets)]
+        if wl.entry == "apply":
+            tk.apply_top_k_top_p(st[0], p, k, out=st[1])
+        else:
+            tk.apply_top_k_top_p_with_sorted(st[2], st[3], p, k, logits=st[0], out=st[1])
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()  # the library launches on this stream
+    ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev0[i].record(stream)
+        step(i)
+        ev1[i].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    kernel_ms = float(np.mean([a.elapsed_time(b) for a, b in zip(ev0, ev1)]))
+    nbytes = algorithmic_bytes(wl)
+    achieved = nbytes / (kernel_ms * 1e-3) / 1e9
+    rows_per_s = wl.B / (ms_per_step * 1e-3)
+
+    line = {
+        "metric": METRIC,
+        "value": round(rows_per_s, 1),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dt,
+        "data": "synthetic",
+        "config": {
+            "workload": WORKLOAD_TEXT[args.workload],
+            "B": wl.B,
+            "V": wl.V,
+            "buffer_sets": len(sets),
+            "plan_policy": args.policy,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "kernel_us": round(kernel_ms * 1e3, 3),
+            "algorithmic_bytes_per_launch": nbytes,
+        },
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,130 @@
+/*
+ * libtopktopp — per-row top-k / top-p logits filter for AMD Instinct MI355X (gfx950).
+ *
+ * What is computed. For every row b of a [B, V] logits matrix the filter
+ * follows the eight steps of the CANN ops-nn page "ApplyTopKTopPWithSorted 的
+ * top-k/top-p 采样过滤原理与 aclnn 调用指南" (cited below as AKP), §2:
+ *   1-3. the k-th largest value of the row is the top-k threshold and every
+ *        value strictly below it is masked;
+ *   4-5. a softmax (fp32 or wider) of the surviving values is accumulated
+ *        from the smallest probability upwards;
+ *   6-7. every position whose cumulative probability is <= 1 - p[b] is masked,
+ *        except the last (largest) position, which always survives;
+ *   8.   the result is returned in the original vocabulary order.
+ * The order is the stable ascending sort of the row: equal values (and -0.0
+ * next to +0.0, which compare equal) keep their original index order, so at
+ * a top-p boundary inside a run of equal values the lower indices are masked
+ * first. A kept position holds the input bits unchanged; a masked position
+ * holds the dtype's -inf (fp32 0xFF800000, fp16 0xFC00, bf16 0xFF80; AKP §6.3).
+ *
+ * Modes (AKP §4, §5.2). p and k are each optional, but not both. k[b] <= 0 or
+ * k[b] >= V disables top-k for that row. p[b] >= 1 disables top-p in effect
+ * (nothing with positive probability is masked); p[b] <= 0 keeps only the
+ * last sorted position. Values of p are applied as given, without clamping.
+ *
+ * Numerics. t = 1 - p[b] is formed in fp32 from p widened exactly. The
+ * cumulative probabilities are computed on the device in fp32/fixed-point
+ * arithmetic whose summation order differs from a sequential sum; only
+ * positions whose exact cumulative probability lies within about 1e-5 of t
+ * can be decided differently from an exact evaluation. The top-k mask and
+ * the kept values are exact. Results are deterministic: the same inputs give
+ * the same output bits on every call.
+ *
+ * Memory and streams. Every data pointer is a device pointer owned by the
+ * caller; nothing is retained after the call returns. Work is enqueued on
+ * `stream` (a hipStream_t; NULL means the default stream) and the call
+ * returns without synchronising. The library allocates no device memory
+ * and the entry points never call hipMalloc. `out` must not overlap any input.
+ * Rows are dense and row-major: element (b, v) sits at offset b * V + v.
+ *
+ * Errors. Arguments are checked on the host before anything is enqueued, in
+ * the order of the aclnn checks (AKP §5.3): null pointers first, then dtype,
+ * then shape. On an error nothing is enqueued, and topktopp_last_error()
+ * describes the problem. Device data (the values of p, k, sortedness) is not
+ * validated.
+ */
+#ifndef TOPKTOPP_H
+#define TOPKTOPP_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of logits, sorted values, p and out (AKP §3 and §5.2 tables). */
+typedef enum {
+  TOPKTOPP_F32 = 0,
+  TOPKTOPP_F16 = 1,
+  TOPKTOPP_BF16 = 2
+} topktopp_dtype;
+
+/* Return codes, mirroring the aclnn ones of AKP §5.3. */
+typedef enum {
+  TOPKTOPP_OK = 0,
+  TOPKTOPP_ERR_NULLPTR = 1, /* logits/sorted input/out is NULL, or p and k are both NULL (aclnn 161001) */
+  TOPKTOPP_ERR_INVALID = 2, /* unsupported dtype, negative or too large shape, overlapping out (aclnn 161002) */
+  TOPKTOPP_ERR_RUNTIME = 3  /* a HIP launch failed; the message names the HIP error */
+} topktopp_status;
+
+/* Largest supported row length, 2^20 (the same bound the companion sampling
+ * operator, aclnnTopKTopPSampleV2, states for its vocabulary size). */
+#define TOPKTOPP_MAX_V (1 << 20)
+
+/*
+ * apply_top_k_top_p — filter raw logits (the aclnn entry of AKP §5 and §6.1,
+ * which sorts internally). No sort is materialised: the threshold pair that
+ * the stable sort would produce is found by radix selection.
+ *
+ *   logits  [B, V] device buffer of `dtype` values.
+ *   dtype   one of topktopp_dtype.
+ *   B, V    rows and row length; B == 0 or V == 0 is a successful no-op;
+ *           V == 1 copies logits to out (AKP §6.1); V <= TOPKTOPP_MAX_V.
+ *   p       [B] device buffer of `dtype` values, or NULL for no top-p.
+ *   k       [B] device buffer of int32, or NULL for no top-k.
+ *   out     [B, V] device buffer of `dtype`, written completely.
+ *   stream  hipStream_t to enqueue on, or NULL.
+ */
+topktopp_status apply_top_k_top_p(const void* logits, int dtype, int64_t B, int64_t V,
+                                  const void* p, const int32_t* k, void* out, void* stream);
+
+/*
+ * apply_top_k_top_p_with_sorted — the sorted-input operator
+ * ApplyTopKTopPWithSorted (AKP §1 and the §3 parameter table).
+ *
+ *   sorted_value    [B, V] device buffer, each row ascending.
+ *   sorted_indices  [B, V] int32 device buffer, each row the permutation that
+ *                   produced sorted_value from the original row. Positions in
+ *                   this order decide ties.
+ *   dtype, B, V, p, k, out, stream   as for apply_top_k_top_p.
+ *   logits          [B, V] original (unsorted) values, or NULL. When given,
+ *                   kept outputs are read from it in the original order and
+ *                   sorted_value[b][j] must equal logits[b][sorted_indices[b][j]].
+ *                   When NULL, out is written by scattering through
+ *                   sorted_indices.
+ * Sortedness and the permutation are the caller's contract and are not checked.
+ */
+topktopp_status apply_top_k_top_p_with_sorted(const void* sorted_value, const int32_t* sorted_indices,
+                                              int dtype, int64_t B, int64_t V, const void* p,
+                                              const int32_t* k, const void* logits, void* out,
+                                              void* stream);
+
+/* Text of the most recent error on the calling thread ("" if none); the
+ * counterpart of aclGetRecentErrMsg (AKP §8). Valid until the next call on
+ * the same thread. */
+const char* topktopp_last_error(void);
+
+/*
+ * Launch-plan override, for tests and measurement. policy 0 (default) lets
+ * the library choose per call; 1 forces the general multi-pass path for every
+ * row; 2 forces the register-resident path wherever the row fits. The result
+ * is the same under every policy. Returns the previous policy, or -1 for an
+ * unknown value (which is ignored). The setting is process-wide.
+ */
+int topktopp_set_plan_policy(int policy);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TOPKTOPP_H */

@@ -1,0 +1,95 @@
+"""GPU-vs-oracle comparison rule for the top-k / top-p filter.
+
+Per row, with o the oracle output and its trace, and g the GPU output:
+  1. every position the oracle masks by top-k is -inf in g (bit-exact);
+  2. every position the oracle keeps holds the input bits in g, unless it is a
+     band position;
+  3. every position the oracle masks only by top-p is -inf in g, unless it is a
+     band position;
+  4. g holds nothing but input bits or the dtype's -inf pattern;
+  5. g's survivors form a suffix of the stable ascending order.
+A band position is a sorted position j != V-1 whose oracle fp32 cumulative
+probability lies within ``tol`` (1e-5) of t = 1 - p. Summation order on the GPU
+differs from the oracle's, so only there may the top-p decision differ.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+NEG_INF_WORD = {"f32": 0xFF800000, "f16": 0xFC00, "bf16": 0xFF80}
+BAND_TOL = 1e-5
+
+
+@dataclass
+class ParityReport:
+    rows: int = 0
+    positions: int = 0
+    band_positions: int = 0
+    band_mismatches: int = 0
+    hard_mismatches: int = 0
+    details: list = field(default_factory=list)
+
+    def merge(self, other: "ParityReport"):
+        self.rows += other.rows
+        self.positions += other.positions
+        self.band_positions += other.band_positions
+        self.band_mismatches += other.band_mismatches
+        self.hard_mismatches += other.hard_mismatches
+        self.details.extend(other.details)
+        return self
+
+    def __str__(self):
+        return (f"rows={self.rows} positions={self.positions} band={self.band_positions} "
+                f"band_mismatches={self.band_mismatches} hard_mismatches={self.hard_mismatches}")
+
+
+def compare_row(g_row, x_row, trace, dtype, tol=BAND_TOL, row_id=None) -> ParityReport:
+    """Apply the rule to one row; x_row are the bits the kept values must equal."""
+    rep = ParityReport(rows=1, positions=len(g_row))
+    neg = np.asarray(NEG_INF_WORD[dtype], dtype=g_row.dtype)
+    perm = trace.sorted_indices
+    V = len(g_row)
+    gs = g_row[perm]
+    xs = x_row[perm]
+    is_neg = gs == neg
+    is_x = gs == xs
+    o_masked = trace.top_k_mask | trace.top_p_mask
+    band = np.zeros(V, dtype=bool)
+    if trace.probs_sum32 is not None and trace.t is not None:
+        band = np.abs(trace.probs_sum32.astype(np.float64) - np.float64(trace.t)) <= tol
+        band[V - 1] = False
+    ambiguous_val = xs == neg  # input already -inf: kept and masked look the same
+    bad = ~(is_neg | is_x)  # rule 4
+    bad |= trace.top_k_mask & ~is_neg  # rule 1
+    bad |= ~o_masked & ~band & ~is_x  # rule 2
+    bad |= trace.top_p_mask & ~trace.top_k_mask & ~band & ~is_neg  # rule 3
+    # rule 5: survivors are a suffix of the stable order
+    kept = is_x & ~is_neg
+    kept_or_amb = kept | ambiguous_val
+    if kept.any():
+        first = int(np.argmax(kept))
+        if not kept_or_amb[first:].all():
+            bad[first:] |= ~kept_or_amb[first:]
+    n_bad = int(bad.sum())
+    rep.hard_mismatches = n_bad
+    rep.band_positions = int(band.sum())
+    g_masked = is_neg & ~ambiguous_val
+    rep.band_mismatches = int((band & (g_masked != (o_masked & ~ambiguous_val))).sum())
+    if n_bad:
+        js = np.nonzero(bad)[0][:5]
+        rep.details.append(dict(row=row_id, sorted_positions=js.tolist(), orig=perm[js].tolist(),
+                                g=gs[js].tolist(), x=xs[js].tolist(), maskK=trace.top_k_mask[js].tolist(),
+                                maskP=trace.top_p_mask[js].tolist()))
+    return rep
+
+
+def compare(g, x_bits, oracle_result, dtype, tol=BAND_TOL, row_ids=None) -> ParityReport:
+    """Apply the rule to every row of a batch."""
+    rep = ParityReport()
+    for b, tr in enumerate(oracle_result.traces):
+        rid = b if row_ids is None else int(row_ids[b])
+        rep.merge(compare_row(g[b], x_bits[b], tr, dtype, tol, rid))
+    return rep

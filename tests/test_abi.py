@@ -1,0 +1,89 @@
+"""The C ABI without a GPU: the library loads, exports what the header
+declares, and rejects bad arguments on the host before touching HIP."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import top_logits_filtering_amd as tk
+from top_logits_filtering_amd.binding import LIB_PATH
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "topktopp.h")
+
+NULLPTR, INVALID = 1, 2
+FAKE = 1 << 40  # a device-looking address; never dereferenced on these paths
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\([^;{]*\)\s*;", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB_PATH):
+        from top_logits_filtering_amd.build import build
+
+        build()
+    return tk.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(tk.EXPORTED_SYMBOLS), names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_null_pointers(lib):
+    f = lib.apply_top_k_top_p
+    assert f(None, 0, 2, 8, FAKE, FAKE, FAKE, None) == NULLPTR
+    assert "logits" in tk.last_error()
+    assert f(FAKE, 0, 2, 8, FAKE, FAKE, None, None) == NULLPTR
+    assert f(FAKE, 0, 2, 8, None, None, FAKE + (1 << 30), None) == NULLPTR
+    assert "p and k" in tk.last_error()
+    g = lib.apply_top_k_top_p_with_sorted
+    assert g(None, FAKE, 0, 2, 8, FAKE, None, None, FAKE + (1 << 30), None) == NULLPTR
+    assert g(FAKE, None, 0, 2, 8, FAKE, None, None, FAKE + (1 << 30), None) == NULLPTR
+    assert g(FAKE, FAKE, 0, 2, 8, None, None, None, FAKE + (1 << 30), None) == NULLPTR
+
+
+def test_invalid_dtype_and_shape(lib):
+    f = lib.apply_top_k_top_p
+    out = FAKE + (1 << 32)
+    assert f(FAKE, 3, 2, 8, FAKE, None, out, None) == INVALID
+    assert "dtype" in tk.last_error()
+    assert f(FAKE, -1, 2, 8, FAKE, None, out, None) == INVALID
+    assert f(FAKE, 0, -1, 8, FAKE, None, out, None) == INVALID
+    assert f(FAKE, 0, 2, -8, FAKE, None, out, None) == INVALID
+    assert f(FAKE, 2, 2, (1 << 20) + 1, FAKE, None, out, None) == INVALID
+    assert "maximum" in tk.last_error()
+
+
+def test_overlap_rejected(lib):
+    f = lib.apply_top_k_top_p
+    assert f(FAKE, 2, 4, 100, FAKE + (1 << 32), None, FAKE + 64, None) == INVALID
+    assert "overlap" in tk.last_error()
+
+
+def test_empty_is_ok_without_launch(lib):
+    f = lib.apply_top_k_top_p
+    assert f(FAKE, 1, 0, 100, None, FAKE + 8, FAKE + (1 << 32), None) == 0
+    assert f(FAKE, 1, 5, 0, None, FAKE + 8, FAKE + (1 << 32), None) == 0
+    assert tk.last_error() == ""
+
+
+def test_plan_policy_roundtrip(lib):
+    prev = tk.set_plan_policy(1)
+    assert tk.set_plan_policy(prev) == 1
+    assert lib.topktopp_set_plan_policy(7) == -1
+    with pytest.raises(ValueError):
+        tk.set_plan_policy(9)
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(RuntimeError, match="no fallback"):
+        tk.load_library(str(tmp_path / "nope.so"))

@@ -1,0 +1,185 @@
+"""HIP path vs the CPU oracle, through the C ABI (needs an MI355X)."""
+
+import numpy as np
+import pytest
+
+from oracle import apply_top_k_top_p as oracle_apply
+from oracle import apply_top_k_top_p_with_sorted as oracle_sorted
+from tests.golden_io import load_hand_cases
+from tests.gpu_util import gpu_apply, gpu_with_sorted, need_gpu, say
+from tests.parity import NEG_INF_WORD, ParityReport, compare
+from workloads.synth import (
+    bits_to_f32,
+    f32_to_bits,
+    make_workload,
+    random_params,
+    random_rows,
+    split_modes,
+    stable_ascending_sort,
+)
+
+pytestmark = pytest.mark.gpu
+
+POLICIES = {"auto": 0, "general": 1, "registers": 2}
+
+
+@pytest.fixture(params=sorted(POLICIES), scope="module")
+def policy(request):
+    need_gpu()
+    import top_logits_filtering_amd as tk
+
+    prev = tk.set_plan_policy(POLICIES[request.param])
+    yield request.param
+    tk.set_plan_policy(prev)
+
+
+def _check(rep: ParityReport, what):
+    say(f"{what}: {rep}")
+    assert rep.hard_mismatches == 0, rep.details[:3]
+
+
+def test_hand_cases(policy):
+    for case in load_hand_cases():
+        got = gpu_apply(case.x, case.dtype, case.p, case.k)
+        assert np.array_equal(got, case.expect), (policy, case.name, got, case.expect)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_random_rows(dtype, policy):
+    """Several tiles plus ragged tails, every mode, odd k and p values."""
+    total = ParityReport()
+    seed = {"f32": 1, "f16": 2, "bf16": 3}[dtype] * 100
+    for V in (2, 3, 7, 64, 1000, 1031, 4099, 20011, 70001):
+        for kind in ("normal", "ties", "zeros", "gumbel", "spikes", "const", "wide"):
+            seed += 1
+            B = 6 if V < 20000 else 3
+            xb = random_rows(seed, B, V, dtype, kind=kind)
+            k, p = random_params(seed, B, V, dtype)
+            k_small = np.minimum(np.abs(k), max(1, V // 3)).astype(np.int32)
+            for pp, kk in ((None, k), (p, None), (p, k), (p, k_small)):
+                got = gpu_apply(xb, dtype, pp, kk)
+                ref = oracle_apply(xb, dtype, pp, kk)
+                rep = compare(got, xb, ref, dtype)
+                assert rep.hard_mismatches == 0, (V, kind, pp is None, kk is None, rep.details[:2])
+                total.merge(rep)
+    say(f"{dtype}/{policy}: {total}")
+
+
+def test_extreme_p_and_k(policy):
+    """p <= 0, p >= 1, p > 1, k = 1, k = V-1, k out of range."""
+    dtype = "bf16"
+    V = 3001
+    xb = random_rows(55, 8, V, dtype, kind="ties")
+    for pv in (-0.5, 0.0, 1e-7, 0.999999, 1.0, 1.5):
+        for kv in (None, 1, 2, V - 1, V, 0, -4):
+            p = None if pv is None else f32_to_bits(np.full(8, pv, np.float32), dtype)
+            k = None if kv is None else np.full(8, kv, np.int32)
+            got = gpu_apply(xb, dtype, p, k)
+            ref = oracle_apply(xb, dtype, p, k)
+            _check(compare(got, xb, ref, dtype), f"p={pv} k={kv}")
+
+
+def test_single_column_and_empty():
+    torch = need_gpu()
+    import top_logits_filtering_amd as tk
+
+    xb = random_rows(9, 5, 1, "f32")
+    got = gpu_apply(xb, "f32", np.zeros(5, np.uint32), np.ones(5, np.int32))
+    assert np.array_equal(got, xb)
+    empty = torch.empty((0, 7), device="cuda", dtype=torch.bfloat16)
+    assert tk.apply_top_k_top_p(empty, None, torch.ones(0, dtype=torch.int32, device="cuda")).shape == (0, 7)
+
+
+@pytest.mark.parametrize("c", [1, 2])
+def test_small_workloads_full(c, policy):
+    wl = make_workload(c)
+    got = gpu_apply(wl.logits, wl.dtype, wl.p, wl.k)
+    ref = oracle_apply(wl.logits, wl.dtype, wl.p, wl.k)
+    _check(compare(got, wl.logits, ref, wl.dtype), f"workload {c} ({policy})")
+
+
+def _all_rows_properties(got, wl):
+    neg = NEG_INF_WORD[wl.dtype]
+    x = wl.logits
+    vals = bits_to_f32(x, wl.dtype).reshape(x.shape)
+    kept = got != neg
+    assert np.all((got == x) | (got == neg)), "values other than input bits or -inf"
+    assert kept.any(axis=1).all(), "a row lost every position"
+    # the maximum at its highest index always survives
+    mx = vals.max(axis=1)
+    last_max = (vals.shape[1] - 1) - np.argmax((vals == mx[:, None])[:, ::-1], axis=1)
+    assert kept[np.arange(len(x)), last_max].all()
+    if wl.k is not None:
+        for b in range(len(x)):
+            kb = int(wl.k[b])
+            if 1 <= kb < wl.V:
+                kth = np.partition(vals[b], wl.V - kb)[wl.V - kb]
+                assert not (kept[b] & (vals[b] < kth)).any(), f"row {b} keeps a value below the k-th largest"
+
+
+@pytest.mark.parametrize("c", [3, 4])
+def test_large_workloads_sampled(c, policy):
+    """Full-size batch in the timed configuration; oracle on sampled rows, properties on all."""
+    wl = make_workload(c)
+    say(f"workload {c}: B={wl.B} V={wl.V} {wl.dtype} ({policy})")
+    got = gpu_apply(wl.logits, wl.dtype, wl.p, wl.k)
+    rng = np.random.default_rng(c)
+    rows = np.unique(np.concatenate([[0, 1, 2, wl.B - 1], rng.choice(wl.B, 10, replace=False)]))
+    ref = oracle_apply(wl.logits[rows], wl.dtype, wl.p[rows], wl.k[rows])
+    _check(compare(got[rows], wl.logits[rows], ref, wl.dtype, row_ids=rows), f"workload {c} sampled")
+    _all_rows_properties(got, wl)
+
+
+def test_workload3_absent_p_and_k():
+    """The three modes called with truly absent p / k match the single timed call."""
+    need_gpu()
+    wl = make_workload(3, rows=range(30))
+    full = gpu_apply(wl.logits, wl.dtype, wl.p, wl.k)
+    for pos, p, k in split_modes(wl):
+        sub = gpu_apply(wl.logits[pos], wl.dtype, p, k)
+        assert np.array_equal(sub, full[pos])
+
+
+def test_determinism():
+    need_gpu()
+    wl = make_workload(3, rows=range(64))
+    a = gpu_apply(wl.logits, wl.dtype, wl.p, wl.k)
+    b = gpu_apply(wl.logits, wl.dtype, wl.p, wl.k)
+    assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_with_sorted_random(dtype):
+    need_gpu()
+    total = ParityReport()
+    seed = 900
+    for V in (2, 5, 1000, 4099, 70001):
+        for kind in ("normal", "ties", "zeros", "gumbel", "const"):
+            seed += 1
+            B = 5
+            xb = random_rows(seed, B, V, dtype, kind=kind)
+            k, p = random_params(seed, B, V, dtype)
+            idx, sv = stable_ascending_sort(xb, dtype)
+            for pp, kk in ((None, k), (p, None), (p, k)):
+                ref = oracle_sorted(sv, idx, dtype, pp, kk, logits_bits=xb)
+                for use_logits in (True, False):
+                    got = gpu_with_sorted(sv, idx, dtype, pp, kk, xb if use_logits else None)
+                    rep = compare(got, xb, ref, dtype)
+                    assert rep.hard_mismatches == 0, (V, kind, use_logits, rep.details[:2])
+                    total.merge(rep)
+    say(f"with_sorted {dtype}: {total}")
+
+
+def test_with_sorted_workload5_sampled():
+    need_gpu()
+    wl = make_workload(5)
+    say(f"workload 5: B={wl.B} V={wl.V}")
+    got = gpu_with_sorted(wl.sorted_value, wl.sorted_indices, wl.dtype, wl.p, wl.k, wl.logits)
+    rows = np.array([0, 1, 17, 64, 100, wl.B - 1])
+    ref = oracle_sorted(wl.sorted_value[rows], wl.sorted_indices[rows], wl.dtype, wl.p[rows], wl.k[rows],
+                        logits_bits=wl.logits[rows])
+    _check(compare(got[rows], wl.logits[rows], ref, wl.dtype, row_ids=rows), "workload 5 sampled")
+    _all_rows_properties(got, wl)
+    # the sorting entry on the same logits agrees with the pre-sorted entry
+    again = gpu_apply(wl.logits[rows], wl.dtype, wl.p[rows], wl.k[rows])
+    assert np.array_equal(again, got[rows])

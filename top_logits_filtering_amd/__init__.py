@@ -1,0 +1,12 @@
+"""MI355X-native top-k / top-p logits filter (libtopktopp) and its Python binding."""
+
+from .binding import (  # noqa: F401
+    EXPORTED_SYMBOLS,
+    LIB_PATH,
+    TopKTopPError,
+    apply_top_k_top_p,
+    apply_top_k_top_p_with_sorted,
+    last_error,
+    load_library,
+    set_plan_policy,
+)

@@ -1,0 +1,140 @@
+"""ctypes binding of libtopktopp (include/topktopp.h).
+
+Argument marshalling only: tensors are turned into device pointers and the
+current HIP stream, and every step of the filter runs in the library's HIP
+kernels. If the library has not been built this module raises instead of
+falling back to anything else.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libtopktopp.so")
+
+TOPKTOPP_F32, TOPKTOPP_F16, TOPKTOPP_BF16 = 0, 1, 2
+STATUS_NAMES = {0: "OK", 1: "ERR_NULLPTR", 2: "ERR_INVALID", 3: "ERR_RUNTIME"}
+EXPORTED_SYMBOLS = (
+    "apply_top_k_top_p",
+    "apply_top_k_top_p_with_sorted",
+    "topktopp_last_error",
+    "topktopp_set_plan_policy",
+)
+
+_lib = None
+
+
+class TopKTopPError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+        self.message = message
+
+
+def load_library(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load libtopktopp.so (once) and declare the C signatures."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(
+            f"{p} is missing: build it first (python -m top_logits_filtering_amd.build); "
+            "there is no fallback implementation"
+        )
+    lib = ctypes.CDLL(p)
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.apply_top_k_top_p.argtypes = [vp, i32, i64, i64, vp, vp, vp, vp]
+    lib.apply_top_k_top_p.restype = i32
+    lib.apply_top_k_top_p_with_sorted.argtypes = [vp, vp, i32, i64, i64, vp, vp, vp, vp, vp]
+    lib.apply_top_k_top_p_with_sorted.restype = i32
+    lib.topktopp_last_error.argtypes = []
+    lib.topktopp_last_error.restype = ctypes.c_char_p
+    lib.topktopp_set_plan_policy.argtypes = [i32]
+    lib.topktopp_set_plan_policy.restype = i32
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def last_error() -> str:
+    return load_library().topktopp_last_error().decode()
+
+
+def set_plan_policy(policy: int) -> int:
+    """0 auto, 1 general multi-pass, 2 register-resident where the row fits."""
+    prev = load_library().topktopp_set_plan_policy(int(policy))
+    if prev < 0:
+        raise ValueError(f"unknown plan policy {policy}")
+    return prev
+
+
+def _dtype_code(t) -> int:
+    import torch
+
+    codes = {torch.float32: TOPKTOPP_F32, torch.float16: TOPKTOPP_F16, torch.bfloat16: TOPKTOPP_BF16}
+    if t.dtype not in codes:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return codes[t.dtype]
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream, device) -> int:
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _check(status: int):
+    if status != 0:
+        raise TopKTopPError(status, last_error())
+
+
+def apply_top_k_top_p(logits, p=None, k=None, out=None, stream=None):
+    """Filter raw logits [B, V]; p [B] (logits dtype) and k [B] (int32) are optional."""
+    import torch
+
+    lib = load_library()
+    if logits.dim() != 2:
+        raise ValueError("logits must be 2-D [B, V]")
+    B, V = logits.shape
+    if out is None:
+        out = torch.empty_like(logits)
+    status = lib.apply_top_k_top_p(
+        _ptr(logits), _dtype_code(logits), B, V, _ptr(p), _ptr(k), _ptr(out), _stream(stream, logits.device)
+    )
+    _check(status)
+    return out
+
+
+def apply_top_k_top_p_with_sorted(sorted_value, sorted_indices, p=None, k=None, logits=None, out=None,
+                                  stream=None):
+    """Filter pre-sorted rows (ascending sorted_value, int32 sorted_indices)."""
+    import torch
+
+    lib = load_library()
+    if sorted_value.dim() != 2:
+        raise ValueError("sorted_value must be 2-D [B, V]")
+    B, V = sorted_value.shape
+    if out is None:
+        out = torch.empty_like(sorted_value)
+    status = lib.apply_top_k_top_p_with_sorted(
+        _ptr(sorted_value), _ptr(sorted_indices), _dtype_code(sorted_value), B, V, _ptr(p), _ptr(k),
+        _ptr(logits), _ptr(out), _stream(stream, sorted_value.device)
+    )
+    _check(status)
+    return out

@@ -1,0 +1,114 @@
+// C ABI of libtopktopp: argument checks and dispatch to the HIP launchers.
+// The checks follow the order of the aclnn parameter checks described in the
+// ApplyTopKTopPWithSorted guide (§5.3): null pointers, then dtype, then shape.
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdint>
+#include <string>
+
+#include "../../include/topktopp.h"
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+std::atomic<int> g_policy{tkp::kPlanAuto};
+
+topktopp_status fail(topktopp_status code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+size_t elem_size(int dtype) { return dtype == TOPKTOPP_F32 ? 4 : 2; }
+
+bool valid_dtype(int dtype) { return dtype == TOPKTOPP_F32 || dtype == TOPKTOPP_F16 || dtype == TOPKTOPP_BF16; }
+
+// [a, a + na) and [b, b + nb) overlap (byte ranges).
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (a == nullptr || b == nullptr || na == 0 || nb == 0) return false;
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+topktopp_status check_shape(int64_t B, int64_t V) {
+  if (B < 0 || V < 0) return fail(TOPKTOPP_ERR_INVALID, "shape [%lld, %lld] has a negative extent", (long long)B, (long long)V);
+  if (V > TOPKTOPP_MAX_V)
+    return fail(TOPKTOPP_ERR_INVALID, "row length V=%lld exceeds the supported maximum %d", (long long)V, TOPKTOPP_MAX_V);
+  if (B > 0x7FFFFFFFLL / 64)
+    return fail(TOPKTOPP_ERR_INVALID, "B=%lld rows exceeds the launch limit", (long long)B);
+  return TOPKTOPP_OK;
+}
+
+topktopp_status check_launch(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(TOPKTOPP_ERR_RUNTIME, "%s failed: %s", what, hipGetErrorString(e));
+  return TOPKTOPP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* topktopp_last_error(void) { return g_last_error.c_str(); }
+
+int topktopp_set_plan_policy(int policy) {
+  if (policy < tkp::kPlanAuto || policy > tkp::kPlanRegisters) return -1;
+  return g_policy.exchange(policy);
+}
+
+topktopp_status apply_top_k_top_p(const void* logits, int dtype, int64_t B, int64_t V, const void* p,
+                                  const int32_t* k, void* out, void* stream) {
+  g_last_error.clear();
+  if (logits == nullptr) return fail(TOPKTOPP_ERR_NULLPTR, "logits is NULL");
+  if (out == nullptr) return fail(TOPKTOPP_ERR_NULLPTR, "out is NULL");
+  if (p == nullptr && k == nullptr) return fail(TOPKTOPP_ERR_NULLPTR, "p and k are both NULL; at least one is required");
+  if (!valid_dtype(dtype)) return fail(TOPKTOPP_ERR_INVALID, "dtype %d is not one of F32, F16, BF16", dtype);
+  if (topktopp_status s = check_shape(B, V)) return s;
+  const size_t es = elem_size(dtype);
+  const size_t nbytes = static_cast<size_t>(B) * static_cast<size_t>(V) * es;
+  if (overlaps(out, nbytes, logits, nbytes) || overlaps(out, nbytes, p, static_cast<size_t>(B) * es) ||
+      overlaps(out, nbytes, k, static_cast<size_t>(B) * 4))
+    return fail(TOPKTOPP_ERR_INVALID, "out overlaps an input buffer");
+  if (B == 0 || V == 0) return TOPKTOPP_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (V == 1)  // a last dimension of 1 is copied through unfiltered
+    return check_launch(hipMemcpyAsync(out, logits, nbytes, hipMemcpyDeviceToDevice, st), "hipMemcpyAsync");
+  return check_launch(tkp::launch_apply(dtype, logits, p, k, out, B, V, g_policy.load(), st), "filter launch");
+}
+
+topktopp_status apply_top_k_top_p_with_sorted(const void* sorted_value, const int32_t* sorted_indices, int dtype,
+                                              int64_t B, int64_t V, const void* p, const int32_t* k,
+                                              const void* logits, void* out, void* stream) {
+  g_last_error.clear();
+  if (sorted_value == nullptr) return fail(TOPKTOPP_ERR_NULLPTR, "sorted_value is NULL");
+  if (sorted_indices == nullptr) return fail(TOPKTOPP_ERR_NULLPTR, "sorted_indices is NULL");
+  if (out == nullptr) return fail(TOPKTOPP_ERR_NULLPTR, "out is NULL");
+  if (p == nullptr && k == nullptr) return fail(TOPKTOPP_ERR_NULLPTR, "p and k are both NULL; at least one is required");
+  if (!valid_dtype(dtype)) return fail(TOPKTOPP_ERR_INVALID, "dtype %d is not one of F32, F16, BF16", dtype);
+  if (topktopp_status s = check_shape(B, V)) return s;
+  const size_t es = elem_size(dtype);
+  const size_t nbytes = static_cast<size_t>(B) * static_cast<size_t>(V) * es;
+  if (overlaps(out, nbytes, sorted_value, nbytes) ||
+      overlaps(out, nbytes, sorted_indices, static_cast<size_t>(B) * static_cast<size_t>(V) * 4) ||
+      overlaps(out, nbytes, logits, nbytes) || overlaps(out, nbytes, p, static_cast<size_t>(B) * es) ||
+      overlaps(out, nbytes, k, static_cast<size_t>(B) * 4))
+    return fail(TOPKTOPP_ERR_INVALID, "out overlaps an input buffer");
+  if (B == 0 || V == 0) return TOPKTOPP_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (V == 1)  // the single element is always kept; sorted_indices is 0
+    return check_launch(hipMemcpyAsync(out, logits != nullptr ? logits : sorted_value, nbytes,
+                                       hipMemcpyDeviceToDevice, st),
+                        "hipMemcpyAsync");
+  return check_launch(tkp::launch_with_sorted(dtype, sorted_value, sorted_indices, p, k, logits, out, B, V, st),
+                      "filter launch");
+}
+
+}  // extern "C"

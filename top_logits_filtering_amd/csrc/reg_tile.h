@@ -1,0 +1,110 @@
+// A slice of one row held in registers: NVEC 16-byte vectors per thread.
+// Element e of the slice lives in vector layer e / (1024 * P), thread
+// (e % (1024 * P)) / P, lane e % P, with P elements per vector (4 for fp32, 8
+// for fp16/bf16). Consecutive threads therefore touch consecutive 16-byte
+// chunks, and each layer is one fully coalesced 16 KiB access per block.
+// All loops are unrolled at compile time so the array stays in VGPRs.
+#pragma once
+
+#include "device_common.h"
+
+namespace tkp {
+
+template <class DT, int NVEC>
+struct RegTile {
+  using raw_t = typename DT::raw_t;
+  static constexpr int kPV = DT::kPerVec;
+  static constexpr int kSpan = kThreads * kPV;  // elements per vector layer
+  static constexpr int kCapacity = NVEC * kSpan;
+
+  uint4 v[NVEC];
+  int base;  // index of the slice's first element within the row
+  int len;   // valid elements in the slice
+
+  // Element access by (vector, lane). Both indices are compile-time constants
+  // after unrolling, so these fold to register moves and shifts.
+  static __device__ inline uint32_t word(const uint4& q, int w) {
+    return w == 0 ? q.x : (w == 1 ? q.y : (w == 2 ? q.z : q.w));
+  }
+  static __device__ inline void set_word(uint4& q, int w, uint32_t x) {
+    if (w == 0) q.x = x;
+    else if (w == 1) q.y = x;
+    else if (w == 2) q.z = x;
+    else q.w = x;
+  }
+  static __device__ inline raw_t lane_of(const uint4& q, int j) {
+    if constexpr (sizeof(raw_t) == 4) {
+      return word(q, j);
+    } else {
+      return static_cast<raw_t>(word(q, j >> 1) >> ((j & 1) * 16));
+    }
+  }
+  static __device__ inline void set_lane(uint4& q, int j, raw_t r) {
+    if constexpr (sizeof(raw_t) == 4) {
+      set_word(q, j, r);
+    } else {
+      const int w = j >> 1, sh = (j & 1) * 16;
+      set_word(q, w, (word(q, w) & ~(0xFFFFu << sh)) | (static_cast<uint32_t>(r) << sh));
+    }
+  }
+  __device__ inline raw_t get(int i, int j) const { return lane_of(v[i], j); }
+  __device__ inline void set(int i, int j, raw_t r) { set_lane(v[i], j, r); }
+
+  __device__ inline void load(const raw_t* __restrict__ row, int v0, int n) {
+    base = v0;
+    len = n;
+    const raw_t* src = row + v0;
+    const bool aligned = (reinterpret_cast<uintptr_t>(src) & 15u) == 0;
+#pragma unroll
+    for (int i = 0; i < NVEC; ++i) {
+      const int e0 = i * kSpan + static_cast<int>(threadIdx.x) * kPV;
+      if (aligned && e0 + kPV <= n) {
+        v[i] = *reinterpret_cast<const uint4*>(src + e0);
+      } else {
+#pragma unroll
+        for (int j = 0; j < kPV; ++j) set(i, j, (e0 + j < n) ? src[e0 + j] : static_cast<raw_t>(0));
+      }
+    }
+  }
+
+  // f(raw, idx) for every valid element held by this thread; idx is the
+  // element's index within the row.
+  template <class F>
+  __device__ inline void for_each(F&& f) const {
+#pragma unroll
+    for (int i = 0; i < NVEC; ++i) {
+      const int e0 = i * kSpan + static_cast<int>(threadIdx.x) * kPV;
+      if ((i + 1) * kSpan <= len) {  // whole layer valid: uniform over the block
+#pragma unroll
+        for (int j = 0; j < kPV; ++j) f(get(i, j), base + e0 + j);
+      } else {
+#pragma unroll
+        for (int j = 0; j < kPV; ++j)
+          if (e0 + j < len) f(get(i, j), base + e0 + j);
+      }
+    }
+  }
+
+  // row[idx] = g(raw, idx) for every valid element held by this thread.
+  template <class G>
+  __device__ inline void store(raw_t* __restrict__ row, G&& g) const {
+    raw_t* dst = row + base;
+    const bool aligned = (reinterpret_cast<uintptr_t>(dst) & 15u) == 0;
+#pragma unroll
+    for (int i = 0; i < NVEC; ++i) {
+      const int e0 = i * kSpan + static_cast<int>(threadIdx.x) * kPV;
+      if (aligned && e0 + kPV <= len) {
+        uint4 o = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+        for (int j = 0; j < kPV; ++j) set_lane(o, j, g(get(i, j), base + e0 + j));
+        *reinterpret_cast<uint4*>(dst + e0) = o;
+      } else {
+#pragma unroll
+        for (int j = 0; j < kPV; ++j)
+          if (e0 + j < len) dst[e0 + j] = g(get(i, j), base + e0 + j);
+      }
+    }
+  }
+};
+
+}  // namespace tkp

@@ -1,0 +1,240 @@
+// The sorted-input operator ApplyTopKTopPWithSorted (ApplyTopKTopPWithSorted
+// guide, §1 and the §3 parameter table): sorted_value ascending,
+// sorted_indices the permutation, p / k / logits optional.
+//
+// With the sort given, no selection is needed. Per row, in sorted positions:
+//   * top-k: the threshold is sorted_value[V - k]; the first position holding
+//     its key, `start`, is found by scanning down from V - k (equal values are
+//     contiguous);
+//   * top-p: Z sums the mass of positions [start, V); scanning down from the
+//     top in 1024-position chunks with a block-wide prefix sum of the mass
+//     gives F, the lowest position whose mass strictly above is below
+//     (1 - t) * Z (a wave-level Kogge-Stone scan per chunk, in the spirit of
+//     the guide's §6.3 CumsumKoggleStone / FindFirstIndex);
+//   * survivors are the sorted positions >= F.
+// With logits: out[v] = logits[v] when key(logits[v]) > key(s_F), -inf when
+// below, and for equal keys the survivors are exactly the positions >= F of
+// that run of equal values: the run's positions a..F-1 are collected into a
+// shared-memory bitmap (the guide's ScatterBoundary idea) and masked, so the
+// single coalesced pass over logits is the only full-row traffic.
+// Without logits: out[sorted_indices[j]] = j >= F ? sorted_value[j] : -inf.
+//
+// Each row is split into slices handled by separate blocks; every block
+// repeats the (cheap) boundary search, so no block waits on another and no
+// global scratch is needed. The logits slice is loaded into registers before
+// the boundary search so its latency overlaps that search.
+
+#include "launch.h"
+#include "reg_tile.h"
+
+namespace tkp {
+
+__device__ inline int block_max_i32(int v, RowSmem& sm) {
+  return static_cast<int>(block_max_u32(static_cast<uint32_t>(v + 1), sm)) - 1;
+}
+
+// Exclusive prefix sum over threadIdx.x; also returns the block total.
+__device__ inline uint64_t block_exscan_u64(uint64_t v, RowSmem& sm, uint64_t& total) {
+  const int l = threadIdx.x & (kWave - 1);
+  const int w = threadIdx.x / kWave;
+  uint64_t incl = v;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    uint64_t n = __shfl_up(incl, o);
+    if (l >= o) incl += n;
+  }
+  if (l == kWave - 1) sm.redu[w] = incl;
+  __syncthreads();
+  uint64_t wbase = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) {
+    const uint64_t x = sm.redu[i];
+    wbase += (i < w) ? x : 0;
+    tot += x;
+  }
+  __syncthreads();
+  total = tot;
+  return wbase + incl - v;
+}
+
+// Smallest j <= hi such that key(sv[j..hi]) >= K, given key(sv[hi]) >= K and
+// an ascending row.
+template <class DT>
+__device__ int first_at_or_above(const typename DT::raw_t* __restrict__ sv, int hi, uint32_t K, RowSmem& sm) {
+  int top = hi;
+  for (;;) {
+    const int j = top - 1 - static_cast<int>(threadIdx.x);
+    const int cand = (j >= 0 && DT::key(sv[j]) < K) ? j : -1;
+    const int best = block_max_i32(cand, sm);
+    if (best >= 0) return best + 1;
+    top -= kThreads;
+    if (top <= 0) return 0;
+  }
+}
+
+// Lowest sorted position F >= start whose mass strictly above is < thr.
+template <class DT>
+__device__ int scan_boundary(const typename DT::raw_t* __restrict__ sv, int start, int V, float m, uint64_t thr,
+                             RowSmem& sm) {
+  int hi = V;
+  uint64_t base = 0;
+  for (;;) {
+    const int lo = max(start, hi - kThreads);
+    const int j = hi - 1 - static_cast<int>(threadIdx.x);
+    const bool valid = j >= lo;
+    const uint64_t e = valid ? mass_fx(DT::value(sv[j]), m) : 0;
+    uint64_t total;
+    const uint64_t excl = block_exscan_u64(e, sm, total);
+    const int cand = (valid && base + excl < thr) ? static_cast<int>(threadIdx.x) : -1;
+    const int tb = block_max_i32(cand, sm);
+    if (tb < 0) return min(hi, V - 1);  // only after a chunk whose lowest position survived
+    const int jb = hi - 1 - tb;
+    if (jb > lo || lo == start) return jb;
+    base += total;
+    hi = lo;
+  }
+}
+
+struct SortedBoundary {
+  uint32_t KF;  // key of the lowest survivor
+  int F;        // lowest surviving sorted position
+  int a;        // first sorted position holding key KF (positions a..F-1 are masked)
+};
+
+template <class DT>
+__device__ SortedBoundary sorted_boundary(const typename DT::raw_t* __restrict__ sv, const RowParams& rp, int V,
+                                          RowSmem& sm) {
+  int start = 0;
+  uint32_t Kk = 0;
+  if (rp.k_on) {
+    const int hi = V - static_cast<int>(rp.k);
+    Kk = DT::key(sv[hi]);
+    start = first_at_or_above<DT>(sv, hi, Kk, sm);
+  }
+  int F = start;
+  if (rp.pmode == kPTopOnly) {
+    F = V - 1;
+  } else if (rp.pmode == kPBoundary) {
+    const float m = DT::value(sv[V - 1]);
+    uint64_t z = 0;
+    for (int j = start + static_cast<int>(threadIdx.x); j < V; j += kThreads) z += mass_fx(DT::value(sv[j]), m);
+    const uint64_t Z = block_sum_u64(z, sm);
+    const uint64_t thr = topp_threshold(rp.t, Z);
+    F = (thr == 0) ? V - 1 : scan_boundary<DT>(sv, start, V, m, thr, sm);
+  }
+  SortedBoundary bd;
+  bd.F = F;
+  bd.KF = DT::key(sv[F]);
+  bd.a = (rp.k_on && bd.KF == Kk) ? start : first_at_or_above<DT>(sv, F, bd.KF, sm);
+  return bd;
+}
+
+constexpr int kSortedVecs = 8;  // logits slice held in registers: 8 vectors per thread
+constexpr int kMaxSliceWords = (kThreads * kSortedVecs * 8) / 32;
+
+template <class DT>
+__global__ __launch_bounds__(kThreads) void sorted_logits_kernel(
+    const typename DT::raw_t* __restrict__ sorted_value, const int32_t* __restrict__ sorted_indices,
+    const typename DT::raw_t* __restrict__ p, const int32_t* __restrict__ k,
+    const typename DT::raw_t* __restrict__ logits, typename DT::raw_t* __restrict__ out, int V, int S) {
+  using raw_t = typename DT::raw_t;
+  using Tile = RegTile<DT, kSortedVecs>;
+  __shared__ RowSmem sm;
+  __shared__ uint32_t ties[kMaxSliceWords];
+
+  const int b = blockIdx.x / S;
+  const int s = blockIdx.x - b * S;
+  const int v0 = s * Tile::kCapacity;
+  const int len = min(Tile::kCapacity, V - v0);
+  const size_t row_off = static_cast<size_t>(b) * V;
+
+  Tile tile;
+  tile.load(logits + row_off, v0, len);
+
+  const RowParams rp = decode_row_params<DT>(p, k, b, V);
+  raw_t* __restrict__ orow = out + row_off;
+  if (!rp.k_on && rp.pmode == kPNone) {
+    tile.store(orow, [](raw_t r, int) { return r; });
+    return;
+  }
+  const SortedBoundary bd = sorted_boundary<DT>(sorted_value + row_off, rp, V, sm);
+
+  const int words = (len + 31) / 32;
+  for (int i = threadIdx.x; i < words; i += kThreads) ties[i] = 0;
+  __syncthreads();
+  const int32_t* __restrict__ si = sorted_indices + row_off;
+  for (int j = bd.a + static_cast<int>(threadIdx.x); j < bd.F; j += kThreads) {
+    const int v = si[j] - v0;
+    if (v >= 0 && v < len) atomicOr(&ties[v >> 5], 1u << (v & 31));
+  }
+  __syncthreads();
+
+  const uint32_t KF = bd.KF;
+  tile.store(orow, [&](raw_t r, int idx) {
+    const uint32_t key = DT::key(r);
+    bool keep = key > KF;
+    if (key == KF) {
+      const int v = idx - v0;
+      keep = ((ties[v >> 5] >> (v & 31)) & 1u) == 0;
+    }
+    return keep ? r : DT::kNegInf;
+  });
+}
+
+constexpr int kScatterSlice = 65536;
+
+template <class DT>
+__global__ __launch_bounds__(kThreads) void sorted_scatter_kernel(
+    const typename DT::raw_t* __restrict__ sorted_value, const int32_t* __restrict__ sorted_indices,
+    const typename DT::raw_t* __restrict__ p, const int32_t* __restrict__ k, typename DT::raw_t* __restrict__ out,
+    int V, int S) {
+  __shared__ RowSmem sm;
+  const int b = blockIdx.x / S;
+  const int s = blockIdx.x - b * S;
+  const size_t row_off = static_cast<size_t>(b) * V;
+  const auto* __restrict__ sv = sorted_value + row_off;
+  const int32_t* __restrict__ si = sorted_indices + row_off;
+  const RowParams rp = decode_row_params<DT>(p, k, b, V);
+  int F = 0;
+  if (rp.k_on || rp.pmode != kPNone) F = sorted_boundary<DT>(sv, rp, V, sm).F;
+  const int j0 = s * kScatterSlice;
+  const int j1 = min(V, j0 + kScatterSlice);
+  auto* __restrict__ orow = out + row_off;
+  for (int j = j0 + static_cast<int>(threadIdx.x); j < j1; j += kThreads) {
+    const int v = si[j];
+    if (static_cast<unsigned>(v) < static_cast<unsigned>(V)) orow[v] = (j >= F) ? sv[j] : DT::kNegInf;
+  }
+}
+
+template <class DT>
+static hipError_t launch_sorted_t(const void* sorted_value, const int32_t* sorted_indices, const void* p,
+                                  const int32_t* k, const void* logits, void* out, int64_t B, int64_t V,
+                                  hipStream_t stream) {
+  using raw_t = typename DT::raw_t;
+  if (logits != nullptr) {
+    constexpr int cap = RegTile<DT, kSortedVecs>::kCapacity;
+    const int S = static_cast<int>((V + cap - 1) / cap);
+    hipLaunchKernelGGL(sorted_logits_kernel<DT>, dim3(static_cast<unsigned>(B * S)), dim3(kThreads), 0, stream,
+                       static_cast<const raw_t*>(sorted_value), sorted_indices, static_cast<const raw_t*>(p), k,
+                       static_cast<const raw_t*>(logits), static_cast<raw_t*>(out), static_cast<int>(V), S);
+  } else {
+    const int S = static_cast<int>((V + kScatterSlice - 1) / kScatterSlice);
+    hipLaunchKernelGGL(sorted_scatter_kernel<DT>, dim3(static_cast<unsigned>(B * S)), dim3(kThreads), 0, stream,
+                       static_cast<const raw_t*>(sorted_value), sorted_indices, static_cast<const raw_t*>(p), k,
+                       static_cast<raw_t*>(out), static_cast<int>(V), S);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_with_sorted(int dtype, const void* sorted_value, const int32_t* sorted_indices, const void* p,
+                              const int32_t* k, const void* logits, void* out, int64_t B, int64_t V,
+                              hipStream_t stream) {
+  switch (dtype) {
+    case 0: return launch_sorted_t<F32T>(sorted_value, sorted_indices, p, k, logits, out, B, V, stream);
+    case 1: return launch_sorted_t<F16T>(sorted_value, sorted_indices, p, k, logits, out, B, V, stream);
+    case 2: return launch_sorted_t<BF16T>(sorted_value, sorted_indices, p, k, logits, out, B, V, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace tkp

@@ -34,9 +34,13 @@ DTYPES = ("f32", "f16", "bf16")
 
 def bf16_bits_from_f32(x: np.ndarray) -> np.ndarray:
     """Round fp32 values to bf16, nearest-even, and return the uint16 bits."""
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
-    return rounded.astype(np.uint16)
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    # finite values stay below 0xFF800000, so the uint32 sum cannot wrap
+    r = (u >> np.uint32(16)) & np.uint32(1)
+    r += np.uint32(0x7FFF)
+    r += u
+    r >>= np.uint32(16)
+    return r.astype(np.uint16)
 
 
 def bits_to_f32(bits: np.ndarray, dtype: str) -> np.ndarray:

@@ -78,7 +78,8 @@ typedef enum {
  *
  *   logits  [B, V] device buffer of `dtype` values.
  *   dtype   one of topktopp_dtype.
- *   B, V    rows and row length; B == 0 or V == 0 is a successful no-op;
+ *   B, V    rows and row length; B == 0 or V == 0 is a successful no-op
+ *           (every pointer may then be NULL; only dtype is checked);
  *           V == 1 copies logits to out (AKP §6.1); V <= TOPKTOPP_MAX_V.
  *   p       [B] device buffer of `dtype` values, or NULL for no top-p.
  *   k       [B] device buffer of int32, or NULL for no top-k.

@@ -74,6 +74,10 @@ def test_empty_is_ok_without_launch(lib):
     assert f(FAKE, 1, 0, 100, None, FAKE + 8, FAKE + (1 << 32), None) == 0
     assert f(FAKE, 1, 5, 0, None, FAKE + 8, FAKE + (1 << 32), None) == 0
     assert tk.last_error() == ""
+    # empty buffers may be NULL (torch hands out NULL for empty tensors)
+    assert f(None, 2, 0, 151936, None, None, None, None) == 0
+    assert lib.apply_top_k_top_p_with_sorted(None, None, 0, 7, 0, None, None, None, None, None) == 0
+    assert f(None, 9, 0, 4, None, None, None, None) == INVALID
 
 
 def test_plan_policy_roundtrip(lib):

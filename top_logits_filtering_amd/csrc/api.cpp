@@ -67,6 +67,10 @@ int topktopp_set_plan_policy(int policy) {
 topktopp_status apply_top_k_top_p(const void* logits, int dtype, int64_t B, int64_t V, const void* p,
                                   const int32_t* k, void* out, void* stream) {
   g_last_error.clear();
+  if (B >= 0 && V >= 0 && (B == 0 || V == 0)) {  // empty: nothing is read or written, pointers may be NULL
+    if (!valid_dtype(dtype)) return fail(TOPKTOPP_ERR_INVALID, "dtype %d is not one of F32, F16, BF16", dtype);
+    return TOPKTOPP_OK;
+  }
   if (logits == nullptr) return fail(TOPKTOPP_ERR_NULLPTR, "logits is NULL");
   if (out == nullptr) return fail(TOPKTOPP_ERR_NULLPTR, "out is NULL");
   if (p == nullptr && k == nullptr) return fail(TOPKTOPP_ERR_NULLPTR, "p and k are both NULL; at least one is required");
@@ -77,7 +81,6 @@ topktopp_status apply_top_k_top_p(const void* logits, int dtype, int64_t B, int6
   if (overlaps(out, nbytes, logits, nbytes) || overlaps(out, nbytes, p, static_cast<size_t>(B) * es) ||
       overlaps(out, nbytes, k, static_cast<size_t>(B) * 4))
     return fail(TOPKTOPP_ERR_INVALID, "out overlaps an input buffer");
-  if (B == 0 || V == 0) return TOPKTOPP_OK;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (V == 1)  // a last dimension of 1 is copied through unfiltered
     return check_launch(hipMemcpyAsync(out, logits, nbytes, hipMemcpyDeviceToDevice, st), "hipMemcpyAsync");
@@ -88,6 +91,10 @@ topktopp_status apply_top_k_top_p_with_sorted(const void* sorted_value, const in
                                               int64_t B, int64_t V, const void* p, const int32_t* k,
                                               const void* logits, void* out, void* stream) {
   g_last_error.clear();
+  if (B >= 0 && V >= 0 && (B == 0 || V == 0)) {  // empty: nothing is read or written, pointers may be NULL
+    if (!valid_dtype(dtype)) return fail(TOPKTOPP_ERR_INVALID, "dtype %d is not one of F32, F16, BF16", dtype);
+    return TOPKTOPP_OK;
+  }
   if (sorted_value == nullptr) return fail(TOPKTOPP_ERR_NULLPTR, "sorted_value is NULL");
   if (sorted_indices == nullptr) return fail(TOPKTOPP_ERR_NULLPTR, "sorted_indices is NULL");
   if (out == nullptr) return fail(TOPKTOPP_ERR_NULLPTR, "out is NULL");
@@ -101,7 +108,6 @@ topktopp_status apply_top_k_top_p_with_sorted(const void* sorted_value, const in
       overlaps(out, nbytes, logits, nbytes) || overlaps(out, nbytes, p, static_cast<size_t>(B) * es) ||
       overlaps(out, nbytes, k, static_cast<size_t>(B) * 4))
     return fail(TOPKTOPP_ERR_INVALID, "out overlaps an input buffer");
-  if (B == 0 || V == 0) return TOPKTOPP_OK;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (V == 1)  // the single element is always kept; sorted_indices is 0
     return check_launch(hipMemcpyAsync(out, logits != nullptr ? logits : sorted_value, nbytes,

@@ -36,6 +36,10 @@ struct F32T {
     uint32_t u = (r == 0x80000000u) ? 0u : r;  // -0.0 -> +0.0
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
   }
+  // inverse of key() (zero comes back as +0.0)
+  __device__ static inline raw_t raw_of_key(uint32_t K) { return (K & 0x80000000u) ? (K & 0x7FFFFFFFu) : ~K; }
+  // bits of a value known to be representable in this dtype
+  __device__ static inline raw_t raw_of_value(float f) { return __float_as_uint(f); }
 };
 
 struct F16T {
@@ -50,6 +54,12 @@ struct F16T {
     uint32_t u = (r == 0x8000u) ? 0u : r;
     return (u & 0x8000u) ? (~u & 0xFFFFu) : (u | 0x8000u);
   }
+  __device__ static inline raw_t raw_of_key(uint32_t K) {
+    return static_cast<raw_t>((K & 0x8000u) ? (K & 0x7FFFu) : (~K & 0xFFFFu));
+  }
+  __device__ static inline raw_t raw_of_value(float f) {
+    return __builtin_bit_cast(raw_t, static_cast<_Float16>(f));
+  }
 };
 
 struct BF16T {
@@ -62,6 +72,10 @@ struct BF16T {
     uint32_t u = (r == 0x8000u) ? 0u : r;
     return (u & 0x8000u) ? (~u & 0xFFFFu) : (u | 0x8000u);
   }
+  __device__ static inline raw_t raw_of_key(uint32_t K) {
+    return static_cast<raw_t>((K & 0x8000u) ? (K & 0x7FFFu) : (~K & 0xFFFFu));
+  }
+  __device__ static inline raw_t raw_of_value(float f) { return static_cast<raw_t>(__float_as_uint(f) >> 16); }
 };
 
 // exp(x - m) as 43-bit fixed point, for x <= m. Uses the hardware exp2; the

@@ -85,6 +85,25 @@ struct RegTile {
     }
   }
 
+  // f(x) for every vector held by this thread, x[] holding the values as
+  // fp32 with invalid slots (past the row end) set to -inf.
+  template <class F>
+  __device__ inline void for_each_vec_values(F&& f) const {
+#pragma unroll
+    for (int i = 0; i < NVEC; ++i) {
+      const int e0 = i * kSpan + static_cast<int>(threadIdx.x) * kPV;
+      float x[kPV];
+      if ((i + 1) * kSpan <= len) {
+#pragma unroll
+        for (int j = 0; j < kPV; ++j) x[j] = DT::value(get(i, j));
+      } else {
+#pragma unroll
+        for (int j = 0; j < kPV; ++j) x[j] = (e0 + j < len) ? DT::value(get(i, j)) : -INFINITY;
+      }
+      f(x);
+    }
+  }
+
   // row[idx] = g(raw, idx) for every valid element held by this thread.
   template <class G>
   __device__ inline void store(raw_t* __restrict__ row, G&& g) const {
@@ -102,6 +121,91 @@ struct RegTile {
 #pragma unroll
         for (int j = 0; j < kPV; ++j)
           if (e0 + j < len) dst[e0 + j] = g(get(i, j), base + e0 + j);
+      }
+    }
+  }
+};
+
+}  // namespace tkp
+
+namespace tkp {
+
+// The same interface as RegTile for rows too long to keep in registers: every
+// traversal reads the row again from global memory (16-byte loads, the same
+// element-to-thread layout), so later traversals mostly hit L2 or the
+// Infinity Cache.
+template <class DT>
+struct GlobalTile {
+  using raw_t = typename DT::raw_t;
+  static constexpr int kPV = DT::kPerVec;
+  static constexpr int kSpan = kThreads * kPV;
+
+  const raw_t* src;
+  int base;
+  int len;
+  bool aligned;
+
+  __device__ inline void load(const raw_t* __restrict__ row, int v0, int n) {
+    src = row + v0;
+    base = v0;
+    len = n;
+    aligned = (reinterpret_cast<uintptr_t>(src) & 15u) == 0;
+  }
+
+  // raw elements e0 .. e0+kPV-1 (zero past the end)
+  __device__ inline void read(int e0, raw_t (&r)[kPV]) const {
+    if (aligned && e0 + kPV <= len) {
+      const uint4 q = *reinterpret_cast<const uint4*>(src + e0);
+#pragma unroll
+      for (int j = 0; j < kPV; ++j) r[j] = RegTile<DT, 1>::lane_of(q, j);
+    } else {
+#pragma unroll
+      for (int j = 0; j < kPV; ++j) r[j] = (e0 + j < len) ? src[e0 + j] : static_cast<raw_t>(0);
+    }
+  }
+
+  template <class F>
+  __device__ inline void for_each(F&& f) const {
+#pragma unroll 2
+    for (int e0 = static_cast<int>(threadIdx.x) * kPV; e0 < len; e0 += kSpan) {
+      raw_t r[kPV];
+      read(e0, r);
+#pragma unroll
+      for (int j = 0; j < kPV; ++j)
+        if (e0 + j < len) f(r[j], base + e0 + j);
+    }
+  }
+
+  template <class F>
+  __device__ inline void for_each_vec_values(F&& f) const {
+#pragma unroll 2
+    for (int e0 = static_cast<int>(threadIdx.x) * kPV; e0 < len; e0 += kSpan) {
+      raw_t r[kPV];
+      read(e0, r);
+      float x[kPV];
+#pragma unroll
+      for (int j = 0; j < kPV; ++j) x[j] = (e0 + j < len) ? DT::value(r[j]) : -INFINITY;
+      f(x);
+    }
+  }
+
+  template <class G>
+  __device__ inline void store(raw_t* __restrict__ row, G&& g) const {
+    raw_t* dst = row + base;
+    const bool dst_aligned = (reinterpret_cast<uintptr_t>(dst) & 15u) == 0;
+#pragma unroll 2
+    for (int e0 = static_cast<int>(threadIdx.x) * kPV; e0 < len; e0 += kSpan) {
+      raw_t r[kPV];
+      read(e0, r);
+      if (dst_aligned && e0 + kPV <= len) {
+        uint4 o = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+        for (int j = 0; j < kPV; ++j) RegTile<DT, 1>::set_lane(o, j, g(r[j], base + e0 + j));
+        *reinterpret_cast<uint4*>(dst + e0) = o;
+      } else {
+#pragma unroll
+        for (int j = 0; j < kPV; ++j)
+          if (e0 + j < len) dst[e0 + j] = g(r[j], base + e0 + j);
       }
     }
   }

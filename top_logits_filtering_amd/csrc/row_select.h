@@ -66,9 +66,11 @@ __device__ void top_position(const Src& src, RowSmem& sm, uint32_t& K, uint32_t&
 // thr (1 <= thr <= Z) is the fixed-point threshold (1 - t) * Z, m the row
 // maximum. Returns (Kp, Ip): survivors are key > Kp, or key == Kp with
 // idx >= Ip.
+// With with_index == false only Kp is computed (Ip = 0), which is enough when
+// the result is used as a lower bound on the boundary key.
 template <class DT, class Src>
 __device__ void topp_boundary(const Src& src, uint32_t Kk, float m, uint64_t thr, RowSmem& sm, uint32_t& Kp,
-                              uint32_t& Ip) {
+                              uint32_t& Ip, bool with_index = true) {
   uint32_t prefix = 0, pmask = 0;
   uint64_t acc = 0;  // mass strictly above the current prefix range
   for (int shift = DT::kKeyBits - 8; shift >= 0; shift -= 8) {
@@ -96,7 +98,7 @@ __device__ void topp_boundary(const Src& src, uint32_t Kk, float m, uint64_t thr
   uint32_t ns = ns64 >= cnt ? cnt : static_cast<uint32_t>(ns64);
   if (ns < 1) ns = 1;
   __syncthreads();  // everyone has read sel_* before it is reused
-  if (ns >= cnt) {
+  if (ns >= cnt || !with_index) {
     Ip = 0;
   } else {
     const uint32_t kp = Kp;

@@ -117,9 +117,11 @@ const char* topktopp_last_error(void);
 
 /*
  * Launch-plan override, for tests and measurement. policy 0 (default) lets
- * the library choose per call; 1 forces the general multi-pass path for every
- * row; 2 forces the register-resident path wherever the row fits. The result
- * is the same under every policy. Returns the previous policy, or -1 for an
+ * the library choose: the candidate plan, with the row held in registers
+ * when it fits; 1 forces the multi-pass plan for every row; 2 forces the
+ * candidate plan with the row re-read from global memory. Every policy
+ * computes the same filter; top-p decisions may differ only inside the
+ * tolerance band described above. Returns the previous policy, or -1 for an
  * unknown value (which is ignored). The setting is process-wide.
  */
 int topktopp_set_plan_policy(int policy);

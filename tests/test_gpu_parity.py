@@ -20,7 +20,7 @@ from workloads.synth import (
 
 pytestmark = pytest.mark.gpu
 
-POLICIES = {"auto": 0, "general": 1, "registers": 2}
+POLICIES = {"auto": 0, "multipass": 1, "stream": 2}
 
 
 @pytest.fixture(params=sorted(POLICIES), scope="module")
@@ -49,10 +49,10 @@ def test_random_rows(dtype, policy):
     """Several tiles plus ragged tails, every mode, odd k and p values."""
     total = ParityReport()
     seed = {"f32": 1, "f16": 2, "bf16": 3}[dtype] * 100
-    for V in (2, 3, 7, 64, 1000, 1031, 4099, 20011, 70001):
+    for V in (2, 3, 7, 64, 1000, 1031, 4099, 20011, 70001, 170001):
         for kind in ("normal", "ties", "zeros", "gumbel", "spikes", "const", "wide"):
             seed += 1
-            B = 6 if V < 20000 else 3
+            B = 6 if V < 20000 else (3 if V < 100000 else 2)
             xb = random_rows(seed, B, V, dtype, kind=kind)
             k, p = random_params(seed, B, V, dtype)
             k_small = np.minimum(np.abs(k), max(1, V // 3)).astype(np.int32)

@@ -65,7 +65,7 @@ def last_error() -> str:
 
 
 def set_plan_policy(policy: int) -> int:
-    """0 auto, 1 general multi-pass, 2 register-resident where the row fits."""
+    """0 auto (candidate plan), 1 multi-pass plan, 2 candidate plan re-reading global memory."""
     prev = load_library().topktopp_set_plan_policy(int(policy))
     if prev < 0:
         raise ValueError(f"unknown plan policy {policy}")

@@ -20,7 +20,7 @@ BUILD_DIR = os.path.join(PKG_DIR, "_build")
 LIB_NAME = "libtopktopp.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
-SOURCES = ["api.cpp", "apply_kernels.hip", "sorted_kernels.hip"]
+SOURCES = ["api.cpp", "apply_f32.hip", "apply_f16.hip", "apply_bf16.hip", "sorted_kernels.hip"]
 
 ARCH = "gfx950"
 COMMON_FLAGS = [
@@ -61,7 +61,7 @@ def _compile(src: str, verbose: bool) -> str:
 def build(verbose: bool = False) -> str:
     """Compile every source and link libtopktopp.so; returns the library path."""
     os.makedirs(BUILD_DIR, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(len(SOURCES), 4)) as ex:
+    with ThreadPoolExecutor(max_workers=min(len(SOURCES), 6)) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
     tmp = LIB_PATH + ".tmp%d" % os.getpid()
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]

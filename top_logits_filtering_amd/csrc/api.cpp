@@ -60,7 +60,7 @@ extern "C" {
 const char* topktopp_last_error(void) { return g_last_error.c_str(); }
 
 int topktopp_set_plan_policy(int policy) {
-  if (policy < tkp::kPlanAuto || policy > tkp::kPlanRegisters) return -1;
+  if (policy < tkp::kPlanAuto || policy > tkp::kPlanStream) return -1;
   return g_policy.exchange(policy);
 }
 

@@ -1,0 +1,13 @@
+// apply_top_k_top_p kernels instantiated for f16 (one file per dtype so
+// the three builds run in parallel).
+
+#include "apply_kernels.h"
+
+namespace tkp {
+
+hipError_t launch_apply_f16(const void* logits, const void* p, const int32_t* k, void* out, int64_t B, int64_t V,
+                          int policy, hipStream_t stream) {
+  return launch_apply_t<F16T>(logits, p, k, out, B, V, policy, stream);
+}
+
+}  // namespace tkp

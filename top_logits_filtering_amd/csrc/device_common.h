@@ -31,15 +31,15 @@ struct F32T {
   static constexpr int kKeyBits = 32;
   static constexpr raw_t kNegInf = 0xFF800000u;
   static constexpr int kPerVec = 4;  // elements per 16-byte vector
-  __device__ static inline float value(raw_t r) { return __uint_as_float(r); }
-  __device__ static inline uint32_t key(raw_t r) {
+  __device__ static __forceinline__ float value(raw_t r) { return __uint_as_float(r); }
+  __device__ static __forceinline__ uint32_t key(raw_t r) {
     uint32_t u = (r == 0x80000000u) ? 0u : r;  // -0.0 -> +0.0
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
   }
   // inverse of key() (zero comes back as +0.0)
-  __device__ static inline raw_t raw_of_key(uint32_t K) { return (K & 0x80000000u) ? (K & 0x7FFFFFFFu) : ~K; }
+  __device__ static __forceinline__ raw_t raw_of_key(uint32_t K) { return (K & 0x80000000u) ? (K & 0x7FFFFFFFu) : ~K; }
   // bits of a value known to be representable in this dtype
-  __device__ static inline raw_t raw_of_value(float f) { return __float_as_uint(f); }
+  __device__ static __forceinline__ raw_t raw_of_value(float f) { return __float_as_uint(f); }
 };
 
 struct F16T {
@@ -47,17 +47,17 @@ struct F16T {
   static constexpr int kKeyBits = 16;
   static constexpr raw_t kNegInf = 0xFC00u;
   static constexpr int kPerVec = 8;
-  __device__ static inline float value(raw_t r) {
+  __device__ static __forceinline__ float value(raw_t r) {
     return static_cast<float>(__builtin_bit_cast(_Float16, r));
   }
-  __device__ static inline uint32_t key(raw_t r) {
+  __device__ static __forceinline__ uint32_t key(raw_t r) {
     uint32_t u = (r == 0x8000u) ? 0u : r;
     return (u & 0x8000u) ? (~u & 0xFFFFu) : (u | 0x8000u);
   }
-  __device__ static inline raw_t raw_of_key(uint32_t K) {
+  __device__ static __forceinline__ raw_t raw_of_key(uint32_t K) {
     return static_cast<raw_t>((K & 0x8000u) ? (K & 0x7FFFu) : (~K & 0xFFFFu));
   }
-  __device__ static inline raw_t raw_of_value(float f) {
+  __device__ static __forceinline__ raw_t raw_of_value(float f) {
     return __builtin_bit_cast(raw_t, static_cast<_Float16>(f));
   }
 };
@@ -67,21 +67,21 @@ struct BF16T {
   static constexpr int kKeyBits = 16;
   static constexpr raw_t kNegInf = 0xFF80u;
   static constexpr int kPerVec = 8;
-  __device__ static inline float value(raw_t r) { return __uint_as_float(static_cast<uint32_t>(r) << 16); }
-  __device__ static inline uint32_t key(raw_t r) {
+  __device__ static __forceinline__ float value(raw_t r) { return __uint_as_float(static_cast<uint32_t>(r) << 16); }
+  __device__ static __forceinline__ uint32_t key(raw_t r) {
     uint32_t u = (r == 0x8000u) ? 0u : r;
     return (u & 0x8000u) ? (~u & 0xFFFFu) : (u | 0x8000u);
   }
-  __device__ static inline raw_t raw_of_key(uint32_t K) {
+  __device__ static __forceinline__ raw_t raw_of_key(uint32_t K) {
     return static_cast<raw_t>((K & 0x8000u) ? (K & 0x7FFFu) : (~K & 0xFFFFu));
   }
-  __device__ static inline raw_t raw_of_value(float f) { return static_cast<raw_t>(__float_as_uint(f) >> 16); }
+  __device__ static __forceinline__ raw_t raw_of_value(float f) { return static_cast<raw_t>(__float_as_uint(f) >> 16); }
 };
 
 // exp(x - m) as 43-bit fixed point, for x <= m. Uses the hardware exp2; the
 // relative error of a term is about |x - m| * 1e-7, far below the 1e-5 band in
 // which top-p decisions may differ from an exact evaluation.
-__device__ inline uint64_t mass_fx(float x, float m) {
+__device__ __forceinline__ uint64_t mass_fx(float x, float m) {
   float e = __builtin_amdgcn_exp2f((x - m) * 1.4426950408889634f);
   e = fminf(e, 1.0f);
   float hi_f = e * 2048.0f;  // 2^11, exact
@@ -93,13 +93,13 @@ __device__ inline uint64_t mass_fx(float x, float m) {
 
 // ------------------------------------------------------------- reductions ---
 
-__device__ inline float wave_max_f32(float v) {
+__device__ __forceinline__ float wave_max_f32(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
   return v;
 }
 
-__device__ inline uint32_t wave_max_u32(uint32_t v) {
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     uint32_t w = __shfl_xor(v, o);
@@ -108,13 +108,13 @@ __device__ inline uint32_t wave_max_u32(uint32_t v) {
   return v;
 }
 
-__device__ inline uint64_t wave_sum_u64(uint64_t v) {
+__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
   return v;
 }
 
-__device__ inline uint32_t wave_sum_u32(uint32_t v) {
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
   return v;
@@ -136,7 +136,7 @@ struct RowSmem {
   uint32_t bcast[4];
 };
 
-__device__ inline float block_max_f32(float v, RowSmem& sm) {
+__device__ __forceinline__ float block_max_f32(float v, RowSmem& sm) {
   v = wave_max_f32(v);
   const int w = threadIdx.x / kWave;
   if ((threadIdx.x & (kWave - 1)) == 0) sm.redf[w] = v;
@@ -148,7 +148,7 @@ __device__ inline float block_max_f32(float v, RowSmem& sm) {
   return r;
 }
 
-__device__ inline uint32_t block_max_u32(uint32_t v, RowSmem& sm) {
+__device__ __forceinline__ uint32_t block_max_u32(uint32_t v, RowSmem& sm) {
   v = wave_max_u32(v);
   const int w = threadIdx.x / kWave;
   if ((threadIdx.x & (kWave - 1)) == 0) sm.redw[w] = v;
@@ -160,7 +160,7 @@ __device__ inline uint32_t block_max_u32(uint32_t v, RowSmem& sm) {
   return r;
 }
 
-__device__ inline uint64_t block_sum_u64(uint64_t v, RowSmem& sm) {
+__device__ __forceinline__ uint64_t block_sum_u64(uint64_t v, RowSmem& sm) {
   v = wave_sum_u64(v);
   const int w = threadIdx.x / kWave;
   if ((threadIdx.x & (kWave - 1)) == 0) sm.redu[w] = v;
@@ -172,7 +172,7 @@ __device__ inline uint64_t block_sum_u64(uint64_t v, RowSmem& sm) {
   return r;
 }
 
-__device__ inline uint32_t block_sum_u32(uint32_t v, RowSmem& sm) {
+__device__ __forceinline__ uint32_t block_sum_u32(uint32_t v, RowSmem& sm) {
   v = wave_sum_u32(v);
   const int w = threadIdx.x / kWave;
   if ((threadIdx.x & (kWave - 1)) == 0) sm.redw[w] = v;
@@ -191,7 +191,7 @@ __device__ inline uint32_t block_sum_u32(uint32_t v, RowSmem& sm) {
 // lands in sm.sel_* and is visible to the whole block after the call. If the
 // target exceeds the grand total, bin 0 is selected.
 
-__device__ inline void select_bin_count(RowSmem& sm, uint32_t target) {
+__device__ __forceinline__ void select_bin_count(RowSmem& sm, uint32_t target) {
   if (threadIdx.x < kWave) {
     const int l = threadIdx.x;
     const int b0 = 255 - 4 * l;
@@ -223,7 +223,7 @@ __device__ inline void select_bin_count(RowSmem& sm, uint32_t target) {
   __syncthreads();
 }
 
-__device__ inline void select_bin_mass(RowSmem& sm, uint64_t target) {
+__device__ __forceinline__ void select_bin_mass(RowSmem& sm, uint64_t target) {
   if (threadIdx.x < kWave) {
     const int l = threadIdx.x;
     const int b0 = 255 - 4 * l;
@@ -256,7 +256,7 @@ __device__ inline void select_bin_mass(RowSmem& sm, uint64_t target) {
   __syncthreads();
 }
 
-__device__ inline void clear_hists(RowSmem& sm, bool with_mass) {
+__device__ __forceinline__ void clear_hists(RowSmem& sm, bool with_mass) {
   if (threadIdx.x < 256) {
     sm.hist[threadIdx.x] = 0;
     if (with_mass) sm.mhist[threadIdx.x] = 0;
@@ -276,7 +276,7 @@ struct RowParams {
 };
 
 template <class DT>
-__device__ inline RowParams decode_row_params(const typename DT::raw_t* p, const int32_t* k, int b, int V) {
+__device__ __forceinline__ RowParams decode_row_params(const typename DT::raw_t* p, const int32_t* k, int b, int V) {
   RowParams rp;
   rp.k_on = false;
   rp.k = 0;
@@ -303,7 +303,7 @@ __device__ inline RowParams decode_row_params(const typename DT::raw_t* p, const
 // Fixed-point threshold: a position survives top-p iff the mass strictly above
 // it (in the stable descending order) is below (1 - t) * Z; for an integer
 // mass D that is D < ceil((1 - t) * Z). The result never exceeds Z.
-__device__ inline uint64_t topp_threshold(float t, uint64_t Z) {
+__device__ __forceinline__ uint64_t topp_threshold(float t, uint64_t Z) {
   double thr_d = ceil((1.0 - static_cast<double>(t)) * static_cast<double>(Z));
   if (!(thr_d > 0.0)) return 0;
   if (thr_d >= static_cast<double>(Z)) return Z;

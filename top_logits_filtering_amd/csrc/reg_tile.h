@@ -23,23 +23,23 @@ struct RegTile {
 
   // Element access by (vector, lane). Both indices are compile-time constants
   // after unrolling, so these fold to register moves and shifts.
-  static __device__ inline uint32_t word(const uint4& q, int w) {
+  static __device__ __forceinline__ uint32_t word(const uint4& q, int w) {
     return w == 0 ? q.x : (w == 1 ? q.y : (w == 2 ? q.z : q.w));
   }
-  static __device__ inline void set_word(uint4& q, int w, uint32_t x) {
+  static __device__ __forceinline__ void set_word(uint4& q, int w, uint32_t x) {
     if (w == 0) q.x = x;
     else if (w == 1) q.y = x;
     else if (w == 2) q.z = x;
     else q.w = x;
   }
-  static __device__ inline raw_t lane_of(const uint4& q, int j) {
+  static __device__ __forceinline__ raw_t lane_of(const uint4& q, int j) {
     if constexpr (sizeof(raw_t) == 4) {
       return word(q, j);
     } else {
       return static_cast<raw_t>(word(q, j >> 1) >> ((j & 1) * 16));
     }
   }
-  static __device__ inline void set_lane(uint4& q, int j, raw_t r) {
+  static __device__ __forceinline__ void set_lane(uint4& q, int j, raw_t r) {
     if constexpr (sizeof(raw_t) == 4) {
       set_word(q, j, r);
     } else {
@@ -47,10 +47,27 @@ struct RegTile {
       set_word(q, w, (word(q, w) & ~(0xFFFFu << sh)) | (static_cast<uint32_t>(r) << sh));
     }
   }
-  __device__ inline raw_t get(int i, int j) const { return lane_of(v[i], j); }
-  __device__ inline void set(int i, int j, raw_t r) { set_lane(v[i], j, r); }
+  __device__ __forceinline__ raw_t get(int i, int j) const { return lane_of(v[i], j); }
+  __device__ __forceinline__ void set(int i, int j, raw_t r) { set_lane(v[i], j, r); }
 
-  __device__ inline void load(const raw_t* __restrict__ row, int v0, int n) {
+  // Vector i as an opaque copy. Every traversal reads the tile through this,
+  // so values derived from the tile in one traversal (keys, exponentials)
+  // cannot be hoisted out of the selection loops and kept alive across
+  // traversals, which would exhaust the register file.
+  __device__ __forceinline__ uint4 fresh(int i) const {
+    uint4 q = v[i];
+    asm volatile("" : "+v"(q.x), "+v"(q.y), "+v"(q.z), "+v"(q.w));
+    return q;
+  }
+  // threadIdx.x behind the same barrier, so per-element indices are
+  // recomputed in each traversal instead of living in registers throughout.
+  static __device__ __forceinline__ int fresh_tid() {
+    int t = static_cast<int>(threadIdx.x);
+    asm volatile("" : "+v"(t));
+    return t;
+  }
+
+  __device__ __forceinline__ void load(const raw_t* __restrict__ row, int v0, int n) {
     base = v0;
     len = n;
     const raw_t* src = row + v0;
@@ -70,17 +87,19 @@ struct RegTile {
   // f(raw, idx) for every valid element held by this thread; idx is the
   // element's index within the row.
   template <class F>
-  __device__ inline void for_each(F&& f) const {
+  __device__ __forceinline__ void for_each(F&& f) const {
+    const int tid = fresh_tid();
 #pragma unroll
     for (int i = 0; i < NVEC; ++i) {
-      const int e0 = i * kSpan + static_cast<int>(threadIdx.x) * kPV;
+      const int e0 = i * kSpan + tid * kPV;
+      const uint4 q = fresh(i);
       if ((i + 1) * kSpan <= len) {  // whole layer valid: uniform over the block
 #pragma unroll
-        for (int j = 0; j < kPV; ++j) f(get(i, j), base + e0 + j);
+        for (int j = 0; j < kPV; ++j) f(lane_of(q, j), base + e0 + j);
       } else {
 #pragma unroll
         for (int j = 0; j < kPV; ++j)
-          if (e0 + j < len) f(get(i, j), base + e0 + j);
+          if (e0 + j < len) f(lane_of(q, j), base + e0 + j);
       }
     }
   }
@@ -88,17 +107,19 @@ struct RegTile {
   // f(x) for every vector held by this thread, x[] holding the values as
   // fp32 with invalid slots (past the row end) set to -inf.
   template <class F>
-  __device__ inline void for_each_vec_values(F&& f) const {
+  __device__ __forceinline__ void for_each_vec_values(F&& f) const {
+    const int tid = fresh_tid();
 #pragma unroll
     for (int i = 0; i < NVEC; ++i) {
-      const int e0 = i * kSpan + static_cast<int>(threadIdx.x) * kPV;
+      const int e0 = i * kSpan + tid * kPV;
       float x[kPV];
+      const uint4 q = fresh(i);
       if ((i + 1) * kSpan <= len) {
 #pragma unroll
-        for (int j = 0; j < kPV; ++j) x[j] = DT::value(get(i, j));
+        for (int j = 0; j < kPV; ++j) x[j] = DT::value(lane_of(q, j));
       } else {
 #pragma unroll
-        for (int j = 0; j < kPV; ++j) x[j] = (e0 + j < len) ? DT::value(get(i, j)) : -INFINITY;
+        for (int j = 0; j < kPV; ++j) x[j] = (e0 + j < len) ? DT::value(lane_of(q, j)) : -INFINITY;
       }
       f(x);
     }
@@ -106,21 +127,23 @@ struct RegTile {
 
   // row[idx] = g(raw, idx) for every valid element held by this thread.
   template <class G>
-  __device__ inline void store(raw_t* __restrict__ row, G&& g) const {
+  __device__ __forceinline__ void store(raw_t* __restrict__ row, G&& g) const {
     raw_t* dst = row + base;
     const bool aligned = (reinterpret_cast<uintptr_t>(dst) & 15u) == 0;
+    const int tid = fresh_tid();
 #pragma unroll
     for (int i = 0; i < NVEC; ++i) {
-      const int e0 = i * kSpan + static_cast<int>(threadIdx.x) * kPV;
+      const int e0 = i * kSpan + tid * kPV;
+      const uint4 q = fresh(i);
       if (aligned && e0 + kPV <= len) {
         uint4 o = make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
-        for (int j = 0; j < kPV; ++j) set_lane(o, j, g(get(i, j), base + e0 + j));
+        for (int j = 0; j < kPV; ++j) set_lane(o, j, g(lane_of(q, j), base + e0 + j));
         *reinterpret_cast<uint4*>(dst + e0) = o;
       } else {
 #pragma unroll
         for (int j = 0; j < kPV; ++j)
-          if (e0 + j < len) dst[e0 + j] = g(get(i, j), base + e0 + j);
+          if (e0 + j < len) dst[e0 + j] = g(lane_of(q, j), base + e0 + j);
       }
     }
   }
@@ -145,7 +168,7 @@ struct GlobalTile {
   int len;
   bool aligned;
 
-  __device__ inline void load(const raw_t* __restrict__ row, int v0, int n) {
+  __device__ __forceinline__ void load(const raw_t* __restrict__ row, int v0, int n) {
     src = row + v0;
     base = v0;
     len = n;
@@ -153,7 +176,7 @@ struct GlobalTile {
   }
 
   // raw elements e0 .. e0+kPV-1 (zero past the end)
-  __device__ inline void read(int e0, raw_t (&r)[kPV]) const {
+  __device__ __forceinline__ void read(int e0, raw_t (&r)[kPV]) const {
     if (aligned && e0 + kPV <= len) {
       const uint4 q = *reinterpret_cast<const uint4*>(src + e0);
 #pragma unroll
@@ -165,7 +188,7 @@ struct GlobalTile {
   }
 
   template <class F>
-  __device__ inline void for_each(F&& f) const {
+  __device__ __forceinline__ void for_each(F&& f) const {
 #pragma unroll 2
     for (int e0 = static_cast<int>(threadIdx.x) * kPV; e0 < len; e0 += kSpan) {
       raw_t r[kPV];
@@ -177,7 +200,7 @@ struct GlobalTile {
   }
 
   template <class F>
-  __device__ inline void for_each_vec_values(F&& f) const {
+  __device__ __forceinline__ void for_each_vec_values(F&& f) const {
 #pragma unroll 2
     for (int e0 = static_cast<int>(threadIdx.x) * kPV; e0 < len; e0 += kSpan) {
       raw_t r[kPV];
@@ -190,7 +213,7 @@ struct GlobalTile {
   }
 
   template <class G>
-  __device__ inline void store(raw_t* __restrict__ row, G&& g) const {
+  __device__ __forceinline__ void store(raw_t* __restrict__ row, G&& g) const {
     raw_t* dst = row + base;
     const bool dst_aligned = (reinterpret_cast<uintptr_t>(dst) & 15u) == 0;
 #pragma unroll 2

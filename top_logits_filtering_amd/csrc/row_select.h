@@ -26,7 +26,7 @@ namespace tkp {
 // elements with pred(raw, idx), by 8-bit digits from the top. key_bits is a
 // multiple of 8. Every thread of the block must call it.
 template <class Src, class KeyFn, class Pred>
-__device__ uint32_t radix_select_desc(const Src& src, int key_bits, uint32_t k, KeyFn keyfn, Pred pred,
+__device__ __forceinline__ uint32_t radix_select_desc(const Src& src, int key_bits, uint32_t k, KeyFn keyfn, Pred pred,
                                       RowSmem& sm) {
   uint32_t prefix = 0, pmask = 0;
   for (int shift = key_bits - 8; shift >= 0; shift -= 8) {
@@ -47,7 +47,7 @@ __device__ uint32_t radix_select_desc(const Src& src, int key_bits, uint32_t k, 
 
 // Key of the maximum and the highest original index holding it.
 template <class DT, class Src>
-__device__ void top_position(const Src& src, RowSmem& sm, uint32_t& K, uint32_t& I) {
+__device__ __forceinline__ void top_position(const Src& src, RowSmem& sm, uint32_t& K, uint32_t& I) {
   uint32_t kmax = 0;
   src.for_each([&](auto raw, int) {
     uint32_t key = DT::key(raw);
@@ -69,7 +69,7 @@ __device__ void top_position(const Src& src, RowSmem& sm, uint32_t& K, uint32_t&
 // With with_index == false only Kp is computed (Ip = 0), which is enough when
 // the result is used as a lower bound on the boundary key.
 template <class DT, class Src>
-__device__ void topp_boundary(const Src& src, uint32_t Kk, float m, uint64_t thr, RowSmem& sm, uint32_t& Kp,
+__device__ __forceinline__ void topp_boundary(const Src& src, uint32_t Kk, float m, uint64_t thr, RowSmem& sm, uint32_t& Kp,
                               uint32_t& Ip, bool with_index = true) {
   uint32_t prefix = 0, pmask = 0;
   uint64_t acc = 0;  // mass strictly above the current prefix range
@@ -110,7 +110,7 @@ __device__ void topp_boundary(const Src& src, uint32_t Kk, float m, uint64_t thr
 
 // Full threshold pair (K, I) of a row, every statistic computed from `src`.
 template <class DT, class Src>
-__device__ void solve_row(const Src& src, const RowParams& rp, RowSmem& sm, uint32_t& K, uint32_t& I) {
+__device__ __forceinline__ void solve_row(const Src& src, const RowParams& rp, RowSmem& sm, uint32_t& K, uint32_t& I) {
   K = 0;
   I = 0;
   if (!rp.k_on && rp.pmode == kPNone) return;

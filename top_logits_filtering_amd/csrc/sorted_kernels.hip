@@ -29,12 +29,12 @@
 
 namespace tkp {
 
-__device__ inline int block_max_i32(int v, RowSmem& sm) {
+__device__ __forceinline__ int block_max_i32(int v, RowSmem& sm) {
   return static_cast<int>(block_max_u32(static_cast<uint32_t>(v + 1), sm)) - 1;
 }
 
 // Exclusive prefix sum over threadIdx.x; also returns the block total.
-__device__ inline uint64_t block_exscan_u64(uint64_t v, RowSmem& sm, uint64_t& total) {
+__device__ __forceinline__ uint64_t block_exscan_u64(uint64_t v, RowSmem& sm, uint64_t& total) {
   const int l = threadIdx.x & (kWave - 1);
   const int w = threadIdx.x / kWave;
   uint64_t incl = v;
@@ -60,7 +60,7 @@ __device__ inline uint64_t block_exscan_u64(uint64_t v, RowSmem& sm, uint64_t& t
 // Smallest j <= hi such that key(sv[j..hi]) >= K, given key(sv[hi]) >= K and
 // an ascending row.
 template <class DT>
-__device__ int first_at_or_above(const typename DT::raw_t* __restrict__ sv, int hi, uint32_t K, RowSmem& sm) {
+__device__ __forceinline__ int first_at_or_above(const typename DT::raw_t* __restrict__ sv, int hi, uint32_t K, RowSmem& sm) {
   int top = hi;
   for (;;) {
     const int j = top - 1 - static_cast<int>(threadIdx.x);
@@ -74,7 +74,7 @@ __device__ int first_at_or_above(const typename DT::raw_t* __restrict__ sv, int 
 
 // Lowest sorted position F >= start whose mass strictly above is < thr.
 template <class DT>
-__device__ int scan_boundary(const typename DT::raw_t* __restrict__ sv, int start, int V, float m, uint64_t thr,
+__device__ __forceinline__ int scan_boundary(const typename DT::raw_t* __restrict__ sv, int start, int V, float m, uint64_t thr,
                              RowSmem& sm) {
   int hi = V;
   uint64_t base = 0;
@@ -102,7 +102,7 @@ struct SortedBoundary {
 };
 
 template <class DT>
-__device__ SortedBoundary sorted_boundary(const typename DT::raw_t* __restrict__ sv, const RowParams& rp, int V,
+__device__ __forceinline__ SortedBoundary sorted_boundary(const typename DT::raw_t* __restrict__ sv, const RowParams& rp, int V,
                                           RowSmem& sm) {
   int start = 0;
   uint32_t Kk = 0;

@@ -30,6 +30,8 @@ COMMON_FLAGS = [
     f"--offload-arch={ARCH}",
     # keep the compiler from forming packed-fp32 instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # no NaN handling in min/max (NaN inputs are outside the filter's contract)
+    "-fno-honor-nans",
     "-I", os.path.join(REPO_ROOT, "include"),
     "-Wall",
     "-Wno-unused-command-line-argument",

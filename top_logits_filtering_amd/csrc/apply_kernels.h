@@ -9,30 +9,34 @@
 // values) or is re-read from global memory on every traversal (GlobalTile).
 //
 // Candidate plan (default). Typical decoding rows keep a tiny top set, so:
-//  1. while the row arrives, each thread tracks the two largest of its
-//     vector maxima and, for top-p rows without top-k, an online
+//  1. while the row arrives, each thread tracks the two largest maxima of
+//     its 16-byte vectors and, for top-p rows without top-k, an online
 //     (running-max rescaled) sum of exp(x - max);
-//  2. the 2048 per-thread maxima are actual row elements, so the k-th largest
-//     of them is a lower bound L on the top-k threshold; for top-p-only rows,
-//     L is the key at which the mass of those maxima, walked from the top,
-//     reaches (1 - t) * Z, so every element >= L carries at least that mass
-//     and the top-p boundary cannot lie below L;
-//  3. the whole output row is written as -inf right away (it does not depend
-//     on the data), so these stores drain while the block works on;
-//  4. every element >= L is appended to a shared-memory candidate list with a
-//     wave ballot;
-//  5. the exact selection (row_select.h) runs on the candidates only;
-//  6. after the -inf stores have completed, the survivors are written over
-//     them from the candidate list.
-// Whenever a bound cannot be formed (k > 2048, top-p mass not reached) or the
-// candidates overflow the list, the block falls back to the multi-pass plan,
-// which rewrites the whole row; the same thread writes the same addresses in
-// the same order, so the earlier -inf stores are overwritten.
+//  2. the whole output row is written as -inf (it does not depend on the
+//     data), so these stores drain while the block works on in registers
+//     and shared memory only (a vector load or a register spill now would
+//     wait for them: vector memory operations complete in order);
+//  3-4. the 2048 per-thread maxima are actual row elements, so the k-th
+//     largest of them bounds the top-k threshold from below; for top-p-only
+//     rows the bound is where the mass of those maxima, walked from the top,
+//     reaches (1 - t) * Z, so every element above it carries at least that
+//     mass and the top-p boundary cannot lie below it. One 1024-bin
+//     histogram pass gives the bound L as a bin edge;
+//  5. every vector whose maximum is >= L is copied into its wave's region of
+//     shared memory, placed by a wave ballot (no atomics);
+//  6. the exact selection (row_select.h) runs on the elements >= L of those
+//     vectors only;
+//  7. after the -inf stores have completed, the survivors are written over
+//     them.
+// Whenever a bound cannot be formed (k > 2048, top-p mass not reached) or a
+// wave's region overflows, the block falls back to the multi-pass plan, which
+// rewrites the whole row; the same thread writes the same addresses in the
+// same order, so the earlier -inf stores are overwritten.
 //
 // Multi-pass plan: the selection of row_select.h over every element of the
-// row, re-read from global memory on each traversal (one per radix digit),
-// then one coalesced write. Only the candidate plan's three traversals run
-// over the register tile, which keeps the unrolled code small.
+// row, re-read from global memory on each traversal, then one coalesced
+// write. Only the candidate plan's traversals run over the register tile,
+// which keeps the unrolled code small.
 
 #pragma once
 
@@ -42,54 +46,93 @@
 
 namespace tkp {
 
-constexpr int kCandCap = 8192;
 constexpr int kTop2 = 2 * kThreads;
 constexpr int kMaxVecs = 20;
+constexpr int kCandVecCap = 2048;  // candidate vectors kept in shared memory
 
-// (raw, index) items held in shared memory.
+// When the -inf stores of a register tile are issued, as cumulative shares (in
+// percent) of its vector slots: while the row arrives, then before the row
+// statistics, the bound, the compaction and the selection. A wave cannot run
+// ahead of its stores once the memory pipeline is full, so the stores are
+// spread over the steps that follow the loads instead of issued at once;
+// they then drain while those steps run.
+constexpr int kStoreShare[5] = {0, 0, 0, 40, 100};
+template <int NV, int STAGE>
+constexpr int store_upto() {
+  return (NV * kStoreShare[STAGE] + 99) / 100;
+}
+
+// (raw, index) items held in shared memory; index unused (reads as 0).
 template <class DT>
-struct LdsItems {
+struct LdsValues {
   using raw_t = typename DT::raw_t;
   const uint32_t* raw;
-  const uint32_t* idx;  // may be null: every index reads as 0
   int n;
   template <class F>
   __device__ __forceinline__ void for_each(F&& f) const {
-    for (int c = threadIdx.x; c < n; c += kThreads)
-      f(static_cast<raw_t>(raw[c]), idx != nullptr ? static_cast<int>(idx[c]) : 0);
+    for (int c = threadIdx.x; c < n; c += kThreads) f(static_cast<raw_t>(raw[c]), 0);
   }
 };
 
-__device__ __forceinline__ double block_sum_f64(double v, RowSmem& sm, double* red) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  const int w = threadIdx.x / kWave;
-  if ((threadIdx.x & (kWave - 1)) == 0) red[w] = v;
+struct ApplySmem {
+  RowSmem row;
+  SelSmem sel;
+  double redd[kWaves];
+  uint32_t top2[kTop2];
+  float run[kThreads];  // per-thread running max and rescaled exp sum (top-p-only rows)
+  float acc[kThreads];
+  uint32_t vmw[(kMaxVecs + 1) / 2][kThreads];  // per-vector maxima (16-bit bounds, two per word)
+  vec_t cvec[kCandVecCap];
+  uint32_t ce0[kCandVecCap];
+  uint32_t nvec;  // candidate vectors reserved so far
+};
+
+// Elements >= Lf of the candidate vectors (every element >= Lf of the row lies
+// in one of them).
+template <class DT>
+struct CandVecs {
+  using raw_t = typename DT::raw_t;
+  static constexpr int kPV = DT::kPerVec;
+  static constexpr int kShift = kPV == 8 ? 3 : 2;
+  const ApplySmem* S;
+  int nvec;
+  int V;
+  float Lf;
+  template <class F>
+  __device__ __forceinline__ void for_each(F&& f) const {
+    const uint32_t* words = reinterpret_cast<const uint32_t*>(S->cvec);
+    const int n = nvec << kShift;
+    for (int q = threadIdx.x; q < n; q += kThreads) {
+      const int vi = q >> kShift, j = q & (kPV - 1);
+      raw_t raw;
+      if constexpr (sizeof(raw_t) == 4) {
+        raw = words[(vi << 2) + j];
+      } else {
+        raw = static_cast<raw_t>(words[(vi << 2) + (j >> 1)] >> ((j & 1) * 16));
+      }
+      const int idx = static_cast<int>(S->ce0[vi]) + j;
+      if (idx < V && DT::value(raw) >= Lf) f(raw, idx);
+    }
+  }
+};
+
+__device__ __forceinline__ double block_sum_f64(double v, double* red) {
+  v = wave_sum_f64(v);
+  const int l = threadIdx.x & (kWave - 1);
+  if (l == 0) red[threadIdx.x / kWave] = v;
   __syncthreads();
-  double r = 0.0;
-#pragma unroll
-  for (int i = 0; i < kWaves; ++i) r += red[i];
+  const double r = wave_sum_f64(l < kWaves ? red[l] : 0.0);
   __syncthreads();
-  (void)sm;
   return r;
 }
 
-struct ApplySmem {
-  RowSmem row;
-  double redd[kWaves];
-  uint32_t top2[kTop2];
-  uint32_t cand_raw[kCandCap];
-  uint32_t cand_idx[kCandCap];
-  int ncand;
-};
-
 // Multi-pass plan over any tile, then one write of the whole row.
 template <class DT, class Tile>
-__device__ __forceinline__ void filter_multipass(const Tile& tile, const RowParams& rp, RowSmem& sm,
-                                 typename DT::raw_t* __restrict__ orow) {
+__device__ __forceinline__ void filter_multipass(const Tile& tile, const RowParams& rp, int V, ApplySmem& S,
+                                                 typename DT::raw_t* __restrict__ orow) {
   using raw_t = typename DT::raw_t;
   uint32_t K, I;
-  solve_row<DT>(tile, rp, sm, K, I);
+  solve_row<DT>(tile, rp, V, S.row, S.sel, K, I);
   tile.store(orow, [K, I](raw_t r, int idx) {
     const uint32_t key = DT::key(r);
     return (key > K || (key == K && static_cast<uint32_t>(idx) >= I)) ? r : DT::kNegInf;
@@ -105,6 +148,7 @@ __device__ __forceinline__ void filter_row(const Tile& tile, const typename DT::
   using raw_t = typename DT::raw_t;
   constexpr int kPV = DT::kPerVec;
   RowSmem& sm = S.row;
+  SelSmem& ss = S.sel;
   GlobalTile<DT> gt;
   gt.load(irow, 0, V);
 
@@ -113,7 +157,7 @@ __device__ __forceinline__ void filter_row(const Tile& tile, const typename DT::
     return;
   }
   if (!use_candidates) {
-    filter_multipass<DT>(gt, rp, sm, orow);
+    filter_multipass<DT>(gt, rp, V, S, orow);
     return;
   }
 
@@ -121,11 +165,29 @@ __device__ __forceinline__ void filter_row(const Tile& tile, const typename DT::
   const bool ponly = rp.pmode == kPBoundary && !rp.k_on;
   constexpr float kLog2e = 1.4426950408889634f;
   float M1 = -INFINITY, M2 = -INFINITY;  // two largest vector maxima of this thread
-  float run = -INFINITY, acc = 0.0f;     // acc = sum of exp(x - run), ponly rows
-  tile.for_each_vec_values([&](const float (&x)[kPV]) {
+  float run = -INFINITY, acc = 0.0f;     // acc = sum of exp(x - run), top-p-only rows
+  // 16-bit upper bounds of each register vector's maximum go to shared
+  // memory, two per word, so the compaction below need not revisit the data
+  uint32_t vm_even = 0;
+  tile.for_each_vec_values([&](int i, const float (&x)[kPV]) {
+    // the -inf store of this slot goes out as soon as its data is in (the
+    // output does not depend on it): stores then drain alongside the loads
+    // still in flight, and waits for later loads do not wait for them
+    if constexpr (Tile::kRegisters) {
+      if (i < store_upto<Tile::kVecs, 0>()) tile.store_const_slot(orow, i, DT::kNegInf);
+    }
     float vm = x[0];
 #pragma unroll
     for (int j = 1; j < kPV; ++j) vm = fmaxf(vm, x[j]);
+    if constexpr (Tile::kRegisters) {
+      const uint32_t h = DT::ub16(vm);
+      if ((i & 1) == 0) {
+        vm_even = h;
+        if (i == Tile::kVecs - 1) S.vmw[i >> 1][threadIdx.x] = h;
+      } else {
+        S.vmw[i >> 1][threadIdx.x] = vm_even | (h << 16);
+      }
+    }
     M2 = fmaxf(M2, fminf(M1, vm));
     M1 = fmaxf(M1, vm);
     if (ponly) {
@@ -145,128 +207,180 @@ __device__ __forceinline__ void filter_row(const Tile& tile, const typename DT::
     }
   });
 
-  // 2. row maximum, per-thread maxima to shared memory, Z for top-p-only rows
-  const float m = block_max_f32(M1, sm);
+  // The per-thread statistics go to shared memory, so no vector register
+  // holds them across the stores below.
   S.top2[2 * threadIdx.x] = DT::raw_of_value(M1);
   S.top2[2 * threadIdx.x + 1] = DT::raw_of_value(M2);
+  S.run[threadIdx.x] = run;
+  S.acc[threadIdx.x] = acc;
+  if (threadIdx.x == 0) S.nvec = 0;  // read after the barriers of step 3
+
+  // 2. the whole row as -inf (register tiles stored theirs in step 1). From
+  // here until the survivors are written the block touches only registers
+  // and shared memory, so nothing waits behind these stores while they drain.
+  if constexpr (!Tile::kRegisters) tile.store_const(orow, DT::kNegInf);
+
+  if constexpr (Tile::kRegisters)
+    tile.template store_const_range<store_upto<Tile::kVecs, 0>(), store_upto<Tile::kVecs, 1>()>(orow, DT::kNegInf);
+  // 3. row maximum, smallest finite per-thread maximum, Z for top-p-only rows
+  const float M1s = DT::value(static_cast<raw_t>(S.top2[2 * threadIdx.x]));
+  const float M2s = DT::value(static_cast<raw_t>(S.top2[2 * threadIdx.x + 1]));
+  uint32_t klo = 0xFFFFFFFFu;  // smallest key among finite maxima
+  if (M1s > -INFINITY) klo = DT::key(DT::raw_of_value(M1s));
+  if (M2s > -INFINITY) klo = DT::key(DT::raw_of_value(M2s));
+  float m;
+  block_max_f32_min_u32(M1s, klo, sm, m, klo);
+  const uint32_t kmax = DT::key(DT::raw_of_value(m));
   uint64_t thr = 0;
   if (ponly) {
-    const double zt =
-        (run > -INFINITY) ? static_cast<double>(acc) * static_cast<double>(__builtin_amdgcn_exp2f((run - m) * kLog2e))
-                          : 0.0;
-    const double Z = block_sum_f64(zt, sm, S.redd);  // >= 1: the maximum contributes exp(0)
-    const uint64_t Zfx = static_cast<uint64_t>(Z * 8796093022208.0);  // 2^43
-    thr = topp_threshold(rp.t, Zfx);
+    const float r = S.run[threadIdx.x];
+    const double zt = (r > -INFINITY) ? static_cast<double>(S.acc[threadIdx.x]) *
+                                            static_cast<double>(__builtin_amdgcn_exp2f((r - m) * kLog2e))
+                                      : 0.0;
+    const double Z = block_sum_f64(zt, S.redd);  // >= 1: the maximum contributes exp(0)
+    thr = topp_threshold(rp.t, static_cast<uint64_t>(Z * 8796093022208.0));  // Z * 2^43
   }
-  __syncthreads();
 
-  // 3. candidate bound L
-  const LdsItems<DT> top2{S.top2, nullptr, kTop2};
+  if constexpr (Tile::kRegisters)
+    tile.template store_const_range<store_upto<Tile::kVecs, 1>(), store_upto<Tile::kVecs, 2>()>(orow, DT::kNegInf);
+  // 4. candidate bound L
+  const LdsValues<DT> top2{S.top2, kTop2};
   const bool top_only = rp.pmode == kPTopOnly || (ponly && thr == 0);
-  uint32_t L = 0;
-  bool fast = true;
+  uint32_t L = kmax;
+  bool fast = klo <= kmax;
   if (rp.k_on) {
-    fast = rp.k <= static_cast<uint32_t>(kTop2);
-    if (fast)
-      L = radix_select_desc(
-          top2, DT::kKeyBits, rp.k, [](auto raw, int) { return DT::key(raw); }, [](auto, int) { return true; },
-          sm);
-  } else if (top_only) {
-    L = DT::key(DT::raw_of_value(m));
-  } else {
-    uint64_t mt = 0;
-    top2.for_each([&](auto raw, int) { mt += mass_fx(DT::value(raw), m); });
-    mt = block_sum_u64(mt, sm);
-    fast = mt >= thr;
-    if (fast) {
-      uint32_t Kb, Ib;
-      topp_boundary<DT>(top2, 0u, m, thr, sm, Kb, Ib, false);
-      L = Kb;
-    }
+    fast = fast && rp.k <= static_cast<uint32_t>(kTop2) &&
+           kth_largest_bound(top2, rp.k, klo, kmax, [](auto raw, int) { return DT::key(raw); }, ss, L);
+  } else if (!top_only) {
+    fast = fast && topp_bound<DT>(top2, klo, kmax, m, thr, ss, L);
   }
-  if (!fast) {
-    filter_multipass<DT>(gt, rp, sm, orow);
-    return;
-  }
+  // Fallbacks are taken at the very end, after the candidate plan's code:
+  // keeping the multi-pass plan's global loads out of the paths above keeps
+  // the compiler from waiting on the -inf stores before they are needed.
+  bool fallback = !fast;
 
-  // 4. the whole row as -inf; these stores drain while the block continues
-  tile.store(orow, [](raw_t, int) { return DT::kNegInf; });
-
-  // 5. candidates: every element >= L (compared as values: -0.0 == +0.0)
-  if (threadIdx.x == 0) S.ncand = 0;
-  __syncthreads();
+  if constexpr (Tile::kRegisters)
+    tile.template store_const_range<store_upto<Tile::kVecs, 2>(), store_upto<Tile::kVecs, 3>()>(orow, DT::kNegInf);
+  // 5. candidate vectors: every vector whose maximum is >= L, packed into one
+  // list placed by wave ballots (the list order does not matter: every
+  // statistic taken from it below is order-independent)
   const float Lf = DT::value(DT::raw_of_key(L));
-  const int lane = threadIdx.x & (kWave - 1);
-  tile.for_each([&](raw_t raw, int idx) {
-    const bool c = DT::value(raw) >= Lf;
-    const uint64_t mask = __ballot(c);
-    if (mask != 0) {
-      const int leader = __ffsll(static_cast<unsigned long long>(mask)) - 1;
-      int base = 0;
-      if (lane == leader) base = atomicAdd(&S.ncand, __popcll(mask));
-      base = __shfl(base, leader);
-      if (c) {
-        const int pos = base + __popcll(mask & ((1ull << lane) - 1ull));
-        if (pos < kCandCap) {
-          S.cand_raw[pos] = raw;
-          S.cand_idx[pos] = static_cast<uint32_t>(idx);
-        }
+  uint32_t nvec = 0;
+  if (!fallback) {
+    const uint64_t below = (1ull << (threadIdx.x & (kWave - 1))) - 1ull;
+    auto is_cand = [&](int i, int e0) {
+      float vmv;
+      if constexpr (Tile::kRegisters) {
+        vmv = DT::ub16_value((S.vmw[i >> 1][threadIdx.x] >> ((i & 1) * 16)) & 0xFFFFu);
+      } else {
+        const vec_t q = tile.vec_at(i, e0);
+        vmv = -INFINITY;
+  #pragma unroll
+        for (int j = 0; j < kPV; ++j)
+          if (e0 + j < V) vmv = fmaxf(vmv, DT::value(lane_of<raw_t>(q, j)));
       }
+      return vmv >= Lf;
+    };
+    const uint64_t lane_bit = 1ull << (threadIdx.x & (kWave - 1));
+    if constexpr (Tile::kRegisters) {
+      // one pass over the register slots: each slot's ballot is kept (uniform,
+      // so in scalar registers); one shared-memory atomic per wave reserves the
+      // wave's run of the list
+      uint64_t masks[Tile::kVecs];
+      uint32_t wtotal = 0;
+      tile.for_each_slot([&](int i, int e0) {
+        masks[i] = __ballot(is_cand(i, e0));
+        wtotal += static_cast<uint32_t>(__popcll(masks[i]));
+      });
+      uint32_t pos0 = 0;
+      if ((threadIdx.x & (kWave - 1)) == 0) pos0 = atomicAdd(&S.nvec, wtotal);
+      pos0 = __builtin_amdgcn_readfirstlane(pos0);
+      tile.for_each_slot([&](int i, int e0) {
+        if (masks[i] & lane_bit) {
+          const uint32_t pos = pos0 + static_cast<uint32_t>(__popcll(masks[i] & below));
+          if (pos < static_cast<uint32_t>(kCandVecCap)) {
+            S.cvec[pos] = tile.vec_at(i, e0);
+            S.ce0[pos] = static_cast<uint32_t>(e0);
+          }
+        }
+        pos0 += static_cast<uint32_t>(__popcll(masks[i]));
+      });
+    } else {
+      // streamed rows: one atomic per wave for each slot holding candidates
+      tile.for_each_slot([&](int i, int e0) {
+        const bool c = is_cand(i, e0);
+        const uint64_t mask = __ballot(c);
+        if (mask != 0) {
+          uint32_t pos0 = 0;
+          if ((threadIdx.x & (kWave - 1)) == 0) pos0 = atomicAdd(&S.nvec, static_cast<uint32_t>(__popcll(mask)));
+          pos0 = __builtin_amdgcn_readfirstlane(pos0);
+          if (c) {
+            const uint32_t pos = pos0 + static_cast<uint32_t>(__popcll(mask & below));
+            if (pos < static_cast<uint32_t>(kCandVecCap)) {
+              S.cvec[pos] = tile.vec_at(i, e0);
+              S.ce0[pos] = static_cast<uint32_t>(e0);
+            }
+          }
+        }
+      });
     }
-  });
-  __syncthreads();
-  const int n = S.ncand;
-  if (n > kCandCap) {
-    filter_multipass<DT>(gt, rp, sm, orow);
-    return;
+    __syncthreads();
+    nvec = S.nvec;
+    fallback = nvec > static_cast<uint32_t>(kCandVecCap);
+
   }
 
-  // 6. exact selection on the candidates
-  const LdsItems<DT> cs{S.cand_raw, S.cand_idx, n};
+  if constexpr (Tile::kRegisters)
+    tile.template store_const_range<store_upto<Tile::kVecs, 3>(), store_upto<Tile::kVecs, 4>()>(orow, DT::kNegInf);
+  // 6. exact selection on the candidates (all elements with key in [L, kmax])
+  const CandVecs<DT> cs{&S, static_cast<int>(nvec), V, Lf};
   uint32_t K = 0, I = 0;
-  if (top_only && !rp.k_on) {
-    top_position<DT>(cs, sm, K, I);
-  } else {
-    uint32_t Kk = 0;
-    if (rp.k_on)
-      Kk = radix_select_desc(
-          cs, DT::kKeyBits, rp.k, [](auto raw, int) { return DT::key(raw); }, [](auto, int) { return true; }, sm);
-    if (rp.pmode == kPNone) {
-      K = Kk;
-    } else if (rp.pmode == kPTopOnly) {
+  if (!fallback) {
+    if (top_only && !rp.k_on) {
       top_position<DT>(cs, sm, K, I);
-    } else if (rp.k_on) {
-      uint64_t z = 0;
-      cs.for_each([&](auto raw, int) {
-        if (DT::key(raw) >= Kk) z += mass_fx(DT::value(raw), m);
-      });
-      const uint64_t Z = block_sum_u64(z, sm);
-      const uint64_t thr2 = topp_threshold(rp.t, Z);
-      if (thr2 == 0)
-        top_position<DT>(cs, sm, K, I);
-      else
-        topp_boundary<DT>(cs, Kk, m, thr2, sm, K, I);
     } else {
-      uint64_t a = 0;
-      cs.for_each([&](auto raw, int) { a += mass_fx(DT::value(raw), m); });
-      const uint64_t A = block_sum_u64(a, sm);
-      if (A < thr) {  // the boundary lies below the candidates
-        filter_multipass<DT>(gt, rp, sm, orow);
-        return;
+      uint32_t Kk = L;
+      if (rp.k_on)
+        Kk = kth_largest_key(
+            cs, rp.k, L, kmax, [](auto raw, int) { return DT::key(raw); }, [](auto, int) { return true; }, ss);
+      if (rp.pmode == kPNone) {
+        K = Kk;
+      } else if (rp.pmode == kPTopOnly) {
+        top_position<DT>(cs, sm, K, I);
+      } else if (rp.k_on) {
+        uint64_t z = 0;
+        cs.for_each([&](auto raw, int) {
+          if (DT::key(raw) >= Kk) z += mass_fx(DT::value(raw), m);
+        });
+        const uint64_t Z = block_sum_u64(z, sm);
+        const uint64_t thr2 = topp_threshold(rp.t, Z);
+        if (thr2 == 0)
+          top_position<DT>(cs, sm, K, I);
+        else
+          topp_boundary<DT>(cs, Kk, kmax, m, thr2, V, ss, K, I);
+      } else {
+        uint64_t a = 0;
+        cs.for_each([&](auto raw, int) { a += mass_fx(DT::value(raw), m); });
+        const uint64_t A = block_sum_u64(a, sm);
+        if (A < thr)  // the boundary lies below the candidates
+          fallback = true;
+        else
+          topp_boundary<DT>(cs, L, kmax, m, thr, V, ss, K, I);
       }
-      topp_boundary<DT>(cs, 0u, m, thr, sm, K, I);
     }
   }
 
   // 7. survivors over the -inf row, once every -inf store has completed
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  for (int c = threadIdx.x; c < n; c += kThreads) {
-    const raw_t raw = static_cast<raw_t>(S.cand_raw[c]);
-    const uint32_t idx = S.cand_idx[c];
-    const uint32_t key = DT::key(raw);
-    if (key > K || (key == K && idx >= I)) orow[idx] = raw;
+  if (!fallback) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    cs.for_each([&](auto raw, int idx) {
+      const uint32_t key = DT::key(raw);
+      if (key > K || (key == K && static_cast<uint32_t>(idx) >= I)) orow[idx] = raw;
+    });
+  } else {
+    filter_multipass<DT>(gt, rp, V, S, orow);
   }
 }
 
@@ -279,9 +393,11 @@ __global__ __launch_bounds__(kThreads) void apply_regs_kernel(const typename DT:
   __shared__ ApplySmem S;
   const int b = blockIdx.x;
   const size_t off = static_cast<size_t>(b) * V;
+  // p[b] and k[b] are fetched before the row and used after it is requested
+  const RowParamsRaw<DT> rpr = fetch_row_params<DT>(p, k, b);
   RegTile<DT, NVEC> tile;
   tile.load(logits + off, 0, V);
-  const RowParams rp = decode_row_params<DT>(p, k, b, V);
+  const RowParams rp = decode_row_params<DT>(rpr, V);
   filter_row<DT>(tile, logits + off, V, rp, use_candidates != 0, S, out + off);
 }
 
@@ -294,15 +410,15 @@ __global__ __launch_bounds__(kThreads) void apply_stream_kernel(const typename D
   __shared__ ApplySmem S;
   const int b = blockIdx.x;
   const size_t off = static_cast<size_t>(b) * V;
+  const RowParams rp = decode_row_params<DT>(p, k, b, V);
   GlobalTile<DT> tile;
   tile.load(logits + off, 0, V);
-  const RowParams rp = decode_row_params<DT>(p, k, b, V);
   filter_row<DT>(tile, logits + off, V, rp, use_candidates != 0, S, out + off);
 }
 
 template <class DT, int NVEC>
 void launch_regs(const void* logits, const void* p, const int32_t* k, void* out, int64_t B, int64_t V,
-                        int use_candidates, hipStream_t stream) {
+                 int use_candidates, hipStream_t stream) {
   using raw_t = typename DT::raw_t;
   hipLaunchKernelGGL((apply_regs_kernel<DT, NVEC>), dim3(static_cast<unsigned>(B)), dim3(kThreads), 0, stream,
                      static_cast<const raw_t*>(logits), static_cast<const raw_t*>(p), k, static_cast<raw_t*>(out),
@@ -310,13 +426,16 @@ void launch_regs(const void* logits, const void* p, const int32_t* k, void* out,
 }
 
 template <class DT>
-hipError_t launch_apply_t(const void* logits, const void* p, const int32_t* k, void* out, int64_t B,
-                                 int64_t V, int policy, hipStream_t stream) {
+hipError_t launch_apply_t(const void* logits, const void* p, const int32_t* k, void* out, int64_t B, int64_t V,
+                          int policy, hipStream_t stream) {
   using raw_t = typename DT::raw_t;
   constexpr int span = kThreads * DT::kPerVec;
   const int64_t vecs = (V + span - 1) / span;
   const int use_candidates = policy == kPlanGeneral ? 0 : 1;
-  if (policy != kPlanAuto || vecs > kMaxVecs) {
+  // register tiles move whole 16-byte vectors: rows must start 16-byte aligned
+  const bool vec_ok = (V % DT::kPerVec) == 0 && (reinterpret_cast<uintptr_t>(logits) & 15u) == 0 &&
+                      (reinterpret_cast<uintptr_t>(out) & 15u) == 0;
+  if (policy != kPlanAuto || vecs > kMaxVecs || !vec_ok) {
     hipLaunchKernelGGL(apply_stream_kernel<DT>, dim3(static_cast<unsigned>(B)), dim3(kThreads), 0, stream,
                        static_cast<const raw_t*>(logits), static_cast<const raw_t*>(p), k, static_cast<raw_t*>(out),
                        static_cast<int>(V), use_candidates);

@@ -40,6 +40,13 @@ struct F32T {
   __device__ static __forceinline__ raw_t raw_of_key(uint32_t K) { return (K & 0x80000000u) ? (K & 0x7FFFFFFFu) : ~K; }
   // bits of a value known to be representable in this dtype
   __device__ static __forceinline__ raw_t raw_of_value(float f) { return __float_as_uint(f); }
+  // 16-bit upper bound of a value (bf16 rounded toward +inf) and its value
+  __device__ static __forceinline__ uint32_t ub16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0xFFFFu) != 0u && (u & 0x80000000u) == 0u) u += 0x10000u;
+    return u >> 16;
+  }
+  __device__ static __forceinline__ float ub16_value(uint32_t h) { return __uint_as_float(h << 16); }
 };
 
 struct F16T {
@@ -60,6 +67,9 @@ struct F16T {
   __device__ static __forceinline__ raw_t raw_of_value(float f) {
     return __builtin_bit_cast(raw_t, static_cast<_Float16>(f));
   }
+  // values are fp16 already: the 16-bit form is exact
+  __device__ static __forceinline__ uint32_t ub16(float f) { return raw_of_value(f); }
+  __device__ static __forceinline__ float ub16_value(uint32_t h) { return value(static_cast<raw_t>(h)); }
 };
 
 struct BF16T {
@@ -76,6 +86,8 @@ struct BF16T {
     return static_cast<raw_t>((K & 0x8000u) ? (K & 0x7FFFu) : (~K & 0xFFFFu));
   }
   __device__ static __forceinline__ raw_t raw_of_value(float f) { return static_cast<raw_t>(__float_as_uint(f) >> 16); }
+  __device__ static __forceinline__ uint32_t ub16(float f) { return raw_of_value(f); }
+  __device__ static __forceinline__ float ub16_value(uint32_t h) { return value(static_cast<raw_t>(h)); }
 };
 
 // exp(x - m) as 43-bit fixed point, for x <= m. Uses the hardware exp2; the
@@ -92,176 +104,196 @@ __device__ __forceinline__ uint64_t mass_fx(float x, float m) {
 }
 
 // ------------------------------------------------------------- reductions ---
+// Wave-wide reductions and scans with DPP lane moves (gfx9 encodings), which
+// stay in the VALU instead of going through the LDS crossbar:
+//   quad_perm [1,0,3,2] and [2,3,0,1] combine within quads, row_half_mirror and
+//   row_mirror within 8 and 16 lanes, row_shr:n shifts within a 16-lane row,
+//   row_bcast:15 / row_bcast:31 carry a row's last lane into the following
+//   rows. Lanes a move does not write (row_mask) or whose source is outside the
+//   row receive `old`, which is always the operation's identity here.
+
+namespace dpp {
+constexpr int kQuad1032 = 0xB1;
+constexpr int kQuad2301 = 0x4E;
+constexpr int kRowMirror = 0x140;
+constexpr int kRowHalfMirror = 0x141;
+constexpr int kRowBcast15 = 0x142;
+constexpr int kRowBcast31 = 0x143;
+constexpr int kRowShr1 = 0x111;
+constexpr int kRowShr2 = 0x112;
+constexpr int kRowShr4 = 0x114;
+constexpr int kRowShr8 = 0x118;
+}  // namespace dpp
+
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v, uint32_t old) {
+  return static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(static_cast<int>(old), static_cast<int>(v), CTRL, ROW_MASK, 0xF, false));
+}
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v, uint64_t old) {
+  const uint32_t lo = dpp_u32<CTRL, ROW_MASK>(static_cast<uint32_t>(v), static_cast<uint32_t>(old));
+  const uint32_t hi = dpp_u32<CTRL, ROW_MASK>(static_cast<uint32_t>(v >> 32), static_cast<uint32_t>(old >> 32));
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+__device__ __forceinline__ uint32_t lane63_u32(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 63));
+}
+__device__ __forceinline__ uint64_t lane63_u64(uint64_t v) {
+  return (static_cast<uint64_t>(lane63_u32(static_cast<uint32_t>(v >> 32))) << 32) |
+         lane63_u32(static_cast<uint32_t>(v));
+}
+
+// Reduction of v over the wave with a commutative, associative op and its
+// identity; the result is uniform (every lane gets it).
+template <class Op>
+__device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v, uint32_t id, Op op) {
+  v = op(v, dpp_u32<dpp::kQuad1032>(v, id));
+  v = op(v, dpp_u32<dpp::kQuad2301>(v, id));
+  v = op(v, dpp_u32<dpp::kRowHalfMirror>(v, id));
+  v = op(v, dpp_u32<dpp::kRowMirror>(v, id));
+  v = op(v, dpp_u32<dpp::kRowBcast15, 0xA>(v, id));
+  v = op(v, dpp_u32<dpp::kRowBcast31, 0x8>(v, id));
+  return lane63_u32(v);
+}
+template <class Op>
+__device__ __forceinline__ uint64_t wave_reduce_u64(uint64_t v, uint64_t id, Op op) {
+  v = op(v, dpp_u64<dpp::kQuad1032>(v, id));
+  v = op(v, dpp_u64<dpp::kQuad2301>(v, id));
+  v = op(v, dpp_u64<dpp::kRowHalfMirror>(v, id));
+  v = op(v, dpp_u64<dpp::kRowMirror>(v, id));
+  v = op(v, dpp_u64<dpp::kRowBcast15, 0xA>(v, id));
+  v = op(v, dpp_u64<dpp::kRowBcast31, 0x8>(v, id));
+  return lane63_u64(v);
+}
+
+// Inclusive prefix sums over the lanes of a wave.
+__device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t v) {
+  v += dpp_u32<dpp::kRowShr1>(v, 0u);
+  v += dpp_u32<dpp::kRowShr2>(v, 0u);
+  v += dpp_u32<dpp::kRowShr4>(v, 0u);
+  v += dpp_u32<dpp::kRowShr8>(v, 0u);
+  v += dpp_u32<dpp::kRowBcast15, 0xA>(v, 0u);
+  v += dpp_u32<dpp::kRowBcast31, 0xC>(v, 0u);
+  return v;
+}
+__device__ __forceinline__ uint64_t wave_incl_scan_u64(uint64_t v) {
+  v += dpp_u64<dpp::kRowShr1>(v, 0ull);
+  v += dpp_u64<dpp::kRowShr2>(v, 0ull);
+  v += dpp_u64<dpp::kRowShr4>(v, 0ull);
+  v += dpp_u64<dpp::kRowShr8>(v, 0ull);
+  v += dpp_u64<dpp::kRowBcast15, 0xA>(v, 0ull);
+  v += dpp_u64<dpp::kRowBcast31, 0xC>(v, 0ull);
+  return v;
+}
 
 __device__ __forceinline__ float wave_max_f32(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
+  const uint32_t r = wave_reduce_u32(__float_as_uint(v), __float_as_uint(-INFINITY), [](uint32_t a, uint32_t b) {
+    return __float_as_uint(fmaxf(__uint_as_float(a), __uint_as_float(b)));
+  });
+  return __uint_as_float(r);
 }
 
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    uint32_t w = __shfl_xor(v, o);
-    v = v > w ? v : w;
-  }
-  return v;
+  return wave_reduce_u32(v, 0u, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
+}
+
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  return wave_reduce_u32(v, 0xFFFFFFFFu, [](uint32_t a, uint32_t b) { return a < b ? a : b; });
 }
 
 __device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  return wave_reduce_u64(v, 0ull, [](uint64_t a, uint64_t b) { return a + b; });
 }
 
 __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  return wave_reduce_u32(v, 0u, [](uint32_t a, uint32_t b) { return a + b; });
 }
 
-// Shared-memory workspace of one row-block.
+__device__ __forceinline__ double wave_sum_f64(double v) {
+  const uint64_t r = wave_reduce_u64(__builtin_bit_cast(uint64_t, v), 0ull, [](uint64_t a, uint64_t b) {
+    return __builtin_bit_cast(uint64_t, __builtin_bit_cast(double, a) + __builtin_bit_cast(double, b));
+  });
+  return __builtin_bit_cast(double, r);
+}
+
+// Shared-memory workspace for block reductions and broadcasts.
 struct RowSmem {
-  uint32_t hist[256];   // digit counts
-  uint64_t mhist[256];  // digit mass (fixed point)
   float redf[kWaves];
   uint64_t redu[kWaves];
   uint32_t redw[kWaves];
-  // result of a bin search, broadcast to the block
-  int sel_bin;
-  uint32_t sel_above;    // count strictly above the selected bin
-  uint64_t sel_above64;  // mass strictly above the selected bin
-  uint32_t sel_cnt;      // count in the selected bin
-  uint64_t sel_mass;     // mass in the selected bin
-  uint32_t bcast[4];
 };
+
+// Block-wide reductions: one DPP reduction per wave, the 16 wave results
+// through shared memory, and a second DPP reduction in which lane i holds
+// wave i's result (lanes >= 16 hold the identity). Every thread gets the
+// result. Two barriers, the second one so the slots can be reused.
 
 __device__ __forceinline__ float block_max_f32(float v, RowSmem& sm) {
   v = wave_max_f32(v);
-  const int w = threadIdx.x / kWave;
-  if ((threadIdx.x & (kWave - 1)) == 0) sm.redf[w] = v;
+  const int l = threadIdx.x & (kWave - 1);
+  if (l == 0) sm.redf[threadIdx.x / kWave] = v;
   __syncthreads();
-  float r = sm.redf[0];
-#pragma unroll
-  for (int i = 1; i < kWaves; ++i) r = fmaxf(r, sm.redf[i]);
+  const float r = wave_max_f32(l < kWaves ? sm.redf[l] : -INFINITY);
   __syncthreads();
   return r;
 }
 
 __device__ __forceinline__ uint32_t block_max_u32(uint32_t v, RowSmem& sm) {
   v = wave_max_u32(v);
-  const int w = threadIdx.x / kWave;
-  if ((threadIdx.x & (kWave - 1)) == 0) sm.redw[w] = v;
+  const int l = threadIdx.x & (kWave - 1);
+  if (l == 0) sm.redw[threadIdx.x / kWave] = v;
   __syncthreads();
-  uint32_t r = sm.redw[0];
-#pragma unroll
-  for (int i = 1; i < kWaves; ++i) r = r > sm.redw[i] ? r : sm.redw[i];
+  const uint32_t r = wave_max_u32(l < kWaves ? sm.redw[l] : 0u);
   __syncthreads();
   return r;
 }
 
+__device__ __forceinline__ uint32_t block_min_u32(uint32_t v, RowSmem& sm) {
+  v = wave_min_u32(v);
+  const int l = threadIdx.x & (kWave - 1);
+  if (l == 0) sm.redw[threadIdx.x / kWave] = v;
+  __syncthreads();
+  const uint32_t r = wave_min_u32(l < kWaves ? sm.redw[l] : 0xFFFFFFFFu);
+  __syncthreads();
+  return r;
+}
+
+// max of a float and min of a u32 in one exchange round
+__device__ __forceinline__ void block_max_f32_min_u32(float a, uint32_t b, RowSmem& sm, float& amax,
+                                                      uint32_t& bmin) {
+  a = wave_max_f32(a);
+  b = wave_min_u32(b);
+  const int l = threadIdx.x & (kWave - 1);
+  if (l == 0) {
+    sm.redf[threadIdx.x / kWave] = a;
+    sm.redw[threadIdx.x / kWave] = b;
+  }
+  __syncthreads();
+  amax = wave_max_f32(l < kWaves ? sm.redf[l] : -INFINITY);
+  bmin = wave_min_u32(l < kWaves ? sm.redw[l] : 0xFFFFFFFFu);
+  __syncthreads();
+}
+
 __device__ __forceinline__ uint64_t block_sum_u64(uint64_t v, RowSmem& sm) {
   v = wave_sum_u64(v);
-  const int w = threadIdx.x / kWave;
-  if ((threadIdx.x & (kWave - 1)) == 0) sm.redu[w] = v;
+  const int l = threadIdx.x & (kWave - 1);
+  if (l == 0) sm.redu[threadIdx.x / kWave] = v;
   __syncthreads();
-  uint64_t r = 0;
-#pragma unroll
-  for (int i = 0; i < kWaves; ++i) r += sm.redu[i];
+  const uint64_t r = wave_sum_u64(l < kWaves ? sm.redu[l] : 0ull);
   __syncthreads();
   return r;
 }
 
 __device__ __forceinline__ uint32_t block_sum_u32(uint32_t v, RowSmem& sm) {
   v = wave_sum_u32(v);
-  const int w = threadIdx.x / kWave;
-  if ((threadIdx.x & (kWave - 1)) == 0) sm.redw[w] = v;
+  const int l = threadIdx.x & (kWave - 1);
+  if (l == 0) sm.redw[threadIdx.x / kWave] = v;
   __syncthreads();
-  uint32_t r = 0;
-#pragma unroll
-  for (int i = 0; i < kWaves; ++i) r += sm.redw[i];
+  const uint32_t r = wave_sum_u32(l < kWaves ? sm.redw[l] : 0u);
   __syncthreads();
   return r;
-}
-
-// ------------------------------------------------------------ bin search ---
-// Walks the 256 bins from the highest down and selects the first bin whose
-// inclusive running total reaches `target` (target >= 1). Wave 0 does the walk
-// with a wave-wide prefix sum (lane l owns bins 255-4l .. 252-4l); the result
-// lands in sm.sel_* and is visible to the whole block after the call. If the
-// target exceeds the grand total, bin 0 is selected.
-
-__device__ __forceinline__ void select_bin_count(RowSmem& sm, uint32_t target) {
-  if (threadIdx.x < kWave) {
-    const int l = threadIdx.x;
-    const int b0 = 255 - 4 * l;
-    uint32_t c0 = sm.hist[b0], c1 = sm.hist[b0 - 1], c2 = sm.hist[b0 - 2], c3 = sm.hist[b0 - 3];
-    uint32_t tot = c0 + c1 + c2 + c3;
-    uint32_t incl = tot;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      uint32_t n = __shfl_up(incl, o);
-      if (l >= o) incl += n;
-    }
-    uint32_t excl = incl - tot;
-    bool hit = (excl < target && target <= incl) || (l == kWave - 1 && target > incl);
-    if (hit) {
-      uint32_t a = excl;
-      int bin;
-      uint32_t cnt;
-      if (a + c0 >= target) { bin = b0; cnt = c0; }
-      else { a += c0;
-        if (a + c1 >= target) { bin = b0 - 1; cnt = c1; }
-        else { a += c1;
-          if (a + c2 >= target) { bin = b0 - 2; cnt = c2; }
-          else { a += c2; bin = b0 - 3; cnt = c3; } } }
-      sm.sel_bin = bin;
-      sm.sel_above = a;
-      sm.sel_cnt = cnt;
-    }
-  }
-  __syncthreads();
-}
-
-__device__ __forceinline__ void select_bin_mass(RowSmem& sm, uint64_t target) {
-  if (threadIdx.x < kWave) {
-    const int l = threadIdx.x;
-    const int b0 = 255 - 4 * l;
-    uint64_t c0 = sm.mhist[b0], c1 = sm.mhist[b0 - 1], c2 = sm.mhist[b0 - 2], c3 = sm.mhist[b0 - 3];
-    uint64_t tot = c0 + c1 + c2 + c3;
-    uint64_t incl = tot;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      uint64_t n = __shfl_up(incl, o);
-      if (l >= o) incl += n;
-    }
-    uint64_t excl = incl - tot;
-    bool hit = (excl < target && target <= incl) || (l == kWave - 1 && target > incl);
-    if (hit) {
-      uint64_t a = excl;
-      int bin;
-      uint64_t mass;
-      if (a + c0 >= target) { bin = b0; mass = c0; }
-      else { a += c0;
-        if (a + c1 >= target) { bin = b0 - 1; mass = c1; }
-        else { a += c1;
-          if (a + c2 >= target) { bin = b0 - 2; mass = c2; }
-          else { a += c2; bin = b0 - 3; mass = c3; } } }
-      sm.sel_bin = bin;
-      sm.sel_above64 = a;
-      sm.sel_mass = mass;
-      sm.sel_cnt = sm.hist[bin];
-    }
-  }
-  __syncthreads();
-}
-
-__device__ __forceinline__ void clear_hists(RowSmem& sm, bool with_mass) {
-  if (threadIdx.x < 256) {
-    sm.hist[threadIdx.x] = 0;
-    if (with_mass) sm.mhist[threadIdx.x] = 0;
-  }
-  __syncthreads();
 }
 
 // ------------------------------------------------------------- row modes ---
@@ -275,13 +307,35 @@ struct RowParams {
   float t;       // 1 - p in fp32
 };
 
+// The per-row parameters are the same for every thread of the block. They are
+// fetched first (fetch_row_params) and decoded later (decode_row_params), so a
+// kernel can put its row loads in between: vector loads complete in order, and
+// waiting for p[b] and k[b] must not mean waiting for the row. Decoded values
+// live in scalar registers.
 template <class DT>
-__device__ __forceinline__ RowParams decode_row_params(const typename DT::raw_t* p, const int32_t* k, int b, int V) {
+struct RowParamsRaw {
+  int32_t k;
+  typename DT::raw_t p;
+  bool has_k, has_p;
+};
+
+template <class DT>
+__device__ __forceinline__ RowParamsRaw<DT> fetch_row_params(const typename DT::raw_t* p, const int32_t* k, int b) {
+  RowParamsRaw<DT> r;
+  r.has_k = k != nullptr;
+  r.has_p = p != nullptr;
+  r.k = r.has_k ? k[b] : 0;
+  r.p = r.has_p ? p[b] : static_cast<typename DT::raw_t>(0);
+  return r;
+}
+
+template <class DT>
+__device__ __forceinline__ RowParams decode_row_params(const RowParamsRaw<DT>& r, int V) {
   RowParams rp;
   rp.k_on = false;
   rp.k = 0;
-  if (k != nullptr) {
-    int32_t kb = k[b];
+  if (r.has_k) {
+    const int32_t kb = __builtin_amdgcn_readfirstlane(r.k);
     if (kb >= 1 && kb <= V - 1) {
       rp.k_on = true;
       rp.k = static_cast<uint32_t>(kb);
@@ -289,15 +343,20 @@ __device__ __forceinline__ RowParams decode_row_params(const typename DT::raw_t*
   }
   rp.pmode = kPNone;
   rp.t = 0.0f;
-  if (p != nullptr) {
-    float pb = DT::value(p[b]);
-    float t = 1.0f - pb;
+  if (r.has_p) {
+    const float pb = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(DT::value(r.p))));
+    const float t = 1.0f - pb;
     rp.t = t;
     if (t >= 1.0f) rp.pmode = kPTopOnly;
     else if (t > 0.0f) rp.pmode = kPBoundary;
     // t <= 0 (p >= 1) or NaN: no position with positive mass is masked
   }
   return rp;
+}
+
+template <class DT>
+__device__ __forceinline__ RowParams decode_row_params(const typename DT::raw_t* p, const int32_t* k, int b, int V) {
+  return decode_row_params<DT>(fetch_row_params<DT>(p, k, b), V);
 }
 
 // Fixed-point threshold: a position survives top-p iff the mass strictly above

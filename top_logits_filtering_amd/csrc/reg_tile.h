@@ -1,87 +1,166 @@
-// A slice of one row held in registers: NVEC 16-byte vectors per thread.
-// Element e of the slice lives in vector layer e / (1024 * P), thread
-// (e % (1024 * P)) / P, lane e % P, with P elements per vector (4 for fp32, 8
-// for fp16/bf16). Consecutive threads therefore touch consecutive 16-byte
-// chunks, and each layer is one fully coalesced 16 KiB access per block.
-// All loops are unrolled at compile time so the array stays in VGPRs.
+// Row storage for the apply kernels: a slice of one row either held in
+// registers (RegTile, NVEC 16-byte vectors per thread) or re-read from global
+// memory on every traversal (GlobalTile). Both use one layout: element e of
+// the slice lives in vector layer e / (1024 * P), thread (e % (1024 * P)) / P,
+// lane e % P, with P elements per vector (4 for fp32, 8 for fp16/bf16).
+// Consecutive threads touch consecutive 16-byte chunks, so each layer is one
+// fully coalesced 16 KiB access per block, and a thread always writes the
+// output addresses it read.
 #pragma once
 
 #include "device_common.h"
 
 namespace tkp {
 
+using vec_t = uint32_t __attribute__((ext_vector_type(4)));
+
+// Streaming (nontemporal) 16-byte loads of the row: it is read once.
+constexpr bool kNtLoads = true;
+// Output stores: nontemporal as well (measured faster for this kernel: the
+// output is not read again by the kernel, and less of it lingers dirty in L2).
+constexpr bool kNtStores = true;
+
+__device__ __forceinline__ uint32_t vword(const vec_t& q, int w) {
+  return w == 0 ? q.x : (w == 1 ? q.y : (w == 2 ? q.z : q.w));
+}
+__device__ __forceinline__ void set_vword(vec_t& q, int w, uint32_t x) {
+  if (w == 0) q.x = x;
+  else if (w == 1) q.y = x;
+  else if (w == 2) q.z = x;
+  else q.w = x;
+}
+// Element j of a vector (j is a compile-time constant after unrolling).
+template <class raw_t>
+__device__ __forceinline__ raw_t lane_of(const vec_t& q, int j) {
+  if constexpr (sizeof(raw_t) == 4) {
+    return vword(q, j);
+  } else {
+    return static_cast<raw_t>(vword(q, j >> 1) >> ((j & 1) * 16));
+  }
+}
+template <class raw_t>
+__device__ __forceinline__ void set_lane(vec_t& q, int j, raw_t r) {
+  if constexpr (sizeof(raw_t) == 4) {
+    set_vword(q, j, r);
+  } else {
+    const int w = j >> 1, sh = (j & 1) * 16;
+    set_vword(q, w, (vword(q, w) & ~(0xFFFFu << sh)) | (static_cast<uint32_t>(r) << sh));
+  }
+}
+// Element j of a vector with a runtime j.
+template <class raw_t>
+__device__ __forceinline__ raw_t lane_of_dyn(const vec_t& q, int j) {
+  if constexpr (sizeof(raw_t) == 4) {
+    return q[j];
+  } else {
+    return static_cast<raw_t>(q[j >> 1] >> ((j & 1) * 16));
+  }
+}
+
+__device__ __forceinline__ void store_vec(void* p, const vec_t& q) {
+  vec_t* v = reinterpret_cast<vec_t*>(p);
+  if constexpr (kNtStores) __builtin_nontemporal_store(q, v);
+  else *v = q;
+}
+
+// threadIdx.x behind an empty asm, so per-element indices are recomputed in
+// each traversal instead of being hoisted and kept alive in registers.
+__device__ __forceinline__ int fresh_tid() {
+  int t = static_cast<int>(threadIdx.x);
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
+// Buffer resource word 3 for raw (untyped, stride-0) buffer access on gfx9.
+constexpr int kRsrcWord3 = 0x00020000;
+
+template <class raw_t>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const raw_t* p, int n) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<raw_t*>(p), static_cast<short>(0),
+                                           n * static_cast<int>(sizeof(raw_t)), kRsrcWord3);
+}
+
+// A slice held in registers. All global accesses are raw buffer instructions
+// on a descriptor bounded to the slice, so vectors past the slice end read
+// as zero and their stores are dropped by the hardware: every lane issues
+// exactly the same memory instructions, with no branches around them, and
+// the compiler can count outstanding operations exactly (vector memory
+// operations complete in order). Requires the slice start to be 16-byte
+// aligned and its length a multiple of the vector width; launchers check this.
 template <class DT, int NVEC>
 struct RegTile {
   using raw_t = typename DT::raw_t;
+  static constexpr bool kRegisters = true;
   static constexpr int kPV = DT::kPerVec;
   static constexpr int kSpan = kThreads * kPV;  // elements per vector layer
   static constexpr int kCapacity = NVEC * kSpan;
+  static constexpr int kVecs = NVEC;
+  static constexpr int kBytes = static_cast<int>(sizeof(raw_t)) * kPV;  // 16
 
-  uint4 v[NVEC];
+  vec_t v[NVEC];
   int base;  // index of the slice's first element within the row
   int len;   // valid elements in the slice
-
-  // Element access by (vector, lane). Both indices are compile-time constants
-  // after unrolling, so these fold to register moves and shifts.
-  static __device__ __forceinline__ uint32_t word(const uint4& q, int w) {
-    return w == 0 ? q.x : (w == 1 ? q.y : (w == 2 ? q.z : q.w));
-  }
-  static __device__ __forceinline__ void set_word(uint4& q, int w, uint32_t x) {
-    if (w == 0) q.x = x;
-    else if (w == 1) q.y = x;
-    else if (w == 2) q.z = x;
-    else q.w = x;
-  }
-  static __device__ __forceinline__ raw_t lane_of(const uint4& q, int j) {
-    if constexpr (sizeof(raw_t) == 4) {
-      return word(q, j);
-    } else {
-      return static_cast<raw_t>(word(q, j >> 1) >> ((j & 1) * 16));
-    }
-  }
-  static __device__ __forceinline__ void set_lane(uint4& q, int j, raw_t r) {
-    if constexpr (sizeof(raw_t) == 4) {
-      set_word(q, j, r);
-    } else {
-      const int w = j >> 1, sh = (j & 1) * 16;
-      set_word(q, w, (word(q, w) & ~(0xFFFFu << sh)) | (static_cast<uint32_t>(r) << sh));
-    }
-  }
-  __device__ __forceinline__ raw_t get(int i, int j) const { return lane_of(v[i], j); }
-  __device__ __forceinline__ void set(int i, int j, raw_t r) { set_lane(v[i], j, r); }
 
   // Vector i as an opaque copy. Every traversal reads the tile through this,
   // so values derived from the tile in one traversal (keys, exponentials)
   // cannot be hoisted out of the selection loops and kept alive across
   // traversals, which would exhaust the register file.
-  __device__ __forceinline__ uint4 fresh(int i) const {
-    uint4 q = v[i];
-    asm volatile("" : "+v"(q.x), "+v"(q.y), "+v"(q.z), "+v"(q.w));
+  __device__ __forceinline__ vec_t fresh(int i) const {
+    vec_t q = v[i];
+    asm volatile("" : "+v"(q));
     return q;
-  }
-  // threadIdx.x behind the same barrier, so per-element indices are
-  // recomputed in each traversal instead of living in registers throughout.
-  static __device__ __forceinline__ int fresh_tid() {
-    int t = static_cast<int>(threadIdx.x);
-    asm volatile("" : "+v"(t));
-    return t;
   }
 
   __device__ __forceinline__ void load(const raw_t* __restrict__ row, int v0, int n) {
     base = v0;
     len = n;
-    const raw_t* src = row + v0;
-    const bool aligned = (reinterpret_cast<uintptr_t>(src) & 15u) == 0;
+    const __amdgpu_buffer_rsrc_t rs = row_rsrc(row + v0, n);
+    const int off = static_cast<int>(threadIdx.x) * kBytes;
 #pragma unroll
-    for (int i = 0; i < NVEC; ++i) {
-      const int e0 = i * kSpan + static_cast<int>(threadIdx.x) * kPV;
-      if (aligned && e0 + kPV <= n) {
-        v[i] = *reinterpret_cast<const uint4*>(src + e0);
-      } else {
+    for (int i = 0; i < NVEC; ++i)
+      v[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, off + i * kSpan * static_cast<int>(sizeof(raw_t)), 0,
+                                                   kNtLoads ? 2 : 0);
+  }
+
+  // f(i, q, e0) for every vector slot of this thread: q the data (zero past
+  // the row end), e0 the slice index of its first element.
+  template <class F>
+  __device__ __forceinline__ void for_each_vec(F&& f) const {
+    const int tid = fresh_tid();
 #pragma unroll
-        for (int j = 0; j < kPV; ++j) set(i, j, (e0 + j < n) ? src[e0 + j] : static_cast<raw_t>(0));
-      }
-    }
+    for (int i = 0; i < NVEC; ++i) f(i, fresh(i), i * kSpan + tid * kPV);
+  }
+
+  // f(i, e0) for every vector slot of this thread, without touching its data.
+  template <class F>
+  __device__ __forceinline__ void for_each_slot(F&& f) const {
+    const int tid = fresh_tid();
+#pragma unroll
+    for (int i = 0; i < NVEC; ++i) f(i, i * kSpan + tid * kPV);
+  }
+  __device__ __forceinline__ vec_t vec_at(int i, int) const { return fresh(i); }
+
+  // row[idx] = c for the elements of vector slot i of this thread.
+  __device__ __forceinline__ void store_const_slot(raw_t* __restrict__ row, int i, raw_t c) const {
+    vec_t cv = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int j = 0; j < kPV; ++j) set_lane<raw_t>(cv, j, c);
+    __builtin_amdgcn_raw_buffer_store_b128(cv, row_rsrc(row + base, len),
+                                           fresh_tid() * kBytes + i * kSpan * static_cast<int>(sizeof(raw_t)), 0,
+                                           kNtStores ? 2 : 0);
+  }
+
+  // row[idx] = c for every valid element of this thread, without its data.
+  __device__ __forceinline__ void store_const(raw_t* __restrict__ row, raw_t c) const {
+#pragma unroll
+    for (int i = 0; i < NVEC; ++i) store_const_slot(row, i, c);
+  }
+
+  // The same for vector slots [I0, I1) only.
+  template <int I0, int I1>
+  __device__ __forceinline__ void store_const_range(raw_t* __restrict__ row, raw_t c) const {
+#pragma unroll
+    for (int i = I0; i < (I1 < NVEC ? I1 : NVEC); ++i) store_const_slot(row, i, c);
   }
 
   // f(raw, idx) for every valid element held by this thread; idx is the
@@ -92,19 +171,19 @@ struct RegTile {
 #pragma unroll
     for (int i = 0; i < NVEC; ++i) {
       const int e0 = i * kSpan + tid * kPV;
-      const uint4 q = fresh(i);
+      const vec_t q = fresh(i);
       if ((i + 1) * kSpan <= len) {  // whole layer valid: uniform over the block
 #pragma unroll
-        for (int j = 0; j < kPV; ++j) f(lane_of(q, j), base + e0 + j);
+        for (int j = 0; j < kPV; ++j) f(lane_of<raw_t>(q, j), base + e0 + j);
       } else {
 #pragma unroll
         for (int j = 0; j < kPV; ++j)
-          if (e0 + j < len) f(lane_of(q, j), base + e0 + j);
+          if (e0 + j < len) f(lane_of<raw_t>(q, j), base + e0 + j);
       }
     }
   }
 
-  // f(x) for every vector held by this thread, x[] holding the values as
+  // f(i, x) for every vector slot of this thread, x[] holding the values as
   // fp32 with invalid slots (past the row end) set to -inf.
   template <class F>
   __device__ __forceinline__ void for_each_vec_values(F&& f) const {
@@ -113,55 +192,46 @@ struct RegTile {
     for (int i = 0; i < NVEC; ++i) {
       const int e0 = i * kSpan + tid * kPV;
       float x[kPV];
-      const uint4 q = fresh(i);
+      const vec_t q = fresh(i);
       if ((i + 1) * kSpan <= len) {
 #pragma unroll
-        for (int j = 0; j < kPV; ++j) x[j] = DT::value(lane_of(q, j));
+        for (int j = 0; j < kPV; ++j) x[j] = DT::value(lane_of<raw_t>(q, j));
       } else {
+        const bool valid = e0 < len;  // whole vectors: the length is a multiple of the width
 #pragma unroll
-        for (int j = 0; j < kPV; ++j) x[j] = (e0 + j < len) ? DT::value(lane_of(q, j)) : -INFINITY;
+        for (int j = 0; j < kPV; ++j) x[j] = valid ? DT::value(lane_of<raw_t>(q, j)) : -INFINITY;
       }
-      f(x);
+      f(i, x);
     }
   }
 
   // row[idx] = g(raw, idx) for every valid element held by this thread.
   template <class G>
   __device__ __forceinline__ void store(raw_t* __restrict__ row, G&& g) const {
-    raw_t* dst = row + base;
-    const bool aligned = (reinterpret_cast<uintptr_t>(dst) & 15u) == 0;
+    const __amdgpu_buffer_rsrc_t rs = row_rsrc(row + base, len);
     const int tid = fresh_tid();
 #pragma unroll
     for (int i = 0; i < NVEC; ++i) {
       const int e0 = i * kSpan + tid * kPV;
-      const uint4 q = fresh(i);
-      if (aligned && e0 + kPV <= len) {
-        uint4 o = make_uint4(0u, 0u, 0u, 0u);
+      const vec_t q = fresh(i);
+      vec_t o = {0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int j = 0; j < kPV; ++j) set_lane(o, j, g(lane_of(q, j), base + e0 + j));
-        *reinterpret_cast<uint4*>(dst + e0) = o;
-      } else {
-#pragma unroll
-        for (int j = 0; j < kPV; ++j)
-          if (e0 + j < len) dst[e0 + j] = g(lane_of(q, j), base + e0 + j);
-      }
+      for (int j = 0; j < kPV; ++j) set_lane<raw_t>(o, j, g(lane_of<raw_t>(q, j), base + e0 + j));
+      __builtin_amdgcn_raw_buffer_store_b128(o, rs, e0 * static_cast<int>(sizeof(raw_t)), 0, kNtStores ? 2 : 0);
     }
   }
 };
 
-}  // namespace tkp
-
-namespace tkp {
-
-// The same interface as RegTile for rows too long to keep in registers: every
-// traversal reads the row again from global memory (16-byte loads, the same
-// element-to-thread layout), so later traversals mostly hit L2 or the
-// Infinity Cache.
+// The same interface for rows too long to keep in registers: every traversal
+// reads the row again from global memory, so later traversals mostly hit L2
+// or the Infinity Cache.
 template <class DT>
 struct GlobalTile {
   using raw_t = typename DT::raw_t;
+  static constexpr bool kRegisters = false;
   static constexpr int kPV = DT::kPerVec;
   static constexpr int kSpan = kThreads * kPV;
+  static constexpr int kVecs = 1;  // no per-vector state is kept for a streamed row
 
   const raw_t* src;
   int base;
@@ -175,15 +245,42 @@ struct GlobalTile {
     aligned = (reinterpret_cast<uintptr_t>(src) & 15u) == 0;
   }
 
-  // raw elements e0 .. e0+kPV-1 (zero past the end)
-  __device__ __forceinline__ void read(int e0, raw_t (&r)[kPV]) const {
-    if (aligned && e0 + kPV <= len) {
-      const uint4 q = *reinterpret_cast<const uint4*>(src + e0);
+  // elements e0 .. e0+kPV-1 (zero past the end)
+  __device__ __forceinline__ vec_t read(int e0) const {
+    if (aligned && e0 + kPV <= len) return *reinterpret_cast<const vec_t*>(src + e0);
+    vec_t q = {0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int j = 0; j < kPV; ++j) r[j] = RegTile<DT, 1>::lane_of(q, j);
-    } else {
+    for (int j = 0; j < kPV; ++j) set_lane<raw_t>(q, j, (e0 + j < len) ? src[e0 + j] : static_cast<raw_t>(0));
+    return q;
+  }
+
+  template <class F>
+  __device__ __forceinline__ void for_each_vec(F&& f) const {
+    int i = 0;
+    for (int e0 = static_cast<int>(threadIdx.x) * kPV; e0 < len; e0 += kSpan, ++i) f(i, read(e0), e0);
+  }
+
+  template <class F>
+  __device__ __forceinline__ void for_each_slot(F&& f) const {
+    int i = 0;
+    for (int e0 = static_cast<int>(threadIdx.x) * kPV; e0 < len; e0 += kSpan, ++i) f(i, e0);
+  }
+  __device__ __forceinline__ vec_t vec_at(int, int e0) const { return read(e0); }
+
+  __device__ __forceinline__ void store_const(raw_t* __restrict__ row, raw_t c) const {
+    raw_t* dst = row + base;
+    const bool dst_aligned = (reinterpret_cast<uintptr_t>(dst) & 15u) == 0;
+    vec_t cv = {0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int j = 0; j < kPV; ++j) r[j] = (e0 + j < len) ? src[e0 + j] : static_cast<raw_t>(0);
+    for (int j = 0; j < kPV; ++j) set_lane<raw_t>(cv, j, c);
+    for (int e0 = static_cast<int>(threadIdx.x) * kPV; e0 < len; e0 += kSpan) {
+      if (dst_aligned && e0 + kPV <= len) {
+        store_vec(dst + e0, cv);
+      } else {
+#pragma unroll
+        for (int j = 0; j < kPV; ++j)
+          if (e0 + j < len) dst[e0 + j] = c;
+      }
     }
   }
 
@@ -191,24 +288,23 @@ struct GlobalTile {
   __device__ __forceinline__ void for_each(F&& f) const {
 #pragma unroll 2
     for (int e0 = static_cast<int>(threadIdx.x) * kPV; e0 < len; e0 += kSpan) {
-      raw_t r[kPV];
-      read(e0, r);
+      const vec_t q = read(e0);
 #pragma unroll
       for (int j = 0; j < kPV; ++j)
-        if (e0 + j < len) f(r[j], base + e0 + j);
+        if (e0 + j < len) f(lane_of<raw_t>(q, j), base + e0 + j);
     }
   }
 
   template <class F>
   __device__ __forceinline__ void for_each_vec_values(F&& f) const {
+    int i = 0;
 #pragma unroll 2
-    for (int e0 = static_cast<int>(threadIdx.x) * kPV; e0 < len; e0 += kSpan) {
-      raw_t r[kPV];
-      read(e0, r);
+    for (int e0 = static_cast<int>(threadIdx.x) * kPV; e0 < len; e0 += kSpan, ++i) {
+      const vec_t q = read(e0);
       float x[kPV];
 #pragma unroll
-      for (int j = 0; j < kPV; ++j) x[j] = (e0 + j < len) ? DT::value(r[j]) : -INFINITY;
-      f(x);
+      for (int j = 0; j < kPV; ++j) x[j] = (e0 + j < len) ? DT::value(lane_of<raw_t>(q, j)) : -INFINITY;
+      f(i, x);
     }
   }
 
@@ -218,17 +314,16 @@ struct GlobalTile {
     const bool dst_aligned = (reinterpret_cast<uintptr_t>(dst) & 15u) == 0;
 #pragma unroll 2
     for (int e0 = static_cast<int>(threadIdx.x) * kPV; e0 < len; e0 += kSpan) {
-      raw_t r[kPV];
-      read(e0, r);
+      const vec_t q = read(e0);
       if (dst_aligned && e0 + kPV <= len) {
-        uint4 o = make_uint4(0u, 0u, 0u, 0u);
+        vec_t o = {0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int j = 0; j < kPV; ++j) RegTile<DT, 1>::set_lane(o, j, g(r[j], base + e0 + j));
-        *reinterpret_cast<uint4*>(dst + e0) = o;
+        for (int j = 0; j < kPV; ++j) set_lane<raw_t>(o, j, g(lane_of<raw_t>(q, j), base + e0 + j));
+        store_vec(dst + e0, o);
       } else {
 #pragma unroll
         for (int j = 0; j < kPV; ++j)
-          if (e0 + j < len) dst[e0 + j] = g(r[j], base + e0 + j);
+          if (e0 + j < len) dst[e0 + j] = g(lane_of<raw_t>(q, j), base + e0 + j);
       }
     }
   }

@@ -24,6 +24,8 @@
 // global scratch is needed. The logits slice is loaded into registers before
 // the boundary search so its latency overlaps that search.
 
+#include <type_traits>
+
 #include "launch.h"
 #include "reg_tile.h"
 
@@ -37,21 +39,12 @@ __device__ __forceinline__ int block_max_i32(int v, RowSmem& sm) {
 __device__ __forceinline__ uint64_t block_exscan_u64(uint64_t v, RowSmem& sm, uint64_t& total) {
   const int l = threadIdx.x & (kWave - 1);
   const int w = threadIdx.x / kWave;
-  uint64_t incl = v;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    uint64_t n = __shfl_up(incl, o);
-    if (l >= o) incl += n;
-  }
+  const uint64_t incl = wave_incl_scan_u64(v);
   if (l == kWave - 1) sm.redu[w] = incl;
   __syncthreads();
-  uint64_t wbase = 0, tot = 0;
-#pragma unroll
-  for (int i = 0; i < kWaves; ++i) {
-    const uint64_t x = sm.redu[i];
-    wbase += (i < w) ? x : 0;
-    tot += x;
-  }
+  const uint64_t x = l < kWaves ? sm.redu[l] : 0ull;
+  const uint64_t wbase = wave_sum_u64(l < w ? x : 0ull);
+  const uint64_t tot = wave_sum_u64(x);
   __syncthreads();
   total = tot;
   return wbase + incl - v;
@@ -132,20 +125,21 @@ __device__ __forceinline__ SortedBoundary sorted_boundary(const typename DT::raw
 constexpr int kSortedVecs = 8;  // logits slice held in registers: 8 vectors per thread
 constexpr int kMaxSliceWords = (kThreads * kSortedVecs * 8) / 32;
 
-template <class DT>
+template <class DT, bool kRegs>
 __global__ __launch_bounds__(kThreads) void sorted_logits_kernel(
     const typename DT::raw_t* __restrict__ sorted_value, const int32_t* __restrict__ sorted_indices,
     const typename DT::raw_t* __restrict__ p, const int32_t* __restrict__ k,
     const typename DT::raw_t* __restrict__ logits, typename DT::raw_t* __restrict__ out, int V, int S) {
   using raw_t = typename DT::raw_t;
-  using Tile = RegTile<DT, kSortedVecs>;
+  using Tile = std::conditional_t<kRegs, RegTile<DT, kSortedVecs>, GlobalTile<DT>>;
+  constexpr int kCap = RegTile<DT, kSortedVecs>::kCapacity;
   __shared__ RowSmem sm;
   __shared__ uint32_t ties[kMaxSliceWords];
 
   const int b = blockIdx.x / S;
   const int s = blockIdx.x - b * S;
-  const int v0 = s * Tile::kCapacity;
-  const int len = min(Tile::kCapacity, V - v0);
+  const int v0 = s * kCap;
+  const int len = min(kCap, V - v0);
   const size_t row_off = static_cast<size_t>(b) * V;
 
   Tile tile;
@@ -214,9 +208,18 @@ static hipError_t launch_sorted_t(const void* sorted_value, const int32_t* sorte
   if (logits != nullptr) {
     constexpr int cap = RegTile<DT, kSortedVecs>::kCapacity;
     const int S = static_cast<int>((V + cap - 1) / cap);
-    hipLaunchKernelGGL(sorted_logits_kernel<DT>, dim3(static_cast<unsigned>(B * S)), dim3(kThreads), 0, stream,
-                       static_cast<const raw_t*>(sorted_value), sorted_indices, static_cast<const raw_t*>(p), k,
-                       static_cast<const raw_t*>(logits), static_cast<raw_t*>(out), static_cast<int>(V), S);
+    const bool vec_ok = (V % DT::kPerVec) == 0 && (reinterpret_cast<uintptr_t>(logits) & 15u) == 0 &&
+                        (reinterpret_cast<uintptr_t>(out) & 15u) == 0;
+    if (vec_ok)
+      hipLaunchKernelGGL((sorted_logits_kernel<DT, true>), dim3(static_cast<unsigned>(B * S)), dim3(kThreads), 0,
+                         stream, static_cast<const raw_t*>(sorted_value), sorted_indices,
+                         static_cast<const raw_t*>(p), k, static_cast<const raw_t*>(logits),
+                         static_cast<raw_t*>(out), static_cast<int>(V), S);
+    else
+      hipLaunchKernelGGL((sorted_logits_kernel<DT, false>), dim3(static_cast<unsigned>(B * S)), dim3(kThreads), 0,
+                         stream, static_cast<const raw_t*>(sorted_value), sorted_indices,
+                         static_cast<const raw_t*>(p), k, static_cast<const raw_t*>(logits),
+                         static_cast<raw_t*>(out), static_cast<int>(V), S);
   } else {
     const int S = static_cast<int>((V + kScatterSlice - 1) / kScatterSlice);
     hipLaunchKernelGGL(sorted_scatter_kernel<DT>, dim3(static_cast<unsigned>(B * S)), dim3(kThreads), 0, stream,

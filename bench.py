@@ -16,7 +16,9 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1..5]
 """
 
 import argparse
+import hashlib
 import json
+import re
 import os
 import sys
 import time
@@ -37,6 +39,36 @@ WORKLOAD_TEXT = {
     4: "apply_top_k_top_p tie stress, B=1024 V=128256 fp32 N(0,2) snapped to 0.25",
     5: "apply_top_k_top_p_with_sorted with logits, B=128 V=262144 bf16 N(0,3)",
 }
+
+
+# HBM bytes per launch of the filter kernel on workload 3, from the FETCH_SIZE
+# and WRITE_SIZE counter passes (scaled by a plain copy's readings), together
+# with a digest of the kernel sources they were taken on.
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "hbm_traffic_apply_regs_kernel_bf16_B256_V151936.md")
+
+
+def kernel_source_digest():
+    """sha256 over the library's kernel sources and build flags."""
+    pkg = os.path.join(ROOT, "top_logits_filtering_amd")
+    names = sorted(os.path.join("csrc", n) for n in os.listdir(os.path.join(pkg, "csrc"))) + ["build.py"]
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(pkg, n), "rb") as f:
+            h.update(n.encode() + b"\0" + f.read() + b"\0")
+    return h.hexdigest()
+
+
+def measured_traffic(args):
+    """Counter-measured HBM bytes per launch, or None when no counters were
+    taken for this workload or the kernel sources changed since."""
+    if args.workload != 3 or args.policy != 0 or args.copy_calibration or not os.path.exists(TRAFFIC_PROFILE):
+        return None
+    text = open(TRAFFIC_PROFILE).read()
+    m_bytes = re.search(r"traffic_bytes_per_launch:\s*(\d+)", text)
+    m_hash = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
+    if not (m_bytes and m_hash) or m_hash.group(1) != kernel_source_digest():
+        return None
+    return int(m_bytes.group(1))
 
 
 def dev(bits, dtype):
@@ -60,28 +92,29 @@ def algorithmic_bytes(wl):
     return total
 
 
-def cpu_baseline(wl, budget_s=10.0):
+def cpu_baseline(wl, budget_s=12.0):
     """The CPU oracle, as it stands, on the first rows of the same workload."""
     from oracle import apply_top_k_top_p, apply_top_k_top_p_with_sorted
 
     done = 0
     t0 = time.perf_counter()
-    while done < wl.B and (time.perf_counter() - t0) < budget_s:
-        r = slice(done, min(wl.B, done + 8))
+    while (time.perf_counter() - t0) < budget_s:
+        lo = done % wl.B
+        r = slice(lo, min(wl.B, lo + 8))
         if wl.entry == "apply":
             apply_top_k_top_p(wl.logits[r], wl.dtype, wl.p[r], wl.k[r], keep_traces=False)
         else:
             apply_top_k_top_p_with_sorted(wl.sorted_value[r], wl.sorted_indices[r], wl.dtype, wl.p[r], wl.k[r],
                                           logits_bits=wl.logits[r], keep_traces=False)
-        done = r.stop
+        done += r.stop - r.start
     dt = time.perf_counter() - t0
     return {
         "value": round(done / dt, 3),
         "unit": "rows/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": f"first {done} of {wl.B} rows of the timed workload, numpy float64 oracle, one thread, "
-                  f"{dt:.1f} s",
+        "sample": f"{done} rows (the workload's rows in order, wrapping after {wl.B}), numpy float64 oracle, "
+                  f"one thread, {dt:.1f} s",
     }
 
 
@@ -92,9 +125,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", type=int, default=3, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--sets", type=int, default=4, help="rotating input/output buffer sets")
-    ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds for the CPU oracle sample")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds for the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--policy", type=int, default=0, help="plan policy: 0 auto, 1 general, 2 registers")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="time a plain device-to-device copy of the logits instead of the filter (the reference "
+                         "kernel whose HBM counters scale the filter's)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -127,7 +163,9 @@ def main():
 
     def step(i):
         st = sets[i % len(sets)]
-        if wl.entry == "apply":
+        if args.copy_calibration:
+            st[1].copy_(st[0])
+        elif wl.entry == "apply":
             tk.apply_top_k_top_p(st[0], p, k, out=st[1])
         else:
             tk.apply_top_k_top_p_with_sorted(st[2], st[3], p, k, logits=st[0], out=st[1])
@@ -136,21 +174,23 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    stream = torch.cuda.current_stream()  # the library launches on this stream
-    ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    # The library launches on torch's current stream; the two events bracket
+    # the K launches on that same stream.
+    stream = torch.cuda.current_stream()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    ev0.record(stream)
     for i in range(args.steps):
-        ev0[i].record(stream)
         step(i)
-        ev1[i].record(stream)
+    ev1.record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
 
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    kernel_ms = float(np.mean([a.elapsed_time(b) for a, b in zip(ev0, ev1)]))
-    nbytes = algorithmic_bytes(wl)
+    kernel_ms = ev0.elapsed_time(ev1) / args.steps
+    nbytes = 2 * wl.B * wl.V * wl.elem_bytes if args.copy_calibration else algorithmic_bytes(wl)
     achieved = nbytes / (kernel_ms * 1e-3) / 1e9
     rows_per_s = wl.B / (ms_per_step * 1e-3)
 
@@ -180,12 +220,17 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(args),
             "kernel_us": round(kernel_ms * 1e3, 3),
             "algorithmic_bytes_per_launch": nbytes,
         },
     }
-    if not args.no_cpu_baseline:
+    if args.copy_calibration:
+        line["metric"] = "device copy of the logits (HBM counter calibration)"
+        line["value"] = round(nbytes / (ms_per_step * 1e-3) / 1e9, 1)
+        line["unit"] = "GB/s"
+        line["config"]["workload"] = "torch copy_ of " + WORKLOAD_TEXT[args.workload]
+    elif not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
     print(json.dumps(line), flush=True)
 

@@ -72,13 +72,19 @@ def set_plan_policy(policy: int) -> int:
     return prev
 
 
-def _dtype_code(t) -> int:
-    import torch
+_DTYPE_CODES = None
 
-    codes = {torch.float32: TOPKTOPP_F32, torch.float16: TOPKTOPP_F16, torch.bfloat16: TOPKTOPP_BF16}
-    if t.dtype not in codes:
+
+def _dtype_code(t) -> int:
+    global _DTYPE_CODES
+    if _DTYPE_CODES is None:
+        import torch
+
+        _DTYPE_CODES = {torch.float32: TOPKTOPP_F32, torch.float16: TOPKTOPP_F16, torch.bfloat16: TOPKTOPP_BF16}
+    code = _DTYPE_CODES.get(t.dtype)
+    if code is None:
         raise TypeError(f"unsupported dtype {t.dtype}")
-    return codes[t.dtype]
+    return code
 
 
 def _ptr(t) -> Optional[int]:
@@ -92,10 +98,12 @@ def _ptr(t) -> Optional[int]:
 
 
 def _stream(stream, device) -> int:
-    import torch
-
+    """The HIP stream handle to launch on: the given one, else torch's current
+    stream of the tensors' device."""
     if stream is None:
-        stream = torch.cuda.current_stream(device)
+        import torch
+
+        return torch._C._cuda_getCurrentRawStream(device.index)
     return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
 
 

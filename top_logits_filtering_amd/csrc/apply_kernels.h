@@ -13,23 +13,24 @@
 //     its 16-byte vectors and, for top-p rows without top-k, an online
 //     (running-max rescaled) sum of exp(x - max);
 //  2. the whole output row is written as -inf (it does not depend on the
-//     data), so these stores drain while the block works on in registers
-//     and shared memory only (a vector load or a register spill now would
-//     wait for them: vector memory operations complete in order);
+//     data), in portions issued between the steps below, so these stores
+//     drain while the block works on in registers and shared memory only (a
+//     vector load or a register spill now would wait for them: vector memory
+//     operations complete in order);
 //  3-4. the 2048 per-thread maxima are actual row elements, so the k-th
 //     largest of them bounds the top-k threshold from below; for top-p-only
 //     rows the bound is where the mass of those maxima, walked from the top,
 //     reaches (1 - t) * Z, so every element above it carries at least that
 //     mass and the top-p boundary cannot lie below it. One 1024-bin
 //     histogram pass gives the bound L as a bin edge;
-//  5. every vector whose maximum is >= L is copied into its wave's region of
-//     shared memory, placed by a wave ballot (no atomics);
+//  5. every vector whose maximum is >= L is copied into a list in shared
+//     memory, placed by wave ballots (one shared-memory atomic per wave);
 //  6. the exact selection (row_select.h) runs on the elements >= L of those
 //     vectors only;
 //  7. after the -inf stores have completed, the survivors are written over
 //     them.
-// Whenever a bound cannot be formed (k > 2048, top-p mass not reached) or a
-// wave's region overflows, the block falls back to the multi-pass plan, which
+// Whenever a bound cannot be formed (k > 2048, top-p mass not reached) or the
+// list overflows, the block falls back to the multi-pass plan, which
 // rewrites the whole row; the same thread writes the same addresses in the
 // same order, so the earlier -inf stores are overwritten.
 //

@@ -48,13 +48,19 @@ TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "hbm_traffic_apply_regs_kernel_
 
 
 def kernel_source_digest():
-    """sha256 over the library's kernel sources and build flags."""
+    """sha256 over the code of the library's kernel sources and build script,
+    with C/C++ comments and whitespace removed (a comment edit does not change
+    the kernel)."""
     pkg = os.path.join(ROOT, "top_logits_filtering_amd")
     names = sorted(os.path.join("csrc", n) for n in os.listdir(os.path.join(pkg, "csrc"))) + ["build.py"]
     h = hashlib.sha256()
     for n in names:
         with open(os.path.join(pkg, n), "rb") as f:
-            h.update(n.encode() + b"\0" + f.read() + b"\0")
+            text = f.read()
+        if not n.endswith(".py"):
+            text = re.sub(rb"/\*.*?\*/", b"", text, flags=re.S)
+            text = re.sub(rb"//[^\n]*", b"", text)
+        h.update(n.encode() + b"\0" + b"".join(text.split()) + b"\0")
     return h.hexdigest()
 
 

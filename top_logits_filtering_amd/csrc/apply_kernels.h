@@ -50,6 +50,8 @@ namespace tkp {
 constexpr int kTop2 = 2 * kThreads;
 constexpr int kMaxVecs = 20;
 constexpr int kCandVecCap = 2048;  // candidate vectors kept in shared memory
+constexpr int kCandPerThread = 5;
+constexpr int kCandCap = kCandPerThread * kThreads;  // candidate elements kept in shared memory
 
 // When the -inf stores of a register tile are issued, as cumulative shares (in
 // percent) of its vector slots: while the row arrives, then before the row
@@ -82,37 +84,46 @@ struct ApplySmem {
   uint32_t top2[kTop2];
   float run[kThreads];  // per-thread running max and rescaled exp sum (top-p-only rows)
   float acc[kThreads];
-  uint32_t vmw[(kMaxVecs + 1) / 2][kThreads];  // per-vector maxima (16-bit bounds, two per word)
-  vec_t cvec[kCandVecCap];
+  union {
+    uint32_t vmw[(kMaxVecs + 1) / 2][kThreads];  // per-vector maxima (16-bit bounds, two per word), steps 1-5
+    struct {
+      uint32_t raw[kCandCap];  // candidate elements: raw bits
+      uint32_t idx[kCandCap];  // and row indices
+    } cel;                     // steps 5-7
+  };
+  vec_t cvec[kCandVecCap];  // candidate vectors
   uint32_t ce0[kCandVecCap];
-  uint32_t nvec;  // candidate vectors reserved so far
+  uint32_t nvec;   // candidate vectors reserved so far
+  uint32_t ncand;  // candidate elements reserved so far
 };
+static_assert(sizeof(uint32_t) * 2 * kCandCap <= sizeof(uint32_t) * ((kMaxVecs + 1) / 2) * kThreads,
+              "the candidate element list reuses the space of the per-vector maxima");
 
-// Elements >= Lf of the candidate vectors (every element >= Lf of the row lies
-// in one of them).
+// The candidate elements (every element >= the bound of the row), read once
+// from shared memory into registers: element c of the list goes to thread
+// c % 1024, slot c / 1024.
 template <class DT>
-struct CandVecs {
+struct CandElems {
   using raw_t = typename DT::raw_t;
-  static constexpr int kPV = DT::kPerVec;
-  static constexpr int kShift = kPV == 8 ? 3 : 2;
-  const ApplySmem* S;
-  int nvec;
-  int V;
-  float Lf;
+  uint32_t raw[kCandPerThread];
+  uint32_t idx[kCandPerThread];
+  int n;
+  __device__ __forceinline__ void load(const ApplySmem& S, int count) {
+    n = count;
+#pragma unroll
+    for (int s = 0; s < kCandPerThread; ++s) {
+      const int c = s * kThreads + static_cast<int>(threadIdx.x);
+      raw[s] = c < n ? S.cel.raw[c] : 0u;
+      idx[s] = c < n ? S.cel.idx[c] : 0u;
+    }
+  }
   template <class F>
   __device__ __forceinline__ void for_each(F&& f) const {
-    const uint32_t* words = reinterpret_cast<const uint32_t*>(S->cvec);
-    const int n = nvec << kShift;
-    for (int q = threadIdx.x; q < n; q += kThreads) {
-      const int vi = q >> kShift, j = q & (kPV - 1);
-      raw_t raw;
-      if constexpr (sizeof(raw_t) == 4) {
-        raw = words[(vi << 2) + j];
-      } else {
-        raw = static_cast<raw_t>(words[(vi << 2) + (j >> 1)] >> ((j & 1) * 16));
+#pragma unroll
+    for (int s = 0; s < kCandPerThread; ++s) {
+      if (s * kThreads < n) {  // uniform
+        if (s * kThreads + static_cast<int>(threadIdx.x) < n) f(static_cast<raw_t>(raw[s]), static_cast<int>(idx[s]));
       }
-      const int idx = static_cast<int>(S->ce0[vi]) + j;
-      if (idx < V && DT::value(raw) >= Lf) f(raw, idx);
     }
   }
 };
@@ -214,7 +225,10 @@ __device__ __forceinline__ void filter_row(const Tile& tile, const typename DT::
   S.top2[2 * threadIdx.x + 1] = DT::raw_of_value(M2);
   S.run[threadIdx.x] = run;
   S.acc[threadIdx.x] = acc;
-  if (threadIdx.x == 0) S.nvec = 0;  // read after the barriers of step 3
+  if (threadIdx.x == 0) {  // read after the barriers of step 3
+    S.nvec = 0;
+    S.ncand = 0;
+  }
 
   // 2. the whole row as -inf (register tiles stored theirs in step 1). From
   // here until the survivors are written the block touches only registers
@@ -262,11 +276,15 @@ __device__ __forceinline__ void filter_row(const Tile& tile, const typename DT::
 
   if constexpr (Tile::kRegisters)
     tile.template store_const_range<store_upto<Tile::kVecs, 2>(), store_upto<Tile::kVecs, 3>()>(orow, DT::kNegInf);
-  // 5. candidate vectors: every vector whose maximum is >= L, packed into one
-  // list placed by wave ballots (the list order does not matter: every
-  // statistic taken from it below is order-independent)
+  // 5. candidates: every vector whose maximum is >= L is packed into a list
+  // in shared memory (placed by wave ballots); then the elements >= L of
+  // those vectors are packed into a second list (raw bits and row index),
+  // each thread taking one or two listed vectors. The list orders do not
+  // matter: every statistic taken below is order-independent, and ties are
+  // resolved by the stored indices.
   const float Lf = DT::value(DT::raw_of_key(L));
   uint32_t nvec = 0;
+  int ncand = 0;
   if (!fallback) {
     const uint64_t below = (1ull << (threadIdx.x & (kWave - 1))) - 1ull;
     auto is_cand = [&](int i, int e0) {
@@ -328,13 +346,45 @@ __device__ __forceinline__ void filter_row(const Tile& tile, const typename DT::
     __syncthreads();
     nvec = S.nvec;
     fallback = nvec > static_cast<uint32_t>(kCandVecCap);
-
+    if (!fallback) {
+      uint32_t c = 0;
+      for (int vi = static_cast<int>(threadIdx.x); vi < static_cast<int>(nvec); vi += kThreads) {
+        const vec_t q = S.cvec[vi];
+        const int e0 = static_cast<int>(S.ce0[vi]);
+#pragma unroll
+        for (int j = 0; j < kPV; ++j) c += (e0 + j < V && DT::value(lane_of<raw_t>(q, j)) >= Lf) ? 1u : 0u;
+      }
+      const uint32_t incl = wave_incl_scan_u32(c);
+      const uint32_t wtot = lane63_u32(incl);
+      uint32_t pos0 = 0;
+      if ((threadIdx.x & (kWave - 1)) == 0 && wtot != 0) pos0 = atomicAdd(&S.ncand, wtot);
+      uint32_t pos = __builtin_amdgcn_readfirstlane(pos0) + incl - c;
+      for (int vi = static_cast<int>(threadIdx.x); vi < static_cast<int>(nvec); vi += kThreads) {
+        const vec_t q = S.cvec[vi];
+        const int e0 = static_cast<int>(S.ce0[vi]);
+#pragma unroll
+        for (int j = 0; j < kPV; ++j) {
+          const raw_t r = lane_of<raw_t>(q, j);
+          if (e0 + j < V && DT::value(r) >= Lf) {
+            if (pos < static_cast<uint32_t>(kCandCap)) {
+              S.cel.raw[pos] = r;
+              S.cel.idx[pos] = static_cast<uint32_t>(e0 + j);
+            }
+            ++pos;
+          }
+        }
+      }
+      __syncthreads();
+      ncand = static_cast<int>(S.ncand);
+      fallback = ncand > kCandCap;
+    }
   }
 
   if constexpr (Tile::kRegisters)
     tile.template store_const_range<store_upto<Tile::kVecs, 3>(), store_upto<Tile::kVecs, 4>()>(orow, DT::kNegInf);
   // 6. exact selection on the candidates (all elements with key in [L, kmax])
-  const CandVecs<DT> cs{&S, static_cast<int>(nvec), V, Lf};
+  CandElems<DT> cs;
+  cs.load(S, fallback ? 0 : ncand);
   uint32_t K = 0, I = 0;
   if (!fallback) {
     if (top_only && !rp.k_on) {

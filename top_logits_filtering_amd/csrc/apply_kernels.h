@@ -59,7 +59,7 @@ constexpr int kCandCap = kCandPerThread * kThreads;  // candidate elements kept 
 // ahead of its stores once the memory pipeline is full, so the stores are
 // spread over the steps that follow the loads instead of issued at once;
 // they then drain while those steps run.
-constexpr int kStoreShare[5] = {0, 0, 0, 40, 100};
+constexpr int kStoreShare[5] = {0, 0, 20, 60, 100};
 template <int NV, int STAGE>
 constexpr int store_upto() {
   return (NV * kStoreShare[STAGE] + 99) / 100;
@@ -95,6 +95,7 @@ struct ApplySmem {
   uint32_t ce0[kCandVecCap];
   uint32_t nvec;   // candidate vectors reserved so far
   uint32_t ncand;  // candidate elements reserved so far
+  uint32_t sK, sI, sFallback;  // result of the one-wave selection
 };
 static_assert(sizeof(uint32_t) * 2 * kCandCap <= sizeof(uint32_t) * ((kMaxVecs + 1) / 2) * kThreads,
               "the candidate element list reuses the space of the per-vector maxima");
@@ -144,11 +145,79 @@ __device__ __forceinline__ void filter_multipass(const Tile& tile, const RowPara
                                                  typename DT::raw_t* __restrict__ orow) {
   using raw_t = typename DT::raw_t;
   uint32_t K, I;
+  __syncthreads();  // histograms cleared (sel_reset) before the first pass
   solve_row<DT>(tile, rp, V, S.row, S.sel, K, I);
   tile.store(orow, [K, I](raw_t r, int idx) {
     const uint32_t key = DT::key(r);
     return (key > K || (key == K && static_cast<uint32_t>(idx) >= I)) ? r : DT::kNegInf;
   });
+}
+
+// Selection among at most one wave's worth of candidates (lane j of wave 0
+// holds candidate j): each candidate's rank in the descending (key, index)
+// order, which is the stable ascending order read from the top, and the
+// fixed-point mass strictly above it come from one sweep over the others;
+// the survivors are then a prefix of that order and (K, I) is the key and
+// index of the last one. Decisions match the histogram selection exactly:
+// the same masses and sums, in the same integer arithmetic. Wave 0 only;
+// the caller publishes the result.
+template <class DT>
+__device__ __forceinline__ void select_small(const ApplySmem& S, int n, const RowParams& rp, float m,
+                                             uint64_t thr_ponly, bool top_only, uint32_t& K, uint32_t& I,
+                                             bool& fallback) {
+  fallback = n == 0;  // never: the row maximum is always a candidate
+  if (fallback) return;
+  const int j = static_cast<int>(threadIdx.x);
+  const bool has = j < n;
+  const uint32_t raw = has ? S.cel.raw[j] : 0u;
+  const uint32_t idx = has ? S.cel.idx[j] : 0u;
+  const uint32_t key = has ? DT::key(static_cast<typename DT::raw_t>(raw)) : 0u;
+  const uint64_t comp = has ? (static_cast<uint64_t>(key) << 32 | idx) : 0ull;
+  const uint64_t mass = has ? mass_fx(DT::value(static_cast<typename DT::raw_t>(raw)), m) : 0ull;
+  uint32_t rank = 0;
+  uint64_t above = 0;
+  for (int i = 0; i < n; ++i) {
+    const uint64_t ci = static_cast<uint64_t>(__builtin_amdgcn_readlane(static_cast<int>(comp >> 32), i)) << 32 |
+                        static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(comp), i));
+    const uint64_t mi = static_cast<uint64_t>(__builtin_amdgcn_readlane(static_cast<int>(mass >> 32), i)) << 32 |
+                        static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(mass), i));
+    if (ci > comp) {
+      ++rank;
+      above += mi;
+    }
+  }
+  uint32_t Kk = 0;
+  if (rp.k_on) {
+    const uint64_t at = __ballot(has && rank == rp.k - 1);
+    if (at == 0) {  // fewer than k candidates: cannot happen with a valid bound
+      fallback = true;
+      return;
+    }
+    Kk = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(key), __ffsll(static_cast<unsigned long long>(at)) - 1));
+  }
+  bool surv;
+  if (top_only || rp.pmode == kPTopOnly) {
+    surv = has && rank == 0;
+  } else if (rp.pmode == kPNone) {
+    K = Kk;
+    I = 0;
+    return;
+  } else if (rp.k_on) {
+    const uint64_t Z = wave_sum_u64(has && key >= Kk ? mass : 0ull);
+    const uint64_t thr2 = topp_threshold(rp.t, Z);
+    surv = has && (thr2 == 0 ? rank == 0 : (key >= Kk && above < thr2));
+  } else {
+    const uint64_t A = wave_sum_u64(mass);
+    if (A < thr_ponly) {  // the boundary lies below the candidates
+      fallback = true;
+      return;
+    }
+    surv = has && above < thr_ponly;
+  }
+  const uint64_t last = wave_reduce_u64(surv ? comp : ~0ull, ~0ull,
+                                        [](uint64_t a, uint64_t b) { return a < b ? a : b; });
+  K = static_cast<uint32_t>(last >> 32);
+  I = static_cast<uint32_t>(last);
 }
 
 // `tile` holds the row (registers or global); `irow` is the same row in
@@ -163,6 +232,7 @@ __device__ __forceinline__ void filter_row(const Tile& tile, const typename DT::
   SelSmem& ss = S.sel;
   GlobalTile<DT> gt;
   gt.load(irow, 0, V);
+  sel_reset(ss);
 
   if (!rp.k_on && rp.pmode == kPNone) {  // nothing to filter
     tile.store(orow, [](raw_t r, int) { return r; });
@@ -225,6 +295,7 @@ __device__ __forceinline__ void filter_row(const Tile& tile, const typename DT::
   S.top2[2 * threadIdx.x + 1] = DT::raw_of_value(M2);
   S.run[threadIdx.x] = run;
   S.acc[threadIdx.x] = acc;
+
   if (threadIdx.x == 0) {  // read after the barriers of step 3
     S.nvec = 0;
     S.ncand = 0;
@@ -386,7 +457,21 @@ __device__ __forceinline__ void filter_row(const Tile& tile, const typename DT::
   CandElems<DT> cs;
   cs.load(S, fallback ? 0 : ncand);
   uint32_t K = 0, I = 0;
-  if (!fallback) {
+  if (!fallback && ncand <= kWave) {
+    if (threadIdx.x < kWave) {
+      bool fb;
+      select_small<DT>(S, ncand, rp, m, thr, top_only, K, I, fb);
+      if (threadIdx.x == 0) {
+        S.sK = K;
+        S.sI = I;
+        S.sFallback = fb ? 1u : 0u;
+      }
+    }
+    __syncthreads();
+    K = S.sK;
+    I = S.sI;
+    fallback = S.sFallback != 0;
+  } else if (!fallback) {
     if (top_only && !rp.k_on) {
       top_position<DT>(cs, sm, K, I);
     } else {

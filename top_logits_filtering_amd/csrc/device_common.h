@@ -19,6 +19,10 @@
 
 namespace tkp {
 
+// 16 bytes: the unit of row loads and stores and of shared-memory vector access.
+using vec_t = uint32_t __attribute__((ext_vector_type(4)));
+
+
 constexpr int kThreads = 1024;           // threads per row-block
 constexpr int kWave = 64;                // gfx950 wavefront
 constexpr int kWaves = kThreads / kWave; // 16

@@ -12,8 +12,6 @@
 
 namespace tkp {
 
-using vec_t = uint32_t __attribute__((ext_vector_type(4)));
-
 // Streaming (nontemporal) 16-byte loads of the row: it is read once.
 constexpr bool kNtLoads = true;
 // Output stores: nontemporal as well (measured faster for this kernel: the

@@ -32,9 +32,9 @@ constexpr int kBinBits = 10;
 constexpr int kBins = 1 << kBinBits;  // == kThreads: one bin per thread in the scans
 static_assert(kBins == kThreads, "bin scans assume one bin per thread");
 
-struct SelSmem {
-  uint32_t cnt[kBins];
-  uint64_t mass[kBins];
+struct alignas(16) SelSmem {
+  alignas(16) uint32_t cnt[kBins];
+  alignas(16) uint64_t mass[kBins];
   uint32_t wtot32[kWaves];
   uint64_t wtot64[kWaves];
   int bin;
@@ -69,41 +69,122 @@ __device__ __forceinline__ uint64_t block_incl_scan_u64(uint64_t v, uint64_t* wt
   return v + base;
 }
 
-__device__ __forceinline__ void sel_clear(SelSmem& ss, bool with_mass) {
+// The histograms are kept all-zero between passes: they are cleared once
+// (sel_reset, before a barrier) and every pick clears what it read, so a pass
+// costs one barrier after its histogram and one after its pick.
+__device__ __forceinline__ void sel_reset(SelSmem& ss) {
   ss.cnt[threadIdx.x] = 0;
-  if (with_mass) ss.mass[threadIdx.x] = 0;
-  __syncthreads();
+  ss.mass[threadIdx.x] = 0;
 }
 
-// Walks the bins from the highest down (thread t owns bin kBins-1-t) and
-// selects the first bin whose inclusive running count reaches target >= 1.
-// If the target exceeds the total, bin 0 is selected. Result in ss.bin,
-// ss.above (count strictly above), ss.bcnt; visible after the call.
+// Bins per lane when one wave scans the whole histogram: lane l owns the 16
+// consecutive bins [kBins - 16 (l + 1), kBins - 16 l), so lanes run from the
+// highest bins down. The pick takes two levels: a wave scan of the lanes'
+// sums finds the lane L holding the target, then the 16 lanes of a DPP row
+// each take one of L's bins (from its top) and a row scan finds the bin.
+constexpr int kPickSpan = kBins / kWave;
+static_assert(kPickSpan == 16, "pick layout assumes 16 bins per lane");
+
+// Inclusive prefix sums over the 16 lanes of each DPP row.
+__device__ __forceinline__ uint32_t row_incl_scan_u32(uint32_t v) {
+  v += dpp_u32<dpp::kRowShr1>(v, 0u);
+  v += dpp_u32<dpp::kRowShr2>(v, 0u);
+  v += dpp_u32<dpp::kRowShr4>(v, 0u);
+  v += dpp_u32<dpp::kRowShr8>(v, 0u);
+  return v;
+}
+__device__ __forceinline__ uint64_t row_incl_scan_u64(uint64_t v) {
+  v += dpp_u64<dpp::kRowShr1>(v, 0ull);
+  v += dpp_u64<dpp::kRowShr2>(v, 0ull);
+  v += dpp_u64<dpp::kRowShr4>(v, 0ull);
+  v += dpp_u64<dpp::kRowShr8>(v, 0ull);
+  return v;
+}
+
+// Walks the bins from the highest down and selects the first bin whose
+// inclusive running count reaches target >= 1; if the target exceeds the
+// total, bin 0 is selected. Result in ss.bin, ss.above (count strictly
+// above) and ss.bcnt, visible after the call. Wave 0 scans (the histogram
+// must be complete: callers place a barrier before) and clears the bins.
 __device__ __forceinline__ void sel_pick_count(SelSmem& ss, uint32_t target) {
-  const int b = kBins - 1 - static_cast<int>(threadIdx.x);
-  const uint32_t c = ss.cnt[b];
-  const uint32_t incl = block_incl_scan_u32(c, ss.wtot32);
-  const uint32_t excl = incl - c;
-  if ((excl < target && target <= incl) || (b == 0 && target > incl)) {
-    ss.bin = b;
-    ss.above = excl;
-    ss.bcnt = c;
+  if (threadIdx.x < kWave) {
+    const int l = static_cast<int>(threadIdx.x);
+    const int base = kBins - kPickSpan * (l + 1);
+    const vec_t* cv = reinterpret_cast<const vec_t*>(&ss.cnt[base]);
+    uint32_t sum = 0;
+#pragma unroll 2
+    for (int q = 0; q < kPickSpan / 4; ++q) {
+      const vec_t c4 = cv[q];
+      sum += c4.x + c4.y + c4.z + c4.w;
+    }
+    const uint32_t incl = wave_incl_scan_u32(sum);
+    const uint32_t total = lane63_u32(incl);
+    const bool short_total = target > total;  // then bin 0, the lowest bin of lane 63
+    const uint64_t hitm = __ballot(incl - sum < target && target <= incl);
+    const int L = short_total ? kWave - 1 : __ffsll(static_cast<unsigned long long>(hitm)) - 1;
+    const uint32_t exclL = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(incl - sum), L));
+    // second level: lane r of each row takes bin (top of L's range) - r
+    const int r = l & 15;
+    const int binr = kBins - kPickSpan * L - 1 - r;
+    const uint32_t c = ss.cnt[binr];
+    const uint32_t rin = row_incl_scan_u32(c);
+    const uint32_t t2 = target - exclL;
+    const uint64_t hit2 = __ballot(l < 16 && rin - c < t2 && t2 <= rin);
+    const int R = short_total ? 15 : __ffsll(static_cast<unsigned long long>(hit2)) - 1;
+    if (l == R) {
+      ss.bin = binr;
+      ss.above = exclL + rin - c;
+      ss.bcnt = c;
+    }
+    const vec_t z = {0u, 0u, 0u, 0u};
+    vec_t* cw = reinterpret_cast<vec_t*>(&ss.cnt[base]);
+#pragma unroll
+    for (int q = 0; q < kPickSpan / 4; ++q) cw[q] = z;
   }
   __syncthreads();
 }
 
 // The same on the mass histogram: first bin whose running mass reaches
-// target >= 1; also reports the bin's count and mass.
+// target >= 1; also reports the bin's count and mass. Clears both histograms.
 __device__ __forceinline__ void sel_pick_mass(SelSmem& ss, uint64_t target) {
-  const int b = kBins - 1 - static_cast<int>(threadIdx.x);
-  const uint64_t c = ss.mass[b];
-  const uint64_t incl = block_incl_scan_u64(c, ss.wtot64);
-  const uint64_t excl = incl - c;
-  if ((excl < target && target <= incl) || (b == 0 && target > incl)) {
-    ss.bin = b;
-    ss.above64 = excl;
-    ss.bmass = c;
-    ss.bcnt = ss.cnt[b];
+  if (threadIdx.x < kWave) {
+    const int l = static_cast<int>(threadIdx.x);
+    const int base = kBins - kPickSpan * (l + 1);
+    const vec_t* mv = reinterpret_cast<const vec_t*>(&ss.mass[base]);  // two u64 per vector
+    uint64_t sum = 0;
+#pragma unroll 2
+    for (int q = 0; q < kPickSpan / 2; ++q) {
+      const vec_t m2 = mv[q];
+      sum += (static_cast<uint64_t>(m2.y) << 32 | m2.x) + (static_cast<uint64_t>(m2.w) << 32 | m2.z);
+    }
+    const uint64_t incl = wave_incl_scan_u64(sum);
+    const uint64_t total = lane63_u64(incl);
+    const bool short_total = target > total;
+    const uint64_t hitm = __ballot(incl - sum < target && target <= incl);
+    const int L = short_total ? kWave - 1 : __ffsll(static_cast<unsigned long long>(hitm)) - 1;
+    const uint64_t ex = incl - sum;
+    const uint64_t exclL = static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(ex >> 32), L))) << 32 |
+                           static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(ex), L));
+    const int r = l & 15;
+    const int binr = kBins - kPickSpan * L - 1 - r;
+    const uint64_t c = ss.mass[binr];
+    const uint64_t rin = row_incl_scan_u64(c);
+    const uint64_t t2 = target - exclL;
+    const uint64_t hit2 = __ballot(l < 16 && rin - c < t2 && t2 <= rin);
+    const int R = short_total ? 15 : __ffsll(static_cast<unsigned long long>(hit2)) - 1;
+    if (l == R) {
+      ss.bin = binr;
+      ss.above64 = exclL + rin - c;
+      ss.bmass = c;
+      ss.bcnt = ss.cnt[binr];
+    }
+    const vec_t z = {0u, 0u, 0u, 0u};
+    vec_t* mw = reinterpret_cast<vec_t*>(&ss.mass[base]);
+#pragma unroll
+    for (int q = 0; q < kPickSpan / 2; ++q) mw[q] = z;
+    vec_t* cw = reinterpret_cast<vec_t*>(&ss.cnt[base]);
+#pragma unroll
+    for (int q = 0; q < kPickSpan / 4; ++q) cw[q] = z;
   }
   __syncthreads();
 }
@@ -118,7 +199,6 @@ __device__ __forceinline__ uint32_t kth_largest_key(const Src& src, uint32_t k, 
     const uint32_t range = hi - lo;
     if (range == 0) return lo;
     const int shift = shift_for_range(range);
-    sel_clear(ss, false);
     src.for_each([&](auto raw, int idx) {
       const uint32_t key = keyfn(raw, idx);
       if (key >= lo && key <= hi && pred(raw, idx)) atomicAdd(&ss.cnt[(key - lo) >> shift], 1u);
@@ -142,7 +222,6 @@ template <class Src, class KeyFn>
 __device__ __forceinline__ bool kth_largest_bound(const Src& src, uint32_t k, uint32_t lo, uint32_t hi,
                                                   KeyFn keyfn, SelSmem& ss, uint32_t& bound) {
   const int shift = shift_for_range(hi - lo);
-  sel_clear(ss, false);
   src.for_each([&](auto raw, int idx) {
     const uint32_t key = keyfn(raw, idx);
     if (key >= lo && key <= hi) atomicAdd(&ss.cnt[(key - lo) >> shift], 1u);
@@ -151,7 +230,6 @@ __device__ __forceinline__ bool kth_largest_bound(const Src& src, uint32_t k, ui
   sel_pick_count(ss, k);
   const bool ok = !(ss.bin == 0 && ss.above + ss.bcnt < k);
   bound = lo + (static_cast<uint32_t>(ss.bin) << shift);
-  __syncthreads();
   return ok;
 }
 
@@ -185,7 +263,6 @@ __device__ __forceinline__ void topp_boundary(const Src& src, uint32_t lo, uint3
   uint64_t bmass = 0;
   for (;;) {
     const int shift = shift_for_range(hi - lo);
-    sel_clear(ss, true);
     src.for_each([&](auto raw, int) {
       const uint32_t key = DT::key(raw);
       if (key >= lo && key <= hi) {
@@ -203,7 +280,6 @@ __device__ __forceinline__ void topp_boundary(const Src& src, uint32_t lo, uint3
     const uint32_t span = (shift == 0) ? 0u : ((1u << shift) - 1u);
     hi = (hi - nlo > span) ? nlo + span : hi;
     lo = nlo;
-    __syncthreads();
     if (shift == 0) break;
   }
   Kp = lo;
@@ -230,7 +306,6 @@ template <class DT, class Src>
 __device__ __forceinline__ bool topp_bound(const Src& src, uint32_t lo, uint32_t hi, float m, uint64_t thr,
                                            SelSmem& ss, uint32_t& bound) {
   const int shift = shift_for_range(hi - lo);
-  sel_clear(ss, true);
   src.for_each([&](auto raw, int) {
     const uint32_t key = DT::key(raw);
     if (key >= lo && key <= hi) {
@@ -243,7 +318,6 @@ __device__ __forceinline__ bool topp_bound(const Src& src, uint32_t lo, uint32_t
   sel_pick_mass(ss, thr);
   const bool ok = !(ss.bin == 0 && ss.above64 + ss.bmass < thr);
   bound = lo + (static_cast<uint32_t>(ss.bin) << shift);
-  __syncthreads();
   return ok;
 }
 

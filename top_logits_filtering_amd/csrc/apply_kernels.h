@@ -474,6 +474,22 @@ __device__ __forceinline__ void filter_row(const Tile& tile, const typename DT::
   } else if (!fallback) {
     if (top_only && !rp.k_on) {
       top_position<DT>(cs, sm, K, I);
+    } else if (rp.k_on && rp.pmode == kPBoundary && shift_for_range(kmax - L) == 0) {
+      // top-k and top-p from one pass: every bin of [L, kmax] holds one key
+      cs.for_each([&](auto raw, int) {
+        const uint32_t bin = DT::key(raw) - L;
+        atomicAdd(&ss.mass[bin], mass_fx(DT::value(raw), m));
+        atomicAdd(&ss.cnt[bin], 1u);
+      });
+      __syncthreads();
+      sel_pick_joint(ss, rp.k, rp.t);
+      const uint64_t thr2 = ss.thr;
+      if (thr2 == 0) {
+        top_position<DT>(cs, sm, K, I);
+      } else {
+        K = L + static_cast<uint32_t>(ss.bin);
+        I = boundary_index<DT>(cs, K, thr2 - ss.above64, ss.bcnt, ss.bmass, V, ss);
+      }
     } else {
       uint32_t Kk = L;
       if (rp.k_on)

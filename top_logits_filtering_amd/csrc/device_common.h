@@ -144,6 +144,13 @@ __device__ __forceinline__ uint64_t dpp_u64(uint64_t v, uint64_t old) {
 __device__ __forceinline__ uint32_t lane63_u32(uint32_t v) {
   return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 63));
 }
+__device__ __forceinline__ uint32_t readlane_u32(uint32_t v, int lane) {
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), lane));
+}
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int lane) {
+  return (static_cast<uint64_t>(readlane_u32(static_cast<uint32_t>(v >> 32), lane)) << 32) |
+         readlane_u32(static_cast<uint32_t>(v), lane);
+}
 __device__ __forceinline__ uint64_t lane63_u64(uint64_t v) {
   return (static_cast<uint64_t>(lane63_u32(static_cast<uint32_t>(v >> 32))) << 32) |
          lane63_u32(static_cast<uint32_t>(v));

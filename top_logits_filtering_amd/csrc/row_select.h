@@ -42,6 +42,8 @@ struct alignas(16) SelSmem {
   uint64_t above64;
   uint32_t bcnt;
   uint64_t bmass;
+  int kbin;      // joint pick: bin of the k-th largest
+  uint64_t thr;  // joint pick: fixed-point top-p threshold over the top-k survivors
 };
 
 __device__ __forceinline__ int shift_for_range(uint32_t range) {
@@ -189,6 +191,83 @@ __device__ __forceinline__ void sel_pick_mass(SelSmem& ss, uint64_t target) {
   __syncthreads();
 }
 
+// Top-k and top-p together from one pass of both histograms over a range
+// where each bin holds a single key: the bin of the k-th largest (count from
+// the top reaches k; the histogram must hold at least k elements), Z = the
+// mass of that bin and every bin above it, thr = ceil((1 - t) Z), and, when
+// thr > 0, the first bin from the top whose running mass reaches thr, with the
+// mass strictly above it, its mass and its count (ss.bin, ss.above64,
+// ss.bmass, ss.bcnt). ss.kbin and ss.thr hold the others. Wave 0 works and
+// clears both histograms.
+__device__ __forceinline__ void sel_pick_joint(SelSmem& ss, uint32_t k, float t) {
+  if (threadIdx.x < kWave) {
+    const int l = static_cast<int>(threadIdx.x);
+    const int base = kBins - kPickSpan * (l + 1);
+    const vec_t* cv = reinterpret_cast<const vec_t*>(&ss.cnt[base]);
+    const vec_t* mv = reinterpret_cast<const vec_t*>(&ss.mass[base]);
+    uint32_t csum = 0;
+#pragma unroll 2
+    for (int q = 0; q < kPickSpan / 4; ++q) {
+      const vec_t c4 = cv[q];
+      csum += c4.x + c4.y + c4.z + c4.w;
+    }
+    uint64_t msum = 0;
+#pragma unroll 2
+    for (int q = 0; q < kPickSpan / 2; ++q) {
+      const vec_t m2 = mv[q];
+      msum += (static_cast<uint64_t>(m2.y) << 32 | m2.x) + (static_cast<uint64_t>(m2.w) << 32 | m2.z);
+    }
+    const uint32_t cin = wave_incl_scan_u32(csum);
+    const uint64_t min = wave_incl_scan_u64(msum);
+    const uint32_t cex = cin - csum;
+    const uint64_t mex = min - msum;
+    const int r = l & 15;
+    // the k-th largest
+    const uint64_t hk = __ballot(cex < k && k <= cin);
+    const int Lk = hk ? __ffsll(static_cast<unsigned long long>(hk)) - 1 : kWave - 1;
+    const int binrk = kBins - kPickSpan * Lk - 1 - r;
+    const uint32_t ck = ss.cnt[binrk];
+    const uint64_t mk = ss.mass[binrk];
+    const uint32_t ckin = row_incl_scan_u32(ck);
+    const uint64_t mkin = row_incl_scan_u64(mk);
+    const uint32_t tk = k - readlane_u32(cex, Lk);
+    const uint64_t hk2 = __ballot(l < 16 && ckin - ck < tk && tk <= ckin);
+    const int Rk = hk2 ? __ffsll(static_cast<unsigned long long>(hk2)) - 1 : 15;
+    const uint64_t Z = readlane_u64(mex, Lk) + readlane_u64(mkin, Rk);
+    const uint64_t thr = topp_threshold(t, Z);
+    if (l == 0) {
+      ss.kbin = kBins - kPickSpan * Lk - 1 - Rk;
+      ss.thr = thr;
+    }
+    // the top-p boundary: thr <= Z, so at or above the k-th largest's bin
+    if (thr > 0) {
+      const uint64_t hp = __ballot(mex < thr && thr <= min);
+      const int Lp = __ffsll(static_cast<unsigned long long>(hp)) - 1;
+      const uint64_t mexL = readlane_u64(mex, Lp);
+      const int binrp = kBins - kPickSpan * Lp - 1 - r;
+      const uint64_t mp = ss.mass[binrp];
+      const uint64_t mpin = row_incl_scan_u64(mp);
+      const uint64_t tp = thr - mexL;
+      const uint64_t hp2 = __ballot(l < 16 && mpin - mp < tp && tp <= mpin);
+      const int Rp = __ffsll(static_cast<unsigned long long>(hp2)) - 1;
+      if (l == Rp) {
+        ss.bin = binrp;
+        ss.above64 = mexL + mpin - mp;
+        ss.bmass = mp;
+        ss.bcnt = ss.cnt[binrp];
+      }
+    }
+    const vec_t z = {0u, 0u, 0u, 0u};
+    vec_t* mw = reinterpret_cast<vec_t*>(&ss.mass[base]);
+#pragma unroll
+    for (int q = 0; q < kPickSpan / 2; ++q) mw[q] = z;
+    vec_t* cw = reinterpret_cast<vec_t*>(&ss.cnt[base]);
+#pragma unroll
+    for (int q = 0; q < kPickSpan / 4; ++q) cw[q] = z;
+  }
+  __syncthreads();
+}
+
 // k-th largest (1-based, with multiplicity) of keyfn(raw, idx) over the
 // elements with pred(raw, idx), given that all of them lie in [lo, hi].
 // Every thread of the block must call it.
@@ -231,6 +310,24 @@ __device__ __forceinline__ bool kth_largest_bound(const Src& src, uint32_t k, ui
   const bool ok = !(ss.bin == 0 && ss.above + ss.bcnt < k);
   bound = lo + (static_cast<uint32_t>(ss.bin) << shift);
   return ok;
+}
+
+// Index threshold inside the final run of equal values at a top-p boundary:
+// the run (key Kp, cnt elements of equal mass, bmass in total) is entered
+// with `need` (>= 1) of the threshold still to reach; its members are taken
+// from the highest index down until the mass strictly above the next one
+// reaches the threshold. Returns Ip (survivors of the run: index >= Ip).
+template <class DT, class Src>
+__device__ __forceinline__ uint32_t boundary_index(const Src& src, uint32_t Kp, uint64_t need, uint32_t cnt,
+                                                   uint64_t bmass, int V, SelSmem& ss) {
+  const uint64_t eg = bmass / (cnt ? cnt : 1u);
+  const uint64_t ns64 = eg ? (need + eg - 1) / eg : cnt;
+  uint32_t ns = ns64 >= cnt ? cnt : static_cast<uint32_t>(ns64);
+  if (ns < 1) ns = 1;
+  if (ns >= cnt) return 0;
+  return kth_largest_key(
+      src, ns, 0u, static_cast<uint32_t>(V - 1), [](auto, int idx) { return static_cast<uint32_t>(idx); },
+      [Kp](auto raw, int) { return DT::key(raw) == Kp; }, ss);
 }
 
 // Key of the maximum and the highest original index holding it.
@@ -284,19 +381,7 @@ __device__ __forceinline__ void topp_boundary(const Src& src, uint32_t lo, uint3
   }
   Kp = lo;
   // Every element of the final run has the same value, hence the same mass.
-  const uint64_t eg = bmass / (cnt ? cnt : 1u);
-  const uint64_t need = thr - acc;  // >= 1
-  const uint64_t ns64 = eg ? (need + eg - 1) / eg : cnt;
-  uint32_t ns = ns64 >= cnt ? cnt : static_cast<uint32_t>(ns64);
-  if (ns < 1) ns = 1;
-  if (ns >= cnt) {
-    Ip = 0;
-  } else {
-    const uint32_t kp = Kp;
-    Ip = kth_largest_key(
-        src, ns, 0u, static_cast<uint32_t>(V - 1), [](auto, int idx) { return static_cast<uint32_t>(idx); },
-        [kp](auto raw, int) { return DT::key(raw) == kp; }, ss);
-  }
+  Ip = boundary_index<DT>(src, Kp, thr - acc, cnt, bmass, V, ss);
 }
 
 // Coarse lower bound for the top-p boundary: one mass histogram over

@@ -133,9 +133,9 @@ __device__ __forceinline__ double block_sum_f64(double v, double* red) {
   v = wave_sum_f64(v);
   const int l = threadIdx.x & (kWave - 1);
   if (l == 0) red[threadIdx.x / kWave] = v;
-  __syncthreads();
+  lds_barrier();
   const double r = wave_sum_f64(l < kWaves ? red[l] : 0.0);
-  __syncthreads();
+  lds_barrier();
   return r;
 }
 
@@ -145,7 +145,7 @@ __device__ __forceinline__ void filter_multipass(const Tile& tile, const RowPara
                                                  typename DT::raw_t* __restrict__ orow) {
   using raw_t = typename DT::raw_t;
   uint32_t K, I;
-  __syncthreads();  // histograms cleared (sel_reset) before the first pass
+  lds_barrier();  // histograms cleared (sel_reset) before the first pass
   solve_row<DT>(tile, rp, V, S.row, S.sel, K, I);
   tile.store(orow, [K, I](raw_t r, int idx) {
     const uint32_t key = DT::key(r);
@@ -357,7 +357,6 @@ __device__ __forceinline__ void filter_row(const Tile& tile, const typename DT::
   uint32_t nvec = 0;
   int ncand = 0;
   if (!fallback) {
-    const uint64_t below = (1ull << (threadIdx.x & (kWave - 1))) - 1ull;
     auto is_cand = [&](int i, int e0) {
       float vmv;
       if constexpr (Tile::kRegisters) {
@@ -371,7 +370,6 @@ __device__ __forceinline__ void filter_row(const Tile& tile, const typename DT::
       }
       return vmv >= Lf;
     };
-    const uint64_t lane_bit = 1ull << (threadIdx.x & (kWave - 1));
     if constexpr (Tile::kRegisters) {
       // one pass over the register slots: each slot's ballot is kept (uniform,
       // so in scalar registers); one shared-memory atomic per wave reserves the
@@ -385,15 +383,20 @@ __device__ __forceinline__ void filter_row(const Tile& tile, const typename DT::
       uint32_t pos0 = 0;
       if ((threadIdx.x & (kWave - 1)) == 0) pos0 = atomicAdd(&S.nvec, wtotal);
       pos0 = __builtin_amdgcn_readfirstlane(pos0);
+      const uint32_t lane = threadIdx.x & (kWave - 1);
       tile.for_each_slot([&](int i, int e0) {
-        if (masks[i] & lane_bit) {
-          const uint32_t pos = pos0 + static_cast<uint32_t>(__popcll(masks[i] & below));
-          if (pos < static_cast<uint32_t>(kCandVecCap)) {
-            S.cvec[pos] = tile.vec_at(i, e0);
-            S.ce0[pos] = static_cast<uint32_t>(e0);
+        if (masks[i] != 0) {  // uniform: slots without candidates in this wave cost nothing
+          // the lane's bit of the ballot (no second shared-memory read, whose
+          // latency would be paid once per slot)
+          if ((masks[i] >> lane) & 1ull) {
+            const uint32_t pos = pos0 + lanes_below(masks[i]);
+            if (pos < static_cast<uint32_t>(kCandVecCap)) {
+              S.cvec[pos] = tile.vec_at(i, e0);
+              S.ce0[pos] = static_cast<uint32_t>(e0);
+            }
           }
+          pos0 += static_cast<uint32_t>(__popcll(masks[i]));
         }
-        pos0 += static_cast<uint32_t>(__popcll(masks[i]));
       });
     } else {
       // streamed rows: one atomic per wave for each slot holding candidates
@@ -405,7 +408,7 @@ __device__ __forceinline__ void filter_row(const Tile& tile, const typename DT::
           if ((threadIdx.x & (kWave - 1)) == 0) pos0 = atomicAdd(&S.nvec, static_cast<uint32_t>(__popcll(mask)));
           pos0 = __builtin_amdgcn_readfirstlane(pos0);
           if (c) {
-            const uint32_t pos = pos0 + static_cast<uint32_t>(__popcll(mask & below));
+            const uint32_t pos = pos0 + lanes_below(mask);
             if (pos < static_cast<uint32_t>(kCandVecCap)) {
               S.cvec[pos] = tile.vec_at(i, e0);
               S.ce0[pos] = static_cast<uint32_t>(e0);
@@ -414,38 +417,44 @@ __device__ __forceinline__ void filter_row(const Tile& tile, const typename DT::
         }
       });
     }
-    __syncthreads();
+    lds_barrier();
     nvec = S.nvec;
     fallback = nvec > static_cast<uint32_t>(kCandVecCap);
     if (!fallback) {
-      uint32_t c = 0;
+      // each thread takes listed vectors tid and tid + 1024; per element lane
+      // j of the vectors a wave ballot places the elements >= L
       for (int vi = static_cast<int>(threadIdx.x); vi < static_cast<int>(nvec); vi += kThreads) {
         const vec_t q = S.cvec[vi];
         const int e0 = static_cast<int>(S.ce0[vi]);
-#pragma unroll
-        for (int j = 0; j < kPV; ++j) c += (e0 + j < V && DT::value(lane_of<raw_t>(q, j)) >= Lf) ? 1u : 0u;
-      }
-      const uint32_t incl = wave_incl_scan_u32(c);
-      const uint32_t wtot = lane63_u32(incl);
-      uint32_t pos0 = 0;
-      if ((threadIdx.x & (kWave - 1)) == 0 && wtot != 0) pos0 = atomicAdd(&S.ncand, wtot);
-      uint32_t pos = __builtin_amdgcn_readfirstlane(pos0) + incl - c;
-      for (int vi = static_cast<int>(threadIdx.x); vi < static_cast<int>(nvec); vi += kThreads) {
-        const vec_t q = S.cvec[vi];
-        const int e0 = static_cast<int>(S.ce0[vi]);
+        uint64_t mk[kPV];
+        uint32_t wtot = 0;
 #pragma unroll
         for (int j = 0; j < kPV; ++j) {
-          const raw_t r = lane_of<raw_t>(q, j);
-          if (e0 + j < V && DT::value(r) >= Lf) {
-            if (pos < static_cast<uint32_t>(kCandCap)) {
-              S.cel.raw[pos] = r;
-              S.cel.idx[pos] = static_cast<uint32_t>(e0 + j);
+          mk[j] = __ballot(e0 + j < V && DT::value(lane_of<raw_t>(q, j)) >= Lf);
+          wtot += static_cast<uint32_t>(__popcll(mk[j]));
+        }
+        // one shared-memory atomic per wave, by its first active lane
+        const uint64_t active = __ballot(1);
+        uint32_t pos0 = 0;
+        if (static_cast<int>(threadIdx.x & (kWave - 1)) == __ffsll(static_cast<unsigned long long>(active)) - 1)
+          pos0 = atomicAdd(&S.ncand, wtot);
+        uint32_t pos = __builtin_amdgcn_readfirstlane(pos0);
+#pragma unroll
+        for (int j = 0; j < kPV; ++j) {
+          if (mk[j] != 0) {
+            const raw_t r = lane_of<raw_t>(q, j);
+            if (e0 + j < V && DT::value(r) >= Lf) {
+              const uint32_t at = pos + lanes_below(mk[j]);
+              if (at < static_cast<uint32_t>(kCandCap)) {
+                S.cel.raw[at] = r;
+                S.cel.idx[at] = static_cast<uint32_t>(e0 + j);
+              }
             }
-            ++pos;
+            pos += static_cast<uint32_t>(__popcll(mk[j]));
           }
         }
       }
-      __syncthreads();
+      lds_barrier();
       ncand = static_cast<int>(S.ncand);
       fallback = ncand > kCandCap;
     }
@@ -467,7 +476,7 @@ __device__ __forceinline__ void filter_row(const Tile& tile, const typename DT::
         S.sFallback = fb ? 1u : 0u;
       }
     }
-    __syncthreads();
+    lds_barrier();
     K = S.sK;
     I = S.sI;
     fallback = S.sFallback != 0;
@@ -481,7 +490,7 @@ __device__ __forceinline__ void filter_row(const Tile& tile, const typename DT::
         atomicAdd(&ss.mass[bin], mass_fx(DT::value(raw), m));
         atomicAdd(&ss.cnt[bin], 1u);
       });
-      __syncthreads();
+      lds_barrier();
       sel_pick_joint(ss, rp.k, rp.t);
       const uint64_t thr2 = ss.thr;
       if (thr2 == 0) {

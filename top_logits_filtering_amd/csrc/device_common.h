@@ -19,6 +19,16 @@
 
 namespace tkp {
 
+// Workgroup barrier for shared-memory communication only: it orders this
+// wave's shared-memory accesses around the barrier but does not wait for its
+// outstanding global loads and stores (a plain __syncthreads() waits for all
+// of them, which would tie every step to the -inf stores still draining).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // 16 bytes: the unit of row loads and stores and of shared-memory vector access.
 using vec_t = uint32_t __attribute__((ext_vector_type(4)));
 
@@ -144,6 +154,11 @@ __device__ __forceinline__ uint64_t dpp_u64(uint64_t v, uint64_t old) {
 __device__ __forceinline__ uint32_t lane63_u32(uint32_t v) {
   return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 63));
 }
+// Number of set bits of a wave-uniform lane mask below the calling lane.
+__device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(mask >> 32),
+                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0u));
+}
 __device__ __forceinline__ uint32_t readlane_u32(uint32_t v, int lane) {
   return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), lane));
 }
@@ -245,9 +260,9 @@ __device__ __forceinline__ float block_max_f32(float v, RowSmem& sm) {
   v = wave_max_f32(v);
   const int l = threadIdx.x & (kWave - 1);
   if (l == 0) sm.redf[threadIdx.x / kWave] = v;
-  __syncthreads();
+  lds_barrier();
   const float r = wave_max_f32(l < kWaves ? sm.redf[l] : -INFINITY);
-  __syncthreads();
+  lds_barrier();
   return r;
 }
 
@@ -255,9 +270,9 @@ __device__ __forceinline__ uint32_t block_max_u32(uint32_t v, RowSmem& sm) {
   v = wave_max_u32(v);
   const int l = threadIdx.x & (kWave - 1);
   if (l == 0) sm.redw[threadIdx.x / kWave] = v;
-  __syncthreads();
+  lds_barrier();
   const uint32_t r = wave_max_u32(l < kWaves ? sm.redw[l] : 0u);
-  __syncthreads();
+  lds_barrier();
   return r;
 }
 
@@ -265,9 +280,9 @@ __device__ __forceinline__ uint32_t block_min_u32(uint32_t v, RowSmem& sm) {
   v = wave_min_u32(v);
   const int l = threadIdx.x & (kWave - 1);
   if (l == 0) sm.redw[threadIdx.x / kWave] = v;
-  __syncthreads();
+  lds_barrier();
   const uint32_t r = wave_min_u32(l < kWaves ? sm.redw[l] : 0xFFFFFFFFu);
-  __syncthreads();
+  lds_barrier();
   return r;
 }
 
@@ -281,19 +296,19 @@ __device__ __forceinline__ void block_max_f32_min_u32(float a, uint32_t b, RowSm
     sm.redf[threadIdx.x / kWave] = a;
     sm.redw[threadIdx.x / kWave] = b;
   }
-  __syncthreads();
+  lds_barrier();
   amax = wave_max_f32(l < kWaves ? sm.redf[l] : -INFINITY);
   bmin = wave_min_u32(l < kWaves ? sm.redw[l] : 0xFFFFFFFFu);
-  __syncthreads();
+  lds_barrier();
 }
 
 __device__ __forceinline__ uint64_t block_sum_u64(uint64_t v, RowSmem& sm) {
   v = wave_sum_u64(v);
   const int l = threadIdx.x & (kWave - 1);
   if (l == 0) sm.redu[threadIdx.x / kWave] = v;
-  __syncthreads();
+  lds_barrier();
   const uint64_t r = wave_sum_u64(l < kWaves ? sm.redu[l] : 0ull);
-  __syncthreads();
+  lds_barrier();
   return r;
 }
 
@@ -301,9 +316,9 @@ __device__ __forceinline__ uint32_t block_sum_u32(uint32_t v, RowSmem& sm) {
   v = wave_sum_u32(v);
   const int l = threadIdx.x & (kWave - 1);
   if (l == 0) sm.redw[threadIdx.x / kWave] = v;
-  __syncthreads();
+  lds_barrier();
   const uint32_t r = wave_sum_u32(l < kWaves ? sm.redw[l] : 0u);
-  __syncthreads();
+  lds_barrier();
   return r;
 }
 

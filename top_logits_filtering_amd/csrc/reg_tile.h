@@ -12,11 +12,11 @@
 
 namespace tkp {
 
-// Streaming (nontemporal) 16-byte loads of the row: it is read once.
-constexpr bool kNtLoads = true;
-// Output stores: nontemporal as well (measured faster for this kernel: the
-// output is not read again by the kernel, and less of it lingers dirty in L2).
-constexpr bool kNtStores = true;
+// Cache policy bits of the row loads and stores (gfx9 buffer instructions:
+// 1 = sc0, 2 = nt, 16 = sc1). The row is read once: streaming (nt) loads.
+// The output is not read again by the kernel: nontemporal stores as well.
+constexpr int kLoadPolicy = 2;
+constexpr int kStorePolicy = 2;
 
 __device__ __forceinline__ uint32_t vword(const vec_t& q, int w) {
   return w == 0 ? q.x : (w == 1 ? q.y : (w == 2 ? q.z : q.w));
@@ -57,7 +57,7 @@ __device__ __forceinline__ raw_t lane_of_dyn(const vec_t& q, int j) {
 
 __device__ __forceinline__ void store_vec(void* p, const vec_t& q) {
   vec_t* v = reinterpret_cast<vec_t*>(p);
-  if constexpr (kNtStores) __builtin_nontemporal_store(q, v);
+  if constexpr ((kStorePolicy & 2) != 0) __builtin_nontemporal_store(q, v);
   else *v = q;
 }
 
@@ -117,7 +117,7 @@ struct RegTile {
 #pragma unroll
     for (int i = 0; i < NVEC; ++i)
       v[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, off + i * kSpan * static_cast<int>(sizeof(raw_t)), 0,
-                                                   kNtLoads ? 2 : 0);
+                                                   kLoadPolicy);
   }
 
   // f(i, q, e0) for every vector slot of this thread: q the data (zero past
@@ -145,7 +145,7 @@ struct RegTile {
     for (int j = 0; j < kPV; ++j) set_lane<raw_t>(cv, j, c);
     __builtin_amdgcn_raw_buffer_store_b128(cv, row_rsrc(row + base, len),
                                            fresh_tid() * kBytes + i * kSpan * static_cast<int>(sizeof(raw_t)), 0,
-                                           kNtStores ? 2 : 0);
+                                           kStorePolicy);
   }
 
   // row[idx] = c for every valid element of this thread, without its data.
@@ -215,7 +215,7 @@ struct RegTile {
       vec_t o = {0u, 0u, 0u, 0u};
 #pragma unroll
       for (int j = 0; j < kPV; ++j) set_lane<raw_t>(o, j, g(lane_of<raw_t>(q, j), base + e0 + j));
-      __builtin_amdgcn_raw_buffer_store_b128(o, rs, e0 * static_cast<int>(sizeof(raw_t)), 0, kNtStores ? 2 : 0);
+      __builtin_amdgcn_raw_buffer_store_b128(o, rs, e0 * static_cast<int>(sizeof(raw_t)), 0, kStorePolicy);
     }
   }
 };

@@ -56,7 +56,7 @@ __device__ __forceinline__ uint32_t block_incl_scan_u32(uint32_t v, uint32_t* wt
   const int l = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
   v = wave_incl_scan_u32(v);
   if (l == kWave - 1) wtot[w] = v;
-  __syncthreads();
+  lds_barrier();
   // totals of the waves before this one: lane i < w contributes wave i's total
   const uint32_t base = wave_sum_u32(l < w ? wtot[l] : 0u);
   return v + base;
@@ -66,7 +66,7 @@ __device__ __forceinline__ uint64_t block_incl_scan_u64(uint64_t v, uint64_t* wt
   const int l = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
   v = wave_incl_scan_u64(v);
   if (l == kWave - 1) wtot[w] = v;
-  __syncthreads();
+  lds_barrier();
   const uint64_t base = wave_sum_u64(l < w ? wtot[l] : 0ull);
   return v + base;
 }
@@ -108,16 +108,28 @@ __device__ __forceinline__ uint64_t row_incl_scan_u64(uint64_t v) {
 // total, bin 0 is selected. Result in ss.bin, ss.above (count strictly
 // above) and ss.bcnt, visible after the call. Wave 0 scans (the histogram
 // must be complete: callers place a barrier before) and clears the bins.
+// LEAN keeps the histogram reads two at a time (for steps where the row tile
+// still occupies most registers); otherwise all of a lane's bins are read at
+// once, so the scan waits for one shared-memory round trip instead of several.
+template <bool LEAN = false>
 __device__ __forceinline__ void sel_pick_count(SelSmem& ss, uint32_t target) {
   if (threadIdx.x < kWave) {
     const int l = static_cast<int>(threadIdx.x);
     const int base = kBins - kPickSpan * (l + 1);
     const vec_t* cv = reinterpret_cast<const vec_t*>(&ss.cnt[base]);
     uint32_t sum = 0;
+    if constexpr (LEAN) {
 #pragma unroll 2
-    for (int q = 0; q < kPickSpan / 4; ++q) {
-      const vec_t c4 = cv[q];
-      sum += c4.x + c4.y + c4.z + c4.w;
+      for (int q = 0; q < kPickSpan / 4; ++q) {
+        const vec_t c4 = cv[q];
+        sum += c4.x + c4.y + c4.z + c4.w;
+      }
+    } else {
+      vec_t c4[kPickSpan / 4];
+#pragma unroll
+      for (int q = 0; q < kPickSpan / 4; ++q) c4[q] = cv[q];
+#pragma unroll
+      for (int q = 0; q < kPickSpan / 4; ++q) sum += c4[q].x + c4[q].y + c4[q].z + c4[q].w;
     }
     const uint32_t incl = wave_incl_scan_u32(sum);
     const uint32_t total = lane63_u32(incl);
@@ -143,21 +155,31 @@ __device__ __forceinline__ void sel_pick_count(SelSmem& ss, uint32_t target) {
 #pragma unroll
     for (int q = 0; q < kPickSpan / 4; ++q) cw[q] = z;
   }
-  __syncthreads();
+  lds_barrier();
 }
 
 // The same on the mass histogram: first bin whose running mass reaches
 // target >= 1; also reports the bin's count and mass. Clears both histograms.
+template <bool LEAN = false>
 __device__ __forceinline__ void sel_pick_mass(SelSmem& ss, uint64_t target) {
   if (threadIdx.x < kWave) {
     const int l = static_cast<int>(threadIdx.x);
     const int base = kBins - kPickSpan * (l + 1);
     const vec_t* mv = reinterpret_cast<const vec_t*>(&ss.mass[base]);  // two u64 per vector
     uint64_t sum = 0;
+    if constexpr (LEAN) {
 #pragma unroll 2
-    for (int q = 0; q < kPickSpan / 2; ++q) {
-      const vec_t m2 = mv[q];
-      sum += (static_cast<uint64_t>(m2.y) << 32 | m2.x) + (static_cast<uint64_t>(m2.w) << 32 | m2.z);
+      for (int q = 0; q < kPickSpan / 2; ++q) {
+        const vec_t m2 = mv[q];
+        sum += (static_cast<uint64_t>(m2.y) << 32 | m2.x) + (static_cast<uint64_t>(m2.w) << 32 | m2.z);
+      }
+    } else {
+      vec_t m2[kPickSpan / 2];
+#pragma unroll
+      for (int q = 0; q < kPickSpan / 2; ++q) m2[q] = mv[q];
+#pragma unroll
+      for (int q = 0; q < kPickSpan / 2; ++q)
+        sum += (static_cast<uint64_t>(m2[q].y) << 32 | m2[q].x) + (static_cast<uint64_t>(m2[q].w) << 32 | m2[q].z);
     }
     const uint64_t incl = wave_incl_scan_u64(sum);
     const uint64_t total = lane63_u64(incl);
@@ -188,7 +210,7 @@ __device__ __forceinline__ void sel_pick_mass(SelSmem& ss, uint64_t target) {
 #pragma unroll
     for (int q = 0; q < kPickSpan / 4; ++q) cw[q] = z;
   }
-  __syncthreads();
+  lds_barrier();
 }
 
 // Top-k and top-p together from one pass of both histograms over a range
@@ -205,18 +227,18 @@ __device__ __forceinline__ void sel_pick_joint(SelSmem& ss, uint32_t k, float t)
     const int base = kBins - kPickSpan * (l + 1);
     const vec_t* cv = reinterpret_cast<const vec_t*>(&ss.cnt[base]);
     const vec_t* mv = reinterpret_cast<const vec_t*>(&ss.mass[base]);
+    vec_t c4[kPickSpan / 4], m2[kPickSpan / 2];
+#pragma unroll
+    for (int q = 0; q < kPickSpan / 4; ++q) c4[q] = cv[q];
+#pragma unroll
+    for (int q = 0; q < kPickSpan / 2; ++q) m2[q] = mv[q];
     uint32_t csum = 0;
-#pragma unroll 2
-    for (int q = 0; q < kPickSpan / 4; ++q) {
-      const vec_t c4 = cv[q];
-      csum += c4.x + c4.y + c4.z + c4.w;
-    }
+#pragma unroll
+    for (int q = 0; q < kPickSpan / 4; ++q) csum += c4[q].x + c4[q].y + c4[q].z + c4[q].w;
     uint64_t msum = 0;
-#pragma unroll 2
-    for (int q = 0; q < kPickSpan / 2; ++q) {
-      const vec_t m2 = mv[q];
-      msum += (static_cast<uint64_t>(m2.y) << 32 | m2.x) + (static_cast<uint64_t>(m2.w) << 32 | m2.z);
-    }
+#pragma unroll
+    for (int q = 0; q < kPickSpan / 2; ++q)
+      msum += (static_cast<uint64_t>(m2[q].y) << 32 | m2[q].x) + (static_cast<uint64_t>(m2[q].w) << 32 | m2[q].z);
     const uint32_t cin = wave_incl_scan_u32(csum);
     const uint64_t min = wave_incl_scan_u64(msum);
     const uint32_t cex = cin - csum;
@@ -265,7 +287,7 @@ __device__ __forceinline__ void sel_pick_joint(SelSmem& ss, uint32_t k, float t)
 #pragma unroll
     for (int q = 0; q < kPickSpan / 4; ++q) cw[q] = z;
   }
-  __syncthreads();
+  lds_barrier();
 }
 
 // k-th largest (1-based, with multiplicity) of keyfn(raw, idx) over the
@@ -282,7 +304,7 @@ __device__ __forceinline__ uint32_t kth_largest_key(const Src& src, uint32_t k, 
       const uint32_t key = keyfn(raw, idx);
       if (key >= lo && key <= hi && pred(raw, idx)) atomicAdd(&ss.cnt[(key - lo) >> shift], 1u);
     });
-    __syncthreads();
+    lds_barrier();
     sel_pick_count(ss, k);
     const uint32_t bin = static_cast<uint32_t>(ss.bin);
     k -= ss.above;
@@ -305,8 +327,8 @@ __device__ __forceinline__ bool kth_largest_bound(const Src& src, uint32_t k, ui
     const uint32_t key = keyfn(raw, idx);
     if (key >= lo && key <= hi) atomicAdd(&ss.cnt[(key - lo) >> shift], 1u);
   });
-  __syncthreads();
-  sel_pick_count(ss, k);
+  lds_barrier();
+  sel_pick_count<true>(ss, k);
   const bool ok = !(ss.bin == 0 && ss.above + ss.bcnt < k);
   bound = lo + (static_cast<uint32_t>(ss.bin) << shift);
   return ok;
@@ -320,7 +342,8 @@ __device__ __forceinline__ bool kth_largest_bound(const Src& src, uint32_t k, ui
 template <class DT, class Src>
 __device__ __forceinline__ uint32_t boundary_index(const Src& src, uint32_t Kp, uint64_t need, uint32_t cnt,
                                                    uint64_t bmass, int V, SelSmem& ss) {
-  const uint64_t eg = bmass / (cnt ? cnt : 1u);
+  if (cnt <= 1) return 0;  // a single element: it is the last survivor
+  const uint64_t eg = bmass / cnt;
   const uint64_t ns64 = eg ? (need + eg - 1) / eg : cnt;
   uint32_t ns = ns64 >= cnt ? cnt : static_cast<uint32_t>(ns64);
   if (ns < 1) ns = 1;
@@ -368,7 +391,7 @@ __device__ __forceinline__ void topp_boundary(const Src& src, uint32_t lo, uint3
         atomicAdd(&ss.cnt[bin], 1u);
       }
     });
-    __syncthreads();
+    lds_barrier();
     sel_pick_mass(ss, thr - acc);
     acc += ss.above64;
     cnt = ss.bcnt;
@@ -399,8 +422,8 @@ __device__ __forceinline__ bool topp_bound(const Src& src, uint32_t lo, uint32_t
       atomicAdd(&ss.cnt[bin], 1u);
     }
   });
-  __syncthreads();
-  sel_pick_mass(ss, thr);
+  lds_barrier();
+  sel_pick_mass<true>(ss, thr);
   const bool ok = !(ss.bin == 0 && ss.above64 + ss.bmass < thr);
   bound = lo + (static_cast<uint32_t>(ss.bin) << shift);
   return ok;

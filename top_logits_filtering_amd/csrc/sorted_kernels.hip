@@ -41,11 +41,11 @@ __device__ __forceinline__ uint64_t block_exscan_u64(uint64_t v, RowSmem& sm, ui
   const int w = threadIdx.x / kWave;
   const uint64_t incl = wave_incl_scan_u64(v);
   if (l == kWave - 1) sm.redu[w] = incl;
-  __syncthreads();
+  lds_barrier();
   const uint64_t x = l < kWaves ? sm.redu[l] : 0ull;
   const uint64_t wbase = wave_sum_u64(l < w ? x : 0ull);
   const uint64_t tot = wave_sum_u64(x);
-  __syncthreads();
+  lds_barrier();
   total = tot;
   return wbase + incl - v;
 }
@@ -155,13 +155,13 @@ __global__ __launch_bounds__(kThreads) void sorted_logits_kernel(
 
   const int words = (len + 31) / 32;
   for (int i = threadIdx.x; i < words; i += kThreads) ties[i] = 0;
-  __syncthreads();
+  lds_barrier();
   const int32_t* __restrict__ si = sorted_indices + row_off;
   for (int j = bd.a + static_cast<int>(threadIdx.x); j < bd.F; j += kThreads) {
     const int v = si[j] - v0;
     if (v >= 0 && v < len) atomicOr(&ties[v >> 5], 1u << (v & 31));
   }
-  __syncthreads();
+  lds_barrier();
 
   const uint32_t KF = bd.KF;
   tile.store(orow, [&](raw_t r, int idx) {

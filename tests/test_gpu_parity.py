@@ -183,3 +183,28 @@ def test_with_sorted_workload5_sampled():
     # the sorting entry on the same logits agrees with the pre-sorted entry
     again = gpu_apply(wl.logits[rows], wl.dtype, wl.p[rows], wl.k[rows])
     assert np.array_equal(again, got[rows])
+
+
+@pytest.mark.parametrize("dtype,V", [("bf16", 151936), ("f32", 65536), ("f16", 32000)])
+def test_candidate_plan_branch_points(dtype, V):
+    """Rows held in registers, with k and p placed around the plan's branch
+    points: candidate counts of about one wave (one-wave ranking up to 64),
+    the one-pass joint selection, k beyond the 2048 per-thread maxima, and
+    top-p boundaries inside runs of equal values (values on a 0.5 grid)."""
+    total = ParityReport()
+    seed = 900
+    for scale in (1.0, 3.0):
+        seed += 1
+        xb = random_rows(seed, 2, V, dtype, kind="ties", scale=scale)
+        for kv in (0, 1, 5, 40, 63, 64, 65, 100, 500, 1000, 2047, 2048, 2049, 3000):
+            for pv in (None, 0.05, 0.5, 0.9, 0.99):
+                k = np.full(2, kv, np.int32)
+                p = None if pv is None else f32_to_bits(np.full(2, pv, np.float32), dtype)
+                if p is None and kv == 0:
+                    continue
+                got = gpu_apply(xb, dtype, p, k)
+                ref = oracle_apply(xb, dtype, p, k)
+                rep = compare(got, xb, ref, dtype)
+                assert rep.hard_mismatches == 0, (scale, kv, pv, rep.details[:2])
+                total.merge(rep)
+    say(f"{dtype} V={V}: {total}")

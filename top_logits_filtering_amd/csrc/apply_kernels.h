@@ -24,10 +24,14 @@
 //     mass and the top-p boundary cannot lie below it. One 1024-bin
 //     histogram pass gives the bound L as a bin edge;
 //  5. every vector whose maximum is >= L is copied into a list in shared
-//     memory, placed by wave ballots (one shared-memory atomic per wave);
-//  6. the exact selection (row_select.h) runs on the elements >= L of those
-//     vectors only;
-//  7. after the -inf stores have completed, the survivors are written over
+//     memory (placed by wave ballots, one shared-memory atomic per wave),
+//     then the elements >= L of those vectors into a list of (raw, index)
+//     pairs, at most 5 per thread, which the selection keeps in registers;
+//  6. the exact selection (row_select.h) runs on those candidates only: one
+//     wave ranks them directly when there are at most 64; joint rows whose
+//     candidate keys span fewer than 1024 values take one pass of count and
+//     mass histograms; other rows take range-adaptive radix passes;
+//  7. once every -inf store has completed, the survivors are written over
 //     them.
 // Whenever a bound cannot be formed (k > 2048, top-p mass not reached) or the
 // list overflows, the block falls back to the multi-pass plan, which

@@ -54,6 +54,7 @@ namespace tkp {
 constexpr int kTop2 = 2 * kThreads;
 constexpr int kMaxVecs = 20;
 constexpr int kCandVecCap = 2048;  // candidate vectors kept in shared memory
+constexpr int kStreamVmSlots = 32;  // streamed rows: vector maxima kept for this many layers
 constexpr int kCandPerThread = 5;
 constexpr int kCandCap = kCandPerThread * kThreads;  // candidate elements kept in shared memory
 
@@ -90,6 +91,7 @@ struct ApplySmem {
   float acc[kThreads];
   union {
     uint32_t vmw[(kMaxVecs + 1) / 2][kThreads];  // per-vector maxima (16-bit bounds, two per word), steps 1-5
+    uint16_t vmh[kStreamVmSlots][kThreads];      // the same for streamed rows, one per layer
     struct {
       uint32_t raw[kCandCap];  // candidate elements: raw bits
       uint32_t idx[kCandCap];  // and row indices
@@ -101,8 +103,7 @@ struct ApplySmem {
   uint32_t ncand;  // candidate elements reserved so far
   uint32_t sK, sI, sFallback;  // result of the one-wave selection
 };
-static_assert(sizeof(uint32_t) * 2 * kCandCap <= sizeof(uint32_t) * ((kMaxVecs + 1) / 2) * kThreads,
-              "the candidate element list reuses the space of the per-vector maxima");
+
 
 // The candidate elements (every element >= the bound of the row), read once
 // from shared memory into registers: element c of the list goes to thread
@@ -273,6 +274,8 @@ __device__ __forceinline__ void filter_row(const Tile& tile, const typename DT::
       } else {
         S.vmw[i >> 1][threadIdx.x] = vm_even | (h << 16);
       }
+    } else {
+      if (i < kStreamVmSlots) S.vmh[i][threadIdx.x] = static_cast<uint16_t>(DT::ub16(vm));
     }
     M2 = fmaxf(M2, fminf(M1, vm));
     M1 = fmaxf(M1, vm);
@@ -358,6 +361,8 @@ __device__ __forceinline__ void filter_row(const Tile& tile, const typename DT::
   // matter: every statistic taken below is order-independent, and ties are
   // resolved by the stored indices.
   const float Lf = DT::value(DT::raw_of_key(L));
+  // streamed rows: the layers' vector maxima are in shared memory when they fit
+  const bool vm_in_lds = !Tile::kRegisters && V <= kStreamVmSlots * kThreads * kPV;
   uint32_t nvec = 0;
   int ncand = 0;
   if (!fallback) {
@@ -365,6 +370,8 @@ __device__ __forceinline__ void filter_row(const Tile& tile, const typename DT::
       float vmv;
       if constexpr (Tile::kRegisters) {
         vmv = DT::ub16_value((S.vmw[i >> 1][threadIdx.x] >> ((i & 1) * 16)) & 0xFFFFu);
+      } else if (vm_in_lds) {
+        vmv = (e0 < V) ? DT::ub16_value(S.vmh[i][threadIdx.x]) : -INFINITY;
       } else {
         const vec_t q = tile.vec_at(i, e0);
         vmv = -INFINITY;

@@ -235,13 +235,19 @@ struct GlobalTile {
   int base;
   int len;
   bool aligned;
+  bool vec_ok;  // 16-byte aligned and a whole number of vectors: bounded buffer loads
 
   __device__ __forceinline__ void load(const raw_t* __restrict__ row, int v0, int n) {
     src = row + v0;
     base = v0;
     len = n;
     aligned = (reinterpret_cast<uintptr_t>(src) & 15u) == 0;
+    vec_ok = aligned && (n % kPV) == 0;
   }
+
+  // Vector layers handled per batch by the first traversal: their loads are
+  // issued together, so each thread keeps several requests in flight.
+  static constexpr int kBatch = 8;
 
   // elements e0 .. e0+kPV-1 (zero past the end)
   __device__ __forceinline__ vec_t read(int e0) const {
@@ -295,6 +301,28 @@ struct GlobalTile {
 
   template <class F>
   __device__ __forceinline__ void for_each_vec_values(F&& f) const {
+    if (vec_ok) {
+      const __amdgpu_buffer_rsrc_t rs = row_rsrc(src, len);
+      const int tid = static_cast<int>(threadIdx.x);
+      for (int l0 = 0; l0 < len; l0 += kBatch * kSpan) {
+        vec_t q[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u)
+          q[u] = __builtin_amdgcn_raw_buffer_load_b128(
+              rs, (l0 + u * kSpan + tid * kPV) * static_cast<int>(sizeof(raw_t)), 0, kLoadPolicy);
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          const int e0 = l0 + u * kSpan + tid * kPV;
+          if (l0 + u * kSpan < len) {  // uniform: the layer exists
+            float x[kPV];
+#pragma unroll
+            for (int j = 0; j < kPV; ++j) x[j] = (e0 + j < len) ? DT::value(lane_of<raw_t>(q[u], j)) : -INFINITY;
+            f(l0 / kSpan + u, x);
+          }
+        }
+      }
+      return;
+    }
     int i = 0;
 #pragma unroll 2
     for (int e0 = static_cast<int>(threadIdx.x) * kPV; e0 < len; e0 += kSpan, ++i) {

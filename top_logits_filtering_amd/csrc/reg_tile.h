@@ -203,6 +203,20 @@ struct RegTile {
     }
   }
 
+  // Whole output vectors: g(q, e0) returns the vector stored for slot data q
+  // whose first element is slice index e0.
+  template <class G>
+  __device__ __forceinline__ void store_vectors(raw_t* __restrict__ row, G&& g) const {
+    const __amdgpu_buffer_rsrc_t rs = row_rsrc(row + base, len);
+    const int tid = fresh_tid();
+#pragma unroll
+    for (int i = 0; i < NVEC; ++i) {
+      const int e0 = i * kSpan + tid * kPV;
+      const vec_t o = g(fresh(i), e0);
+      __builtin_amdgcn_raw_buffer_store_b128(o, rs, e0 * static_cast<int>(sizeof(raw_t)), 0, kStorePolicy);
+    }
+  }
+
   // row[idx] = g(raw, idx) for every valid element held by this thread.
   template <class G>
   __device__ __forceinline__ void store(raw_t* __restrict__ row, G&& g) const {

@@ -50,14 +50,25 @@ __device__ __forceinline__ uint64_t block_exscan_u64(uint64_t v, RowSmem& sm, ui
   return wbase + incl - v;
 }
 
+// The sorted values of one row: positions >= lo are read from a copy in
+// shared memory (prefetched before the row's logits slice, so reading them
+// does not wait behind that slice's loads), lower positions from global memory.
+// The sorted values of one row, read from global memory.
+template <class DT>
+struct SortedSrcGlobal {
+  using raw_t = typename DT::raw_t;
+  const raw_t* __restrict__ g;
+  __device__ __forceinline__ raw_t at(int j) const { return g[j]; }
+};
+
 // Smallest j <= hi such that key(sv[j..hi]) >= K, given key(sv[hi]) >= K and
 // an ascending row.
-template <class DT>
-__device__ __forceinline__ int first_at_or_above(const typename DT::raw_t* __restrict__ sv, int hi, uint32_t K, RowSmem& sm) {
+template <class DT, class Src>
+__device__ __forceinline__ int first_at_or_above(const Src& sv, int hi, uint32_t K, RowSmem& sm) {
   int top = hi;
   for (;;) {
     const int j = top - 1 - static_cast<int>(threadIdx.x);
-    const int cand = (j >= 0 && DT::key(sv[j]) < K) ? j : -1;
+    const int cand = (j >= 0 && DT::key(sv.at(j)) < K) ? j : -1;
     const int best = block_max_i32(cand, sm);
     if (best >= 0) return best + 1;
     top -= kThreads;
@@ -66,16 +77,16 @@ __device__ __forceinline__ int first_at_or_above(const typename DT::raw_t* __res
 }
 
 // Lowest sorted position F >= start whose mass strictly above is < thr.
-template <class DT>
-__device__ __forceinline__ int scan_boundary(const typename DT::raw_t* __restrict__ sv, int start, int V, float m, uint64_t thr,
-                             RowSmem& sm) {
+template <class DT, class Src>
+__device__ __forceinline__ int scan_boundary(const Src& sv, int start, int V, float m, uint64_t thr,
+                                             RowSmem& sm) {
   int hi = V;
   uint64_t base = 0;
   for (;;) {
     const int lo = max(start, hi - kThreads);
     const int j = hi - 1 - static_cast<int>(threadIdx.x);
     const bool valid = j >= lo;
-    const uint64_t e = valid ? mass_fx(DT::value(sv[j]), m) : 0;
+    const uint64_t e = valid ? mass_fx(DT::value(sv.at(j)), m) : 0;
     uint64_t total;
     const uint64_t excl = block_exscan_u64(e, sm, total);
     const int cand = (valid && base + excl < thr) ? static_cast<int>(threadIdx.x) : -1;
@@ -94,31 +105,96 @@ struct SortedBoundary {
   int a;        // first sorted position holding key KF (positions a..F-1 are masked)
 };
 
-template <class DT>
-__device__ __forceinline__ SortedBoundary sorted_boundary(const typename DT::raw_t* __restrict__ sv, const RowParams& rp, int V,
-                                          RowSmem& sm) {
+template <class DT, class Src>
+__device__ __forceinline__ SortedBoundary sorted_boundary(const Src& sv, const RowParams& rp, int V,
+                                                          RowSmem& sm) {
   int start = 0;
   uint32_t Kk = 0;
   if (rp.k_on) {
     const int hi = V - static_cast<int>(rp.k);
-    Kk = DT::key(sv[hi]);
+    Kk = DT::key(sv.at(hi));
     start = first_at_or_above<DT>(sv, hi, Kk, sm);
   }
   int F = start;
   if (rp.pmode == kPTopOnly) {
     F = V - 1;
   } else if (rp.pmode == kPBoundary) {
-    const float m = DT::value(sv[V - 1]);
+    const float m = DT::value(sv.at(V - 1));
     uint64_t z = 0;
-    for (int j = start + static_cast<int>(threadIdx.x); j < V; j += kThreads) z += mass_fx(DT::value(sv[j]), m);
+    for (int j = start + static_cast<int>(threadIdx.x); j < V; j += kThreads) z += mass_fx(DT::value(sv.at(j)), m);
     const uint64_t Z = block_sum_u64(z, sm);
     const uint64_t thr = topp_threshold(rp.t, Z);
     F = (thr == 0) ? V - 1 : scan_boundary<DT>(sv, start, V, m, thr, sm);
   }
   SortedBoundary bd;
   bd.F = F;
-  bd.KF = DT::key(sv[F]);
+  bd.KF = DT::key(sv.at(F));
   bd.a = (rp.k_on && bd.KF == Kk) ? start : first_at_or_above<DT>(sv, F, bd.KF, sm);
+  return bd;
+}
+
+// Top sorted positions copied to shared memory before the slice loads; the
+// copy serves rows whose k plus a margin for a run of values equal to the
+// k-th largest fits in it.
+constexpr int kSortedPrefetch = 6144;
+constexpr int kSortedTieMargin = 1024;
+
+// The same boundary from the copy of the top R sorted values in shared
+// memory (position V - R + c at index c), for a top-k row whose run of values
+// equal to the k-th largest starts inside the copy. Runs are found by each
+// wave on its own (no barrier); the top-p walk gives every thread 8
+// consecutive positions from the top, so one exclusive scan of their masses
+// and one reduction find F.
+template <class DT>
+__device__ __forceinline__ int copy_run_start(const typename DT::raw_t* top, int c0, uint32_t K) {
+  const int lane = static_cast<int>(threadIdx.x) & (kWave - 1);
+  for (int base = c0;; base -= kWave) {
+    const int c = base - 1 - lane;
+    const bool below = c < 0 || DT::key(top[c]) < K;
+    const uint64_t m = __ballot(below);
+    if (m != 0) return base - (__ffsll(static_cast<unsigned long long>(m)) - 1);
+  }
+}
+
+template <class DT>
+__device__ __forceinline__ SortedBoundary sorted_boundary_copy(const typename DT::raw_t* top, int R, int V,
+                                                               const RowParams& rp, RowSmem& sm) {
+  constexpr int G = kSortedPrefetch / kThreads;  // positions per thread in the top-p walk (the whole copy)
+  const int ck = R - static_cast<int>(rp.k);
+  const uint32_t Kk = DT::key(top[ck]);
+  const int cs = copy_run_start<DT>(top, ck, Kk);
+  int F = cs;
+  if (rp.pmode == kPTopOnly) {
+    F = R - 1;
+  } else if (rp.pmode == kPBoundary) {
+    const float m = DT::value(top[R - 1]);
+    const int hi = R - G * static_cast<int>(threadIdx.x);  // this thread: positions hi-1 down to hi-G
+    // (the masses are computed twice rather than kept, which keeps two blocks
+    // resident per compute unit)
+    auto mass_at = [&](int c) { return c >= cs ? mass_fx(DT::value(top[c]), m) : 0ull; };
+    uint64_t tsum = 0;
+#pragma unroll
+    for (int g = 0; g < G; ++g) tsum += mass_at(hi - 1 - g);
+    uint64_t Z;
+    uint64_t above = block_exscan_u64(tsum, sm, Z);  // threads run from the top down
+    const uint64_t thr = topp_threshold(rp.t, Z);
+    if (thr == 0) {
+      F = R - 1;
+    } else {
+      int low = -1;  // this thread's lowest position whose mass strictly above is below thr
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const int c = hi - 1 - g;
+        if (c >= cs && above < thr) low = c;
+        above += mass_at(c);
+      }
+      F = R - 1 - block_max_i32(low >= 0 ? R - 1 - low : -1, sm);
+    }
+  }
+  SortedBoundary bd;
+  bd.KF = DT::key(top[F]);
+  bd.F = V - R + F;
+  bd.a = V - R + (bd.KF == Kk ? cs : copy_run_start<DT>(top, F, bd.KF));
   return bd;
 }
 
@@ -126,7 +202,7 @@ constexpr int kSortedVecs = 8;  // logits slice held in registers: 8 vectors per
 constexpr int kMaxSliceWords = (kThreads * kSortedVecs * 8) / 32;
 
 template <class DT, bool kRegs>
-__global__ __launch_bounds__(kThreads) void sorted_logits_kernel(
+__global__ __launch_bounds__(kThreads, 8) void sorted_logits_kernel(
     const typename DT::raw_t* __restrict__ sorted_value, const int32_t* __restrict__ sorted_indices,
     const typename DT::raw_t* __restrict__ p, const int32_t* __restrict__ k,
     const typename DT::raw_t* __restrict__ logits, typename DT::raw_t* __restrict__ out, int V, int S) {
@@ -135,23 +211,57 @@ __global__ __launch_bounds__(kThreads) void sorted_logits_kernel(
   constexpr int kCap = RegTile<DT, kSortedVecs>::kCapacity;
   __shared__ RowSmem sm;
   __shared__ uint32_t ties[kMaxSliceWords];
+  __shared__ __align__(16) raw_t top[kSortedPrefetch];
 
   const int b = blockIdx.x / S;
   const int s = blockIdx.x - b * S;
   const int v0 = s * kCap;
   const int len = min(kCap, V - v0);
   const size_t row_off = static_cast<size_t>(b) * V;
+  const raw_t* __restrict__ sv = sorted_value + row_off;
 
+  // p[b] and k[b], the top sorted values the boundary search reads, then the
+  // logits slice: vector loads complete in order, so the search waits only
+  // for what it reads. The top values are requested before k is known.
+  const RowParamsRaw<DT> rpr = fetch_row_params<DT>(p, k, b);
+  const int R = min(V, kSortedPrefetch);
+  constexpr int kPre = kSortedPrefetch / kThreads;
+  raw_t pre[kPre];
+  {
+    // bounded buffer loads of whole elements: no branch per load, so all of
+    // them are in flight together (positions past R read as zero, unused)
+    const __amdgpu_buffer_rsrc_t rs = row_rsrc(sv + (V - R), R);
+#pragma unroll
+    for (int u = 0; u < kPre; ++u) {
+      const int off = (u * kThreads + static_cast<int>(threadIdx.x)) * static_cast<int>(sizeof(raw_t));
+      if constexpr (sizeof(raw_t) == 2)
+        pre[u] = static_cast<raw_t>(__builtin_amdgcn_raw_buffer_load_b16(rs, off, 0, 0));
+      else
+        pre[u] = static_cast<raw_t>(__builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0));
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the slice's
   Tile tile;
   tile.load(logits + row_off, v0, len);
+  const RowParams rp = decode_row_params<DT>(rpr, V);
+#pragma unroll
+  for (int u = 0; u < kPre; ++u) top[u * kThreads + threadIdx.x] = pre[u];  // entries past R: zero, unused
+  lds_barrier();
 
-  const RowParams rp = decode_row_params<DT>(p, k, b, V);
   raw_t* __restrict__ orow = out + row_off;
   if (!rp.k_on && rp.pmode == kPNone) {
     tile.store(orow, [](raw_t r, int) { return r; });
     return;
   }
-  const SortedBoundary bd = sorted_boundary<DT>(sorted_value + row_off, rp, V, sm);
+  // the copy serves the whole search when the run of values equal to the
+  // k-th largest starts inside it (or the copy is the whole row)
+  const bool from_copy = rp.k_on && (R == V || (static_cast<int>(rp.k) + kSortedTieMargin <= R &&
+                                                DT::key(top[0]) < DT::key(top[R - static_cast<int>(rp.k)])));
+  SortedBoundary bd;
+  if (from_copy)
+    bd = sorted_boundary_copy<DT>(top, R, V, rp, sm);
+  else
+    bd = sorted_boundary<DT>(SortedSrcGlobal<DT>{sv}, rp, V, sm);
 
   const int words = (len + 31) / 32;
   for (int i = threadIdx.x; i < words; i += kThreads) ties[i] = 0;
@@ -164,15 +274,33 @@ __global__ __launch_bounds__(kThreads) void sorted_logits_kernel(
   lds_barrier();
 
   const uint32_t KF = bd.KF;
-  tile.store(orow, [&](raw_t r, int idx) {
-    const uint32_t key = DT::key(r);
-    bool keep = key > KF;
-    if (key == KF) {
-      const int v = idx - v0;
-      keep = ((ties[v >> 5] >> (v & 31)) & 1u) == 0;
-    }
-    return keep ? r : DT::kNegInf;
-  });
+  if (bd.a == bd.F) {  // no member of the lowest survivor's run is masked
+    tile.store(orow, [&](raw_t r, int) { return DT::key(r) >= KF ? r : DT::kNegInf; });
+  } else if constexpr (kRegs) {
+    // the masked flags of a vector's elements sit in one bitmap word
+    tile.store_vectors(orow, [&](const vec_t& q, int e0) {
+      const uint32_t w = ties[e0 >> 5] >> (e0 & 31);
+      vec_t o = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int j = 0; j < DT::kPerVec; ++j) {
+        const raw_t r = lane_of<raw_t>(q, j);
+        const uint32_t key = DT::key(r);
+        const bool keep = key > KF || (key == KF && ((w >> j) & 1u) == 0);
+        set_lane<raw_t>(o, j, keep ? r : DT::kNegInf);
+      }
+      return o;
+    });
+  } else {
+    tile.store(orow, [&](raw_t r, int idx) {
+      const uint32_t key = DT::key(r);
+      bool keep = key > KF;
+      if (key == KF) {
+        const int v = idx - v0;
+        keep = ((ties[v >> 5] >> (v & 31)) & 1u) == 0;
+      }
+      return keep ? r : DT::kNegInf;
+    });
+  }
 }
 
 constexpr int kScatterSlice = 65536;
@@ -190,7 +318,8 @@ __global__ __launch_bounds__(kThreads) void sorted_scatter_kernel(
   const int32_t* __restrict__ si = sorted_indices + row_off;
   const RowParams rp = decode_row_params<DT>(p, k, b, V);
   int F = 0;
-  if (rp.k_on || rp.pmode != kPNone) F = sorted_boundary<DT>(sv, rp, V, sm).F;
+  const SortedSrcGlobal<DT> src{sv};
+  if (rp.k_on || rp.pmode != kPNone) F = sorted_boundary<DT>(src, rp, V, sm).F;
   const int j0 = s * kScatterSlice;
   const int j1 = min(V, j0 + kScatterSlice);
   auto* __restrict__ orow = out + row_off;

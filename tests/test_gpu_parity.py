@@ -208,3 +208,27 @@ def test_candidate_plan_branch_points(dtype, V):
                 assert rep.hard_mismatches == 0, (scale, kv, pv, rep.details[:2])
                 total.merge(rep)
     say(f"{dtype} V={V}: {total}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_with_sorted_copy_boundary(dtype):
+    """Pre-sorted rows around the shared-memory copy of the top values: k near
+    the copy's reach (k + the tie margin against its size), long runs of equal
+    values at the k-th largest (values on a 0.5 grid), whole rows that fit."""
+    need_gpu()
+    total = ParityReport()
+    seed = 1300
+    for V, kind in ((6144, "normal"), (70001, "normal"), (70001, "ties"), (262144, "normal")):
+        seed += 1
+        xb = random_rows(seed, 2, V, dtype, kind=kind, scale=3.0)
+        idx, sv = stable_ascending_sort(xb, dtype)
+        for kv in (1, 2, 50, 1000, 4095, 5119, 5120, 5121, 6000):
+            for pv in (None, 0.3, 0.9):
+                k = np.full(2, kv, np.int32)
+                p = None if pv is None else f32_to_bits(np.full(2, pv, np.float32), dtype)
+                ref = oracle_sorted(sv, idx, dtype, p, k, logits_bits=xb)
+                got = gpu_with_sorted(sv, idx, dtype, p, k, xb)
+                rep = compare(got, xb, ref, dtype)
+                assert rep.hard_mismatches == 0, (V, kind, kv, pv, rep.details[:2])
+                total.merge(rep)
+    say(f"with_sorted copy boundary {dtype}: {total}")

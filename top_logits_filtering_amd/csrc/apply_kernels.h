@@ -471,8 +471,17 @@ __device__ __forceinline__ void filter_row(const Tile& tile, const typename DT::
     }
   }
 
-  if constexpr (Tile::kRegisters)
-    tile.template store_const_range<store_upto<Tile::kVecs, 3>(), store_upto<Tile::kVecs, 4>()>(orow, DT::kNegInf);
+  // The last portion of the -inf stores. Joint rows selected in one pass
+  // issue it inside the selection instead: waves 1-15 while wave 0 alone
+  // scans the histograms (so that scan runs while they wait for room to
+  // store), wave 0 right after.
+  auto last_stores = [&]() {
+    if constexpr (Tile::kRegisters)
+      tile.template store_const_range<store_upto<Tile::kVecs, 3>(), store_upto<Tile::kVecs, 4>()>(orow, DT::kNegInf);
+  };
+  const bool joint_one_pass = !fallback && ncand > kWave && rp.k_on && rp.pmode == kPBoundary &&
+                              shift_for_range(kmax - L) == 0;
+  if (!joint_one_pass) last_stores();
   // 6. exact selection on the candidates (all elements with key in [L, kmax])
   CandElems<DT> cs;
   cs.load(S, fallback ? 0 : ncand);
@@ -494,7 +503,7 @@ __device__ __forceinline__ void filter_row(const Tile& tile, const typename DT::
   } else if (!fallback) {
     if (top_only && !rp.k_on) {
       top_position<DT>(cs, sm, K, I);
-    } else if (rp.k_on && rp.pmode == kPBoundary && shift_for_range(kmax - L) == 0) {
+    } else if (joint_one_pass) {
       // top-k and top-p from one pass: every bin of [L, kmax] holds one key
       cs.for_each([&](auto raw, int) {
         const uint32_t bin = DT::key(raw) - L;
@@ -502,7 +511,9 @@ __device__ __forceinline__ void filter_row(const Tile& tile, const typename DT::
         atomicAdd(&ss.cnt[bin], 1u);
       });
       lds_barrier();
+      if (threadIdx.x >= kWave) last_stores();
       sel_pick_joint(ss, rp.k, rp.t);
+      if (threadIdx.x < kWave) last_stores();
       const uint64_t thr2 = ss.thr;
       if (thr2 == 0) {
         top_position<DT>(cs, sm, K, I);

@@ -479,14 +479,19 @@ __device__ __forceinline__ void filter_row(const Tile& tile, const typename DT::
     if constexpr (Tile::kRegisters)
       tile.template store_const_range<store_upto<Tile::kVecs, 3>(), store_upto<Tile::kVecs, 4>()>(orow, DT::kNegInf);
   };
-  const bool joint_one_pass = !fallback && ncand > kWave && rp.k_on && rp.pmode == kPBoundary &&
-                              shift_for_range(kmax - L) == 0;
-  if (!joint_one_pass) last_stores();
+  const bool small = !fallback && ncand <= kWave;
+  const bool one_key_bins = shift_for_range(kmax - L) == 0;
+  const bool joint_one_pass = !fallback && !small && rp.k_on && rp.pmode == kPBoundary && one_key_bins;
+  const bool topk_one_pass = !fallback && !small && rp.k_on && rp.pmode == kPNone && one_key_bins;
+  // paths with a one-wave step take the last stores inside it
+  const bool shadow_stores = small || joint_one_pass || topk_one_pass;
+  if (!shadow_stores) last_stores();
   // 6. exact selection on the candidates (all elements with key in [L, kmax])
   CandElems<DT> cs;
   cs.load(S, fallback ? 0 : ncand);
   uint32_t K = 0, I = 0;
-  if (!fallback && ncand <= kWave) {
+  if (small) {
+    if (threadIdx.x >= kWave) last_stores();
     if (threadIdx.x < kWave) {
       bool fb;
       select_small<DT>(S, ncand, rp, m, thr, top_only, K, I, fb);
@@ -495,6 +500,7 @@ __device__ __forceinline__ void filter_row(const Tile& tile, const typename DT::
         S.sI = I;
         S.sFallback = fb ? 1u : 0u;
       }
+      last_stores();
     }
     lds_barrier();
     K = S.sK;
@@ -503,6 +509,14 @@ __device__ __forceinline__ void filter_row(const Tile& tile, const typename DT::
   } else if (!fallback) {
     if (top_only && !rp.k_on) {
       top_position<DT>(cs, sm, K, I);
+    } else if (topk_one_pass) {
+      // the k-th largest from one count pass: every bin of [L, kmax] holds one key
+      cs.for_each([&](auto raw, int) { atomicAdd(&ss.cnt[DT::key(raw) - L], 1u); });
+      lds_barrier();
+      if (threadIdx.x >= kWave) last_stores();
+      sel_pick_count(ss, rp.k);
+      if (threadIdx.x < kWave) last_stores();
+      K = L + static_cast<uint32_t>(ss.bin);
     } else if (joint_one_pass) {
       // top-k and top-p from one pass: every bin of [L, kmax] holds one key
       cs.for_each([&](auto raw, int) {

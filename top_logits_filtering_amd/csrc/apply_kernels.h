@@ -308,11 +308,11 @@ __device__ __forceinline__ void filter_row(const Tile& tile, const typename DT::
     S.ncand = 0;
   }
 
-  // 2. the whole row as -inf (register tiles stored theirs in step 1). From
-  // here until the survivors are written the block touches only registers
+  // 2. the whole row as -inf, in portions issued from here on (register
+  // tiles) or at once after the compaction, whose reads of candidate vectors
+  // would otherwise wait behind the stores (streamed rows). From here until
+  // the survivors are written a register tile's block touches only registers
   // and shared memory, so nothing waits behind these stores while they drain.
-  if constexpr (!Tile::kRegisters) tile.store_const(orow, DT::kNegInf);
-
   if constexpr (Tile::kRegisters)
     tile.template store_const_range<store_upto<Tile::kVecs, 0>(), store_upto<Tile::kVecs, 1>()>(orow, DT::kNegInf);
   // 3. row maximum, smallest finite per-thread maximum, Z for top-p-only rows
@@ -478,6 +478,8 @@ __device__ __forceinline__ void filter_row(const Tile& tile, const typename DT::
   auto last_stores = [&]() {
     if constexpr (Tile::kRegisters)
       tile.template store_const_range<store_upto<Tile::kVecs, 3>(), store_upto<Tile::kVecs, 4>()>(orow, DT::kNegInf);
+    else
+      tile.store_const(orow, DT::kNegInf);
   };
   const bool small = !fallback && ncand <= kWave;
   const bool one_key_bins = shift_for_range(kmax - L) == 0;
@@ -485,7 +487,7 @@ __device__ __forceinline__ void filter_row(const Tile& tile, const typename DT::
   const bool topk_one_pass = !fallback && !small && rp.k_on && rp.pmode == kPNone && one_key_bins;
   // paths with a one-wave step take the last stores inside it
   const bool shadow_stores = small || joint_one_pass || topk_one_pass;
-  if (!shadow_stores) last_stores();
+  if (!shadow_stores && !fallback) last_stores();  // a fallback rewrites the whole row
   // 6. exact selection on the candidates (all elements with key in [L, kmax])
   CandElems<DT> cs;
   cs.load(S, fallback ? 0 : ncand);

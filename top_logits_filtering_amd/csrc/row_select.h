@@ -44,6 +44,9 @@ struct alignas(16) SelSmem {
   uint64_t bmass;
   int kbin;      // joint pick: bin of the k-th largest
   uint64_t thr;  // joint pick: fixed-point top-p threshold over the top-k survivors
+  uint32_t run_n;              // boundary run gathered for one-wave ranking (zero between uses)
+  uint32_t run_idx[kWave];     // its indices
+  uint32_t run_res;
 };
 
 __device__ __forceinline__ int shift_for_range(uint32_t range) {
@@ -77,6 +80,7 @@ __device__ __forceinline__ uint64_t block_incl_scan_u64(uint64_t v, uint64_t* wt
 __device__ __forceinline__ void sel_reset(SelSmem& ss) {
   ss.cnt[threadIdx.x] = 0;
   ss.mass[threadIdx.x] = 0;
+  if (threadIdx.x == 0) ss.run_n = 0;
 }
 
 // Bins per lane when one wave scans the whole histogram: lane l owns the 16
@@ -348,6 +352,24 @@ __device__ __forceinline__ uint32_t boundary_index(const Src& src, uint32_t Kp, 
   uint32_t ns = ns64 >= cnt ? cnt : static_cast<uint32_t>(ns64);
   if (ns < 1) ns = 1;
   if (ns >= cnt) return 0;
+  if (cnt <= static_cast<uint32_t>(kWave)) {
+    // a short run: gather its indices and let wave 0 take the ns-th largest
+    src.for_each([&](auto raw, int idx) {
+      if (DT::key(raw) == Kp) ss.run_idx[atomicAdd(&ss.run_n, 1u)] = static_cast<uint32_t>(idx);
+    });
+    lds_barrier();
+    if (threadIdx.x < kWave) {
+      const int l = static_cast<int>(threadIdx.x);
+      const int n = static_cast<int>(cnt);
+      const uint32_t mine = l < n ? ss.run_idx[l] : 0u;
+      uint32_t rank = 0;  // indices are distinct: larger ones come first
+      for (int i = 0; i < n; ++i) rank += readlane_u32(mine, i) > mine ? 1u : 0u;
+      if (l < n && rank == ns - 1) ss.run_res = mine;
+      if (l == 0) ss.run_n = 0;
+    }
+    lds_barrier();
+    return ss.run_res;
+  }
   return kth_largest_key(
       src, ns, 0u, static_cast<uint32_t>(V - 1), [](auto, int idx) { return static_cast<uint32_t>(idx); },
       [Kp](auto raw, int) { return DT::key(raw) == Kp; }, ss);

@@ -418,12 +418,9 @@ __device__ __forceinline__ void filter_row(const Tile& tile, const typename DT::
           uint32_t pos0 = 0;
           if ((threadIdx.x & (kWave - 1)) == 0) pos0 = atomicAdd(&S.nvec, static_cast<uint32_t>(__popcll(mask)));
           pos0 = __builtin_amdgcn_readfirstlane(pos0);
-          if (c) {
+          if (c) {  // only the position: the vectors are gathered together below
             const uint32_t pos = pos0 + lanes_below(mask);
-            if (pos < static_cast<uint32_t>(kCandVecCap)) {
-              S.cvec[pos] = tile.vec_at(i, e0);
-              S.ce0[pos] = static_cast<uint32_t>(e0);
-            }
+            if (pos < static_cast<uint32_t>(kCandVecCap)) S.ce0[pos] = static_cast<uint32_t>(e0);
           }
         }
       });
@@ -432,11 +429,30 @@ __device__ __forceinline__ void filter_row(const Tile& tile, const typename DT::
     nvec = S.nvec;
     fallback = nvec > static_cast<uint32_t>(kCandVecCap);
     if (!fallback) {
-      // each thread takes listed vectors tid and tid + 1024; per element lane
-      // j of the vectors a wave ballot places the elements >= L
-      for (int vi = static_cast<int>(threadIdx.x); vi < static_cast<int>(nvec); vi += kThreads) {
-        const vec_t q = S.cvec[vi];
-        const int e0 = static_cast<int>(S.ce0[vi]);
+      // each thread takes listed vectors tid and tid + 1024 (a streamed row
+      // requests both from global memory at once); per element lane j of the
+      // vectors a wave ballot places the elements >= L
+      constexpr int kRounds = kCandVecCap / kThreads;
+      vec_t qs[kRounds];
+      int e0s[kRounds];
+#pragma unroll
+      for (int r = 0; r < kRounds; ++r) {
+        const int vi = static_cast<int>(threadIdx.x) + r * kThreads;
+        qs[r] = vec_t{0u, 0u, 0u, 0u};
+        e0s[r] = V;  // past the row: no element of an unused slot passes
+        if (vi < static_cast<int>(nvec)) {
+          e0s[r] = static_cast<int>(S.ce0[vi]);
+          if constexpr (Tile::kRegisters)
+            qs[r] = S.cvec[vi];
+          else
+            qs[r] = tile.gather(e0s[r]);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < kRounds; ++r) {
+        if (r * kThreads >= static_cast<int>(nvec)) break;  // uniform
+        const vec_t q = qs[r];
+        const int e0 = e0s[r];
         uint64_t mk[kPV];
         uint32_t wtot = 0;
 #pragma unroll
@@ -444,11 +460,9 @@ __device__ __forceinline__ void filter_row(const Tile& tile, const typename DT::
           mk[j] = __ballot(e0 + j < V && DT::value(lane_of<raw_t>(q, j)) >= Lf);
           wtot += static_cast<uint32_t>(__popcll(mk[j]));
         }
-        // one shared-memory atomic per wave, by its first active lane
-        const uint64_t active = __ballot(1);
+        // one shared-memory atomic per wave that has elements
         uint32_t pos0 = 0;
-        if (static_cast<int>(threadIdx.x & (kWave - 1)) == __ffsll(static_cast<unsigned long long>(active)) - 1)
-          pos0 = atomicAdd(&S.ncand, wtot);
+        if (wtot != 0 && (threadIdx.x & (kWave - 1)) == 0) pos0 = atomicAdd(&S.ncand, wtot);
         uint32_t pos = __builtin_amdgcn_readfirstlane(pos0);
 #pragma unroll
         for (int j = 0; j < kPV; ++j) {

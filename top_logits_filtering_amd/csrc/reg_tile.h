@@ -313,27 +313,48 @@ struct GlobalTile {
     }
   }
 
+  // Vector e0 .. e0+kPV-1 of a candidate (e0 < len, a multiple of kPV).
+  __device__ __forceinline__ vec_t gather(int e0) const {
+    if (vec_ok)
+      return __builtin_amdgcn_raw_buffer_load_b128(row_rsrc(src, len), e0 * static_cast<int>(sizeof(raw_t)), 0,
+                                                   kLoadPolicy);
+    return read(e0);
+  }
+
   template <class F>
   __device__ __forceinline__ void for_each_vec_values(F&& f) const {
     if (vec_ok) {
+      // two batches in flight: the next batch is requested before the
+      // current one is consumed. Loads past the row end read zero and are
+      // never consumed.
       const __amdgpu_buffer_rsrc_t rs = row_rsrc(src, len);
       const int tid = static_cast<int>(threadIdx.x);
-      for (int l0 = 0; l0 < len; l0 += kBatch * kSpan) {
-        vec_t q[kBatch];
+      const int layers = (len + kSpan - 1) / kSpan;
+      vec_t qa[kBatch], qb[kBatch];
+      auto request = [&](vec_t(&q)[kBatch], int l0) {
 #pragma unroll
         for (int u = 0; u < kBatch; ++u)
           q[u] = __builtin_amdgcn_raw_buffer_load_b128(
-              rs, (l0 + u * kSpan + tid * kPV) * static_cast<int>(sizeof(raw_t)), 0, kLoadPolicy);
+              rs, ((l0 + u) * kSpan + tid * kPV) * static_cast<int>(sizeof(raw_t)), 0, kLoadPolicy);
+      };
+      auto consume = [&](const vec_t(&q)[kBatch], int l0) {
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
-          const int e0 = l0 + u * kSpan + tid * kPV;
-          if (l0 + u * kSpan < len) {  // uniform: the layer exists
+          const int e0 = (l0 + u) * kSpan + tid * kPV;
+          if (l0 + u < layers) {  // uniform: the layer exists
             float x[kPV];
 #pragma unroll
             for (int j = 0; j < kPV; ++j) x[j] = (e0 + j < len) ? DT::value(lane_of<raw_t>(q[u], j)) : -INFINITY;
-            f(l0 / kSpan + u, x);
+            f(l0 + u, x);
           }
         }
+      };
+      request(qa, 0);
+      for (int l0 = 0; l0 < layers; l0 += 2 * kBatch) {
+        request(qb, l0 + kBatch);
+        consume(qa, l0);
+        request(qa, l0 + 2 * kBatch);
+        consume(qb, l0 + kBatch);
       }
       return;
     }

@@ -370,8 +370,6 @@ __device__ __forceinline__ void filter_row(const Tile& tile, const typename DT::
       float vmv;
       if constexpr (Tile::kRegisters) {
         vmv = DT::ub16_value((S.vmw[i >> 1][threadIdx.x] >> ((i & 1) * 16)) & 0xFFFFu);
-      } else if (vm_in_lds) {
-        vmv = (e0 < V) ? DT::ub16_value(S.vmh[i][threadIdx.x]) : -INFINITY;
       } else {
         const vec_t q = tile.vec_at(i, e0);
         vmv = -INFINITY;
@@ -409,6 +407,38 @@ __device__ __forceinline__ void filter_row(const Tile& tile, const typename DT::
           pos0 += static_cast<uint32_t>(__popcll(masks[i]));
         }
       });
+    } else if (vm_in_lds) {
+      // streamed rows with the layer maxima in shared memory: each thread
+      // marks its candidate layers in a bit mask (the shared-memory reads
+      // are issued together), reserves room for them with one shared-memory
+      // atomic, and lists them
+      static_assert(kStreamVmSlots <= 32, "one mask bit per layer");
+      const int tid = static_cast<int>(threadIdx.x);
+      // every slot is read (entries of layers past the row are not
+      // meaningful and are masked out below), so no read waits on a branch
+      uint32_t h[kStreamVmSlots];
+#pragma unroll
+      for (int i = 0; i < kStreamVmSlots; ++i) h[i] = S.vmh[i][tid];
+      uint32_t mine = 0;
+#pragma unroll
+      for (int i = 0; i < kStreamVmSlots; ++i) {
+        const bool in_row = i * Tile::kSpan + tid * kPV < V;
+        mine |= static_cast<uint32_t>(in_row & (DT::ub16_value(h[i]) >= Lf)) << i;
+      }
+      // the wave's run of the list: a lane scan of the counts, one
+      // shared-memory atomic per wave
+      const uint32_t n = static_cast<uint32_t>(__popc(mine));
+      const uint32_t incl = wave_incl_scan_u32(n);
+      const uint32_t wtot = lane63_u32(incl);
+      uint32_t base = 0;
+      if (wtot != 0 && (threadIdx.x & (kWave - 1)) == 0) base = atomicAdd(&S.nvec, wtot);
+      uint32_t pos = __builtin_amdgcn_readfirstlane(base) + incl - n;
+      while (mine != 0) {
+        const int i = __ffs(mine) - 1;
+        mine &= mine - 1;
+        if (pos < static_cast<uint32_t>(kCandVecCap)) S.ce0[pos] = static_cast<uint32_t>(i * Tile::kSpan + tid * kPV);
+        ++pos;
+      }
     } else {
       // streamed rows: one atomic per wave for each slot holding candidates
       tile.for_each_slot([&](int i, int e0) {

@@ -20,8 +20,11 @@
 // Selection is a range-adaptive radix search: with every candidate key known
 // to lie in [lo, hi], one pass histograms (key - lo) >> shift into at most
 // 1024 bins (shift chosen so the range fits), one block-wide scan picks the
-// bin, and the range shrinks to that bin. A range under 1024 keys is settled
-// in a single pass; a full 32-bit range takes four.
+// bin, and the range shrinks to the smallest and largest key actually present
+// in that bin (each pass also records them per bin). A range under 1024 keys
+// is settled in a single pass, and so is any range whose picked bin holds a
+// single distinct key (equal values, or few elements spread over a wide
+// range); a full 32-bit range takes at most four.
 #pragma once
 
 #include "device_common.h"
@@ -35,6 +38,10 @@ static_assert(kBins == kThreads, "bin scans assume one bin per thread");
 struct alignas(16) SelSmem {
   alignas(16) uint32_t cnt[kBins];
   alignas(16) uint64_t mass[kBins];
+  // per bin, the largest key and the largest complemented key (so the
+  // smallest key is ~knmn): both start at zero like the counts
+  alignas(16) uint32_t kmx[kBins];
+  alignas(16) uint32_t knmn[kBins];
   uint32_t wtot32[kWaves];
   uint64_t wtot64[kWaves];
   int bin;
@@ -42,6 +49,7 @@ struct alignas(16) SelSmem {
   uint64_t above64;
   uint32_t bcnt;
   uint64_t bmass;
+  uint32_t bkmin, bkmax;  // smallest and largest key in the picked bin (passes that record them)
   int kbin;      // joint pick: bin of the k-th largest
   uint64_t thr;  // joint pick: fixed-point top-p threshold over the top-k survivors
   uint32_t run_n;              // boundary run gathered for one-wave ranking (zero between uses)
@@ -80,7 +88,15 @@ __device__ __forceinline__ uint64_t block_incl_scan_u64(uint64_t v, uint64_t* wt
 __device__ __forceinline__ void sel_reset(SelSmem& ss) {
   ss.cnt[threadIdx.x] = 0;
   ss.mass[threadIdx.x] = 0;
+  ss.kmx[threadIdx.x] = 0;
+  ss.knmn[threadIdx.x] = 0;
   if (threadIdx.x == 0) ss.run_n = 0;
+}
+
+// A histogram pass that records key ranges calls this for each element.
+__device__ __forceinline__ void sel_note_key(SelSmem& ss, uint32_t bin, uint32_t key) {
+  atomicMax(&ss.kmx[bin], key);
+  atomicMax(&ss.knmn[bin], ~key);
 }
 
 // Bins per lane when one wave scans the whole histogram: lane l owns the 16
@@ -107,6 +123,18 @@ __device__ __forceinline__ uint64_t row_incl_scan_u64(uint64_t v) {
   return v;
 }
 
+// Zeroes the range arrays over one pick lane's bins [base, base + 16).
+__device__ __forceinline__ void sel_clear_ranges(SelSmem& ss, int base) {
+  const vec_t z = {0u, 0u, 0u, 0u};
+  vec_t* xw = reinterpret_cast<vec_t*>(&ss.kmx[base]);
+  vec_t* nw = reinterpret_cast<vec_t*>(&ss.knmn[base]);
+#pragma unroll
+  for (int q = 0; q < kPickSpan / 4; ++q) {
+    xw[q] = z;
+    nw[q] = z;
+  }
+}
+
 // Walks the bins from the highest down and selects the first bin whose
 // inclusive running count reaches target >= 1; if the target exceeds the
 // total, bin 0 is selected. Result in ss.bin, ss.above (count strictly
@@ -115,7 +143,9 @@ __device__ __forceinline__ uint64_t row_incl_scan_u64(uint64_t v) {
 // LEAN keeps the histogram reads two at a time (for steps where the row tile
 // still occupies most registers); otherwise all of a lane's bins are read at
 // once, so the scan waits for one shared-memory round trip instead of several.
-template <bool LEAN = false>
+// RANGES: the pass recorded key ranges (sel_note_key); the picked bin's range
+// goes to ss.bkmin / ss.bkmax and the range arrays are cleared too.
+template <bool LEAN = false, bool RANGES = false>
 __device__ __forceinline__ void sel_pick_count(SelSmem& ss, uint32_t target) {
   if (threadIdx.x < kWave) {
     const int l = static_cast<int>(threadIdx.x);
@@ -153,18 +183,23 @@ __device__ __forceinline__ void sel_pick_count(SelSmem& ss, uint32_t target) {
       ss.bin = binr;
       ss.above = exclL + rin - c;
       ss.bcnt = c;
+      if constexpr (RANGES) {
+        ss.bkmax = ss.kmx[binr];
+        ss.bkmin = ~ss.knmn[binr];
+      }
     }
     const vec_t z = {0u, 0u, 0u, 0u};
     vec_t* cw = reinterpret_cast<vec_t*>(&ss.cnt[base]);
 #pragma unroll
     for (int q = 0; q < kPickSpan / 4; ++q) cw[q] = z;
+    if constexpr (RANGES) sel_clear_ranges(ss, base);
   }
   lds_barrier();
 }
 
 // The same on the mass histogram: first bin whose running mass reaches
 // target >= 1; also reports the bin's count and mass. Clears both histograms.
-template <bool LEAN = false>
+template <bool LEAN = false, bool RANGES = false>
 __device__ __forceinline__ void sel_pick_mass(SelSmem& ss, uint64_t target) {
   if (threadIdx.x < kWave) {
     const int l = static_cast<int>(threadIdx.x);
@@ -205,6 +240,10 @@ __device__ __forceinline__ void sel_pick_mass(SelSmem& ss, uint64_t target) {
       ss.above64 = exclL + rin - c;
       ss.bmass = c;
       ss.bcnt = ss.cnt[binr];
+      if constexpr (RANGES) {
+        ss.bkmax = ss.kmx[binr];
+        ss.bkmin = ~ss.knmn[binr];
+      }
     }
     const vec_t z = {0u, 0u, 0u, 0u};
     vec_t* mw = reinterpret_cast<vec_t*>(&ss.mass[base]);
@@ -213,6 +252,7 @@ __device__ __forceinline__ void sel_pick_mass(SelSmem& ss, uint64_t target) {
     vec_t* cw = reinterpret_cast<vec_t*>(&ss.cnt[base]);
 #pragma unroll
     for (int q = 0; q < kPickSpan / 4; ++q) cw[q] = z;
+    if constexpr (RANGES) sel_clear_ranges(ss, base);
   }
   lds_barrier();
 }
@@ -304,19 +344,33 @@ __device__ __forceinline__ uint32_t kth_largest_key(const Src& src, uint32_t k, 
     const uint32_t range = hi - lo;
     if (range == 0) return lo;
     const int shift = shift_for_range(range);
+    if (shift == 0) {  // one key per bin: this pass settles it
+      src.for_each([&](auto raw, int idx) {
+        const uint32_t key = keyfn(raw, idx);
+        if (key >= lo && key <= hi && pred(raw, idx)) atomicAdd(&ss.cnt[key - lo], 1u);
+      });
+      lds_barrier();
+      sel_pick_count(ss, k);
+      return lo + static_cast<uint32_t>(ss.bin);
+    }
     src.for_each([&](auto raw, int idx) {
       const uint32_t key = keyfn(raw, idx);
-      if (key >= lo && key <= hi && pred(raw, idx)) atomicAdd(&ss.cnt[(key - lo) >> shift], 1u);
+      if (key >= lo && key <= hi && pred(raw, idx)) {
+        const uint32_t bin = (key - lo) >> shift;
+        atomicAdd(&ss.cnt[bin], 1u);
+        sel_note_key(ss, bin, key);
+      }
     });
     lds_barrier();
-    sel_pick_count(ss, k);
-    const uint32_t bin = static_cast<uint32_t>(ss.bin);
+    sel_pick_count<false, true>(ss, k);
     k -= ss.above;
-    const uint32_t nlo = lo + (bin << shift);
-    const uint32_t span = (shift == 0) ? 0u : ((1u << shift) - 1u);
-    hi = (hi - nlo > span) ? nlo + span : hi;
-    lo = nlo;
-    if (shift == 0) return lo;
+    if (ss.bcnt != 0) {  // the keys present in the bin (it holds the k-th largest)
+      lo = ss.bkmin;
+      hi = ss.bkmax;
+    } else {  // not reached when k is within the count: the bin's whole span
+      lo += static_cast<uint32_t>(ss.bin) << shift;
+      hi = (hi - lo > (1u << shift) - 1u) ? lo + ((1u << shift) - 1u) : hi;
+    }
   }
 }
 
@@ -411,18 +465,29 @@ __device__ __forceinline__ void topp_boundary(const Src& src, uint32_t lo, uint3
         const uint32_t bin = (key - lo) >> shift;
         atomicAdd(&ss.mass[bin], mass_fx(DT::value(raw), m));
         atomicAdd(&ss.cnt[bin], 1u);
+        if (shift != 0) sel_note_key(ss, bin, key);
       }
     });
     lds_barrier();
-    sel_pick_mass(ss, thr - acc);
+    if (shift == 0)
+      sel_pick_mass(ss, thr - acc);
+    else
+      sel_pick_mass<false, true>(ss, thr - acc);
     acc += ss.above64;
     cnt = ss.bcnt;
     bmass = ss.bmass;
-    const uint32_t nlo = lo + (static_cast<uint32_t>(ss.bin) << shift);
-    const uint32_t span = (shift == 0) ? 0u : ((1u << shift) - 1u);
-    hi = (hi - nlo > span) ? nlo + span : hi;
-    lo = nlo;
-    if (shift == 0) break;
+    if (shift == 0) {
+      lo += static_cast<uint32_t>(ss.bin);
+      break;
+    }
+    if (cnt != 0) {  // the keys present in the bin (it holds the boundary)
+      lo = ss.bkmin;
+      hi = ss.bkmax;
+    } else {  // not reached with 1 <= thr <= the range's mass: the bin's whole span
+      lo += static_cast<uint32_t>(ss.bin) << shift;
+      hi = (hi - lo > (1u << shift) - 1u) ? lo + ((1u << shift) - 1u) : hi;
+    }
+    if (lo == hi) break;  // one key left: the bin's count and mass are its run
   }
   Kp = lo;
   // Every element of the final run has the same value, hence the same mass.

@@ -43,12 +43,25 @@ operators were lost in the page text; the prose next to each step gives them):
   * with pre-sorted input, ties follow the given positions; when the original
     logits are passed, kept values are read from them (AKP §3 parameter table).
 
+Min-p (TKS, "minP sampling"), an optional third stage after top-k and top-p.
+Its probabilities are those of step 4 (the softmax over the top-k survivors),
+with the positions top-p masked set aside; the threshold is the largest of
+them times min_p, and positions whose probability is strictly below it are
+masked. min_p <= 0 skips the stage; min_p >= 1 keeps a single token with the
+maximum value, read here as the last position of the stable ascending order
+(the same tie rule as p = 0). min_p is stored in the logits dtype, like p.
+Every stage only masks a prefix of the stable order, so the survivors of the
+three stages together are the intersection of each stage's survivors.
+
 Pins (tests/test_oracle.py) tie every step to something other than this code:
 the worked example of AKP §7 (outputs derived by hand, stored in
 tests/golden/), brute-force counting for top-k, the textbook nucleus
-definition accumulated from the top for top-p, and invariants. The exact fp32
+definition accumulated from the top for top-p, the logit-space form of min-p
+(x - max >= ln(min_p)) evaluated by counting, and invariants. The exact fp32
 cumsum values near 1 - p are parity unpinned: the pages print none, so the
-GPU comparison tolerates differences only inside a 1e-5 band around 1 - p.
+GPU comparison tolerates differences only inside a 1e-5 band around 1 - p;
+likewise min-p decisions only where a probability lies within a relative
+1e-5 of the min-p threshold.
 """
 
 from __future__ import annotations
@@ -102,13 +115,16 @@ class RowTrace:
     top_p_mask: np.ndarray  # bool [V]
     probs_sum32: Optional[np.ndarray]  # float32 [V] cumulative probability, or None
     t: Optional[np.float32]  # 1 - p as compared, or None
+    min_p_mask: Optional[np.ndarray] = None  # bool [V], or None without min-p
+    min_p_ratio: Optional[np.ndarray] = None  # float64 [V] probability / min-p threshold, or None
 
 
 def filter_sorted_row(sorted_value: np.ndarray, k_b: Optional[int], p_bits_b, dtype: str,
-                      t_reading: str = "fp32"):
-    """Steps 1-7 of AKP §2 on one ascending row of float64 values.
+                      t_reading: str = "fp32", min_p_bits_b=None):
+    """Steps 1-7 of AKP §2 on one ascending row of float64 values, then min-p.
 
-    Returns (top_k_mask, top_p_mask, probs_sum32, t), all in sorted order.
+    Returns (top_k_mask, top_p_mask, probs_sum32, t, min_p_mask, min_p_ratio),
+    all in sorted order; the last two are None without min-p.
     """
     V = sorted_value.shape[0]
     s = sorted_value.copy()
@@ -139,7 +155,27 @@ def filter_sorted_row(sorted_value: np.ndarray, k_b: Optional[int], p_bits_b, dt
         t = one_minus_p(p_bits_b, dtype, t_reading)
         top_p_mask = probs_sum32 <= t
         top_p_mask[V - 1] = False
-    return top_k_mask, top_p_mask, probs_sum32, t
+
+    min_p_mask = None
+    min_p_ratio = None
+    if min_p_bits_b is not None:
+        min_p_mask = np.zeros(V, dtype=bool)
+        mp = widen_to_f64(np.asarray([min_p_bits_b]), dtype)[0]
+        if mp >= 1.0:
+            # a single token with the maximum value: the last sorted position
+            min_p_mask[: V - 1] = True
+        elif mp > 0.0:
+            # probabilities of step 4 (softmax over the top-k survivors); the
+            # positions top-p masked hold -inf, as after TKS's top-p stage
+            m = s[V - 1]
+            e = np.exp(s - m)
+            probs = e / np.cumsum(e)[-1]
+            sort_masked = np.where(top_p_mask, -np.inf, probs)
+            threshold = sort_masked.max() * mp
+            min_p_mask = sort_masked < threshold
+            min_p_ratio = probs / threshold
+        # min_p <= 0 (or NaN): the stage is skipped
+    return top_k_mask, top_p_mask, probs_sum32, t, min_p_mask, min_p_ratio
 
 
 @dataclass
@@ -150,22 +186,23 @@ class OracleResult:
     traces: list  # RowTrace per row (empty when traces were not requested)
 
 
-def _check_args(dtype: str, p, k):
+def _check_args(dtype: str, p, k, min_p=None):
     if dtype not in NEG_INF_BITS:
         raise ValueError(f"unknown dtype {dtype!r}")
-    if p is None and k is None:
+    if p is None and k is None and min_p is None:
         raise ValueError("p and k are both absent (at least one is required, AKP §4)")
 
 
 def apply_top_k_top_p(logits_bits: np.ndarray, dtype: str, p_bits: Optional[np.ndarray] = None,
                       k: Optional[np.ndarray] = None, keep_traces: bool = True,
-                      t_reading: str = "fp32") -> OracleResult:
+                      t_reading: str = "fp32", min_p_bits: Optional[np.ndarray] = None) -> OracleResult:
     """The aclnn entry: sort each row, then filter (AKP §6.1 call chain).
 
     logits_bits: [B, V] raw bits (uint32 for f32, uint16 for f16/bf16).
     p_bits: [B] bits in the same dtype, or None. k: [B] int32, or None.
+    min_p_bits: [B] bits in the same dtype, or None (TKS min-p stage).
     """
-    _check_args(dtype, p_bits, k)
+    _check_args(dtype, p_bits, k, min_p_bits)
     logits_bits = np.asarray(logits_bits, dtype=BITS_DTYPE[dtype])
     B, V = logits_bits.shape
     out = np.empty_like(logits_bits)
@@ -183,27 +220,33 @@ def apply_top_k_top_p(logits_bits: np.ndarray, dtype: str, p_bits: Optional[np.n
         sorted_value = x[sorted_indices]
         kb = None if k is None else int(k[b])
         pb = None if p_bits is None else p_bits[b]
-        top_k_mask, top_p_mask, probs_sum32, t = filter_sorted_row(sorted_value, kb, pb, dtype, t_reading)
+        mpb = None if min_p_bits is None else min_p_bits[b]
+        top_k_mask, top_p_mask, probs_sum32, t, min_p_mask, min_p_ratio = filter_sorted_row(
+            sorted_value, kb, pb, dtype, t_reading, mpb)
         masked = top_k_mask | top_p_mask
+        if min_p_mask is not None:
+            masked = masked | min_p_mask
         # Step 8: scatter back to the original order; kept entries are the input bits.
         sorted_bits = np.where(masked, NEG_INF_BITS[dtype], row_bits[sorted_indices])
         out[b, sorted_indices] = sorted_bits
         if keep_traces:
-            traces.append(RowTrace(sorted_indices, top_k_mask, top_p_mask, probs_sum32, t))
+            traces.append(RowTrace(sorted_indices, top_k_mask, top_p_mask, probs_sum32, t, min_p_mask, min_p_ratio))
     return OracleResult(out, traces)
 
 
 def apply_top_k_top_p_with_sorted(sorted_value_bits: np.ndarray, sorted_indices: np.ndarray, dtype: str,
                                   p_bits: Optional[np.ndarray] = None, k: Optional[np.ndarray] = None,
                                   logits_bits: Optional[np.ndarray] = None, keep_traces: bool = True,
-                                  t_reading: str = "fp32") -> OracleResult:
+                                  t_reading: str = "fp32",
+                                  min_p_bits: Optional[np.ndarray] = None) -> OracleResult:
     """The sorted-input operator ApplyTopKTopPWithSorted (AKP §1, §3).
 
     sorted_value_bits must be ascending and sorted_indices the matching
     permutation; positions in the given order decide ties. If logits_bits is
-    given, kept outputs are read from it in the original order.
+    given, kept outputs are read from it in the original order. min_p_bits
+    adds the TKS min-p stage, as in apply_top_k_top_p.
     """
-    _check_args(dtype, p_bits, k)
+    _check_args(dtype, p_bits, k, min_p_bits)
     sorted_value_bits = np.asarray(sorted_value_bits, dtype=BITS_DTYPE[dtype])
     B, V = sorted_value_bits.shape
     out = np.empty_like(sorted_value_bits)
@@ -219,8 +262,12 @@ def apply_top_k_top_p_with_sorted(sorted_value_bits: np.ndarray, sorted_indices:
         s = widen_to_f64(sorted_value_bits[b], dtype)
         kb = None if k is None else int(k[b])
         pb = None if p_bits is None else p_bits[b]
-        top_k_mask, top_p_mask, probs_sum32, t = filter_sorted_row(s, kb, pb, dtype, t_reading)
+        mpb = None if min_p_bits is None else min_p_bits[b]
+        top_k_mask, top_p_mask, probs_sum32, t, min_p_mask, min_p_ratio = filter_sorted_row(
+            s, kb, pb, dtype, t_reading, mpb)
         masked = top_k_mask | top_p_mask
+        if min_p_mask is not None:
+            masked = masked | min_p_mask
         if logits_bits is None:
             out[b, perm] = np.where(masked, NEG_INF_BITS[dtype], sorted_value_bits[b])
         else:
@@ -228,5 +275,5 @@ def apply_top_k_top_p_with_sorted(sorted_value_bits: np.ndarray, sorted_indices:
             keep[perm] = ~masked
             out[b] = np.where(keep, logits_bits[b], NEG_INF_BITS[dtype])
         if keep_traces:
-            traces.append(RowTrace(perm, top_k_mask, top_p_mask, probs_sum32, t))
+            traces.append(RowTrace(perm, top_k_mask, top_p_mask, probs_sum32, t, min_p_mask, min_p_ratio))
     return OracleResult(out, traces)

@@ -22,6 +22,7 @@ class HandCase:
     p: Optional[np.ndarray]  # bits [B]
     k: Optional[np.ndarray]  # int32 [B]
     expect: np.ndarray  # bits [B, V]
+    min_p: Optional[np.ndarray] = None  # bits [B], cases of min_p_cases.txt only
 
 
 def _parse_values(tokens, dtype):
@@ -37,6 +38,7 @@ def _parse_values(tokens, dtype):
 
 
 def load_hand_cases(path: Optional[str] = None) -> List[HandCase]:
+    path = path if path is None or os.path.isabs(path) else os.path.join(GOLDEN_DIR, path)
     path = path or os.path.join(GOLDEN_DIR, "hand_cases.txt")
     cases = []
     cur = None
@@ -47,7 +49,7 @@ def load_hand_cases(path: Optional[str] = None) -> List[HandCase]:
                 continue
             head, *rest = line.split()
             if head == "case":
-                cur = dict(name=rest[0], dtype=rest[1], x=[], p=None, k=None, expect=[])
+                cur = dict(name=rest[0], dtype=rest[1], x=[], p=None, k=None, min_p=None, expect=[])
                 cases.append(cur)
             elif head == "x":
                 cur["x"].append(_parse_values(rest, cur["dtype"]))
@@ -55,11 +57,13 @@ def load_hand_cases(path: Optional[str] = None) -> List[HandCase]:
                 cur["expect"].append(_parse_values(rest, cur["dtype"]))
             elif head == "p":
                 cur["p"] = None if rest == ["none"] else _parse_values(rest, cur["dtype"])
+            elif head == "min_p":
+                cur["min_p"] = None if rest == ["none"] else _parse_values(rest, cur["dtype"])
             elif head == "k":
                 cur["k"] = None if rest == ["none"] else np.array([int(v) for v in rest], dtype=np.int32)
             else:
                 raise ValueError(f"bad golden line: {line}")
     return [
-        HandCase(c["name"], c["dtype"], np.stack(c["x"]), c["p"], c["k"], np.stack(c["expect"]))
+        HandCase(c["name"], c["dtype"], np.stack(c["x"]), c["p"], c["k"], np.stack(c["expect"]), c["min_p"])
         for c in cases
     ]

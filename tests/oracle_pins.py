@@ -221,3 +221,134 @@ ALL_CHECKS = [
     check_permutation_equivariance,
     check_bruteforce_tiny,
 ]
+
+
+# ---------------------------------------------------------------- min-p ---
+# The min-p stage of Ascend's "aclnnTopKTopPSampleV2" page masks positions
+# whose probability is below the largest probability times min_p. The checks
+# below use the equivalent logit-space form, x - max(x) >= ln(min_p) (the
+# softmax normalisation cancels in the ratio), evaluated element by element
+# with Python floats, and the page's special cases: min_p <= 0 skips the
+# stage, min_p >= 1 keeps a single token with the maximum value. Each check
+# takes ``apply_mp_fn(logits_bits, dtype, p_bits, k, min_p_bits) -> out_bits``.
+
+
+def minp_keep_logit_space(x, mp):
+    """Min-p survivors of a row by the logit-space rule; (keep, ambiguous)."""
+    V = len(x)
+    if mp is None or not (mp > 0.0):
+        return np.ones(V, dtype=bool), False
+    m = max(x)
+    if mp >= 1.0:
+        keep = np.zeros(V, dtype=bool)
+        keep[max(i for i in range(V) if x[i] == m)] = True
+        return keep, False
+    ln_mp = math.log(mp)
+    keep = np.array([(v - m) >= ln_mp for v in x])
+    ambiguous = any(abs((v - m) - ln_mp) < 1e-9 for v in x)
+    return keep, ambiguous
+
+
+def check_minp_hand_cases(apply_mp_fn):
+    for case in load_hand_cases("min_p_cases.txt"):
+        got = apply_mp_fn(case.x, case.dtype, case.p, case.k, case.min_p)
+        assert np.array_equal(got, case.expect), (case.name, got, case.expect)
+
+
+def check_minp_bruteforce_tiny(apply_mp_fn, dtypes=("f32", "bf16"), n_rows=4, max_v=7):
+    """Tiny rows: every k, a p grid and a min_p grid against counting, the
+    nucleus walk and the logit-space rule, intersected."""
+    from workloads.synth import f32_to_bits
+
+    mp_grid = [-0.5, 0.0, 1e-3, 0.05, 0.2, 0.5, 0.9, 1.0, 1.5]
+    p_grid = [None, 0.0, 0.35, 0.8, 1.0]
+    seed = 500
+    for dtype in dtypes:
+        for V in range(1, max_v + 1):
+            for kind in ("normal", "ties", "zeros"):
+                seed += 1
+                xb = random_rows(seed, n_rows, V, dtype, kind=kind, scale=1.5)
+                for b in range(n_rows):
+                    row = xb[b : b + 1]
+                    x = list(_vals(row[0], dtype))
+                    for kk in [None, -1, 1, 2, V - 1, V]:
+                        for pv in p_grid:
+                            for mpv in mp_grid:
+                                mp_bits = f32_to_bits(np.array([mpv], np.float32), dtype)
+                                mp = float(_vals(mp_bits, dtype)[0])
+                                p_bits = None
+                                t = None
+                                if pv is not None:
+                                    p_bits = f32_to_bits(np.array([pv], np.float32), dtype)
+                                    t = _t32(p_bits[0], dtype)
+                                k_arr = None if kk is None else np.array([kk], np.int32)
+                                got = apply_mp_fn(row, dtype, p_bits, k_arr, mp_bits)[0]
+                                keep_kp, amb1 = expected_keep_bruteforce(x, kk, t)
+                                keep_m, amb2 = minp_keep_logit_space(x, mp)
+                                if amb1 or amb2:
+                                    continue
+                                exp = np.where(keep_kp & keep_m, row[0], NEG_INF_WORD[dtype]).astype(row.dtype)
+                                assert np.array_equal(got, exp), (dtype, V, kind, b, kk, pv, mpv, x, got, exp)
+
+
+def check_minp_random(apply_mp_fn, dtype="f32", V=300, B=24):
+    """Moderate rows with ties: min-p alone and with top-k / top-p."""
+    from workloads.synth import f32_to_bits
+
+    rng = np.random.default_rng(21)
+    for kind in ("normal", "ties", "gumbel"):
+        xb = random_rows(6000 + V, B, V, dtype, kind=kind)
+        mp = f32_to_bits(np.exp(rng.uniform(-8.0, 0.0, size=B)).astype(np.float32), dtype)
+        k = rng.integers(1, V - 1, size=B, endpoint=True).astype(np.int32)
+        p = f32_to_bits(rng.uniform(0.0, 1.0, size=B).astype(np.float32), dtype)
+        for pp, kk in ((None, None), (None, k), (p, None), (p, k)):
+            got = apply_mp_fn(xb, dtype, pp, kk, mp)
+            for b in range(B):
+                x = list(_vals(xb[b], dtype))
+                t = None if pp is None else _t32(pp[b], dtype)
+                keep_kp, amb1 = expected_keep_bruteforce(x, None if kk is None else int(kk[b]), t)
+                keep_m, amb2 = minp_keep_logit_space(x, float(_vals(mp[b : b + 1], dtype)[0]))
+                if amb1 or amb2:
+                    continue
+                exp = np.where(keep_kp & keep_m, xb[b], NEG_INF_WORD[dtype]).astype(xb.dtype)
+                assert np.array_equal(got[b], exp), (kind, b, pp is None, kk is None)
+
+
+def check_minp_invariants(apply_mp_fn, dtype="bf16", V=257, B=16):
+    """At least one survivor; min_p >= 1 keeps exactly one position; min_p <= 0
+    changes nothing; larger min_p keeps a subset."""
+    from workloads.synth import f32_to_bits
+
+    rng = np.random.default_rng(23)
+    neg = NEG_INF_WORD[dtype]
+    for kind in ("ties", "spikes", "const", "zeros"):
+        xb = random_rows(7000 + V, B, V, dtype, kind=kind)
+        vals = _vals(xb, dtype).reshape(B, V)
+        k = rng.integers(1, V - 1, size=B, endpoint=True).astype(np.int32)
+        p = f32_to_bits(rng.uniform(0.0, 1.0, size=B).astype(np.float32), dtype)
+        ones = f32_to_bits(np.ones(B, np.float32), dtype)
+        out1 = apply_mp_fn(xb, dtype, None, None, ones)
+        for b in range(B):
+            kept = np.nonzero(out1[b] != neg)[0]
+            mx = vals[b].max()
+            assert list(kept) == [int(np.nonzero(vals[b] == mx)[0].max())], (kind, b)
+        for pp, kk in ((p, k), (p, None), (None, k)):
+            base = apply_mp_fn(xb, dtype, pp, kk, None)
+            for z in (0.0, -2.0):
+                zb = f32_to_bits(np.full(B, z, np.float32), dtype)
+                assert np.array_equal(apply_mp_fn(xb, dtype, pp, kk, zb), base), kind
+            prev = base != neg
+            for mpv in (1e-4, 0.01, 0.1, 0.5, 0.99):
+                mb = f32_to_bits(np.full(B, mpv, np.float32), dtype)
+                cur = apply_mp_fn(xb, dtype, pp, kk, mb) != neg
+                assert cur.any(axis=1).all()
+                assert not (cur & ~prev).any(), (kind, mpv)
+                prev = cur
+
+
+MINP_CHECKS = [
+    check_minp_hand_cases,
+    check_minp_invariants,
+    check_minp_random,
+    check_minp_bruteforce_tiny,
+]

@@ -4,13 +4,16 @@ Per row, with o the oracle output and its trace, and g the GPU output:
   1. every position the oracle masks by top-k is -inf in g (bit-exact);
   2. every position the oracle keeps holds the input bits in g, unless it is a
      band position;
-  3. every position the oracle masks only by top-p is -inf in g, unless it is a
-     band position;
+  3. every position the oracle masks only by top-p or min-p is -inf in g,
+     unless it is a band position of that stage;
   4. g holds nothing but input bits or the dtype's -inf pattern;
   5. g's survivors form a suffix of the stable ascending order.
-A band position is a sorted position j != V-1 whose oracle fp32 cumulative
-probability lies within ``tol`` (1e-5) of t = 1 - p. Summation order on the GPU
-differs from the oracle's, so only there may the top-p decision differ.
+A top-p band position is a sorted position j != V-1 whose oracle fp32
+cumulative probability lies within ``tol`` (1e-5) of t = 1 - p. Summation order
+on the GPU differs from the oracle's, so only there may the top-p decision
+differ. A min-p band position is one whose oracle probability lies within a
+relative ``tol`` of the min-p threshold: the GPU takes exp in fp32, so only
+there may the min-p decision differ.
 """
 
 from __future__ import annotations
@@ -56,16 +59,25 @@ def compare_row(g_row, x_row, trace, dtype, tol=BAND_TOL, row_id=None) -> Parity
     xs = x_row[perm]
     is_neg = gs == neg
     is_x = gs == xs
-    o_masked = trace.top_k_mask | trace.top_p_mask
-    band = np.zeros(V, dtype=bool)
+    mask_m = trace.min_p_mask if trace.min_p_mask is not None else np.zeros(V, dtype=bool)
+    o_masked = trace.top_k_mask | trace.top_p_mask | mask_m
+    band_p = np.zeros(V, dtype=bool)
     if trace.probs_sum32 is not None and trace.t is not None:
-        band = np.abs(trace.probs_sum32.astype(np.float64) - np.float64(trace.t)) <= tol
-        band[V - 1] = False
+        band_p = np.abs(trace.probs_sum32.astype(np.float64) - np.float64(trace.t)) <= tol
+        band_p[V - 1] = False
+    band_m = np.zeros(V, dtype=bool)
+    if trace.min_p_ratio is not None:
+        band_m = np.abs(trace.min_p_ratio - 1.0) <= tol
+        band_m[V - 1] = False
+    band = band_p | band_m
     ambiguous_val = xs == neg  # input already -inf: kept and masked look the same
+    # a stage forces a mask where it masks outside its band, and allows a keep
+    # where it keeps or is inside its band
+    must_mask = trace.top_k_mask | (trace.top_p_mask & ~band_p) | (mask_m & ~band_m)
+    must_keep = ~trace.top_k_mask & ~(trace.top_p_mask | band_p) & ~(mask_m | band_m)
     bad = ~(is_neg | is_x)  # rule 4
-    bad |= trace.top_k_mask & ~is_neg  # rule 1
-    bad |= ~o_masked & ~band & ~is_x  # rule 2
-    bad |= trace.top_p_mask & ~trace.top_k_mask & ~band & ~is_neg  # rule 3
+    bad |= must_mask & ~is_neg  # rules 1 and 3
+    bad |= must_keep & ~is_x  # rule 2
     # rule 5: survivors are a suffix of the stable order
     kept = is_x & ~is_neg
     kept_or_amb = kept | ambiguous_val
@@ -82,7 +94,7 @@ def compare_row(g_row, x_row, trace, dtype, tol=BAND_TOL, row_id=None) -> Parity
         js = np.nonzero(bad)[0][:5]
         rep.details.append(dict(row=row_id, sorted_positions=js.tolist(), orig=perm[js].tolist(),
                                 g=gs[js].tolist(), x=xs[js].tolist(), maskK=trace.top_k_mask[js].tolist(),
-                                maskP=trace.top_p_mask[js].tolist()))
+                                maskP=trace.top_p_mask[js].tolist(), maskM=mask_m[js].tolist()))
     return rep
 
 

@@ -17,6 +17,39 @@ def test_oracle_pins(check):
     check(oracle_apply)
 
 
+def oracle_apply_mp(x, dtype, p, k, min_p):
+    return apply_top_k_top_p(x, dtype, p, k, keep_traces=False, min_p_bits=min_p).out
+
+
+@pytest.mark.parametrize("check", pins.MINP_CHECKS, ids=lambda c: c.__name__)
+def test_oracle_min_p_pins(check):
+    check(oracle_apply_mp)
+
+
+def test_min_p_absent_equals_before():
+    """Without min-p the oracle's output is unchanged by the min-p code path."""
+    xb = random_rows(88, 6, 200, "bf16", kind="ties")
+    k, p = pins_params(6, 200, "bf16")
+    a = apply_top_k_top_p(xb, "bf16", p, k, keep_traces=False).out
+    b = apply_top_k_top_p(xb, "bf16", p, k, keep_traces=False, min_p_bits=None).out
+    assert np.array_equal(a, b)
+
+
+def test_with_sorted_min_p_matches_apply():
+    """The pre-sorted entry with min-p equals the sorting entry with min-p."""
+    from workloads.synth import f32_to_bits
+
+    for dtype, kind in (("bf16", "normal"), ("f32", "ties")):
+        xb = random_rows(79, 10, 301, dtype, kind=kind)
+        k, p = pins_params(10, 301, dtype)
+        mp = f32_to_bits(np.linspace(-0.1, 1.1, 10).astype(np.float32), dtype)
+        ref = apply_top_k_top_p(xb, dtype, p, k, keep_traces=False, min_p_bits=mp).out
+        idx, sv = stable_ascending_sort(xb, dtype)
+        for logits in (xb, None):
+            got = apply_top_k_top_p_with_sorted(sv, idx, dtype, p, k, logits_bits=logits, min_p_bits=mp).out
+            assert np.array_equal(got, ref)
+
+
 def test_with_sorted_matches_apply():
     """Pre-sorted entry on a stable sort equals the sorting entry (both forms)."""
     for dtype, kind in (("bf16", "normal"), ("f32", "ties"), ("f16", "zeros")):

@@ -53,6 +53,38 @@ def make_mutant(old, new):
     return mod
 
 
+# Slips in the min-p stage; the min-p pins must catch each.
+MINP_MUTANTS = {
+    "minp_threshold_without_max": ("threshold = sort_masked.max() * mp", "threshold = mp"),
+    "minp_threshold_divides": ("threshold = sort_masked.max() * mp", "threshold = sort_masked.max() / mp"),
+    "minp_at_least_one_keeps_every_max": ("min_p_mask[: V - 1] = True", "min_p_mask = s < s[V - 1]"),
+    "minp_ratio_from_logits": ("e = np.exp(s - m)\n            probs = e / np.cumsum(e)[-1]",
+                               "probs = np.where(np.isfinite(s), s - s.min() + 1e-9, 0.0)"),
+}
+
+MINP_CHECKS = [
+    pins.check_minp_hand_cases,
+    pins.check_minp_invariants,
+    pins.check_minp_random,
+    pins.check_minp_bruteforce_tiny,
+]
+
+
+@pytest.mark.parametrize("name", sorted(MINP_MUTANTS))
+def test_min_p_mutant_is_caught(name):
+    mod = make_mutant(*MINP_MUTANTS[name])
+
+    def apply_mp_fn(x, dtype, p, k, min_p):
+        return mod.apply_top_k_top_p(x, dtype, p, k, keep_traces=False, min_p_bits=min_p).out
+
+    for check in MINP_CHECKS:
+        try:
+            check(apply_mp_fn)
+        except (AssertionError, IndexError, ValueError):
+            return
+    pytest.fail(f"mutant {name} passed every min-p pin")
+
+
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_mutant_is_caught(name):
     mod = make_mutant(*MUTANTS[name])

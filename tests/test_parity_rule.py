@@ -1,0 +1,61 @@
+"""The GPU-vs-oracle comparison rule itself, exercised on the CPU with the
+oracle's own output standing in for a GPU result."""
+
+import numpy as np
+
+from oracle import apply_top_k_top_p
+from tests.parity import NEG_INF_WORD, compare
+from workloads.synth import f32_to_bits, random_rows
+
+
+def _case(min_p=True):
+    dtype = "bf16"
+    xb = random_rows(31, 6, 400, dtype, kind="normal")
+    rng = np.random.default_rng(3)
+    k = rng.integers(1, 399, size=6).astype(np.int32)
+    p = f32_to_bits(rng.uniform(0.3, 0.95, size=6).astype(np.float32), dtype)
+    mp = f32_to_bits(rng.uniform(0.01, 0.3, size=6).astype(np.float32), dtype) if min_p else None
+    ref = apply_top_k_top_p(xb, dtype, p, k, min_p_bits=mp)
+    return dtype, xb, ref
+
+
+def test_oracle_output_passes():
+    for min_p in (False, True):
+        dtype, xb, ref = _case(min_p)
+        rep = compare(ref.out.copy(), xb, ref, dtype)
+        assert rep.hard_mismatches == 0 and rep.band_mismatches == 0
+
+
+def test_flipped_survivor_is_caught():
+    dtype, xb, ref = _case()
+    g = ref.out.copy()
+    b = 0
+    kept = np.nonzero(g[b] != NEG_INF_WORD[dtype])[0]
+    g[b, kept[0]] = NEG_INF_WORD[dtype]  # drop a survivor outside any band
+    tr = ref.traces[b]
+    j = int(np.nonzero(tr.sorted_indices == kept[0])[0][0])
+    in_band = (tr.min_p_ratio is not None and abs(tr.min_p_ratio[j] - 1) <= 1e-5) or (
+        abs(float(tr.probs_sum32[j]) - float(tr.t)) <= 1e-5)
+    rep = compare(g, xb, ref, dtype)
+    assert in_band or rep.hard_mismatches >= 1
+
+
+def test_resurrected_min_p_position_is_caught():
+    dtype, xb, ref = _case()
+    for b, tr in enumerate(ref.traces):
+        only_m = tr.min_p_mask & ~tr.top_k_mask & ~tr.top_p_mask & (np.abs(tr.min_p_ratio - 1) > 1e-5)
+        if only_m.any():
+            j = int(np.nonzero(only_m)[0][-1])
+            g = ref.out.copy()
+            g[b, tr.sorted_indices[j]] = xb[b, tr.sorted_indices[j]]
+            assert compare(g, xb, ref, dtype).hard_mismatches >= 1
+            return
+    raise AssertionError("no row has a position masked by min-p alone")
+
+
+def test_foreign_value_is_caught():
+    dtype, xb, ref = _case(False)
+    g = ref.out.copy()
+    g[1, 5] = np.uint16(0x3F80)  # 1.0, neither the input bits nor -inf (unless equal)
+    rep = compare(g, xb, ref, dtype)
+    assert xb[1, 5] == 0x3F80 or rep.hard_mismatches >= 1

@@ -12,7 +12,10 @@ Prints one JSON line: rows/s (value), the dominant kernel's achieved HBM
 bandwidth against the 8 TB/s peak (roofline), and the CPU oracle timed on a
 bounded sample of the same rows (cpu_baseline).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1..5]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1..5] [--min-p]
+
+--min-p adds the min-p stage (aclnnTopKTopPSampleV2, "minP sampling") with a
+per-row min_p drawn uniformly from [0.01, 0.2] to the chosen workload.
 """
 
 import argparse
@@ -67,7 +70,8 @@ def kernel_source_digest():
 def measured_traffic(args):
     """Counter-measured HBM bytes per launch, or None when no counters were
     taken for this workload or the kernel sources changed since."""
-    if args.workload != 3 or args.policy != 0 or args.copy_calibration or not os.path.exists(TRAFFIC_PROFILE):
+    if (args.workload != 3 or args.policy != 0 or args.copy_calibration or args.min_p
+            or not os.path.exists(TRAFFIC_PROFILE)):
         return None
     text = open(TRAFFIC_PROFILE).read()
     m_bytes = re.search(r"traffic_bytes_per_launch:\s*(\d+)", text)
@@ -86,19 +90,19 @@ def dev(bits, dtype):
     return torch.from_numpy(np.ascontiguousarray(bits).view(getattr(np, iv))).cuda().view(getattr(torch, fv))
 
 
-def algorithmic_bytes(wl):
+def algorithmic_bytes(wl, with_min_p=False):
     """Minimal HBM bytes of one call: read every logit once, write every output
-    once, read p and k; the pre-sorted entry also reads at least the k largest
-    sorted values of each row."""
+    once, read p and k (and min_p); the pre-sorted entry also reads at least
+    the k largest sorted values of each row."""
     s = wl.elem_bytes
-    per_row = 2 * wl.V * s + s + 4
+    per_row = 2 * wl.V * s + s + 4 + (s if with_min_p else 0)
     total = wl.B * per_row
     if wl.entry == "with_sorted":
         total += int(np.clip(wl.k, 0, wl.V).sum()) * s
     return total
 
 
-def cpu_baseline(wl, budget_s=12.0):
+def cpu_baseline(wl, budget_s=12.0, min_p=None):
     """The CPU oracle, as it stands, on the first rows of the same workload."""
     from oracle import apply_top_k_top_p, apply_top_k_top_p_with_sorted
 
@@ -107,11 +111,12 @@ def cpu_baseline(wl, budget_s=12.0):
     while (time.perf_counter() - t0) < budget_s:
         lo = done % wl.B
         r = slice(lo, min(wl.B, lo + 8))
+        mp = None if min_p is None else min_p[r]
         if wl.entry == "apply":
-            apply_top_k_top_p(wl.logits[r], wl.dtype, wl.p[r], wl.k[r], keep_traces=False)
+            apply_top_k_top_p(wl.logits[r], wl.dtype, wl.p[r], wl.k[r], keep_traces=False, min_p_bits=mp)
         else:
             apply_top_k_top_p_with_sorted(wl.sorted_value[r], wl.sorted_indices[r], wl.dtype, wl.p[r], wl.k[r],
-                                          logits_bits=wl.logits[r], keep_traces=False)
+                                          logits_bits=wl.logits[r], keep_traces=False, min_p_bits=mp)
         done += r.stop - r.start
     dt = time.perf_counter() - t0
     return {
@@ -134,6 +139,7 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds for the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--policy", type=int, default=0, help="plan policy: 0 auto, 1 general, 2 registers")
+    ap.add_argument("--min-p", action="store_true", help="add a per-row min_p in [0.01, 0.2] (the min-p stage)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time a plain device-to-device copy of the logits instead of the filter (the reference "
                          "kernel whose HBM counters scale the filter's)")
@@ -148,7 +154,7 @@ def main():
     import torch
 
     import top_logits_filtering_amd as tk
-    from workloads.synth import make_workload
+    from workloads.synth import make_workload, min_p_for_workload
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     tk.load_library()
@@ -157,6 +163,8 @@ def main():
     dt = wl.dtype
     p = dev(wl.p, dt)
     k = torch.from_numpy(wl.k).cuda()
+    mp_bits = min_p_for_workload(args.workload, wl.B, dt) if args.min_p else None
+    mp = dev(mp_bits, dt)
     sets = []
     for _ in range(max(1, args.sets)):
         if wl.entry == "apply":
@@ -172,9 +180,9 @@ def main():
         if args.copy_calibration:
             st[1].copy_(st[0])
         elif wl.entry == "apply":
-            tk.apply_top_k_top_p(st[0], p, k, out=st[1])
+            tk.apply_top_k_top_p(st[0], p, k, out=st[1], min_p=mp)
         else:
-            tk.apply_top_k_top_p_with_sorted(st[2], st[3], p, k, logits=st[0], out=st[1])
+            tk.apply_top_k_top_p_with_sorted(st[2], st[3], p, k, logits=st[0], out=st[1], min_p=mp)
 
     for i in range(args.warmup):
         step(i)
@@ -196,7 +204,7 @@ def main():
 
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     kernel_ms = ev0.elapsed_time(ev1) / args.steps
-    nbytes = 2 * wl.B * wl.V * wl.elem_bytes if args.copy_calibration else algorithmic_bytes(wl)
+    nbytes = 2 * wl.B * wl.V * wl.elem_bytes if args.copy_calibration else algorithmic_bytes(wl, args.min_p)
     achieved = nbytes / (kernel_ms * 1e-3) / 1e9
     rows_per_s = wl.B / (ms_per_step * 1e-3)
 
@@ -214,7 +222,7 @@ def main():
         "dtype": dt,
         "data": "synthetic",
         "config": {
-            "workload": WORKLOAD_TEXT[args.workload],
+            "workload": WORKLOAD_TEXT[args.workload] + (", min-p U[0.01,0.2] per row" if args.min_p else ""),
             "B": wl.B,
             "V": wl.V,
             "buffer_sets": len(sets),
@@ -237,7 +245,7 @@ def main():
         line["unit"] = "GB/s"
         line["config"]["workload"] = "torch copy_ of " + WORKLOAD_TEXT[args.workload]
     elif not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
+        line["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget, mp_bits)
     print(json.dumps(line), flush=True)
 
 

@@ -110,6 +110,44 @@ topktopp_status apply_top_k_top_p_with_sorted(const void* sorted_value, const in
                                               const int32_t* k, const void* logits, void* out,
                                               void* stream);
 
+/*
+ * apply_top_k_top_p_min_p — apply_top_k_top_p followed by the min-p stage of
+ * Ascend's "aclnnTopKTopPSampleV2" page ("minP sampling"; cited as TKS).
+ *
+ *   min_p   [B] device buffer of `dtype` values (like p), or NULL for no
+ *           min-p. Other arguments as for apply_top_k_top_p; p, k and min_p
+ *           may each be NULL, but not all three (ERR_NULLPTR).
+ *
+ * Min-p takes the probabilities left after top-k and top-p (the softmax of
+ * the top-k survivors, step 4 above) and masks every position whose
+ * probability is strictly below the largest one times min_p[b]; as the
+ * ratio of two of those probabilities is exp(x - x_max), a position survives
+ * iff exp(x - x_max) >= min_p[b]. min_p[b] <= 0 (or NaN) skips the stage;
+ * min_p[b] >= 1 keeps a single position, the maximum with the highest
+ * original index (TKS keeps one token with the maximum value; this takes the
+ * stable order's last one, as p <= 0 does). Each stage masks a prefix of the
+ * stable ascending order, so the survivors are those of all stages at once.
+ *
+ * Numerics. exp is taken in fp32 on the device; only positions whose exact
+ * ratio lies within a relative 1e-5 of min_p[b] can be decided differently
+ * from an exact evaluation.
+ */
+topktopp_status apply_top_k_top_p_min_p(const void* logits, int dtype, int64_t B, int64_t V,
+                                        const void* p, const int32_t* k, const void* min_p, void* out,
+                                        void* stream);
+
+/*
+ * apply_top_k_top_p_min_p_with_sorted — apply_top_k_top_p_with_sorted
+ * followed by the min-p stage described for apply_top_k_top_p_min_p.
+ *   min_p   [B] device buffer of `dtype` values, or NULL. Other arguments as
+ *           for apply_top_k_top_p_with_sorted; p, k and min_p may each be
+ *           NULL, but not all three.
+ */
+topktopp_status apply_top_k_top_p_min_p_with_sorted(const void* sorted_value, const int32_t* sorted_indices,
+                                                    int dtype, int64_t B, int64_t V, const void* p,
+                                                    const int32_t* k, const void* min_p, const void* logits,
+                                                    void* out, void* stream);
+
 /* Text of the most recent error on the calling thread ("" if none); the
  * counterpart of aclGetRecentErrMsg (AKP §8). Valid until the next call on
  * the same thread. */

@@ -47,22 +47,22 @@ def from_dev(t, dtype):
     return t.view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-def gpu_apply(bits, dtype, p=None, k=None):
+def gpu_apply(bits, dtype, p=None, k=None, min_p=None):
     import torch
     import top_logits_filtering_amd as tk
 
     x = to_dev(bits, dtype)
-    out = tk.apply_top_k_top_p(x, to_dev(p, dtype), k_dev(k))
+    out = tk.apply_top_k_top_p(x, to_dev(p, dtype), k_dev(k), min_p=to_dev(min_p, dtype))
     torch.cuda.synchronize()
     return from_dev(out, dtype)
 
 
-def gpu_with_sorted(sv, si, dtype, p=None, k=None, logits=None):
+def gpu_with_sorted(sv, si, dtype, p=None, k=None, logits=None, min_p=None):
     import torch
     import top_logits_filtering_amd as tk
 
     out = tk.apply_top_k_top_p_with_sorted(
-        to_dev(sv, dtype), k_dev(si), to_dev(p, dtype), k_dev(k), to_dev(logits, dtype)
+        to_dev(sv, dtype), k_dev(si), to_dev(p, dtype), k_dev(k), to_dev(logits, dtype), min_p=to_dev(min_p, dtype)
     )
     torch.cuda.synchronize()
     return from_dev(out, dtype)

@@ -51,6 +51,21 @@ def test_null_pointers(lib):
     assert g(FAKE, FAKE, 0, 2, 8, None, None, None, FAKE + (1 << 30), None) == NULLPTR
 
 
+def test_min_p_entry_points(lib):
+    f = lib.apply_top_k_top_p_min_p
+    out = FAKE + (1 << 32)
+    # min_p alone is enough; all three absent is not
+    assert f(FAKE, 0, 2, 8, None, None, None, out, None) == NULLPTR
+    assert "min_p" in tk.last_error()
+    assert f(FAKE, 5, 2, 8, None, None, FAKE, out, None) == INVALID  # reaches the dtype check
+    assert f(FAKE, 0, 2, 8, None, None, out + 4, out, None) == INVALID
+    assert "overlap" in tk.last_error()
+    g = lib.apply_top_k_top_p_min_p_with_sorted
+    assert g(FAKE, FAKE, 0, 2, 8, None, None, None, None, out, None) == NULLPTR
+    assert g(FAKE, FAKE, 7, 2, 8, None, None, FAKE, None, out, None) == INVALID
+    assert g(None, None, 0, 0, 9, None, None, None, None, None, None) == 0
+
+
 def test_invalid_dtype_and_shape(lib):
     f = lib.apply_top_k_top_p
     out = FAKE + (1 << 32)

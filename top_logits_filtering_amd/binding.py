@@ -19,6 +19,8 @@ TOPKTOPP_F32, TOPKTOPP_F16, TOPKTOPP_BF16 = 0, 1, 2
 STATUS_NAMES = {0: "OK", 1: "ERR_NULLPTR", 2: "ERR_INVALID", 3: "ERR_RUNTIME"}
 EXPORTED_SYMBOLS = (
     "apply_top_k_top_p",
+    "apply_top_k_top_p_min_p",
+    "apply_top_k_top_p_min_p_with_sorted",
     "apply_top_k_top_p_with_sorted",
     "topktopp_last_error",
     "topktopp_set_plan_policy",
@@ -51,6 +53,10 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.apply_top_k_top_p.restype = i32
     lib.apply_top_k_top_p_with_sorted.argtypes = [vp, vp, i32, i64, i64, vp, vp, vp, vp, vp]
     lib.apply_top_k_top_p_with_sorted.restype = i32
+    lib.apply_top_k_top_p_min_p.argtypes = [vp, i32, i64, i64, vp, vp, vp, vp, vp]
+    lib.apply_top_k_top_p_min_p.restype = i32
+    lib.apply_top_k_top_p_min_p_with_sorted.argtypes = [vp, vp, i32, i64, i64, vp, vp, vp, vp, vp, vp]
+    lib.apply_top_k_top_p_min_p_with_sorted.restype = i32
     lib.topktopp_last_error.argtypes = []
     lib.topktopp_last_error.restype = ctypes.c_char_p
     lib.topktopp_set_plan_policy.argtypes = [i32]
@@ -112,8 +118,9 @@ def _check(status: int):
         raise TopKTopPError(status, last_error())
 
 
-def apply_top_k_top_p(logits, p=None, k=None, out=None, stream=None):
-    """Filter raw logits [B, V]; p [B] (logits dtype) and k [B] (int32) are optional."""
+def apply_top_k_top_p(logits, p=None, k=None, out=None, stream=None, min_p=None):
+    """Filter raw logits [B, V]; p [B] (logits dtype), k [B] (int32) and min_p
+    [B] (logits dtype, the min-p stage) are optional."""
     import torch
 
     lib = load_library()
@@ -122,16 +129,21 @@ def apply_top_k_top_p(logits, p=None, k=None, out=None, stream=None):
     B, V = logits.shape
     if out is None:
         out = torch.empty_like(logits)
-    status = lib.apply_top_k_top_p(
-        _ptr(logits), _dtype_code(logits), B, V, _ptr(p), _ptr(k), _ptr(out), _stream(stream, logits.device)
-    )
+    st = _stream(stream, logits.device)
+    if min_p is None:
+        status = lib.apply_top_k_top_p(_ptr(logits), _dtype_code(logits), B, V, _ptr(p), _ptr(k), _ptr(out), st)
+    else:
+        status = lib.apply_top_k_top_p_min_p(
+            _ptr(logits), _dtype_code(logits), B, V, _ptr(p), _ptr(k), _ptr(min_p), _ptr(out), st
+        )
     _check(status)
     return out
 
 
 def apply_top_k_top_p_with_sorted(sorted_value, sorted_indices, p=None, k=None, logits=None, out=None,
-                                  stream=None):
-    """Filter pre-sorted rows (ascending sorted_value, int32 sorted_indices)."""
+                                  stream=None, min_p=None):
+    """Filter pre-sorted rows (ascending sorted_value, int32 sorted_indices);
+    min_p [B] (logits dtype) adds the min-p stage."""
     import torch
 
     lib = load_library()
@@ -140,9 +152,16 @@ def apply_top_k_top_p_with_sorted(sorted_value, sorted_indices, p=None, k=None, 
     B, V = sorted_value.shape
     if out is None:
         out = torch.empty_like(sorted_value)
-    status = lib.apply_top_k_top_p_with_sorted(
-        _ptr(sorted_value), _ptr(sorted_indices), _dtype_code(sorted_value), B, V, _ptr(p), _ptr(k),
-        _ptr(logits), _ptr(out), _stream(stream, sorted_value.device)
-    )
+    st = _stream(stream, sorted_value.device)
+    if min_p is None:
+        status = lib.apply_top_k_top_p_with_sorted(
+            _ptr(sorted_value), _ptr(sorted_indices), _dtype_code(sorted_value), B, V, _ptr(p), _ptr(k),
+            _ptr(logits), _ptr(out), st
+        )
+    else:
+        status = lib.apply_top_k_top_p_min_p_with_sorted(
+            _ptr(sorted_value), _ptr(sorted_indices), _dtype_code(sorted_value), B, V, _ptr(p), _ptr(k),
+            _ptr(min_p), _ptr(logits), _ptr(out), st
+        )
     _check(status)
     return out

@@ -64,8 +64,21 @@ int topktopp_set_plan_policy(int policy) {
   return g_policy.exchange(policy);
 }
 
-topktopp_status apply_top_k_top_p(const void* logits, int dtype, int64_t B, int64_t V, const void* p,
-                                  const int32_t* k, void* out, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The entry points without min_p pass has_min_p = false: then p and k may
+// not both be NULL, as in the aclnn checks; with it, any one of the three.
+topktopp_status check_params(const void* p, const int32_t* k, const void* min_p, bool has_min_p) {
+  if (p == nullptr && k == nullptr && min_p == nullptr)
+    return has_min_p ? fail(TOPKTOPP_ERR_NULLPTR, "p, k and min_p are all NULL; at least one is required")
+                     : fail(TOPKTOPP_ERR_NULLPTR, "p and k are both NULL; at least one is required");
+  return TOPKTOPP_OK;
+}
+
+topktopp_status apply_impl(const void* logits, int dtype, int64_t B, int64_t V, const void* p, const int32_t* k,
+                           const void* min_p, bool has_min_p, void* out, void* stream) {
   g_last_error.clear();
   if (B >= 0 && V >= 0 && (B == 0 || V == 0)) {  // empty: nothing is read or written, pointers may be NULL
     if (!valid_dtype(dtype)) return fail(TOPKTOPP_ERR_INVALID, "dtype %d is not one of F32, F16, BF16", dtype);
@@ -73,23 +86,24 @@ topktopp_status apply_top_k_top_p(const void* logits, int dtype, int64_t B, int6
   }
   if (logits == nullptr) return fail(TOPKTOPP_ERR_NULLPTR, "logits is NULL");
   if (out == nullptr) return fail(TOPKTOPP_ERR_NULLPTR, "out is NULL");
-  if (p == nullptr && k == nullptr) return fail(TOPKTOPP_ERR_NULLPTR, "p and k are both NULL; at least one is required");
+  if (topktopp_status s = check_params(p, k, min_p, has_min_p)) return s;
   if (!valid_dtype(dtype)) return fail(TOPKTOPP_ERR_INVALID, "dtype %d is not one of F32, F16, BF16", dtype);
   if (topktopp_status s = check_shape(B, V)) return s;
   const size_t es = elem_size(dtype);
   const size_t nbytes = static_cast<size_t>(B) * static_cast<size_t>(V) * es;
   if (overlaps(out, nbytes, logits, nbytes) || overlaps(out, nbytes, p, static_cast<size_t>(B) * es) ||
-      overlaps(out, nbytes, k, static_cast<size_t>(B) * 4))
+      overlaps(out, nbytes, k, static_cast<size_t>(B) * 4) || overlaps(out, nbytes, min_p, static_cast<size_t>(B) * es))
     return fail(TOPKTOPP_ERR_INVALID, "out overlaps an input buffer");
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (V == 1)  // a last dimension of 1 is copied through unfiltered
     return check_launch(hipMemcpyAsync(out, logits, nbytes, hipMemcpyDeviceToDevice, st), "hipMemcpyAsync");
-  return check_launch(tkp::launch_apply(dtype, logits, p, k, out, B, V, g_policy.load(), st), "filter launch");
+  return check_launch(tkp::launch_apply(dtype, logits, p, k, min_p, out, B, V, g_policy.load(), st),
+                      "filter launch");
 }
 
-topktopp_status apply_top_k_top_p_with_sorted(const void* sorted_value, const int32_t* sorted_indices, int dtype,
-                                              int64_t B, int64_t V, const void* p, const int32_t* k,
-                                              const void* logits, void* out, void* stream) {
+topktopp_status with_sorted_impl(const void* sorted_value, const int32_t* sorted_indices, int dtype, int64_t B,
+                                 int64_t V, const void* p, const int32_t* k, const void* min_p, bool has_min_p,
+                                 const void* logits, void* out, void* stream) {
   g_last_error.clear();
   if (B >= 0 && V >= 0 && (B == 0 || V == 0)) {  // empty: nothing is read or written, pointers may be NULL
     if (!valid_dtype(dtype)) return fail(TOPKTOPP_ERR_INVALID, "dtype %d is not one of F32, F16, BF16", dtype);
@@ -98,7 +112,7 @@ topktopp_status apply_top_k_top_p_with_sorted(const void* sorted_value, const in
   if (sorted_value == nullptr) return fail(TOPKTOPP_ERR_NULLPTR, "sorted_value is NULL");
   if (sorted_indices == nullptr) return fail(TOPKTOPP_ERR_NULLPTR, "sorted_indices is NULL");
   if (out == nullptr) return fail(TOPKTOPP_ERR_NULLPTR, "out is NULL");
-  if (p == nullptr && k == nullptr) return fail(TOPKTOPP_ERR_NULLPTR, "p and k are both NULL; at least one is required");
+  if (topktopp_status s = check_params(p, k, min_p, has_min_p)) return s;
   if (!valid_dtype(dtype)) return fail(TOPKTOPP_ERR_INVALID, "dtype %d is not one of F32, F16, BF16", dtype);
   if (topktopp_status s = check_shape(B, V)) return s;
   const size_t es = elem_size(dtype);
@@ -106,15 +120,43 @@ topktopp_status apply_top_k_top_p_with_sorted(const void* sorted_value, const in
   if (overlaps(out, nbytes, sorted_value, nbytes) ||
       overlaps(out, nbytes, sorted_indices, static_cast<size_t>(B) * static_cast<size_t>(V) * 4) ||
       overlaps(out, nbytes, logits, nbytes) || overlaps(out, nbytes, p, static_cast<size_t>(B) * es) ||
-      overlaps(out, nbytes, k, static_cast<size_t>(B) * 4))
+      overlaps(out, nbytes, k, static_cast<size_t>(B) * 4) || overlaps(out, nbytes, min_p, static_cast<size_t>(B) * es))
     return fail(TOPKTOPP_ERR_INVALID, "out overlaps an input buffer");
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (V == 1)  // the single element is always kept; sorted_indices is 0
     return check_launch(hipMemcpyAsync(out, logits != nullptr ? logits : sorted_value, nbytes,
                                        hipMemcpyDeviceToDevice, st),
                         "hipMemcpyAsync");
-  return check_launch(tkp::launch_with_sorted(dtype, sorted_value, sorted_indices, p, k, logits, out, B, V, st),
-                      "filter launch");
+  return check_launch(
+      tkp::launch_with_sorted(dtype, sorted_value, sorted_indices, p, k, min_p, logits, out, B, V, st),
+      "filter launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+topktopp_status apply_top_k_top_p(const void* logits, int dtype, int64_t B, int64_t V, const void* p,
+                                  const int32_t* k, void* out, void* stream) {
+  return apply_impl(logits, dtype, B, V, p, k, nullptr, false, out, stream);
+}
+
+topktopp_status apply_top_k_top_p_min_p(const void* logits, int dtype, int64_t B, int64_t V, const void* p,
+                                        const int32_t* k, const void* min_p, void* out, void* stream) {
+  return apply_impl(logits, dtype, B, V, p, k, min_p, true, out, stream);
+}
+
+topktopp_status apply_top_k_top_p_with_sorted(const void* sorted_value, const int32_t* sorted_indices, int dtype,
+                                              int64_t B, int64_t V, const void* p, const int32_t* k,
+                                              const void* logits, void* out, void* stream) {
+  return with_sorted_impl(sorted_value, sorted_indices, dtype, B, V, p, k, nullptr, false, logits, out, stream);
+}
+
+topktopp_status apply_top_k_top_p_min_p_with_sorted(const void* sorted_value, const int32_t* sorted_indices,
+                                                    int dtype, int64_t B, int64_t V, const void* p,
+                                                    const int32_t* k, const void* min_p, const void* logits,
+                                                    void* out, void* stream) {
+  return with_sorted_impl(sorted_value, sorted_indices, dtype, B, V, p, k, min_p, true, logits, out, stream);
 }
 
 }  // extern "C"

@@ -239,7 +239,7 @@ __device__ __forceinline__ void filter_row(const Tile& tile, const typename DT::
   gt.load(irow, 0, V);
   sel_reset(ss);
 
-  if (!rp.k_on && rp.pmode == kPNone) {  // nothing to filter
+  if (!row_filters(rp)) {  // nothing to filter
     tile.store(orow, [](raw_t r, int) { return r; });
     return;
   }
@@ -339,11 +339,15 @@ __device__ __forceinline__ void filter_row(const Tile& tile, const typename DT::
   // 4. candidate bound L
   const LdsValues<DT> top2{S.top2, kTop2};
   const bool top_only = rp.pmode == kPTopOnly || (ponly && thr == 0);
+  // min-p alone: its survivors lie above m + ln(min_p), so that floor bounds them
+  const bool mp_only = rp.mp_on && !rp.k_on && rp.pmode == kPNone;
   uint32_t L = kmax;
   bool fast = klo <= kmax;
   if (rp.k_on) {
     fast = fast && rp.k <= static_cast<uint32_t>(kTop2) &&
            kth_largest_bound(top2, rp.k, klo, kmax, [](auto raw, int) { return DT::key(raw); }, ss, L);
+  } else if (mp_only) {
+    L = key_floor<DT>(min_p_floor(m, rp.minp));
   } else if (!top_only) {
     fast = fast && topp_bound<DT>(top2, klo, kmax, m, thr, ss, L);
   }
@@ -613,6 +617,11 @@ __device__ __forceinline__ void filter_row(const Tile& tile, const typename DT::
     }
   }
 
+  // min-p: the smallest candidate key that survives it; every stage keeps a
+  // suffix of the stable order, so the tighter pair wins. Its threshold is
+  // either above L (then a candidate holds it) or below every candidate.
+  if (!fallback && rp.mp_on) combine_min_p(min_p_key<DT>(cs, m, rp.minp, sm), K, I);
+
   // 7. survivors over the -inf row, once every -inf store has completed
   if (!fallback) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
@@ -631,13 +640,14 @@ template <class DT, int NVEC>
 __global__ __launch_bounds__(kThreads) void apply_regs_kernel(const typename DT::raw_t* __restrict__ logits,
                                                               const typename DT::raw_t* __restrict__ p,
                                                               const int32_t* __restrict__ k,
+                                                              const typename DT::raw_t* __restrict__ min_p,
                                                               typename DT::raw_t* __restrict__ out, int V,
                                                               int use_candidates) {
   __shared__ ApplySmem S;
   const int b = blockIdx.x;
   const size_t off = static_cast<size_t>(b) * V;
-  // p[b] and k[b] are fetched before the row and used after it is requested
-  const RowParamsRaw<DT> rpr = fetch_row_params<DT>(p, k, b);
+  // p[b], k[b] and min_p[b] are fetched before the row and used after it is requested
+  const RowParamsRaw<DT> rpr = fetch_row_params<DT>(p, k, min_p, b);
   RegTile<DT, NVEC> tile;
   tile.load(logits + off, 0, V);
   const RowParams rp = decode_row_params<DT>(rpr, V);
@@ -648,29 +658,31 @@ template <class DT>
 __global__ __launch_bounds__(kThreads) void apply_stream_kernel(const typename DT::raw_t* __restrict__ logits,
                                                                 const typename DT::raw_t* __restrict__ p,
                                                                 const int32_t* __restrict__ k,
+                                                                const typename DT::raw_t* __restrict__ min_p,
                                                                 typename DT::raw_t* __restrict__ out, int V,
                                                                 int use_candidates) {
   __shared__ ApplySmem S;
   const int b = blockIdx.x;
   const size_t off = static_cast<size_t>(b) * V;
-  const RowParams rp = decode_row_params<DT>(p, k, b, V);
+  const RowParams rp = decode_row_params<DT>(p, k, min_p, b, V);
   GlobalTile<DT> tile;
   tile.load(logits + off, 0, V);
   filter_row<DT>(tile, logits + off, V, rp, use_candidates != 0, S, out + off);
 }
 
 template <class DT, int NVEC>
-void launch_regs(const void* logits, const void* p, const int32_t* k, void* out, int64_t B, int64_t V,
-                 int use_candidates, hipStream_t stream) {
+void launch_regs(const void* logits, const void* p, const int32_t* k, const void* min_p, void* out, int64_t B,
+                 int64_t V, int use_candidates, hipStream_t stream) {
   using raw_t = typename DT::raw_t;
   hipLaunchKernelGGL((apply_regs_kernel<DT, NVEC>), dim3(static_cast<unsigned>(B)), dim3(kThreads), 0, stream,
-                     static_cast<const raw_t*>(logits), static_cast<const raw_t*>(p), k, static_cast<raw_t*>(out),
-                     static_cast<int>(V), use_candidates);
+                     static_cast<const raw_t*>(logits), static_cast<const raw_t*>(p), k,
+                     static_cast<const raw_t*>(min_p), static_cast<raw_t*>(out), static_cast<int>(V),
+                     use_candidates);
 }
 
 template <class DT>
-hipError_t launch_apply_t(const void* logits, const void* p, const int32_t* k, void* out, int64_t B, int64_t V,
-                          int policy, hipStream_t stream) {
+hipError_t launch_apply_t(const void* logits, const void* p, const int32_t* k, const void* min_p, void* out,
+                          int64_t B, int64_t V, int policy, hipStream_t stream) {
   using raw_t = typename DT::raw_t;
   constexpr int span = kThreads * DT::kPerVec;
   const int64_t vecs = (V + span - 1) / span;
@@ -680,24 +692,25 @@ hipError_t launch_apply_t(const void* logits, const void* p, const int32_t* k, v
                       (reinterpret_cast<uintptr_t>(out) & 15u) == 0;
   if (policy != kPlanAuto || vecs > kMaxVecs || !vec_ok) {
     hipLaunchKernelGGL(apply_stream_kernel<DT>, dim3(static_cast<unsigned>(B)), dim3(kThreads), 0, stream,
-                       static_cast<const raw_t*>(logits), static_cast<const raw_t*>(p), k, static_cast<raw_t*>(out),
-                       static_cast<int>(V), use_candidates);
+                       static_cast<const raw_t*>(logits), static_cast<const raw_t*>(p), k,
+                       static_cast<const raw_t*>(min_p), static_cast<raw_t*>(out), static_cast<int>(V),
+                       use_candidates);
   } else if (vecs <= 1) {
-    launch_regs<DT, 1>(logits, p, k, out, B, V, use_candidates, stream);
+    launch_regs<DT, 1>(logits, p, k, min_p, out, B, V, use_candidates, stream);
   } else if (vecs <= 2) {
-    launch_regs<DT, 2>(logits, p, k, out, B, V, use_candidates, stream);
+    launch_regs<DT, 2>(logits, p, k, min_p, out, B, V, use_candidates, stream);
   } else if (vecs <= 4) {
-    launch_regs<DT, 4>(logits, p, k, out, B, V, use_candidates, stream);
+    launch_regs<DT, 4>(logits, p, k, min_p, out, B, V, use_candidates, stream);
   } else if (vecs <= 8) {
-    launch_regs<DT, 8>(logits, p, k, out, B, V, use_candidates, stream);
+    launch_regs<DT, 8>(logits, p, k, min_p, out, B, V, use_candidates, stream);
   } else if (vecs <= 12) {
-    launch_regs<DT, 12>(logits, p, k, out, B, V, use_candidates, stream);
+    launch_regs<DT, 12>(logits, p, k, min_p, out, B, V, use_candidates, stream);
   } else if (vecs <= 16) {
-    launch_regs<DT, 16>(logits, p, k, out, B, V, use_candidates, stream);
+    launch_regs<DT, 16>(logits, p, k, min_p, out, B, V, use_candidates, stream);
   } else if (vecs <= 19) {
-    launch_regs<DT, 19>(logits, p, k, out, B, V, use_candidates, stream);
+    launch_regs<DT, 19>(logits, p, k, min_p, out, B, V, use_candidates, stream);
   } else {
-    launch_regs<DT, kMaxVecs>(logits, p, k, out, B, V, use_candidates, stream);
+    launch_regs<DT, kMaxVecs>(logits, p, k, min_p, out, B, V, use_candidates, stream);
   }
   return hipGetLastError();
 }

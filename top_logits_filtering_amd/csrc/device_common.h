@@ -329,8 +329,10 @@ enum PMode : int { kPNone = 0, kPTopOnly = 1, kPBoundary = 2 };
 struct RowParams {
   bool k_on;     // 1 <= k <= V-1
   uint32_t k;
-  int pmode;     // kPNone: no top-p (p absent, or t <= 0); kPTopOnly: t >= 1
+  int pmode;     // kPNone: no top-p (p absent, or t <= 0); kPTopOnly: t >= 1, or min_p >= 1
   float t;       // 1 - p in fp32
+  bool mp_on;    // 0 < min_p < 1: the min-p stage masks positions with exp(x - max) < min_p
+  float minp;
 };
 
 // The per-row parameters are the same for every thread of the block. They are
@@ -341,17 +343,20 @@ struct RowParams {
 template <class DT>
 struct RowParamsRaw {
   int32_t k;
-  typename DT::raw_t p;
-  bool has_k, has_p;
+  typename DT::raw_t p, mp;
+  bool has_k, has_p, has_mp;
 };
 
 template <class DT>
-__device__ __forceinline__ RowParamsRaw<DT> fetch_row_params(const typename DT::raw_t* p, const int32_t* k, int b) {
+__device__ __forceinline__ RowParamsRaw<DT> fetch_row_params(const typename DT::raw_t* p, const int32_t* k,
+                                                             const typename DT::raw_t* min_p, int b) {
   RowParamsRaw<DT> r;
   r.has_k = k != nullptr;
   r.has_p = p != nullptr;
+  r.has_mp = min_p != nullptr;
   r.k = r.has_k ? k[b] : 0;
   r.p = r.has_p ? p[b] : static_cast<typename DT::raw_t>(0);
+  r.mp = r.has_mp ? min_p[b] : static_cast<typename DT::raw_t>(0);
   return r;
 }
 
@@ -377,12 +382,53 @@ __device__ __forceinline__ RowParams decode_row_params(const RowParamsRaw<DT>& r
     else if (t > 0.0f) rp.pmode = kPBoundary;
     // t <= 0 (p >= 1) or NaN: no position with positive mass is masked
   }
+  // min-p (aclnnTopKTopPSampleV2, "minP sampling"): min_p >= 1 keeps one
+  // token with the maximum value, the same single survivor as t >= 1; min_p
+  // <= 0 (or NaN) skips the stage
+  rp.mp_on = false;
+  rp.minp = 0.0f;
+  if (r.has_mp) {
+    const float mp = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(DT::value(r.mp))));
+    if (mp >= 1.0f) {
+      rp.pmode = kPTopOnly;
+    } else if (mp > 0.0f) {
+      rp.mp_on = true;
+      rp.minp = mp;
+    }
+  }
   return rp;
 }
 
 template <class DT>
-__device__ __forceinline__ RowParams decode_row_params(const typename DT::raw_t* p, const int32_t* k, int b, int V) {
-  return decode_row_params<DT>(fetch_row_params<DT>(p, k, b), V);
+__device__ __forceinline__ RowParams decode_row_params(const typename DT::raw_t* p, const int32_t* k,
+                                                       const typename DT::raw_t* min_p, int b, int V) {
+  return decode_row_params<DT>(fetch_row_params<DT>(p, k, min_p, b), V);
+}
+
+// Largest key whose value is <= f (f finite).
+template <class DT>
+__device__ __forceinline__ uint32_t key_floor(float f) {
+  uint32_t K = DT::key(DT::raw_of_value(f));  // within one step of the answer
+  if (K > 0u && DT::value(DT::raw_of_key(K)) > f) --K;
+  return K;
+}
+
+// The row filters something (top-k, top-p or min-p is active).
+__device__ __forceinline__ bool row_filters(const RowParams& rp) {
+  return rp.k_on || rp.pmode != kPNone || rp.mp_on;
+}
+
+// Min-p decision of one value: exp(x - m) >= min_p, with the exponential
+// taken as in mass_fx (hardware exp2 of (x - m) * log2 e). Non-decreasing in x.
+__device__ __forceinline__ bool min_p_keeps(float x, float m, float minp) {
+  return __builtin_amdgcn_exp2f((x - m) * 1.4426950408889634f) >= minp;
+}
+
+// A value below which nothing passes min_p_keeps: m + ln(min_p), widened by
+// a margin far above the error of the exponential.
+__device__ __forceinline__ float min_p_floor(float m, float minp) {
+  const float l2 = log2f(minp);  // <= 0
+  return m + (l2 * 1.0009765625f - 0.0009765625f) * 0.6931471805599453f;
 }
 
 // Fixed-point threshold: a position survives top-p iff the mass strictly above

@@ -516,11 +516,34 @@ __device__ __forceinline__ bool topp_bound(const Src& src, uint32_t lo, uint32_t
   return ok;
 }
 
+// Smallest key among the elements of `src` that survive min-p (m the row
+// maximum). Every thread of the block must call it.
+template <class DT, class Src>
+__device__ __forceinline__ uint32_t min_p_key(const Src& src, float m, float minp, RowSmem& sm) {
+  uint32_t nk = 0;  // largest complemented key, so the smallest key is ~nk
+  src.for_each([&](auto raw, int) {
+    if (min_p_keeps(DT::value(raw), m, minp)) {
+      const uint32_t c = ~DT::key(raw);
+      nk = c > nk ? c : nk;
+    }
+  });
+  return ~block_max_u32(nk, sm);
+}
+
+// The min-p stage on top of a top-k / top-p pair: every stage keeps a suffix
+// of the stable order, so the result is the larger pair in (key, index) order.
+__device__ __forceinline__ void combine_min_p(uint32_t Kmp, uint32_t& K, uint32_t& I) {
+  if (Kmp > K) {
+    K = Kmp;
+    I = 0;
+  }
+}
+
 // Full threshold pair (K, I) of a row, every statistic computed from `src`,
 // which holds all V elements of the row.
 template <class DT, class Src>
-__device__ __forceinline__ void solve_row(const Src& src, const RowParams& rp, int V, RowSmem& sm, SelSmem& ss,
-                                          uint32_t& K, uint32_t& I) {
+__device__ __forceinline__ void solve_row_kp(const Src& src, const RowParams& rp, int V, RowSmem& sm, SelSmem& ss,
+                                             uint32_t& K, uint32_t& I) {
   K = 0;
   I = 0;
   if (!rp.k_on && rp.pmode == kPNone) return;
@@ -552,6 +575,18 @@ __device__ __forceinline__ void solve_row(const Src& src, const RowParams& rp, i
     return;
   }
   topp_boundary<DT>(src, Kk, kKeyMax, m, thr, V, ss, K, I);
+}
+
+template <class DT, class Src>
+__device__ __forceinline__ void solve_row(const Src& src, const RowParams& rp, int V, RowSmem& sm, SelSmem& ss,
+                                          uint32_t& K, uint32_t& I) {
+  solve_row_kp<DT>(src, rp, V, sm, ss, K, I);
+  if (rp.mp_on) {
+    float mloc = -INFINITY;
+    src.for_each([&](auto raw, int) { mloc = fmaxf(mloc, DT::value(raw)); });
+    const float m = block_max_f32(mloc, sm);
+    combine_min_p(min_p_key<DT>(src, m, rp.minp, sm), K, I);
+  }
 }
 
 }  // namespace tkp

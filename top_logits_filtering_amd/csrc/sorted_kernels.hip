@@ -11,6 +11,9 @@
 //     gives F, the lowest position whose mass strictly above is below
 //     (1 - t) * Z (a wave-level Kogge-Stone scan per chunk, in the spirit of
 //     the guide's §6.3 CumsumKoggleStone / FindFirstIndex);
+//   * min-p (aclnnTopKTopPSampleV2, "minP sampling"): its survivors are the
+//     positions whose value passes exp(x - max) >= min_p, a suffix too, so F
+//     moves up to the lowest of them when that is higher;
 //   * survivors are the sorted positions >= F.
 // With logits: out[v] = logits[v] when key(logits[v]) > key(s_F), -inf when
 // below, and for equal keys the survivors are exactly the positions >= F of
@@ -50,9 +53,6 @@ __device__ __forceinline__ uint64_t block_exscan_u64(uint64_t v, RowSmem& sm, ui
   return wbase + incl - v;
 }
 
-// The sorted values of one row: positions >= lo are read from a copy in
-// shared memory (prefetched before the row's logits slice, so reading them
-// does not wait behind that slice's loads), lower positions from global memory.
 // The sorted values of one row, read from global memory.
 template <class DT>
 struct SortedSrcGlobal {
@@ -99,6 +99,25 @@ __device__ __forceinline__ int scan_boundary(const Src& sv, int start, int V, fl
   }
 }
 
+// Lowest sorted position j >= lo that survives min-p, given that the top
+// position V-1 does (the decision is non-decreasing along the row). Level one
+// tests 1024 positions spaced `stride` apart from the top; level two tests
+// every position between the lowest passing sample and the sample below it.
+template <class DT, class Src>
+__device__ __forceinline__ int first_min_p(const Src& sv, int lo, int V, float minp, RowSmem& sm) {
+  const float m = DT::value(sv.at(V - 1));
+  const int stride = (V - lo + kThreads - 1) / kThreads;  // <= 1024 for V <= 2^20
+  const int j = V - 1 - static_cast<int>(threadIdx.x) * stride;
+  const bool pass = j >= lo && min_p_keeps(DT::value(sv.at(j)), m, minp);
+  const int T = static_cast<int>(block_sum_u32(pass ? 1u : 0u, sm));  // samples 0..T-1 pass
+  const int hi = V - 1 - (T - 1) * stride;  // lowest passing sample
+  const int lo2 = max(lo, hi - stride + 1);
+  if (lo2 >= hi) return hi;
+  const int j2 = hi - 1 - static_cast<int>(threadIdx.x);
+  const bool pass2 = j2 >= lo2 && min_p_keeps(DT::value(sv.at(j2)), m, minp);
+  return hi - static_cast<int>(block_sum_u32(pass2 ? 1u : 0u, sm));
+}
+
 struct SortedBoundary {
   uint32_t KF;  // key of the lowest survivor
   int F;        // lowest surviving sorted position
@@ -126,6 +145,8 @@ __device__ __forceinline__ SortedBoundary sorted_boundary(const Src& sv, const R
     const uint64_t thr = topp_threshold(rp.t, Z);
     F = (thr == 0) ? V - 1 : scan_boundary<DT>(sv, start, V, m, thr, sm);
   }
+  // min-p keeps a suffix of the sorted positions too: the tighter one wins
+  if (rp.mp_on) F = first_min_p<DT>(sv, F, V, rp.minp, sm);
   SortedBoundary bd;
   bd.F = F;
   bd.KF = DT::key(sv.at(F));
@@ -191,6 +212,16 @@ __device__ __forceinline__ SortedBoundary sorted_boundary_copy(const typename DT
       F = R - 1 - block_max_i32(low >= 0 ? R - 1 - low : -1, sm);
     }
   }
+  if (rp.mp_on) {  // min-p survivors are a suffix of the copy (or all of it)
+    const float m = DT::value(top[R - 1]);
+    uint32_t c = 0;
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+      const int ci = u * kThreads + static_cast<int>(threadIdx.x);
+      if (ci < R && min_p_keeps(DT::value(top[ci]), m, rp.minp)) ++c;
+    }
+    F = max(F, R - static_cast<int>(block_sum_u32(c, sm)));
+  }
   SortedBoundary bd;
   bd.KF = DT::key(top[F]);
   bd.F = V - R + F;
@@ -205,7 +236,8 @@ template <class DT, bool kRegs>
 __global__ __launch_bounds__(kThreads, 8) void sorted_logits_kernel(
     const typename DT::raw_t* __restrict__ sorted_value, const int32_t* __restrict__ sorted_indices,
     const typename DT::raw_t* __restrict__ p, const int32_t* __restrict__ k,
-    const typename DT::raw_t* __restrict__ logits, typename DT::raw_t* __restrict__ out, int V, int S) {
+    const typename DT::raw_t* __restrict__ min_p, const typename DT::raw_t* __restrict__ logits,
+    typename DT::raw_t* __restrict__ out, int V, int S) {
   using raw_t = typename DT::raw_t;
   using Tile = std::conditional_t<kRegs, RegTile<DT, kSortedVecs>, GlobalTile<DT>>;
   constexpr int kCap = RegTile<DT, kSortedVecs>::kCapacity;
@@ -223,7 +255,7 @@ __global__ __launch_bounds__(kThreads, 8) void sorted_logits_kernel(
   // p[b] and k[b], the top sorted values the boundary search reads, then the
   // logits slice: vector loads complete in order, so the search waits only
   // for what it reads. The top values are requested before k is known.
-  const RowParamsRaw<DT> rpr = fetch_row_params<DT>(p, k, b);
+  const RowParamsRaw<DT> rpr = fetch_row_params<DT>(p, k, min_p, b);
   const int R = min(V, kSortedPrefetch);
   constexpr int kPre = kSortedPrefetch / kThreads;
   raw_t pre[kPre];
@@ -249,7 +281,7 @@ __global__ __launch_bounds__(kThreads, 8) void sorted_logits_kernel(
   lds_barrier();
 
   raw_t* __restrict__ orow = out + row_off;
-  if (!rp.k_on && rp.pmode == kPNone) {
+  if (!row_filters(rp)) {
     tile.store(orow, [](raw_t r, int) { return r; });
     return;
   }
@@ -308,18 +340,18 @@ constexpr int kScatterSlice = 65536;
 template <class DT>
 __global__ __launch_bounds__(kThreads) void sorted_scatter_kernel(
     const typename DT::raw_t* __restrict__ sorted_value, const int32_t* __restrict__ sorted_indices,
-    const typename DT::raw_t* __restrict__ p, const int32_t* __restrict__ k, typename DT::raw_t* __restrict__ out,
-    int V, int S) {
+    const typename DT::raw_t* __restrict__ p, const int32_t* __restrict__ k,
+    const typename DT::raw_t* __restrict__ min_p, typename DT::raw_t* __restrict__ out, int V, int S) {
   __shared__ RowSmem sm;
   const int b = blockIdx.x / S;
   const int s = blockIdx.x - b * S;
   const size_t row_off = static_cast<size_t>(b) * V;
   const auto* __restrict__ sv = sorted_value + row_off;
   const int32_t* __restrict__ si = sorted_indices + row_off;
-  const RowParams rp = decode_row_params<DT>(p, k, b, V);
+  const RowParams rp = decode_row_params<DT>(p, k, min_p, b, V);
   int F = 0;
   const SortedSrcGlobal<DT> src{sv};
-  if (rp.k_on || rp.pmode != kPNone) F = sorted_boundary<DT>(src, rp, V, sm).F;
+  if (row_filters(rp)) F = sorted_boundary<DT>(src, rp, V, sm).F;
   const int j0 = s * kScatterSlice;
   const int j1 = min(V, j0 + kScatterSlice);
   auto* __restrict__ orow = out + row_off;
@@ -331,8 +363,8 @@ __global__ __launch_bounds__(kThreads) void sorted_scatter_kernel(
 
 template <class DT>
 static hipError_t launch_sorted_t(const void* sorted_value, const int32_t* sorted_indices, const void* p,
-                                  const int32_t* k, const void* logits, void* out, int64_t B, int64_t V,
-                                  hipStream_t stream) {
+                                  const int32_t* k, const void* min_p, const void* logits, void* out, int64_t B,
+                                  int64_t V, hipStream_t stream) {
   using raw_t = typename DT::raw_t;
   if (logits != nullptr) {
     constexpr int cap = RegTile<DT, kSortedVecs>::kCapacity;
@@ -342,29 +374,29 @@ static hipError_t launch_sorted_t(const void* sorted_value, const int32_t* sorte
     if (vec_ok)
       hipLaunchKernelGGL((sorted_logits_kernel<DT, true>), dim3(static_cast<unsigned>(B * S)), dim3(kThreads), 0,
                          stream, static_cast<const raw_t*>(sorted_value), sorted_indices,
-                         static_cast<const raw_t*>(p), k, static_cast<const raw_t*>(logits),
-                         static_cast<raw_t*>(out), static_cast<int>(V), S);
+                         static_cast<const raw_t*>(p), k, static_cast<const raw_t*>(min_p),
+                         static_cast<const raw_t*>(logits), static_cast<raw_t*>(out), static_cast<int>(V), S);
     else
       hipLaunchKernelGGL((sorted_logits_kernel<DT, false>), dim3(static_cast<unsigned>(B * S)), dim3(kThreads), 0,
                          stream, static_cast<const raw_t*>(sorted_value), sorted_indices,
-                         static_cast<const raw_t*>(p), k, static_cast<const raw_t*>(logits),
-                         static_cast<raw_t*>(out), static_cast<int>(V), S);
+                         static_cast<const raw_t*>(p), k, static_cast<const raw_t*>(min_p),
+                         static_cast<const raw_t*>(logits), static_cast<raw_t*>(out), static_cast<int>(V), S);
   } else {
     const int S = static_cast<int>((V + kScatterSlice - 1) / kScatterSlice);
     hipLaunchKernelGGL(sorted_scatter_kernel<DT>, dim3(static_cast<unsigned>(B * S)), dim3(kThreads), 0, stream,
                        static_cast<const raw_t*>(sorted_value), sorted_indices, static_cast<const raw_t*>(p), k,
-                       static_cast<raw_t*>(out), static_cast<int>(V), S);
+                       static_cast<const raw_t*>(min_p), static_cast<raw_t*>(out), static_cast<int>(V), S);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_with_sorted(int dtype, const void* sorted_value, const int32_t* sorted_indices, const void* p,
-                              const int32_t* k, const void* logits, void* out, int64_t B, int64_t V,
-                              hipStream_t stream) {
+                              const int32_t* k, const void* min_p, const void* logits, void* out, int64_t B,
+                              int64_t V, hipStream_t stream) {
   switch (dtype) {
-    case 0: return launch_sorted_t<F32T>(sorted_value, sorted_indices, p, k, logits, out, B, V, stream);
-    case 1: return launch_sorted_t<F16T>(sorted_value, sorted_indices, p, k, logits, out, B, V, stream);
-    case 2: return launch_sorted_t<BF16T>(sorted_value, sorted_indices, p, k, logits, out, B, V, stream);
+    case 0: return launch_sorted_t<F32T>(sorted_value, sorted_indices, p, k, min_p, logits, out, B, V, stream);
+    case 1: return launch_sorted_t<F16T>(sorted_value, sorted_indices, p, k, min_p, logits, out, B, V, stream);
+    case 2: return launch_sorted_t<BF16T>(sorted_value, sorted_indices, p, k, min_p, logits, out, B, V, stream);
     default: return hipErrorInvalidValue;
   }
 }

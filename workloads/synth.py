@@ -277,3 +277,25 @@ def random_params(seed: int, B: int, V: int, dtype: str, k_lo: int = -2, k_hi: O
     k = rng.integers(k_lo, k_hi, size=B, endpoint=True).astype(np.int32)
     p = rng.uniform(p_lo, p_hi, size=B).astype(np.float32)
     return k, f32_to_bits(p, dtype)
+
+
+# Seed stream of the min-p values (a stream of its own, so adding min-p to a
+# workload leaves its logits, k and p unchanged).
+MIN_P_STREAM = 2**32 - 2
+
+
+def min_p_for_workload(c: int, B: int, dtype: str, lo: float = 0.01, hi: float = 0.2) -> np.ndarray:
+    """Per-row min_p bits for workload c: uniform in [lo, hi], stored in the
+    logits dtype like p (the typical range of min-p sampling settings)."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([SEED_BASE + c, MIN_P_STREAM])))
+    return f32_to_bits(rng.uniform(lo, hi, size=B).astype(np.float32), dtype)
+
+
+def random_min_p(seed: int, B: int, dtype: str, specials: bool = True) -> np.ndarray:
+    """Random per-row min_p bits: log-uniform in [1e-6, 1), with every 7th row
+    set to a special value (0, negative, 1, above 1, or tiny) when asked."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([0x3199, seed])))
+    v = np.exp(rng.uniform(np.log(1e-6), 0.0, size=B)).astype(np.float32)
+    if specials:
+        v[::7] = rng.choice(np.array([0.0, -0.5, 1.0, 2.0, 1e-30], np.float32), size=len(v[::7]))
+    return f32_to_bits(v, dtype)

@@ -16,6 +16,8 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1..5] [--
 
 --min-p adds the min-p stage (aclnnTopKTopPSampleV2, "minP sampling") with a
 per-row min_p drawn uniformly from [0.01, 0.2] to the chosen workload.
+--no-logits runs the pre-sorted workload without logits (the output is
+scattered through sorted_indices).
 """
 
 import argparse
@@ -90,15 +92,20 @@ def dev(bits, dtype):
     return torch.from_numpy(np.ascontiguousarray(bits).view(getattr(np, iv))).cuda().view(getattr(torch, fv))
 
 
-def algorithmic_bytes(wl, with_min_p=False):
+def algorithmic_bytes(wl, with_min_p=False, with_logits=True):
     """Minimal HBM bytes of one call: read every logit once, write every output
     once, read p and k (and min_p); the pre-sorted entry also reads at least
-    the k largest sorted values of each row."""
+    the k largest sorted values of each row. Without logits the pre-sorted
+    entry writes every output once and reads the survivors' values and
+    indices, at least min(k, V) per row."""
     s = wl.elem_bytes
-    per_row = 2 * wl.V * s + s + 4 + (s if with_min_p else 0)
-    total = wl.B * per_row
+    kept = int(np.clip(wl.k, 0, wl.V).sum())
+    params = wl.B * (s + 4 + (s if with_min_p else 0))
+    if wl.entry == "with_sorted" and not with_logits:
+        return wl.B * wl.V * s + kept * (s + 4) + params
+    total = 2 * wl.B * wl.V * s + params
     if wl.entry == "with_sorted":
-        total += int(np.clip(wl.k, 0, wl.V).sum()) * s
+        total += kept * s
     return total
 
 
@@ -140,6 +147,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--policy", type=int, default=0, help="plan policy: 0 auto, 1 general, 2 registers")
     ap.add_argument("--min-p", action="store_true", help="add a per-row min_p in [0.01, 0.2] (the min-p stage)")
+    ap.add_argument("--no-logits", action="store_true", help="pre-sorted workload without logits (scattered output)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time a plain device-to-device copy of the logits instead of the filter (the reference "
                          "kernel whose HBM counters scale the filter's)")
@@ -182,7 +190,8 @@ def main():
         elif wl.entry == "apply":
             tk.apply_top_k_top_p(st[0], p, k, out=st[1], min_p=mp)
         else:
-            tk.apply_top_k_top_p_with_sorted(st[2], st[3], p, k, logits=st[0], out=st[1], min_p=mp)
+            tk.apply_top_k_top_p_with_sorted(st[2], st[3], p, k, logits=None if args.no_logits else st[0], out=st[1],
+                                             min_p=mp)
 
     for i in range(args.warmup):
         step(i)
@@ -204,7 +213,8 @@ def main():
 
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     kernel_ms = ev0.elapsed_time(ev1) / args.steps
-    nbytes = 2 * wl.B * wl.V * wl.elem_bytes if args.copy_calibration else algorithmic_bytes(wl, args.min_p)
+    nbytes = (2 * wl.B * wl.V * wl.elem_bytes if args.copy_calibration
+              else algorithmic_bytes(wl, args.min_p, not args.no_logits))
     achieved = nbytes / (kernel_ms * 1e-3) / 1e9
     rows_per_s = wl.B / (ms_per_step * 1e-3)
 
@@ -222,7 +232,8 @@ def main():
         "dtype": dt,
         "data": "synthetic",
         "config": {
-            "workload": WORKLOAD_TEXT[args.workload] + (", min-p U[0.01,0.2] per row" if args.min_p else ""),
+            "workload": WORKLOAD_TEXT[args.workload] + (", min-p U[0.01,0.2] per row" if args.min_p else "")
+                        + (", without logits" if args.no_logits and wl.entry == "with_sorted" else ""),
             "B": wl.B,
             "V": wl.V,
             "buffer_sets": len(sets),

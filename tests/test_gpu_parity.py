@@ -232,3 +232,18 @@ def test_with_sorted_copy_boundary(dtype):
                 assert rep.hard_mismatches == 0, (V, kind, kv, pv, rep.details[:2])
                 total.merge(rep)
     say(f"with_sorted copy boundary {dtype}: {total}")
+
+
+def test_with_sorted_workload5_without_logits_sampled():
+    """The pre-sorted workload without logits: the output is scattered
+    through sorted_indices (-inf slices, then the survivors)."""
+    need_gpu()
+    wl = make_workload(5)
+    got = gpu_with_sorted(wl.sorted_value, wl.sorted_indices, wl.dtype, wl.p, wl.k, None)
+    rows = np.array([0, 2, 31, 64, wl.B - 1])
+    ref = oracle_sorted(wl.sorted_value[rows], wl.sorted_indices[rows], wl.dtype, wl.p[rows], wl.k[rows],
+                        logits_bits=None)
+    _check(compare(got[rows], wl.logits[rows], ref, wl.dtype, row_ids=rows), "workload 5 without logits")
+    _all_rows_properties(got, wl)
+    with_logits = gpu_with_sorted(wl.sorted_value, wl.sorted_indices, wl.dtype, wl.p, wl.k, wl.logits)
+    assert np.array_equal(got, with_logits)

@@ -20,7 +20,8 @@
 // that run of equal values: the run's positions a..F-1 are collected into a
 // shared-memory bitmap (the guide's ScatterBoundary idea) and masked, so the
 // single coalesced pass over logits is the only full-row traffic.
-// Without logits: out[sorted_indices[j]] = j >= F ? sorted_value[j] : -inf.
+// Without logits: the row is written as -inf, then the survivors are
+// scattered over it, out[sorted_indices[j]] = sorted_value[j] for j >= F.
 //
 // Each row is split into slices handled by separate blocks; every block
 // repeats the (cheap) boundary search, so no block waits on another and no
@@ -337,11 +338,19 @@ __global__ __launch_bounds__(kThreads, 8) void sorted_logits_kernel(
 
 constexpr int kScatterSlice = 65536;
 
+// Without logits: out[sorted_indices[j]] = j >= F ? sorted_value[j] : -inf.
+// Block s of a row owns output positions [s * 65536, (s + 1) * 65536): it
+// writes them all as -inf with coalesced stores, waits for those stores, and
+// then writes the survivors (sorted positions F..V-1) whose index falls in
+// its slice. Only the survivors' values and indices are read, instead of the
+// whole permutation. A row with nothing masked is a plain scatter, each block
+// taking a slice of the sorted positions.
 template <class DT>
 __global__ __launch_bounds__(kThreads) void sorted_scatter_kernel(
     const typename DT::raw_t* __restrict__ sorted_value, const int32_t* __restrict__ sorted_indices,
     const typename DT::raw_t* __restrict__ p, const int32_t* __restrict__ k,
     const typename DT::raw_t* __restrict__ min_p, typename DT::raw_t* __restrict__ out, int V, int S) {
+  using raw_t = typename DT::raw_t;
   __shared__ RowSmem sm;
   const int b = blockIdx.x / S;
   const int s = blockIdx.x - b * S;
@@ -349,15 +358,41 @@ __global__ __launch_bounds__(kThreads) void sorted_scatter_kernel(
   const auto* __restrict__ sv = sorted_value + row_off;
   const int32_t* __restrict__ si = sorted_indices + row_off;
   const RowParams rp = decode_row_params<DT>(p, k, min_p, b, V);
+  raw_t* __restrict__ orow = out + row_off;
+  const int v0 = s * kScatterSlice;
+  const int v1 = min(V, v0 + kScatterSlice);
   int F = 0;
-  const SortedSrcGlobal<DT> src{sv};
-  if (row_filters(rp)) F = sorted_boundary<DT>(src, rp, V, sm).F;
-  const int j0 = s * kScatterSlice;
-  const int j1 = min(V, j0 + kScatterSlice);
-  auto* __restrict__ orow = out + row_off;
-  for (int j = j0 + static_cast<int>(threadIdx.x); j < j1; j += kThreads) {
+  if (row_filters(rp)) F = sorted_boundary<DT>(SortedSrcGlobal<DT>{sv}, rp, V, sm).F;
+  if (F > 0) {  // something is masked: the slice as -inf first
+    constexpr int kPV = DT::kPerVec;
+    raw_t* dst = orow + v0;
+    const int n = v1 - v0;
+    if ((reinterpret_cast<uintptr_t>(dst) & 15u) == 0) {
+      vec_t cv = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int j = 0; j < kPV; ++j) set_lane<raw_t>(cv, j, DT::kNegInf);
+      const __amdgpu_buffer_rsrc_t rs = row_rsrc(dst, n);  // bounded: the partial last vector is done below
+      const int nv = n / kPV;
+      for (int e = static_cast<int>(threadIdx.x); e < nv; e += kThreads)
+        __builtin_amdgcn_raw_buffer_store_b128(cv, rs, e * 16, 0, kStorePolicy);
+      for (int e = nv * kPV + static_cast<int>(threadIdx.x); e < n; e += kThreads) dst[e] = DT::kNegInf;
+    } else {
+      for (int e = static_cast<int>(threadIdx.x); e < n; e += kThreads) dst[e] = DT::kNegInf;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+  if (F == 0) {  // nothing masked: a plain scatter, block s taking sorted positions [v0, v1)
+    for (int j = v0 + static_cast<int>(threadIdx.x); j < v1; j += kThreads) {
+      const int v = si[j];
+      if (static_cast<unsigned>(v) < static_cast<unsigned>(V)) orow[v] = sv[j];
+    }
+    return;
+  }
+  for (int j = F + static_cast<int>(threadIdx.x); j < V; j += kThreads) {
     const int v = si[j];
-    if (static_cast<unsigned>(v) < static_cast<unsigned>(V)) orow[v] = (j >= F) ? sv[j] : DT::kNegInf;
+    if (v >= v0 && v < v1) orow[v] = sv[j];
   }
 }
 

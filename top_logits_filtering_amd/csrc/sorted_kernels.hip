@@ -230,6 +230,34 @@ __device__ __forceinline__ SortedBoundary sorted_boundary_copy(const typename DT
   return bd;
 }
 
+constexpr int kPre = kSortedPrefetch / kThreads;
+
+// Requests the top R = min(V, 6144) sorted values of a row as bounded buffer
+// loads of whole elements: no branch per load, so all of them are in flight
+// together (positions past R read as zero and are never used).
+template <class DT>
+__device__ __forceinline__ void prefetch_top(const typename DT::raw_t* __restrict__ sv, int V, int R,
+                                             typename DT::raw_t (&pre)[kPre]) {
+  using raw_t = typename DT::raw_t;
+  const __amdgpu_buffer_rsrc_t rs = row_rsrc(sv + (V - R), R);
+#pragma unroll
+  for (int u = 0; u < kPre; ++u) {
+    const int off = (u * kThreads + static_cast<int>(threadIdx.x)) * static_cast<int>(sizeof(raw_t));
+    if constexpr (sizeof(raw_t) == 2)
+      pre[u] = static_cast<raw_t>(__builtin_amdgcn_raw_buffer_load_b16(rs, off, 0, 0));
+    else
+      pre[u] = static_cast<raw_t>(__builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0));
+  }
+}
+
+// The search runs from the copy when the run of values equal to the k-th
+// largest starts inside it (or the copy is the whole row).
+template <class DT>
+__device__ __forceinline__ bool boundary_from_copy(const typename DT::raw_t* top, int R, int V, const RowParams& rp) {
+  return rp.k_on && (R == V || (static_cast<int>(rp.k) + kSortedTieMargin <= R &&
+                                DT::key(top[0]) < DT::key(top[R - static_cast<int>(rp.k)])));
+}
+
 constexpr int kSortedVecs = 8;  // logits slice held in registers: 8 vectors per thread
 constexpr int kMaxSliceWords = (kThreads * kSortedVecs * 8) / 32;
 
@@ -258,21 +286,8 @@ __global__ __launch_bounds__(kThreads, 8) void sorted_logits_kernel(
   // for what it reads. The top values are requested before k is known.
   const RowParamsRaw<DT> rpr = fetch_row_params<DT>(p, k, min_p, b);
   const int R = min(V, kSortedPrefetch);
-  constexpr int kPre = kSortedPrefetch / kThreads;
   raw_t pre[kPre];
-  {
-    // bounded buffer loads of whole elements: no branch per load, so all of
-    // them are in flight together (positions past R read as zero, unused)
-    const __amdgpu_buffer_rsrc_t rs = row_rsrc(sv + (V - R), R);
-#pragma unroll
-    for (int u = 0; u < kPre; ++u) {
-      const int off = (u * kThreads + static_cast<int>(threadIdx.x)) * static_cast<int>(sizeof(raw_t));
-      if constexpr (sizeof(raw_t) == 2)
-        pre[u] = static_cast<raw_t>(__builtin_amdgcn_raw_buffer_load_b16(rs, off, 0, 0));
-      else
-        pre[u] = static_cast<raw_t>(__builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0));
-    }
-  }
+  prefetch_top<DT>(sv, V, R, pre);
   __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the slice's
   Tile tile;
   tile.load(logits + row_off, v0, len);
@@ -286,12 +301,8 @@ __global__ __launch_bounds__(kThreads, 8) void sorted_logits_kernel(
     tile.store(orow, [](raw_t r, int) { return r; });
     return;
   }
-  // the copy serves the whole search when the run of values equal to the
-  // k-th largest starts inside it (or the copy is the whole row)
-  const bool from_copy = rp.k_on && (R == V || (static_cast<int>(rp.k) + kSortedTieMargin <= R &&
-                                                DT::key(top[0]) < DT::key(top[R - static_cast<int>(rp.k)])));
   SortedBoundary bd;
-  if (from_copy)
+  if (boundary_from_copy<DT>(top, R, V, rp))
     bd = sorted_boundary_copy<DT>(top, R, V, rp, sm);
   else
     bd = sorted_boundary<DT>(SortedSrcGlobal<DT>{sv}, rp, V, sm);
@@ -339,60 +350,102 @@ __global__ __launch_bounds__(kThreads, 8) void sorted_logits_kernel(
 constexpr int kScatterSlice = 65536;
 
 // Without logits: out[sorted_indices[j]] = j >= F ? sorted_value[j] : -inf.
-// Block s of a row owns output positions [s * 65536, (s + 1) * 65536): it
-// writes them all as -inf with coalesced stores, waits for those stores, and
-// then writes the survivors (sorted positions F..V-1) whose index falls in
-// its slice. Only the survivors' values and indices are read, instead of the
-// whole permutation. A row with nothing masked is a plain scatter, each block
-// taking a slice of the sorted positions.
+// Block s of a row owns output positions [s * 65536, (s + 1) * 65536). It
+// requests the row's top sorted values first (as the logits kernel does),
+// writes its slice as -inf with coalesced stores, finds F while they drain,
+// waits for them, and writes the survivors (sorted positions F..V-1) whose
+// index falls in its slice. Only the survivors' values and indices
+// are read, instead of the whole permutation. A row with nothing to filter
+// is a plain scatter, each block taking a slice of the sorted positions.
 template <class DT>
 __global__ __launch_bounds__(kThreads) void sorted_scatter_kernel(
     const typename DT::raw_t* __restrict__ sorted_value, const int32_t* __restrict__ sorted_indices,
     const typename DT::raw_t* __restrict__ p, const int32_t* __restrict__ k,
     const typename DT::raw_t* __restrict__ min_p, typename DT::raw_t* __restrict__ out, int V, int S) {
   using raw_t = typename DT::raw_t;
+  constexpr int kPV = DT::kPerVec;
   __shared__ RowSmem sm;
+  __shared__ __align__(16) raw_t top[kSortedPrefetch];
   const int b = blockIdx.x / S;
   const int s = blockIdx.x - b * S;
   const size_t row_off = static_cast<size_t>(b) * V;
   const auto* __restrict__ sv = sorted_value + row_off;
   const int32_t* __restrict__ si = sorted_indices + row_off;
-  const RowParams rp = decode_row_params<DT>(p, k, min_p, b, V);
   raw_t* __restrict__ orow = out + row_off;
   const int v0 = s * kScatterSlice;
   const int v1 = min(V, v0 + kScatterSlice);
-  int F = 0;
-  if (row_filters(rp)) F = sorted_boundary<DT>(SortedSrcGlobal<DT>{sv}, rp, V, sm).F;
-  if (F > 0) {  // something is masked: the slice as -inf first
-    constexpr int kPV = DT::kPerVec;
-    raw_t* dst = orow + v0;
-    const int n = v1 - v0;
-    if ((reinterpret_cast<uintptr_t>(dst) & 15u) == 0) {
-      vec_t cv = {0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int j = 0; j < kPV; ++j) set_lane<raw_t>(cv, j, DT::kNegInf);
-      const __amdgpu_buffer_rsrc_t rs = row_rsrc(dst, n);  // bounded: the partial last vector is done below
-      const int nv = n / kPV;
-      for (int e = static_cast<int>(threadIdx.x); e < nv; e += kThreads)
-        __builtin_amdgcn_raw_buffer_store_b128(cv, rs, e * 16, 0, kStorePolicy);
-      for (int e = nv * kPV + static_cast<int>(threadIdx.x); e < n; e += kThreads) dst[e] = DT::kNegInf;
-    } else {
-      for (int e = static_cast<int>(threadIdx.x); e < n; e += kThreads) dst[e] = DT::kNegInf;
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-  }
-  if (F == 0) {  // nothing masked: a plain scatter, block s taking sorted positions [v0, v1)
+
+  const RowParamsRaw<DT> rpr = fetch_row_params<DT>(p, k, min_p, b);
+  const int R = min(V, kSortedPrefetch);
+  raw_t pre[kPre];
+  prefetch_top<DT>(sv, V, R, pre);
+  __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the stores below
+  const RowParams rp = decode_row_params<DT>(rpr, V);
+  if (!row_filters(rp)) {  // nothing to filter: a plain scatter of sorted positions [v0, v1)
     for (int j = v0 + static_cast<int>(threadIdx.x); j < v1; j += kThreads) {
       const int v = si[j];
       if (static_cast<unsigned>(v) < static_cast<unsigned>(V)) orow[v] = sv[j];
     }
     return;
   }
-  for (int j = F + static_cast<int>(threadIdx.x); j < V; j += kThreads) {
-    const int v = si[j];
-    if (v >= v0 && v < v1) orow[v] = sv[j];
+#pragma unroll
+  for (int u = 0; u < kPre; ++u) top[u * kThreads + threadIdx.x] = pre[u];  // entries past R: zero, unused
+
+  // The output slice as -inf, in two portions: a quarter before the boundary
+  // search (it drains while the search runs on the shared-memory copy) and
+  // the rest after the survivors' loads are issued (a wave stalls at its
+  // stores once the memory pipeline is full, and loads issued after stores
+  // complete after them).
+  raw_t* dst = orow + v0;
+  const int n = v1 - v0;
+  const bool vec_out = (reinterpret_cast<uintptr_t>(dst) & 15u) == 0;
+  const int nv = vec_out ? n / kPV : 0;  // whole 16-byte vectors
+  vec_t cv = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int j = 0; j < kPV; ++j) set_lane<raw_t>(cv, j, DT::kNegInf);
+  const __amdgpu_buffer_rsrc_t rs = row_rsrc(dst, n);
+  const int nv_a = nv / 4;
+  for (int e = static_cast<int>(threadIdx.x); e < nv_a; e += kThreads)
+    __builtin_amdgcn_raw_buffer_store_b128(cv, rs, e * 16, 0, kStorePolicy);
+  for (int e = nv * kPV + static_cast<int>(threadIdx.x); e < n; e += kThreads) dst[e] = DT::kNegInf;
+  lds_barrier();  // the copy is in place (this barrier does not wait for the stores)
+
+  const int F = boundary_from_copy<DT>(top, R, V, rp) ? sorted_boundary_copy<DT>(top, R, V, rp, sm).F
+                                                      : sorted_boundary<DT>(SortedSrcGlobal<DT>{sv}, rp, V, sm).F;
+  // The survivors, 8 per thread per round with every load of a round in
+  // flight together (bounded buffer loads: positions past V read as zero).
+  // The first round's loads are issued before the wait for the -inf stores,
+  // so they arrive while those stores drain.
+  constexpr int kRound = 8;
+  const int ns = V - F;
+  const __amdgpu_buffer_rsrc_t ri = row_rsrc(si + F, ns);
+  const __amdgpu_buffer_rsrc_t rv = row_rsrc(sv + F, ns);
+  int vv[kRound];
+  raw_t xv[kRound];
+  auto request = [&](int c0) {
+#pragma unroll
+    for (int u = 0; u < kRound; ++u) {
+      const int c = c0 + u * kThreads + static_cast<int>(threadIdx.x);
+      vv[u] = __builtin_amdgcn_raw_buffer_load_b32(ri, c * 4, 0, 0);
+      if constexpr (sizeof(raw_t) == 2)
+        xv[u] = static_cast<raw_t>(__builtin_amdgcn_raw_buffer_load_b16(rv, c * 2, 0, 0));
+      else
+        xv[u] = static_cast<raw_t>(__builtin_amdgcn_raw_buffer_load_b32(rv, c * 4, 0, 0));
+    }
+  };
+  request(0);
+  for (int e = nv_a + static_cast<int>(threadIdx.x); e < nv; e += kThreads)
+    __builtin_amdgcn_raw_buffer_store_b128(cv, rs, e * 16, 0, kStorePolicy);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int c0 = 0; c0 < ns; c0 += kRound * kThreads) {
+    if (c0 > 0) request(c0);
+#pragma unroll
+    for (int u = 0; u < kRound; ++u) {
+      const int c = c0 + u * kThreads + static_cast<int>(threadIdx.x);
+      if (c < ns && vv[u] >= v0 && vv[u] < v1) orow[vv[u]] = xv[u];
+    }
   }
 }
 

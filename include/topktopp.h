@@ -71,6 +71,9 @@ typedef enum {
  * operator, aclnnTopKTopPSampleV2, states for its vocabulary size). */
 #define TOPKTOPP_MAX_V (1 << 20)
 
+/* Largest row stride accepted by the _ex entry points, in elements (2^31). */
+#define TOPKTOPP_MAX_LD (1LL << 31)
+
 /*
  * apply_top_k_top_p — filter raw logits (the aclnn entry of AKP §5 and §6.1,
  * which sorts internally). No sort is materialised: the threshold pair that
@@ -147,6 +150,31 @@ topktopp_status apply_top_k_top_p_min_p_with_sorted(const void* sorted_value, co
                                                     int dtype, int64_t B, int64_t V, const void* p,
                                                     const int32_t* k, const void* min_p, const void* logits,
                                                     void* out, void* stream);
+
+/*
+ * apply_top_k_top_p_ex — apply_top_k_top_p_min_p on row-strided operands: row
+ * b of logits starts at element b * ld_logits and row b of out at element
+ * b * ld_out (a [B, V] view of a wider buffer, e.g. a vocabulary padded to a
+ * multiple of 64; the aclnn entry makes such views contiguous first, AKP
+ * §6.1). Elements within a row are contiguous. Each stride must be >= V and
+ * <= TOPKTOPP_MAX_LD (else ERR_INVALID); the strided extents of out and the
+ * inputs must not overlap. Positions between V and the stride are neither
+ * read nor written. Other arguments as for apply_top_k_top_p_min_p.
+ */
+topktopp_status apply_top_k_top_p_ex(const void* logits, int64_t ld_logits, int dtype, int64_t B, int64_t V,
+                                     const void* p, const int32_t* k, const void* min_p, void* out,
+                                     int64_t ld_out, void* stream);
+
+/*
+ * apply_top_k_top_p_with_sorted_ex — apply_top_k_top_p_min_p_with_sorted on
+ * row-strided operands, one row stride (in elements) per [B, V] operand, with
+ * the rules of apply_top_k_top_p_ex. ld_logits is ignored when logits is NULL.
+ */
+topktopp_status apply_top_k_top_p_with_sorted_ex(const void* sorted_value, int64_t ld_sorted_value,
+                                                 const int32_t* sorted_indices, int64_t ld_sorted_indices,
+                                                 int dtype, int64_t B, int64_t V, const void* p,
+                                                 const int32_t* k, const void* min_p, const void* logits,
+                                                 int64_t ld_logits, void* out, int64_t ld_out, void* stream);
 
 /* Text of the most recent error on the calling thread ("" if none); the
  * counterpart of aclGetRecentErrMsg (AKP §8). Valid until the next call on

@@ -106,3 +106,22 @@ def test_plan_policy_roundtrip(lib):
 def test_missing_library_fails_loudly(tmp_path):
     with pytest.raises(RuntimeError, match="no fallback"):
         tk.load_library(str(tmp_path / "nope.so"))
+
+
+def test_strided_entry_points_check_strides(lib):
+    f = lib.apply_top_k_top_p_ex
+    out = FAKE + (1 << 32)
+    assert f(FAKE, 7, 0, 2, 8, FAKE, None, None, out, 8, None) == INVALID  # ld_logits < V
+    assert "stride" in tk.last_error()
+    assert f(FAKE, 8, 0, 2, 8, FAKE, None, None, out, 4, None) == INVALID  # ld_out < V
+    assert f(FAKE, 1 << 32, 0, 2, 8, FAKE, None, None, out, 8, None) == INVALID
+    assert "maximum" in tk.last_error()
+    # the strided extent of out reaches into logits: [out, out + (2-1)*1000*4 + 8*4)
+    assert f(out + 2000, 8, 0, 2, 8, FAKE, None, None, out, 1000, None) == INVALID
+    assert "overlap" in tk.last_error()
+    assert f(FAKE, 8, 0, 2, 8, None, None, None, out, 8, None) == NULLPTR
+    g = lib.apply_top_k_top_p_with_sorted_ex
+    assert g(FAKE, 8, FAKE + (1 << 34), 6, 0, 2, 8, FAKE, None, None, None, 0, out, 8, None) == INVALID
+    assert "sorted_indices" in tk.last_error()
+    # ld_logits is not checked when logits is NULL
+    assert g(None, 8, FAKE, 8, 0, 0, 8, None, None, None, None, 0, None, 8, None) == 0

@@ -19,9 +19,11 @@ TOPKTOPP_F32, TOPKTOPP_F16, TOPKTOPP_BF16 = 0, 1, 2
 STATUS_NAMES = {0: "OK", 1: "ERR_NULLPTR", 2: "ERR_INVALID", 3: "ERR_RUNTIME"}
 EXPORTED_SYMBOLS = (
     "apply_top_k_top_p",
+    "apply_top_k_top_p_ex",
     "apply_top_k_top_p_min_p",
     "apply_top_k_top_p_min_p_with_sorted",
     "apply_top_k_top_p_with_sorted",
+    "apply_top_k_top_p_with_sorted_ex",
     "topktopp_last_error",
     "topktopp_set_plan_policy",
 )
@@ -57,6 +59,10 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.apply_top_k_top_p_min_p.restype = i32
     lib.apply_top_k_top_p_min_p_with_sorted.argtypes = [vp, vp, i32, i64, i64, vp, vp, vp, vp, vp, vp]
     lib.apply_top_k_top_p_min_p_with_sorted.restype = i32
+    lib.apply_top_k_top_p_ex.argtypes = [vp, i64, i32, i64, i64, vp, vp, vp, vp, i64, vp]
+    lib.apply_top_k_top_p_ex.restype = i32
+    lib.apply_top_k_top_p_with_sorted_ex.argtypes = [vp, i64, vp, i64, i32, i64, i64, vp, vp, vp, vp, i64, vp, i64, vp]
+    lib.apply_top_k_top_p_with_sorted_ex.restype = i32
     lib.topktopp_last_error.argtypes = []
     lib.topktopp_last_error.restype = ctypes.c_char_p
     lib.topktopp_set_plan_policy.argtypes = [i32]
@@ -103,6 +109,22 @@ def _ptr(t) -> Optional[int]:
     return t.data_ptr()
 
 
+def _rows(t):
+    """(pointer, row stride in elements) of a 2-D tensor whose rows are
+    contiguous; None for None."""
+    if t is None:
+        return None, 0
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    if t.dim() != 2:
+        raise ValueError("expected a 2-D [B, V] tensor")
+    B, V = t.shape
+    if V > 1 and t.stride(1) != 1:
+        raise ValueError("rows must be contiguous (stride 1 along the last dimension)")
+    ld = t.stride(0) if B > 1 else V
+    return t.data_ptr(), ld
+
+
 def _stream(stream, device) -> int:
     """The HIP stream handle to launch on: the given one, else torch's current
     stream of the tensors' device."""
@@ -120,7 +142,8 @@ def _check(status: int):
 
 def apply_top_k_top_p(logits, p=None, k=None, out=None, stream=None, min_p=None):
     """Filter raw logits [B, V]; p [B] (logits dtype), k [B] (int32) and min_p
-    [B] (logits dtype, the min-p stage) are optional."""
+    [B] (logits dtype, the min-p stage) are optional. logits and out may be
+    row-strided views (rows contiguous, e.g. a slice of a padded vocabulary)."""
     import torch
 
     lib = load_library()
@@ -128,14 +151,16 @@ def apply_top_k_top_p(logits, p=None, k=None, out=None, stream=None, min_p=None)
         raise ValueError("logits must be 2-D [B, V]")
     B, V = logits.shape
     if out is None:
-        out = torch.empty_like(logits)
+        out = torch.empty((B, V), dtype=logits.dtype, device=logits.device)
     st = _stream(stream, logits.device)
-    if min_p is None:
-        status = lib.apply_top_k_top_p(_ptr(logits), _dtype_code(logits), B, V, _ptr(p), _ptr(k), _ptr(out), st)
+    (xp, ldx), (op, ldo) = _rows(logits), _rows(out)
+    if ldx != V or ldo != V:
+        status = lib.apply_top_k_top_p_ex(xp, ldx, _dtype_code(logits), B, V, _ptr(p), _ptr(k), _ptr(min_p), op, ldo,
+                                          st)
+    elif min_p is None:
+        status = lib.apply_top_k_top_p(xp, _dtype_code(logits), B, V, _ptr(p), _ptr(k), op, st)
     else:
-        status = lib.apply_top_k_top_p_min_p(
-            _ptr(logits), _dtype_code(logits), B, V, _ptr(p), _ptr(k), _ptr(min_p), _ptr(out), st
-        )
+        status = lib.apply_top_k_top_p_min_p(xp, _dtype_code(logits), B, V, _ptr(p), _ptr(k), _ptr(min_p), op, st)
     _check(status)
     return out
 
@@ -151,9 +176,14 @@ def apply_top_k_top_p_with_sorted(sorted_value, sorted_indices, p=None, k=None, 
         raise ValueError("sorted_value must be 2-D [B, V]")
     B, V = sorted_value.shape
     if out is None:
-        out = torch.empty_like(sorted_value)
+        out = torch.empty((B, V), dtype=sorted_value.dtype, device=sorted_value.device)
     st = _stream(stream, sorted_value.device)
-    if min_p is None:
+    (sp, lds), (ip, ldi), (xp, ldx), (op, ldo) = _rows(sorted_value), _rows(sorted_indices), _rows(logits), _rows(out)
+    if lds != V or ldi != V or ldo != V or (logits is not None and ldx != V):
+        status = lib.apply_top_k_top_p_with_sorted_ex(
+            sp, lds, ip, ldi, _dtype_code(sorted_value), B, V, _ptr(p), _ptr(k), _ptr(min_p), xp, ldx, op, ldo, st
+        )
+    elif min_p is None:
         status = lib.apply_top_k_top_p_with_sorted(
             _ptr(sorted_value), _ptr(sorted_indices), _dtype_code(sorted_value), B, V, _ptr(p), _ptr(k),
             _ptr(logits), _ptr(out), st

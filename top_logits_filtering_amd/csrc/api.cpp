@@ -48,6 +48,20 @@ topktopp_status check_shape(int64_t B, int64_t V) {
   return TOPKTOPP_OK;
 }
 
+// Row strides: every operand's rows are at least V elements apart (rows may
+// not overlap one another), and small enough for the byte offsets to fit.
+topktopp_status check_ld(int64_t ld, int64_t V, const char* name) {
+  if (ld < V) return fail(TOPKTOPP_ERR_INVALID, "row stride of %s (%lld) is below V=%lld", name, (long long)ld, (long long)V);
+  if (ld > TOPKTOPP_MAX_LD)
+    return fail(TOPKTOPP_ERR_INVALID, "row stride of %s (%lld) exceeds the supported maximum", name, (long long)ld);
+  return TOPKTOPP_OK;
+}
+
+// Bytes from the first element of a strided [B, V] operand to one past its last.
+size_t extent(int64_t B, int64_t V, int64_t ld, size_t es) {
+  return (static_cast<size_t>(B - 1) * static_cast<size_t>(ld) + static_cast<size_t>(V)) * es;
+}
+
 topktopp_status check_launch(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(TOPKTOPP_ERR_RUNTIME, "%s failed: %s", what, hipGetErrorString(e));
   return TOPKTOPP_OK;
@@ -77,8 +91,9 @@ topktopp_status check_params(const void* p, const int32_t* k, const void* min_p,
   return TOPKTOPP_OK;
 }
 
-topktopp_status apply_impl(const void* logits, int dtype, int64_t B, int64_t V, const void* p, const int32_t* k,
-                           const void* min_p, bool has_min_p, void* out, void* stream) {
+topktopp_status apply_impl(const void* logits, int64_t ldx, int dtype, int64_t B, int64_t V, const void* p,
+                           const int32_t* k, const void* min_p, bool has_min_p, void* out, int64_t ldo,
+                           void* stream) {
   g_last_error.clear();
   if (B >= 0 && V >= 0 && (B == 0 || V == 0)) {  // empty: nothing is read or written, pointers may be NULL
     if (!valid_dtype(dtype)) return fail(TOPKTOPP_ERR_INVALID, "dtype %d is not one of F32, F16, BF16", dtype);
@@ -89,21 +104,27 @@ topktopp_status apply_impl(const void* logits, int dtype, int64_t B, int64_t V, 
   if (topktopp_status s = check_params(p, k, min_p, has_min_p)) return s;
   if (!valid_dtype(dtype)) return fail(TOPKTOPP_ERR_INVALID, "dtype %d is not one of F32, F16, BF16", dtype);
   if (topktopp_status s = check_shape(B, V)) return s;
+  if (topktopp_status s = check_ld(ldx, V, "logits")) return s;
+  if (topktopp_status s = check_ld(ldo, V, "out")) return s;
   const size_t es = elem_size(dtype);
-  const size_t nbytes = static_cast<size_t>(B) * static_cast<size_t>(V) * es;
-  if (overlaps(out, nbytes, logits, nbytes) || overlaps(out, nbytes, p, static_cast<size_t>(B) * es) ||
-      overlaps(out, nbytes, k, static_cast<size_t>(B) * 4) || overlaps(out, nbytes, min_p, static_cast<size_t>(B) * es))
+  const size_t nout = extent(B, V, ldo, es);
+  if (overlaps(out, nout, logits, extent(B, V, ldx, es)) || overlaps(out, nout, p, static_cast<size_t>(B) * es) ||
+      overlaps(out, nout, k, static_cast<size_t>(B) * 4) || overlaps(out, nout, min_p, static_cast<size_t>(B) * es))
     return fail(TOPKTOPP_ERR_INVALID, "out overlaps an input buffer");
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (V == 1)  // a last dimension of 1 is copied through unfiltered
-    return check_launch(hipMemcpyAsync(out, logits, nbytes, hipMemcpyDeviceToDevice, st), "hipMemcpyAsync");
-  return check_launch(tkp::launch_apply(dtype, logits, p, k, min_p, out, B, V, g_policy.load(), st),
+    return check_launch(hipMemcpy2DAsync(out, static_cast<size_t>(ldo) * es, logits, static_cast<size_t>(ldx) * es, es,
+                                         static_cast<size_t>(B), hipMemcpyDeviceToDevice, st),
+                        "hipMemcpy2DAsync");
+  const tkp::RowStrides ld{ldx, ldo, 0, 0};
+  return check_launch(tkp::launch_apply(dtype, logits, p, k, min_p, out, B, V, ld, g_policy.load(), st),
                       "filter launch");
 }
 
-topktopp_status with_sorted_impl(const void* sorted_value, const int32_t* sorted_indices, int dtype, int64_t B,
-                                 int64_t V, const void* p, const int32_t* k, const void* min_p, bool has_min_p,
-                                 const void* logits, void* out, void* stream) {
+topktopp_status with_sorted_impl(const void* sorted_value, int64_t lds, const int32_t* sorted_indices, int64_t ldi,
+                                 int dtype, int64_t B, int64_t V, const void* p, const int32_t* k,
+                                 const void* min_p, bool has_min_p, const void* logits, int64_t ldx, void* out,
+                                 int64_t ldo, void* stream) {
   g_last_error.clear();
   if (B >= 0 && V >= 0 && (B == 0 || V == 0)) {  // empty: nothing is read or written, pointers may be NULL
     if (!valid_dtype(dtype)) return fail(TOPKTOPP_ERR_INVALID, "dtype %d is not one of F32, F16, BF16", dtype);
@@ -115,20 +136,30 @@ topktopp_status with_sorted_impl(const void* sorted_value, const int32_t* sorted
   if (topktopp_status s = check_params(p, k, min_p, has_min_p)) return s;
   if (!valid_dtype(dtype)) return fail(TOPKTOPP_ERR_INVALID, "dtype %d is not one of F32, F16, BF16", dtype);
   if (topktopp_status s = check_shape(B, V)) return s;
+  if (topktopp_status s = check_ld(lds, V, "sorted_value")) return s;
+  if (topktopp_status s = check_ld(ldi, V, "sorted_indices")) return s;
+  if (logits != nullptr)
+    if (topktopp_status s = check_ld(ldx, V, "logits")) return s;
+  if (topktopp_status s = check_ld(ldo, V, "out")) return s;
   const size_t es = elem_size(dtype);
-  const size_t nbytes = static_cast<size_t>(B) * static_cast<size_t>(V) * es;
-  if (overlaps(out, nbytes, sorted_value, nbytes) ||
-      overlaps(out, nbytes, sorted_indices, static_cast<size_t>(B) * static_cast<size_t>(V) * 4) ||
-      overlaps(out, nbytes, logits, nbytes) || overlaps(out, nbytes, p, static_cast<size_t>(B) * es) ||
-      overlaps(out, nbytes, k, static_cast<size_t>(B) * 4) || overlaps(out, nbytes, min_p, static_cast<size_t>(B) * es))
+  const size_t nout = extent(B, V, ldo, es);
+  if (overlaps(out, nout, sorted_value, extent(B, V, lds, es)) ||
+      overlaps(out, nout, sorted_indices, extent(B, V, ldi, 4)) ||
+      (logits != nullptr && overlaps(out, nout, logits, extent(B, V, ldx, es))) ||
+      overlaps(out, nout, p, static_cast<size_t>(B) * es) || overlaps(out, nout, k, static_cast<size_t>(B) * 4) ||
+      overlaps(out, nout, min_p, static_cast<size_t>(B) * es))
     return fail(TOPKTOPP_ERR_INVALID, "out overlaps an input buffer");
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (V == 1)  // the single element is always kept; sorted_indices is 0
-    return check_launch(hipMemcpyAsync(out, logits != nullptr ? logits : sorted_value, nbytes,
-                                       hipMemcpyDeviceToDevice, st),
-                        "hipMemcpyAsync");
+  if (V == 1) {  // the single element is always kept; sorted_indices is 0
+    const void* src = logits != nullptr ? logits : sorted_value;
+    const int64_t lsrc = logits != nullptr ? ldx : lds;
+    return check_launch(hipMemcpy2DAsync(out, static_cast<size_t>(ldo) * es, src, static_cast<size_t>(lsrc) * es, es,
+                                         static_cast<size_t>(B), hipMemcpyDeviceToDevice, st),
+                        "hipMemcpy2DAsync");
+  }
+  const tkp::RowStrides ld{logits != nullptr ? ldx : V, ldo, lds, ldi};
   return check_launch(
-      tkp::launch_with_sorted(dtype, sorted_value, sorted_indices, p, k, min_p, logits, out, B, V, st),
+      tkp::launch_with_sorted(dtype, sorted_value, sorted_indices, p, k, min_p, logits, out, B, V, ld, st),
       "filter launch");
 }
 
@@ -138,25 +169,42 @@ extern "C" {
 
 topktopp_status apply_top_k_top_p(const void* logits, int dtype, int64_t B, int64_t V, const void* p,
                                   const int32_t* k, void* out, void* stream) {
-  return apply_impl(logits, dtype, B, V, p, k, nullptr, false, out, stream);
+  return apply_impl(logits, V, dtype, B, V, p, k, nullptr, false, out, V, stream);
 }
 
 topktopp_status apply_top_k_top_p_min_p(const void* logits, int dtype, int64_t B, int64_t V, const void* p,
                                         const int32_t* k, const void* min_p, void* out, void* stream) {
-  return apply_impl(logits, dtype, B, V, p, k, min_p, true, out, stream);
+  return apply_impl(logits, V, dtype, B, V, p, k, min_p, true, out, V, stream);
+}
+
+topktopp_status apply_top_k_top_p_ex(const void* logits, int64_t ld_logits, int dtype, int64_t B, int64_t V,
+                                     const void* p, const int32_t* k, const void* min_p, void* out, int64_t ld_out,
+                                     void* stream) {
+  return apply_impl(logits, ld_logits, dtype, B, V, p, k, min_p, true, out, ld_out, stream);
 }
 
 topktopp_status apply_top_k_top_p_with_sorted(const void* sorted_value, const int32_t* sorted_indices, int dtype,
                                               int64_t B, int64_t V, const void* p, const int32_t* k,
                                               const void* logits, void* out, void* stream) {
-  return with_sorted_impl(sorted_value, sorted_indices, dtype, B, V, p, k, nullptr, false, logits, out, stream);
+  return with_sorted_impl(sorted_value, V, sorted_indices, V, dtype, B, V, p, k, nullptr, false, logits, V, out, V,
+                          stream);
 }
 
 topktopp_status apply_top_k_top_p_min_p_with_sorted(const void* sorted_value, const int32_t* sorted_indices,
                                                     int dtype, int64_t B, int64_t V, const void* p,
                                                     const int32_t* k, const void* min_p, const void* logits,
                                                     void* out, void* stream) {
-  return with_sorted_impl(sorted_value, sorted_indices, dtype, B, V, p, k, min_p, true, logits, out, stream);
+  return with_sorted_impl(sorted_value, V, sorted_indices, V, dtype, B, V, p, k, min_p, true, logits, V, out, V,
+                          stream);
+}
+
+topktopp_status apply_top_k_top_p_with_sorted_ex(const void* sorted_value, int64_t ld_sorted_value,
+                                                 const int32_t* sorted_indices, int64_t ld_sorted_indices, int dtype,
+                                                 int64_t B, int64_t V, const void* p, const int32_t* k,
+                                                 const void* min_p, const void* logits, int64_t ld_logits, void* out,
+                                                 int64_t ld_out, void* stream) {
+  return with_sorted_impl(sorted_value, ld_sorted_value, sorted_indices, ld_sorted_indices, dtype, B, V, p, k, min_p,
+                          true, logits, ld_logits, out, ld_out, stream);
 }
 
 }  // extern "C"

@@ -6,8 +6,8 @@
 namespace tkp {
 
 hipError_t launch_apply_bf16(const void* logits, const void* p, const int32_t* k, const void* min_p, void* out,
-                          int64_t B, int64_t V, int policy, hipStream_t stream) {
-  return launch_apply_t<BF16T>(logits, p, k, min_p, out, B, V, policy, stream);
+                          int64_t B, int64_t V, RowStrides ld, int policy, hipStream_t stream) {
+  return launch_apply_t<BF16T>(logits, p, k, min_p, out, B, V, ld, policy, stream);
 }
 
 }  // namespace tkp

@@ -642,16 +642,17 @@ __global__ __launch_bounds__(kThreads) void apply_regs_kernel(const typename DT:
                                                               const int32_t* __restrict__ k,
                                                               const typename DT::raw_t* __restrict__ min_p,
                                                               typename DT::raw_t* __restrict__ out, int V,
-                                                              int use_candidates) {
+                                                              RowStrides ld, int use_candidates) {
   __shared__ ApplySmem S;
   const int b = blockIdx.x;
-  const size_t off = static_cast<size_t>(b) * V;
+  const size_t offx = static_cast<size_t>(b) * static_cast<size_t>(ld.x);
+  const size_t offo = static_cast<size_t>(b) * static_cast<size_t>(ld.o);
   // p[b], k[b] and min_p[b] are fetched before the row and used after it is requested
   const RowParamsRaw<DT> rpr = fetch_row_params<DT>(p, k, min_p, b);
   RegTile<DT, NVEC> tile;
-  tile.load(logits + off, 0, V);
+  tile.load(logits + offx, 0, V);
   const RowParams rp = decode_row_params<DT>(rpr, V);
-  filter_row<DT>(tile, logits + off, V, rp, use_candidates != 0, S, out + off);
+  filter_row<DT>(tile, logits + offx, V, rp, use_candidates != 0, S, out + offo);
 }
 
 template <class DT>
@@ -660,57 +661,60 @@ __global__ __launch_bounds__(kThreads) void apply_stream_kernel(const typename D
                                                                 const int32_t* __restrict__ k,
                                                                 const typename DT::raw_t* __restrict__ min_p,
                                                                 typename DT::raw_t* __restrict__ out, int V,
-                                                                int use_candidates) {
+                                                                RowStrides ld, int use_candidates) {
   __shared__ ApplySmem S;
   const int b = blockIdx.x;
-  const size_t off = static_cast<size_t>(b) * V;
+  const size_t offx = static_cast<size_t>(b) * static_cast<size_t>(ld.x);
+  const size_t offo = static_cast<size_t>(b) * static_cast<size_t>(ld.o);
   const RowParams rp = decode_row_params<DT>(p, k, min_p, b, V);
   GlobalTile<DT> tile;
-  tile.load(logits + off, 0, V);
-  filter_row<DT>(tile, logits + off, V, rp, use_candidates != 0, S, out + off);
+  tile.load(logits + offx, 0, V);
+  filter_row<DT>(tile, logits + offx, V, rp, use_candidates != 0, S, out + offo);
 }
 
 template <class DT, int NVEC>
 void launch_regs(const void* logits, const void* p, const int32_t* k, const void* min_p, void* out, int64_t B,
-                 int64_t V, int use_candidates, hipStream_t stream) {
+                 int64_t V, RowStrides ld, int use_candidates, hipStream_t stream) {
   using raw_t = typename DT::raw_t;
   hipLaunchKernelGGL((apply_regs_kernel<DT, NVEC>), dim3(static_cast<unsigned>(B)), dim3(kThreads), 0, stream,
                      static_cast<const raw_t*>(logits), static_cast<const raw_t*>(p), k,
-                     static_cast<const raw_t*>(min_p), static_cast<raw_t*>(out), static_cast<int>(V),
+                     static_cast<const raw_t*>(min_p), static_cast<raw_t*>(out), static_cast<int>(V), ld,
                      use_candidates);
 }
 
 template <class DT>
 hipError_t launch_apply_t(const void* logits, const void* p, const int32_t* k, const void* min_p, void* out,
-                          int64_t B, int64_t V, int policy, hipStream_t stream) {
+                          int64_t B, int64_t V, RowStrides ld, int policy, hipStream_t stream) {
   using raw_t = typename DT::raw_t;
   constexpr int span = kThreads * DT::kPerVec;
   const int64_t vecs = (V + span - 1) / span;
   const int use_candidates = policy == kPlanGeneral ? 0 : 1;
-  // register tiles move whole 16-byte vectors: rows must start 16-byte aligned
+  // register tiles move whole 16-byte vectors: every row must start 16-byte aligned
+  constexpr int64_t es = static_cast<int64_t>(sizeof(raw_t));
   const bool vec_ok = (V % DT::kPerVec) == 0 && (reinterpret_cast<uintptr_t>(logits) & 15u) == 0 &&
-                      (reinterpret_cast<uintptr_t>(out) & 15u) == 0;
+                      (reinterpret_cast<uintptr_t>(out) & 15u) == 0 && (ld.x * es) % 16 == 0 &&
+                      (ld.o * es) % 16 == 0;
   if (policy != kPlanAuto || vecs > kMaxVecs || !vec_ok) {
     hipLaunchKernelGGL(apply_stream_kernel<DT>, dim3(static_cast<unsigned>(B)), dim3(kThreads), 0, stream,
                        static_cast<const raw_t*>(logits), static_cast<const raw_t*>(p), k,
-                       static_cast<const raw_t*>(min_p), static_cast<raw_t*>(out), static_cast<int>(V),
+                       static_cast<const raw_t*>(min_p), static_cast<raw_t*>(out), static_cast<int>(V), ld,
                        use_candidates);
   } else if (vecs <= 1) {
-    launch_regs<DT, 1>(logits, p, k, min_p, out, B, V, use_candidates, stream);
+    launch_regs<DT, 1>(logits, p, k, min_p, out, B, V, ld, use_candidates, stream);
   } else if (vecs <= 2) {
-    launch_regs<DT, 2>(logits, p, k, min_p, out, B, V, use_candidates, stream);
+    launch_regs<DT, 2>(logits, p, k, min_p, out, B, V, ld, use_candidates, stream);
   } else if (vecs <= 4) {
-    launch_regs<DT, 4>(logits, p, k, min_p, out, B, V, use_candidates, stream);
+    launch_regs<DT, 4>(logits, p, k, min_p, out, B, V, ld, use_candidates, stream);
   } else if (vecs <= 8) {
-    launch_regs<DT, 8>(logits, p, k, min_p, out, B, V, use_candidates, stream);
+    launch_regs<DT, 8>(logits, p, k, min_p, out, B, V, ld, use_candidates, stream);
   } else if (vecs <= 12) {
-    launch_regs<DT, 12>(logits, p, k, min_p, out, B, V, use_candidates, stream);
+    launch_regs<DT, 12>(logits, p, k, min_p, out, B, V, ld, use_candidates, stream);
   } else if (vecs <= 16) {
-    launch_regs<DT, 16>(logits, p, k, min_p, out, B, V, use_candidates, stream);
+    launch_regs<DT, 16>(logits, p, k, min_p, out, B, V, ld, use_candidates, stream);
   } else if (vecs <= 19) {
-    launch_regs<DT, 19>(logits, p, k, min_p, out, B, V, use_candidates, stream);
+    launch_regs<DT, 19>(logits, p, k, min_p, out, B, V, ld, use_candidates, stream);
   } else {
-    launch_regs<DT, kMaxVecs>(logits, p, k, min_p, out, B, V, use_candidates, stream);
+    launch_regs<DT, kMaxVecs>(logits, p, k, min_p, out, B, V, ld, use_candidates, stream);
   }
   return hipGetLastError();
 }

@@ -12,26 +12,35 @@ namespace tkp {
 // global memory even when it would fit in registers.
 enum PlanPolicy : int { kPlanAuto = 0, kPlanGeneral = 1, kPlanStream = 2 };
 
+// Elements between the starts of consecutive rows of each [B, V] operand
+// (each >= V; V when the operand is dense).
+struct RowStrides {
+  int64_t x;   // logits
+  int64_t o;   // out
+  int64_t sv;  // sorted_value
+  int64_t si;  // sorted_indices
+};
+
 hipError_t launch_apply_f32(const void* logits, const void* p, const int32_t* k, const void* min_p, void* out,
-                          int64_t B, int64_t V, int policy, hipStream_t stream);
+                          int64_t B, int64_t V, RowStrides ld, int policy, hipStream_t stream);
 hipError_t launch_apply_f16(const void* logits, const void* p, const int32_t* k, const void* min_p, void* out,
-                          int64_t B, int64_t V, int policy, hipStream_t stream);
+                          int64_t B, int64_t V, RowStrides ld, int policy, hipStream_t stream);
 hipError_t launch_apply_bf16(const void* logits, const void* p, const int32_t* k, const void* min_p, void* out,
-                          int64_t B, int64_t V, int policy, hipStream_t stream);
+                          int64_t B, int64_t V, RowStrides ld, int policy, hipStream_t stream);
 
 // p, k and min_p may each be NULL (min_p: no min-p stage).
 inline hipError_t launch_apply(int dtype, const void* logits, const void* p, const int32_t* k, const void* min_p,
-                               void* out, int64_t B, int64_t V, int policy, hipStream_t stream) {
+                               void* out, int64_t B, int64_t V, RowStrides ld, int policy, hipStream_t stream) {
   switch (dtype) {
-    case 0: return launch_apply_f32(logits, p, k, min_p, out, B, V, policy, stream);
-    case 1: return launch_apply_f16(logits, p, k, min_p, out, B, V, policy, stream);
-    case 2: return launch_apply_bf16(logits, p, k, min_p, out, B, V, policy, stream);
+    case 0: return launch_apply_f32(logits, p, k, min_p, out, B, V, ld, policy, stream);
+    case 1: return launch_apply_f16(logits, p, k, min_p, out, B, V, ld, policy, stream);
+    case 2: return launch_apply_bf16(logits, p, k, min_p, out, B, V, ld, policy, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_with_sorted(int dtype, const void* sorted_value, const int32_t* sorted_indices, const void* p,
                               const int32_t* k, const void* min_p, const void* logits, void* out, int64_t B,
-                              int64_t V, hipStream_t stream);
+                              int64_t V, RowStrides ld, hipStream_t stream);
 
 }  // namespace tkp

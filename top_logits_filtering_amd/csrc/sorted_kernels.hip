@@ -266,7 +266,7 @@ __global__ __launch_bounds__(kThreads, 8) void sorted_logits_kernel(
     const typename DT::raw_t* __restrict__ sorted_value, const int32_t* __restrict__ sorted_indices,
     const typename DT::raw_t* __restrict__ p, const int32_t* __restrict__ k,
     const typename DT::raw_t* __restrict__ min_p, const typename DT::raw_t* __restrict__ logits,
-    typename DT::raw_t* __restrict__ out, int V, int S) {
+    typename DT::raw_t* __restrict__ out, int V, int S, RowStrides ld) {
   using raw_t = typename DT::raw_t;
   using Tile = std::conditional_t<kRegs, RegTile<DT, kSortedVecs>, GlobalTile<DT>>;
   constexpr int kCap = RegTile<DT, kSortedVecs>::kCapacity;
@@ -278,8 +278,7 @@ __global__ __launch_bounds__(kThreads, 8) void sorted_logits_kernel(
   const int s = blockIdx.x - b * S;
   const int v0 = s * kCap;
   const int len = min(kCap, V - v0);
-  const size_t row_off = static_cast<size_t>(b) * V;
-  const raw_t* __restrict__ sv = sorted_value + row_off;
+  const raw_t* __restrict__ sv = sorted_value + static_cast<size_t>(b) * static_cast<size_t>(ld.sv);
 
   // p[b] and k[b], the top sorted values the boundary search reads, then the
   // logits slice: vector loads complete in order, so the search waits only
@@ -290,13 +289,13 @@ __global__ __launch_bounds__(kThreads, 8) void sorted_logits_kernel(
   prefetch_top<DT>(sv, V, R, pre);
   __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the slice's
   Tile tile;
-  tile.load(logits + row_off, v0, len);
+  tile.load(logits + static_cast<size_t>(b) * static_cast<size_t>(ld.x), v0, len);
   const RowParams rp = decode_row_params<DT>(rpr, V);
 #pragma unroll
   for (int u = 0; u < kPre; ++u) top[u * kThreads + threadIdx.x] = pre[u];  // entries past R: zero, unused
   lds_barrier();
 
-  raw_t* __restrict__ orow = out + row_off;
+  raw_t* __restrict__ orow = out + static_cast<size_t>(b) * static_cast<size_t>(ld.o);
   if (!row_filters(rp)) {
     tile.store(orow, [](raw_t r, int) { return r; });
     return;
@@ -310,7 +309,7 @@ __global__ __launch_bounds__(kThreads, 8) void sorted_logits_kernel(
   const int words = (len + 31) / 32;
   for (int i = threadIdx.x; i < words; i += kThreads) ties[i] = 0;
   lds_barrier();
-  const int32_t* __restrict__ si = sorted_indices + row_off;
+  const int32_t* __restrict__ si = sorted_indices + static_cast<size_t>(b) * static_cast<size_t>(ld.si);
   for (int j = bd.a + static_cast<int>(threadIdx.x); j < bd.F; j += kThreads) {
     const int v = si[j] - v0;
     if (v >= 0 && v < len) atomicOr(&ties[v >> 5], 1u << (v & 31));
@@ -361,17 +360,17 @@ template <class DT>
 __global__ __launch_bounds__(kThreads) void sorted_scatter_kernel(
     const typename DT::raw_t* __restrict__ sorted_value, const int32_t* __restrict__ sorted_indices,
     const typename DT::raw_t* __restrict__ p, const int32_t* __restrict__ k,
-    const typename DT::raw_t* __restrict__ min_p, typename DT::raw_t* __restrict__ out, int V, int S) {
+    const typename DT::raw_t* __restrict__ min_p, typename DT::raw_t* __restrict__ out, int V, int S,
+    RowStrides ld) {
   using raw_t = typename DT::raw_t;
   constexpr int kPV = DT::kPerVec;
   __shared__ RowSmem sm;
   __shared__ __align__(16) raw_t top[kSortedPrefetch];
   const int b = blockIdx.x / S;
   const int s = blockIdx.x - b * S;
-  const size_t row_off = static_cast<size_t>(b) * V;
-  const auto* __restrict__ sv = sorted_value + row_off;
-  const int32_t* __restrict__ si = sorted_indices + row_off;
-  raw_t* __restrict__ orow = out + row_off;
+  const auto* __restrict__ sv = sorted_value + static_cast<size_t>(b) * static_cast<size_t>(ld.sv);
+  const int32_t* __restrict__ si = sorted_indices + static_cast<size_t>(b) * static_cast<size_t>(ld.si);
+  raw_t* __restrict__ orow = out + static_cast<size_t>(b) * static_cast<size_t>(ld.o);
   const int v0 = s * kScatterSlice;
   const int v1 = min(V, v0 + kScatterSlice);
 
@@ -452,39 +451,41 @@ __global__ __launch_bounds__(kThreads) void sorted_scatter_kernel(
 template <class DT>
 static hipError_t launch_sorted_t(const void* sorted_value, const int32_t* sorted_indices, const void* p,
                                   const int32_t* k, const void* min_p, const void* logits, void* out, int64_t B,
-                                  int64_t V, hipStream_t stream) {
+                                  int64_t V, RowStrides ld, hipStream_t stream) {
   using raw_t = typename DT::raw_t;
   if (logits != nullptr) {
     constexpr int cap = RegTile<DT, kSortedVecs>::kCapacity;
     const int S = static_cast<int>((V + cap - 1) / cap);
+    constexpr int64_t es = static_cast<int64_t>(sizeof(raw_t));
     const bool vec_ok = (V % DT::kPerVec) == 0 && (reinterpret_cast<uintptr_t>(logits) & 15u) == 0 &&
-                        (reinterpret_cast<uintptr_t>(out) & 15u) == 0;
+                        (reinterpret_cast<uintptr_t>(out) & 15u) == 0 && (ld.x * es) % 16 == 0 &&
+                        (ld.o * es) % 16 == 0;
     if (vec_ok)
       hipLaunchKernelGGL((sorted_logits_kernel<DT, true>), dim3(static_cast<unsigned>(B * S)), dim3(kThreads), 0,
                          stream, static_cast<const raw_t*>(sorted_value), sorted_indices,
                          static_cast<const raw_t*>(p), k, static_cast<const raw_t*>(min_p),
-                         static_cast<const raw_t*>(logits), static_cast<raw_t*>(out), static_cast<int>(V), S);
+                         static_cast<const raw_t*>(logits), static_cast<raw_t*>(out), static_cast<int>(V), S, ld);
     else
       hipLaunchKernelGGL((sorted_logits_kernel<DT, false>), dim3(static_cast<unsigned>(B * S)), dim3(kThreads), 0,
                          stream, static_cast<const raw_t*>(sorted_value), sorted_indices,
                          static_cast<const raw_t*>(p), k, static_cast<const raw_t*>(min_p),
-                         static_cast<const raw_t*>(logits), static_cast<raw_t*>(out), static_cast<int>(V), S);
+                         static_cast<const raw_t*>(logits), static_cast<raw_t*>(out), static_cast<int>(V), S, ld);
   } else {
     const int S = static_cast<int>((V + kScatterSlice - 1) / kScatterSlice);
     hipLaunchKernelGGL(sorted_scatter_kernel<DT>, dim3(static_cast<unsigned>(B * S)), dim3(kThreads), 0, stream,
                        static_cast<const raw_t*>(sorted_value), sorted_indices, static_cast<const raw_t*>(p), k,
-                       static_cast<const raw_t*>(min_p), static_cast<raw_t*>(out), static_cast<int>(V), S);
+                       static_cast<const raw_t*>(min_p), static_cast<raw_t*>(out), static_cast<int>(V), S, ld);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_with_sorted(int dtype, const void* sorted_value, const int32_t* sorted_indices, const void* p,
                               const int32_t* k, const void* min_p, const void* logits, void* out, int64_t B,
-                              int64_t V, hipStream_t stream) {
+                              int64_t V, RowStrides ld, hipStream_t stream) {
   switch (dtype) {
-    case 0: return launch_sorted_t<F32T>(sorted_value, sorted_indices, p, k, min_p, logits, out, B, V, stream);
-    case 1: return launch_sorted_t<F16T>(sorted_value, sorted_indices, p, k, min_p, logits, out, B, V, stream);
-    case 2: return launch_sorted_t<BF16T>(sorted_value, sorted_indices, p, k, min_p, logits, out, B, V, stream);
+    case 0: return launch_sorted_t<F32T>(sorted_value, sorted_indices, p, k, min_p, logits, out, B, V, ld, stream);
+    case 1: return launch_sorted_t<F16T>(sorted_value, sorted_indices, p, k, min_p, logits, out, B, V, ld, stream);
+    case 2: return launch_sorted_t<BF16T>(sorted_value, sorted_indices, p, k, min_p, logits, out, B, V, ld, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -8,9 +8,11 @@ from .topktopp_oracle import (  # noqa: F401
     NEG_INF_BITS,
     OracleResult,
     RowTrace,
+    SampleResult,
     apply_top_k_top_p,
     apply_top_k_top_p_with_sorted,
     filter_sorted_row,
     one_minus_p,
+    sample_top_k_top_p,
     widen_to_f64,
 )

@@ -277,3 +277,71 @@ def apply_top_k_top_p_with_sorted(sorted_value_bits: np.ndarray, sorted_indices:
         if keep_traces:
             traces.append(RowTrace(perm, top_k_mask, top_p_mask, probs_sum32, t, min_p_mask, min_p_ratio))
     return OracleResult(out, traces)
+
+
+@dataclass
+class SampleResult:
+    """Selected original index per row, with what the parity rule needs."""
+
+    selected: np.ndarray  # int64 [B]
+    filtered: OracleResult  # the filter's output and traces
+    scores: list  # per row: float64 [V] score by descending rank (0 where the rank is masked), or None
+    raw_scores: list  # per row: the same before the top-p / min-p masks (0 only where top-k masks), or None
+
+
+def sample_top_k_top_p(logits_bits: np.ndarray, dtype: str, p_bits: Optional[np.ndarray] = None,
+                       k: Optional[np.ndarray] = None, min_p_bits: Optional[np.ndarray] = None,
+                       q: Optional[np.ndarray] = None, eps: float = 0.0, t_reading: str = "fp32") -> SampleResult:
+    """Sampling after the filter, TKS "Subsequent processing".
+
+    probs is the filter's result in descending order: the probabilities of
+    step 4 (softmax over the top-k survivors) at the surviving positions, zero
+    elsewhere. Descending order is read as the reverse of the stable ascending
+    sort, so among equal values the higher original index comes first.
+      * None mode (q is None): the index of ArgMax(probs), the first maximum:
+        the maximum value with the highest original index.
+      * QSample (q [B, V] float): probsOpt = probs / (q[b, :qCnt] + eps), where
+        q's entry r pairs with descending rank r, and the index of the first
+        maximum of probsOpt. qCnt counts the positions min-p keeps (every
+        position when min-p is skipped); positions masked by any stage have
+        zero probability and cannot win, so the ranks that matter are those
+        of the survivors, 0 .. n_s - 1.
+    """
+    res = apply_top_k_top_p(logits_bits, dtype, p_bits, k, keep_traces=True, t_reading=t_reading,
+                            min_p_bits=min_p_bits)
+    B, V = np.asarray(logits_bits).shape
+    selected = np.zeros(B, dtype=np.int64)
+    scores = []
+    raw_scores = []
+    for b in range(B):
+        tr = res.traces[b]
+        perm = tr.sorted_indices  # ascending
+        if V == 1:
+            selected[b] = 0
+            scores.append(None)
+            raw_scores.append(None)
+            continue
+        masked = tr.top_k_mask | tr.top_p_mask
+        if tr.min_p_mask is not None:
+            masked = masked | tr.min_p_mask
+        desc = perm[::-1]  # descending rank r -> original index
+        kept_desc = ~masked[::-1]
+        if q is None:
+            selected[b] = int(desc[0])
+            scores.append(None)
+            raw_scores.append(None)
+            continue
+        x = widen_to_f64(np.asarray(logits_bits)[b], dtype)[desc]
+        # step 4 probabilities: softmax over the top-k survivors
+        xk = np.where(tr.top_k_mask[::-1], -np.inf, x)
+        e = np.exp(xk - xk[0])
+        step4 = e / e.sum()
+        probs = np.where(kept_desc, step4, 0.0)
+        qb = np.asarray(q[b], dtype=np.float64)
+        score = probs / (qb + float(eps))
+        score = np.where(kept_desc, score, 0.0)
+        r = int(np.argmax(score))  # first maximum
+        selected[b] = int(desc[r])
+        scores.append(score)
+        raw_scores.append(step4 / (qb + float(eps)))
+    return SampleResult(selected, res, scores, raw_scores)

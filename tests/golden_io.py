@@ -22,7 +22,10 @@ class HandCase:
     p: Optional[np.ndarray]  # bits [B]
     k: Optional[np.ndarray]  # int32 [B]
     expect: np.ndarray  # bits [B, V]
-    min_p: Optional[np.ndarray] = None  # bits [B], cases of min_p_cases.txt only
+    min_p: Optional[np.ndarray] = None  # bits [B], cases of min_p_cases.txt and sample_cases.txt
+    q: Optional[np.ndarray] = None  # float64 [B, V] by descending rank (sample_cases.txt)
+    eps: float = 0.0
+    expect_idx: Optional[np.ndarray] = None  # int64 [B] (sample_cases.txt)
 
 
 def _parse_values(tokens, dtype):
@@ -49,7 +52,8 @@ def load_hand_cases(path: Optional[str] = None) -> List[HandCase]:
                 continue
             head, *rest = line.split()
             if head == "case":
-                cur = dict(name=rest[0], dtype=rest[1], x=[], p=None, k=None, min_p=None, expect=[])
+                cur = dict(name=rest[0], dtype=rest[1], x=[], p=None, k=None, min_p=None, expect=[], q=[],
+                           eps=0.0, expect_idx=None)
                 cases.append(cur)
             elif head == "x":
                 cur["x"].append(_parse_values(rest, cur["dtype"]))
@@ -57,6 +61,13 @@ def load_hand_cases(path: Optional[str] = None) -> List[HandCase]:
                 cur["expect"].append(_parse_values(rest, cur["dtype"]))
             elif head == "p":
                 cur["p"] = None if rest == ["none"] else _parse_values(rest, cur["dtype"])
+            elif head == "q":
+                if rest != ["none"]:
+                    cur["q"].append(np.array([float(v) for v in rest], dtype=np.float64))
+            elif head == "eps":
+                cur["eps"] = float(rest[0])
+            elif head == "expect_idx":
+                cur["expect_idx"] = np.array([int(v) for v in rest], dtype=np.int64)
             elif head == "min_p":
                 cur["min_p"] = None if rest == ["none"] else _parse_values(rest, cur["dtype"])
             elif head == "k":
@@ -64,6 +75,8 @@ def load_hand_cases(path: Optional[str] = None) -> List[HandCase]:
             else:
                 raise ValueError(f"bad golden line: {line}")
     return [
-        HandCase(c["name"], c["dtype"], np.stack(c["x"]), c["p"], c["k"], np.stack(c["expect"]), c["min_p"])
+        HandCase(c["name"], c["dtype"], np.stack(c["x"]), c["p"], c["k"],
+                 np.stack(c["expect"]) if c["expect"] else None, c["min_p"],
+                 np.stack(c["q"]) if c["q"] else None, c["eps"], c["expect_idx"])
         for c in cases
     ]

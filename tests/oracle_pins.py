@@ -352,3 +352,121 @@ MINP_CHECKS = [
     check_minp_random,
     check_minp_bruteforce_tiny,
 ]
+
+
+# ------------------------------------------------------------- sampling ---
+# Sampling after the filter ("Subsequent processing" of the TKS page). Each
+# check takes ``sample_fn(logits_bits, dtype, p_bits, k, min_p_bits, q, eps)
+# -> selected int array``. The facts used: hand-derived cases
+# (tests/golden/sample_cases.txt); brute force with the survivors from
+# counting, the nucleus walk and the logit-space min-p rule, and the ranks
+# from sorting (value, index) pairs in descending order; and the exponential
+# race theorem: with q drawn i.i.d. from Exp(1), argmax_r prob_r / q_r picks
+# each survivor with probability equal to its probability renormalised over
+# the survivors.
+
+
+def check_sample_hand_cases(sample_fn):
+    for case in load_hand_cases("sample_cases.txt"):
+        got = sample_fn(case.x, case.dtype, case.p, case.k, case.min_p, case.q, case.eps)
+        assert np.array_equal(np.asarray(got), case.expect_idx), (case.name, got, case.expect_idx)
+
+
+def _expected_sample(x, kk, t, mp, q_row, eps):
+    """Brute-force pick; (index or None when ambiguous)."""
+    keep_kp, amb1 = expected_keep_bruteforce(x, kk, t)
+    keep_m, amb2 = minp_keep_logit_space(x, mp)
+    if amb1 or amb2:
+        return None
+    keep = keep_kp & keep_m
+    order = sorted(range(len(x)), key=lambda i: (x[i], i), reverse=True)  # descending rank -> index
+    m = x[order[0]]
+    if q_row is None:
+        return order[0]
+    scores = []
+    for r, i in enumerate(order):
+        scores.append(math.exp(x[i] - m) / (q_row[r] + eps) if keep[i] else -1.0)
+    best = max(scores)
+    near = [s for s in scores if s >= 0 and abs(s - best) <= 1e-9 * max(best, 1e-300) and s != best]
+    if near:
+        return None
+    return order[scores.index(best)]
+
+
+def check_sample_bruteforce_tiny(sample_fn, dtypes=("f32", "bf16"), n_rows=4, max_v=7):
+    from workloads.synth import f32_to_bits
+
+    rng = np.random.default_rng(41)
+    seed = 900
+    for dtype in dtypes:
+        for V in range(2, max_v + 1):
+            for kind in ("normal", "ties"):
+                seed += 1
+                xb = random_rows(seed, n_rows, V, dtype, kind=kind, scale=1.5)
+                for b in range(n_rows):
+                    row = xb[b : b + 1]
+                    x = list(_vals(row[0], dtype))
+                    for kk in (None, 1, 2, V - 1):
+                        for pv in (None, 0.5, 0.9):
+                            for mpv in (None, 0.1):
+                                for use_q in (False, True):
+                                    if kk is None and pv is None and mpv is None:
+                                        continue
+                                    q = rng.exponential(1.0, size=(1, V)) if use_q else None
+                                    eps = 1e-6
+                                    p_bits = None if pv is None else f32_to_bits(np.array([pv], np.float32), dtype)
+                                    t = None if pv is None else _t32(p_bits[0], dtype)
+                                    mp_bits = None if mpv is None else f32_to_bits(np.array([mpv], np.float32), dtype)
+                                    mp = None if mpv is None else float(_vals(mp_bits, dtype)[0])
+                                    k_arr = None if kk is None else np.array([kk], np.int32)
+                                    exp = _expected_sample(x, kk, t, mp, None if q is None else q[0], eps)
+                                    if exp is None:
+                                        continue
+                                    got = sample_fn(row, dtype, p_bits, k_arr, mp_bits, q, eps)
+                                    assert int(got[0]) == exp, (dtype, V, kind, b, kk, pv, mpv, use_q, x, got, exp)
+
+
+def check_sample_race_distribution(sample_fn, draws=20000):
+    """With q ~ Exp(1), the pick frequencies match the survivors' renormalised
+    probabilities (each within 4.5 standard errors)."""
+    from workloads.synth import f32_to_bits
+
+    x = np.array([0.0, 1.0, 1.5, -2.0, 2.0, 0.5], np.float32)
+    V = len(x)
+    k = 4  # keeps 2.0, 1.5, 1.0, 0.5
+    xb = np.repeat(f32_to_bits(x, "f32")[None, :], draws, axis=0)
+    rng = np.random.default_rng(12345)
+    q = rng.exponential(1.0, size=(draws, V))
+    got = np.asarray(sample_fn(xb, "f32", None, np.full(draws, k, np.int32), None, q, 0.0))
+    kept = [4, 2, 1, 5]
+    w = np.exp(x[kept].astype(np.float64) - 2.0)
+    w /= w.sum()
+    for i, pi in zip(kept, w):
+        f = np.mean(got == i)
+        se = math.sqrt(pi * (1 - pi) / draws)
+        assert abs(f - pi) <= 4.5 * se, (i, f, pi)
+    assert np.isin(got, kept).all()
+
+
+def check_sample_none_is_top(sample_fn, dtype="bf16", V=300, B=12):
+    """Without q the pick is the maximum value with the highest index."""
+    from workloads.synth import f32_to_bits
+
+    rng = np.random.default_rng(43)
+    for kind in ("ties", "normal", "const"):
+        xb = random_rows(8000 + V, B, V, dtype, kind=kind)
+        k = rng.integers(1, V - 1, size=B, endpoint=True).astype(np.int32)
+        p = f32_to_bits(rng.uniform(0.0, 1.0, size=B).astype(np.float32), dtype)
+        got = np.asarray(sample_fn(xb, dtype, p, k, None, None, 0.0))
+        vals = _vals(xb, dtype).reshape(B, V)
+        for b in range(B):
+            mx = vals[b].max()
+            assert int(got[b]) == int(np.nonzero(vals[b] == mx)[0].max()), (kind, b)
+
+
+SAMPLE_CHECKS = [
+    check_sample_hand_cases,
+    check_sample_none_is_top,
+    check_sample_bruteforce_tiny,
+    check_sample_race_distribution,
+]

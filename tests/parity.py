@@ -105,3 +105,41 @@ def compare(g, x_bits, oracle_result, dtype, tol=BAND_TOL, row_ids=None) -> Pari
         rid = b if row_ids is None else int(row_ids[b])
         rep.merge(compare_row(g[b], x_bits[b], tr, dtype, tol, rid))
     return rep
+
+
+def compare_samples(g_sel, sample_result, tol=BAND_TOL):
+    """Sampling rule: per row the GPU's pick equals the oracle's, unless the
+    row is a near tie: the GPU's pick must then be an oracle survivor or a
+    band position of top-p or min-p (kept or masked on the GPU within the
+    tolerance), and its score (probability over q + eps, at its descending
+    rank) must be within a relative ``tol`` of the best oracle survivor's.
+    Returns (hard mismatches, near-tie mismatches, details)."""
+    hard, soft, details = 0, 0, []
+    for b, (o, tr) in enumerate(zip(sample_result.selected, sample_result.filtered.traces)):
+        g = int(g_sel[b])
+        if g == int(o):
+            continue
+        sc = sample_result.scores[b]
+        raw = sample_result.raw_scores[b]
+        ok = False
+        if sc is not None and 0 <= g < len(tr.sorted_indices):
+            V = len(tr.sorted_indices)
+            pos = int(np.nonzero(tr.sorted_indices == g)[0][0])  # ascending position
+            r = V - 1 - pos
+            masked = tr.top_k_mask | tr.top_p_mask
+            if tr.min_p_mask is not None:
+                masked = masked | tr.min_p_mask
+            band = np.zeros(V, dtype=bool)
+            if tr.probs_sum32 is not None and tr.t is not None:
+                band |= np.abs(tr.probs_sum32.astype(np.float64) - np.float64(tr.t)) <= tol
+            if tr.min_p_ratio is not None:
+                band |= np.abs(tr.min_p_ratio - 1.0) <= tol
+            eligible = (not masked[pos]) or (band[pos] and not tr.top_k_mask[pos])
+            best = float(sc.max())
+            ok = eligible and raw[r] >= best * (1.0 - tol)
+        if ok:
+            soft += 1
+        else:
+            hard += 1
+            details.append(dict(row=b, gpu=g, oracle=int(o)))
+    return hard, soft, details

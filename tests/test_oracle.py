@@ -26,6 +26,17 @@ def test_oracle_min_p_pins(check):
     check(oracle_apply_mp)
 
 
+def oracle_sample(x, dtype, p, k, min_p, q, eps):
+    from oracle import sample_top_k_top_p
+
+    return sample_top_k_top_p(x, dtype, p, k, min_p, q, eps).selected
+
+
+@pytest.mark.parametrize("check", pins.SAMPLE_CHECKS, ids=lambda c: c.__name__)
+def test_oracle_sample_pins(check):
+    check(oracle_sample)
+
+
 def test_min_p_absent_equals_before():
     """Without min-p the oracle's output is unchanged by the min-p code path."""
     xb = random_rows(88, 6, 200, "bf16", kind="ties")

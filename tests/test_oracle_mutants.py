@@ -85,6 +85,47 @@ def test_min_p_mutant_is_caught(name):
     pytest.fail(f"mutant {name} passed every min-p pin")
 
 
+# Slips in the sampling stage; the sampling pins must catch each.
+SAMPLE_MUTANTS = {
+    "sample_q_by_vocabulary_index": ("qb = np.asarray(q[b], dtype=np.float64)",
+                                     "qb = np.asarray(q[b], dtype=np.float64)[desc]"),
+    "sample_last_maximum": ("r = int(np.argmax(score))  # first maximum",
+                            "r = len(score) - 1 - int(np.argmax(score[::-1]))"),
+    "sample_ascending_ranks": ("desc = perm[::-1]  # descending rank r -> original index",
+                               "desc = perm"),
+    "sample_eps_ignored": ("score = probs / (qb + float(eps))", "score = probs / qb"),
+    "sample_none_lowest_index": ("selected[b] = int(desc[0])",
+                                 "selected[b] = int(np.nonzero(x0 == x0.max())[0].min()) "
+                                 "if (x0 := widen_to_f64(np.asarray(logits_bits)[b], dtype)) is not None else 0"),
+}
+
+SAMPLE_CHECKS = [
+    pins.check_sample_hand_cases,
+    pins.check_sample_none_is_top,
+    pins.check_sample_bruteforce_tiny,
+    pins.check_sample_race_distribution,
+]
+
+
+@pytest.mark.parametrize("name", sorted(SAMPLE_MUTANTS))
+def test_sample_mutant_is_caught(name):
+    mod = make_mutant(*SAMPLE_MUTANTS[name])
+
+    def sample_fn(x, dtype, p, k, min_p, q, eps):
+        import warnings
+
+        with warnings.catch_warnings():
+            warnings.simplefilter("ignore")
+            return mod.sample_top_k_top_p(x, dtype, p, k, min_p, q, eps).selected
+
+    for check in SAMPLE_CHECKS:
+        try:
+            check(sample_fn)
+        except (AssertionError, IndexError, ValueError):
+            return
+    pytest.fail(f"mutant {name} passed every sampling pin")
+
+
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_mutant_is_caught(name):
     mod = make_mutant(*MUTANTS[name])

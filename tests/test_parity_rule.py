@@ -59,3 +59,20 @@ def test_foreign_value_is_caught():
     g[1, 5] = np.uint16(0x3F80)  # 1.0, neither the input bits nor -inf (unless equal)
     rep = compare(g, xb, ref, dtype)
     assert xb[1, 5] == 0x3F80 or rep.hard_mismatches >= 1
+
+
+def test_sample_rule():
+    from oracle import sample_top_k_top_p
+    from tests.parity import compare_samples
+
+    dtype = "bf16"
+    xb = random_rows(37, 8, 300, dtype, kind="normal")
+    rng = np.random.default_rng(5)
+    k = rng.integers(5, 200, size=8).astype(np.int32)
+    q = rng.exponential(1.0, size=(8, 300))
+    res = sample_top_k_top_p(xb, dtype, None, k, None, q, 0.0)
+    assert compare_samples(res.selected, res)[0] == 0
+    bad = res.selected.copy()
+    # a masked position (the row's minimum) is never an allowed pick
+    bad[0] = int(res.filtered.traces[0].sorted_indices[0])
+    assert compare_samples(bad, res)[0] == 1

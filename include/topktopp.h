@@ -176,6 +176,37 @@ topktopp_status apply_top_k_top_p_with_sorted_ex(const void* sorted_value, int64
                                                  const int32_t* k, const void* min_p, const void* logits,
                                                  int64_t ld_logits, void* out, int64_t ld_out, void* stream);
 
+/*
+ * sample_top_k_top_p — the filter (top-k, top-p, min-p as in
+ * apply_top_k_top_p_min_p) followed by the sampling stage of TKS
+ * ("Subsequent processing"), one index per row. probs are the filtered
+ * probabilities in descending order; descending order is the reverse of the
+ * stable ascending order, so among equal values the higher original index
+ * comes first.
+ *
+ *   logits, dtype, B, V, p, k, min_p   as for apply_top_k_top_p_min_p, except
+ *            that p, k and min_p may all be NULL (sampling from the whole row).
+ *   q        [B, V] fp32 device buffer, or NULL.
+ *            NULL ("None" mode): selected[b] is the index of the first
+ *            maximum of probs, the maximum value with the highest index.
+ *            Given ("QSample"): selected[b] is the index of the first maximum
+ *            of probs / (q[b][r] + eps), q[b][r] pairing with the survivor of
+ *            descending rank r; only the first n_b entries of a row are read,
+ *            n_b being the row's survivor count.
+ *   eps      added to q; finite and >= 0 (the pages give it no value).
+ *   out      [B, V] device buffer for the filtered logits, or NULL to skip
+ *            them (then the row is only read, not written).
+ *   selected [B] int32 device buffer, written completely. In QSample a row
+ *            whose survivors exceed 5120 positions outside the candidate plan
+ *            (the ranking's shared-memory capacity) gets -1.
+ * Errors as for apply_top_k_top_p_min_p; selected NULL is ERR_NULLPTR, a
+ * negative or non-finite eps ERR_INVALID, and out or selected overlapping
+ * another buffer ERR_INVALID.
+ */
+topktopp_status sample_top_k_top_p(const void* logits, int dtype, int64_t B, int64_t V, const void* p,
+                                   const int32_t* k, const void* min_p, const float* q, float eps, void* out,
+                                   int32_t* selected, void* stream);
+
 /* Text of the most recent error on the calling thread ("" if none); the
  * counterpart of aclGetRecentErrMsg (AKP §8). Valid until the next call on
  * the same thread. */

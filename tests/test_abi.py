@@ -125,3 +125,19 @@ def test_strided_entry_points_check_strides(lib):
     assert "sorted_indices" in tk.last_error()
     # ld_logits is not checked when logits is NULL
     assert g(None, 8, FAKE, 8, 0, 0, 8, None, None, None, None, 0, None, 8, None) == 0
+
+
+def test_sample_entry_point_checks(lib):
+    f = lib.sample_top_k_top_p
+    sel = FAKE + (1 << 36)
+    assert f(None, 0, 2, 8, None, None, None, None, 0.0, None, sel, None) == NULLPTR
+    assert "logits" in tk.last_error()
+    assert f(FAKE, 0, 2, 8, None, None, None, None, 0.0, None, None, None) == NULLPTR
+    assert "selected" in tk.last_error()
+    assert f(FAKE, 4, 2, 8, None, None, None, None, 0.0, None, sel, None) == INVALID
+    assert f(FAKE, 0, 2, 8, None, None, None, None, -1.0, None, sel, None) == INVALID
+    assert "eps" in tk.last_error()
+    assert f(FAKE, 0, 2, 8, None, None, None, None, float("nan"), None, sel, None) == INVALID
+    assert f(FAKE, 0, 2, 8, None, None, None, None, 0.0, None, FAKE + 8, None) == INVALID  # selected inside logits
+    assert "overlap" in tk.last_error()
+    assert f(None, 1, 0, 8, None, None, None, None, 0.0, None, None, None) == 0  # empty

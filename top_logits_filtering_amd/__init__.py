@@ -8,5 +8,6 @@ from .binding import (  # noqa: F401
     apply_top_k_top_p_with_sorted,
     last_error,
     load_library,
+    sample_top_k_top_p,
     set_plan_policy,
 )

@@ -24,6 +24,7 @@ EXPORTED_SYMBOLS = (
     "apply_top_k_top_p_min_p_with_sorted",
     "apply_top_k_top_p_with_sorted",
     "apply_top_k_top_p_with_sorted_ex",
+    "sample_top_k_top_p",
     "topktopp_last_error",
     "topktopp_set_plan_policy",
 )
@@ -63,6 +64,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.apply_top_k_top_p_ex.restype = i32
     lib.apply_top_k_top_p_with_sorted_ex.argtypes = [vp, i64, vp, i64, i32, i64, i64, vp, vp, vp, vp, i64, vp, i64, vp]
     lib.apply_top_k_top_p_with_sorted_ex.restype = i32
+    lib.sample_top_k_top_p.argtypes = [vp, i32, i64, i64, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp]
+    lib.sample_top_k_top_p.restype = i32
     lib.topktopp_last_error.argtypes = []
     lib.topktopp_last_error.restype = ctypes.c_char_p
     lib.topktopp_set_plan_policy.argtypes = [i32]
@@ -195,3 +198,27 @@ def apply_top_k_top_p_with_sorted(sorted_value, sorted_indices, p=None, k=None, 
         )
     _check(status)
     return out
+
+
+def sample_top_k_top_p(logits, p=None, k=None, min_p=None, q=None, eps=0.0, out=None, selected=None, stream=None):
+    """Filter logits [B, V] and pick one index per row (int32 [B], returned).
+
+    q [B, V] float32 by descending survivor rank (QSample), or None (the
+    argmax). out, if given, receives the filtered logits; otherwise the rows
+    are only read."""
+    import torch
+
+    lib = load_library()
+    if logits.dim() != 2:
+        raise ValueError("logits must be 2-D [B, V]")
+    B, V = logits.shape
+    if q is not None and (q.dtype != torch.float32 or tuple(q.shape) != (B, V)):
+        raise ValueError("q must be float32 [B, V]")
+    if selected is None:
+        selected = torch.empty((B,), dtype=torch.int32, device=logits.device)
+    status = lib.sample_top_k_top_p(
+        _ptr(logits), _dtype_code(logits), B, V, _ptr(p), _ptr(k), _ptr(min_p), _ptr(q), float(eps), _ptr(out),
+        _ptr(selected), _stream(stream, logits.device)
+    )
+    _check(status)
+    return selected

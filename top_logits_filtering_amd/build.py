@@ -20,7 +20,7 @@ BUILD_DIR = os.path.join(PKG_DIR, "_build")
 LIB_NAME = "libtopktopp.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
-SOURCES = ["api.cpp", "apply_f32.hip", "apply_f16.hip", "apply_bf16.hip", "sorted_kernels.hip"]
+SOURCES = ["api.cpp", "apply_f32.hip", "apply_f16.hip", "apply_bf16.hip", "sorted_kernels.hip", "util_kernels.hip"]
 
 ARCH = "gfx950"
 COMMON_FLAGS = [

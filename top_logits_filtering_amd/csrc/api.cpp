@@ -163,9 +163,54 @@ topktopp_status with_sorted_impl(const void* sorted_value, int64_t lds, const in
       "filter launch");
 }
 
+topktopp_status sample_impl(const void* logits, int dtype, int64_t B, int64_t V, const void* p, const int32_t* k,
+                            const void* min_p, const float* q, float eps, void* out, int32_t* selected,
+                            void* stream) {
+  g_last_error.clear();
+  if (B >= 0 && V >= 0 && (B == 0 || V == 0)) {  // empty: nothing is read or written, pointers may be NULL
+    if (!valid_dtype(dtype)) return fail(TOPKTOPP_ERR_INVALID, "dtype %d is not one of F32, F16, BF16", dtype);
+    return TOPKTOPP_OK;
+  }
+  if (logits == nullptr) return fail(TOPKTOPP_ERR_NULLPTR, "logits is NULL");
+  if (selected == nullptr) return fail(TOPKTOPP_ERR_NULLPTR, "selected is NULL");
+  if (!valid_dtype(dtype)) return fail(TOPKTOPP_ERR_INVALID, "dtype %d is not one of F32, F16, BF16", dtype);
+  if (topktopp_status s = check_shape(B, V)) return s;
+  if (!(eps >= 0.0f) || eps > 3.0e38f) return fail(TOPKTOPP_ERR_INVALID, "eps must be finite and >= 0");
+  const size_t es = elem_size(dtype);
+  const size_t nx = static_cast<size_t>(B) * static_cast<size_t>(V) * es;
+  const size_t nq = static_cast<size_t>(B) * static_cast<size_t>(V) * 4;
+  const size_t nsel = static_cast<size_t>(B) * 4;
+  if (out != nullptr &&
+      (overlaps(out, nx, logits, nx) || overlaps(out, nx, p, static_cast<size_t>(B) * es) ||
+       overlaps(out, nx, k, static_cast<size_t>(B) * 4) || overlaps(out, nx, min_p, static_cast<size_t>(B) * es) ||
+       overlaps(out, nx, q, nq) || overlaps(out, nx, selected, nsel)))
+    return fail(TOPKTOPP_ERR_INVALID, "out overlaps another buffer");
+  if (overlaps(selected, nsel, logits, nx) || overlaps(selected, nsel, p, static_cast<size_t>(B) * es) ||
+      overlaps(selected, nsel, k, static_cast<size_t>(B) * 4) ||
+      overlaps(selected, nsel, min_p, static_cast<size_t>(B) * es) || overlaps(selected, nsel, q, nq))
+    return fail(TOPKTOPP_ERR_INVALID, "selected overlaps an input buffer");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (V == 1) {  // one element per row: it is kept and it is the pick
+    if (out != nullptr)
+      if (topktopp_status s = check_launch(hipMemcpyAsync(out, logits, nx, hipMemcpyDeviceToDevice, st), "hipMemcpyAsync"))
+        return s;
+    return check_launch(tkp::launch_fill_zero_i32(selected, B, st), "fill launch");
+  }
+  const tkp::RowStrides ld{V, V, 0, 0};
+  return check_launch(tkp::launch_sample(dtype, logits, p, k, min_p, q, V, eps, out, selected, B, V, ld,
+                                         g_policy.load(), st),
+                      "sample launch");
+}
+
 }  // namespace
 
 extern "C" {
+
+topktopp_status sample_top_k_top_p(const void* logits, int dtype, int64_t B, int64_t V, const void* p,
+                                   const int32_t* k, const void* min_p, const float* q, float eps, void* out,
+                                   int32_t* selected, void* stream) {
+  return sample_impl(logits, dtype, B, V, p, k, min_p, q, eps, out, selected, stream);
+}
 
 topktopp_status apply_top_k_top_p(const void* logits, int dtype, int64_t B, int64_t V, const void* p,
                                   const int32_t* k, void* out, void* stream) {

@@ -48,6 +48,7 @@
 #include "launch.h"
 #include "reg_tile.h"
 #include "row_select.h"
+#include "sample.h"
 
 namespace tkp {
 
@@ -89,7 +90,7 @@ struct ApplySmem {
   uint32_t top2[kTop2];
   float run[kThreads];  // per-thread running max and rescaled exp sum (top-p-only rows)
   float acc[kThreads];
-  union {
+  union alignas(16) {
     uint32_t vmw[(kMaxVecs + 1) / 2][kThreads];  // per-vector maxima (16-bit bounds, two per word), steps 1-5
     uint16_t vmh[kStreamVmSlots][kThreads];      // the same for streamed rows, one per layer
     struct {
@@ -144,18 +145,65 @@ __device__ __forceinline__ double block_sum_f64(double v, double* red) {
   return r;
 }
 
-// Multi-pass plan over any tile, then one write of the whole row.
+// Multi-pass plan over any tile, then one write of the whole row (when wr).
 template <class DT, class Tile>
 __device__ __forceinline__ void filter_multipass(const Tile& tile, const RowParams& rp, int V, ApplySmem& S,
-                                                 typename DT::raw_t* __restrict__ orow) {
+                                                 typename DT::raw_t* __restrict__ orow, bool wr, uint32_t& K,
+                                                 uint32_t& I) {
   using raw_t = typename DT::raw_t;
-  uint32_t K, I;
   lds_barrier();  // histograms cleared (sel_reset) before the first pass
   solve_row<DT>(tile, rp, V, S.row, S.sel, K, I);
-  tile.store(orow, [K, I](raw_t r, int idx) {
-    const uint32_t key = DT::key(r);
-    return (key > K || (key == K && static_cast<uint32_t>(idx) >= I)) ? r : DT::kNegInf;
-  });
+  if (wr) {
+    tile.store(orow, [K, I](raw_t r, int idx) {
+      const uint32_t key = DT::key(r);
+      return (key > K || (key == K && static_cast<uint32_t>(idx) >= I)) ? r : DT::kNegInf;
+    });
+  }
+}
+
+// Sampling for a row whose survivors ((key, idx) >= (K, I)) are not in a
+// candidate list: None mode from the row's top position; QSample gathers
+// the survivors into shared memory when they fit (kCandCap), else the row's
+// pick is -1.
+template <class DT, class Tile>
+__device__ __forceinline__ void sample_general(const Tile& tile, uint32_t K, uint32_t I, ApplySmem& S,
+                                               const SampleArgs& sa, int b) {
+  RowSmem& sm = S.row;
+  int32_t pick = -1;
+  if (sa.q == nullptr) {
+    uint32_t Kt, It;
+    top_position<DT>(tile, sm, Kt, It);
+    pick = static_cast<int32_t>(It);
+  } else {
+    float mloc = -INFINITY;
+    uint32_t n = 0;
+    tile.for_each([&](auto raw, int idx) {
+      const uint32_t key = DT::key(raw);
+      mloc = fmaxf(mloc, DT::value(raw));
+      n += (key > K || (key == K && static_cast<uint32_t>(idx) >= I)) ? 1u : 0u;
+    });
+    const float m = block_max_f32(mloc, sm);
+    n = block_sum_u32(n, sm);
+    if (n <= static_cast<uint32_t>(kCandCap)) {
+      if (threadIdx.x == 0) S.ncand = 0;
+      lds_barrier();
+      tile.for_each([&](auto raw, int idx) {
+        const uint32_t key = DT::key(raw);
+        if (key > K || (key == K && static_cast<uint32_t>(idx) >= I)) {
+          const uint32_t at = atomicAdd(&S.ncand, 1u);
+          S.cel.raw[at] = raw;
+          S.cel.idx[at] = static_cast<uint32_t>(idx);
+        }
+      });
+      lds_barrier();
+      CandElems<DT> cs;
+      cs.load(S, static_cast<int>(n));
+      lds_barrier();  // the list below reuses the same shared memory
+      pick = qsample_pick<DT>(cs, K, I, DT::key(DT::raw_of_value(m)), m, sa.q + static_cast<size_t>(b) * sa.ld_q,
+                              sa.eps, S.sel, reinterpret_cast<uint64_t*>(S.cel.raw), sm);
+    }
+  }
+  if (threadIdx.x == 0) sa.sel[b] = pick;
 }
 
 // Selection among at most one wave's worth of candidates (lane j of wave 0
@@ -226,11 +274,14 @@ __device__ __forceinline__ void select_small(const ApplySmem& S, int n, const Ro
 }
 
 // `tile` holds the row (registers or global); `irow` is the same row in
-// global memory, re-read by the multi-pass fallback.
-template <class DT, class Tile>
+// global memory, re-read by the multi-pass fallback. kSample adds the
+// sampling stage (sample.h) and makes the row's output optional (wr).
+template <class DT, bool kSample, class Tile>
 __device__ __forceinline__ void filter_row(const Tile& tile, const typename DT::raw_t* __restrict__ irow, int V,
                                            const RowParams& rp, bool use_candidates, ApplySmem& S,
-                                           typename DT::raw_t* __restrict__ orow) {
+                                           typename DT::raw_t* __restrict__ orow, bool wr_out,
+                                           const SampleArgs& sa, int b) {
+  const bool wr = kSample ? wr_out : true;
   using raw_t = typename DT::raw_t;
   constexpr int kPV = DT::kPerVec;
   RowSmem& sm = S.row;
@@ -240,11 +291,14 @@ __device__ __forceinline__ void filter_row(const Tile& tile, const typename DT::
   sel_reset(ss);
 
   if (!row_filters(rp)) {  // nothing to filter
-    tile.store(orow, [](raw_t r, int) { return r; });
+    if (wr) tile.store(orow, [](raw_t r, int) { return r; });
+    if constexpr (kSample) sample_general<DT>(gt, 0u, 0u, S, sa, b);
     return;
   }
   if (!use_candidates) {
-    filter_multipass<DT>(gt, rp, V, S, orow);
+    uint32_t K, I;
+    filter_multipass<DT>(gt, rp, V, S, orow, wr, K, I);
+    if constexpr (kSample) sample_general<DT>(gt, K, I, S, sa, b);
     return;
   }
 
@@ -261,7 +315,7 @@ __device__ __forceinline__ void filter_row(const Tile& tile, const typename DT::
     // output does not depend on it): stores then drain alongside the loads
     // still in flight, and waits for later loads do not wait for them
     if constexpr (Tile::kRegisters) {
-      if (i < store_upto<Tile::kVecs, 0>()) tile.store_const_slot(orow, i, DT::kNegInf);
+      if (wr && i < store_upto<Tile::kVecs, 0>()) tile.store_const_slot(orow, i, DT::kNegInf);
     }
     float vm = x[0];
 #pragma unroll
@@ -314,7 +368,7 @@ __device__ __forceinline__ void filter_row(const Tile& tile, const typename DT::
   // the survivors are written a register tile's block touches only registers
   // and shared memory, so nothing waits behind these stores while they drain.
   if constexpr (Tile::kRegisters)
-    tile.template store_const_range<store_upto<Tile::kVecs, 0>(), store_upto<Tile::kVecs, 1>()>(orow, DT::kNegInf);
+    if (wr) tile.template store_const_range<store_upto<Tile::kVecs, 0>(), store_upto<Tile::kVecs, 1>()>(orow, DT::kNegInf);
   // 3. row maximum, smallest finite per-thread maximum, Z for top-p-only rows
   const float M1s = DT::value(static_cast<raw_t>(S.top2[2 * threadIdx.x]));
   const float M2s = DT::value(static_cast<raw_t>(S.top2[2 * threadIdx.x + 1]));
@@ -335,7 +389,7 @@ __device__ __forceinline__ void filter_row(const Tile& tile, const typename DT::
   }
 
   if constexpr (Tile::kRegisters)
-    tile.template store_const_range<store_upto<Tile::kVecs, 1>(), store_upto<Tile::kVecs, 2>()>(orow, DT::kNegInf);
+    if (wr) tile.template store_const_range<store_upto<Tile::kVecs, 1>(), store_upto<Tile::kVecs, 2>()>(orow, DT::kNegInf);
   // 4. candidate bound L
   const LdsValues<DT> top2{S.top2, kTop2};
   const bool top_only = rp.pmode == kPTopOnly || (ponly && thr == 0);
@@ -357,7 +411,7 @@ __device__ __forceinline__ void filter_row(const Tile& tile, const typename DT::
   bool fallback = !fast;
 
   if constexpr (Tile::kRegisters)
-    tile.template store_const_range<store_upto<Tile::kVecs, 2>(), store_upto<Tile::kVecs, 3>()>(orow, DT::kNegInf);
+    if (wr) tile.template store_const_range<store_upto<Tile::kVecs, 2>(), store_upto<Tile::kVecs, 3>()>(orow, DT::kNegInf);
   // 5. candidates: every vector whose maximum is >= L is packed into a list
   // in shared memory (placed by wave ballots); then the elements >= L of
   // those vectors are packed into a second list (raw bits and row index),
@@ -524,6 +578,7 @@ __device__ __forceinline__ void filter_row(const Tile& tile, const typename DT::
   // scans the histograms (so that scan runs while they wait for room to
   // store), wave 0 right after.
   auto last_stores = [&]() {
+    if (!wr) return;
     if constexpr (Tile::kRegisters)
       tile.template store_const_range<store_upto<Tile::kVecs, 3>(), store_upto<Tile::kVecs, 4>()>(orow, DT::kNegInf);
     else
@@ -622,27 +677,45 @@ __device__ __forceinline__ void filter_row(const Tile& tile, const typename DT::
   // either above L (then a candidate holds it) or below every candidate.
   if (!fallback && rp.mp_on) combine_min_p(min_p_key<DT>(cs, m, rp.minp, sm), K, I);
 
+  if constexpr (kSample) {
+    if (!fallback) {  // every survivor is a candidate
+      int32_t pick;
+      if (sa.q == nullptr) {
+        uint32_t Kt, It;
+        top_position<DT>(cs, sm, Kt, It);
+        pick = static_cast<int32_t>(It);
+      } else {
+        pick = qsample_pick<DT>(cs, K, I, kmax, m, sa.q + static_cast<size_t>(b) * sa.ld_q, sa.eps, ss,
+                                reinterpret_cast<uint64_t*>(S.cel.raw), sm);
+      }
+      if (threadIdx.x == 0) sa.sel[b] = pick;
+    }
+  }
+
   // 7. survivors over the -inf row, once every -inf store has completed
   if (!fallback) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    cs.for_each([&](auto raw, int idx) {
-      const uint32_t key = DT::key(raw);
-      if (key > K || (key == K && static_cast<uint32_t>(idx) >= I)) orow[idx] = raw;
-    });
+    if (wr) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      cs.for_each([&](auto raw, int idx) {
+        const uint32_t key = DT::key(raw);
+        if (key > K || (key == K && static_cast<uint32_t>(idx) >= I)) orow[idx] = raw;
+      });
+    }
   } else {
-    filter_multipass<DT>(gt, rp, V, S, orow);
+    filter_multipass<DT>(gt, rp, V, S, orow, wr, K, I);
+    if constexpr (kSample) sample_general<DT>(gt, K, I, S, sa, b);
   }
 }
 
-template <class DT, int NVEC>
+template <class DT, int NVEC, bool kSample>
 __global__ __launch_bounds__(kThreads) void apply_regs_kernel(const typename DT::raw_t* __restrict__ logits,
                                                               const typename DT::raw_t* __restrict__ p,
                                                               const int32_t* __restrict__ k,
                                                               const typename DT::raw_t* __restrict__ min_p,
                                                               typename DT::raw_t* __restrict__ out, int V,
-                                                              RowStrides ld, int use_candidates) {
+                                                              RowStrides ld, int use_candidates, SampleArgs sa) {
   __shared__ ApplySmem S;
   const int b = blockIdx.x;
   const size_t offx = static_cast<size_t>(b) * static_cast<size_t>(ld.x);
@@ -652,16 +725,16 @@ __global__ __launch_bounds__(kThreads) void apply_regs_kernel(const typename DT:
   RegTile<DT, NVEC> tile;
   tile.load(logits + offx, 0, V);
   const RowParams rp = decode_row_params<DT>(rpr, V);
-  filter_row<DT>(tile, logits + offx, V, rp, use_candidates != 0, S, out + offo);
+  filter_row<DT, kSample>(tile, logits + offx, V, rp, use_candidates != 0, S, out + offo, out != nullptr, sa, b);
 }
 
-template <class DT>
+template <class DT, bool kSample>
 __global__ __launch_bounds__(kThreads) void apply_stream_kernel(const typename DT::raw_t* __restrict__ logits,
                                                                 const typename DT::raw_t* __restrict__ p,
                                                                 const int32_t* __restrict__ k,
                                                                 const typename DT::raw_t* __restrict__ min_p,
                                                                 typename DT::raw_t* __restrict__ out, int V,
-                                                                RowStrides ld, int use_candidates) {
+                                                                RowStrides ld, int use_candidates, SampleArgs sa) {
   __shared__ ApplySmem S;
   const int b = blockIdx.x;
   const size_t offx = static_cast<size_t>(b) * static_cast<size_t>(ld.x);
@@ -669,22 +742,24 @@ __global__ __launch_bounds__(kThreads) void apply_stream_kernel(const typename D
   const RowParams rp = decode_row_params<DT>(p, k, min_p, b, V);
   GlobalTile<DT> tile;
   tile.load(logits + offx, 0, V);
-  filter_row<DT>(tile, logits + offx, V, rp, use_candidates != 0, S, out + offo);
+  filter_row<DT, kSample>(tile, logits + offx, V, rp, use_candidates != 0, S, out + offo, out != nullptr, sa, b);
 }
 
-template <class DT, int NVEC>
+template <class DT, int NVEC, bool kSample>
 void launch_regs(const void* logits, const void* p, const int32_t* k, const void* min_p, void* out, int64_t B,
-                 int64_t V, RowStrides ld, int use_candidates, hipStream_t stream) {
+                 int64_t V, RowStrides ld, int use_candidates, const SampleArgs& sa, hipStream_t stream) {
   using raw_t = typename DT::raw_t;
-  hipLaunchKernelGGL((apply_regs_kernel<DT, NVEC>), dim3(static_cast<unsigned>(B)), dim3(kThreads), 0, stream,
-                     static_cast<const raw_t*>(logits), static_cast<const raw_t*>(p), k,
+  hipLaunchKernelGGL((apply_regs_kernel<DT, NVEC, kSample>), dim3(static_cast<unsigned>(B)), dim3(kThreads), 0,
+                     stream, static_cast<const raw_t*>(logits), static_cast<const raw_t*>(p), k,
                      static_cast<const raw_t*>(min_p), static_cast<raw_t*>(out), static_cast<int>(V), ld,
-                     use_candidates);
+                     use_candidates, sa);
 }
 
-template <class DT>
+// kSample: the sampling stage (sa), and out may be NULL; otherwise sa is unused.
+template <class DT, bool kSample = false>
 hipError_t launch_apply_t(const void* logits, const void* p, const int32_t* k, const void* min_p, void* out,
-                          int64_t B, int64_t V, RowStrides ld, int policy, hipStream_t stream) {
+                          int64_t B, int64_t V, RowStrides ld, int policy, hipStream_t stream,
+                          const SampleArgs& sa = SampleArgs{nullptr, 0, 0.0f, nullptr}) {
   using raw_t = typename DT::raw_t;
   constexpr int span = kThreads * DT::kPerVec;
   const int64_t vecs = (V + span - 1) / span;
@@ -693,28 +768,28 @@ hipError_t launch_apply_t(const void* logits, const void* p, const int32_t* k, c
   constexpr int64_t es = static_cast<int64_t>(sizeof(raw_t));
   const bool vec_ok = (V % DT::kPerVec) == 0 && (reinterpret_cast<uintptr_t>(logits) & 15u) == 0 &&
                       (reinterpret_cast<uintptr_t>(out) & 15u) == 0 && (ld.x * es) % 16 == 0 &&
-                      (ld.o * es) % 16 == 0;
+                      (out == nullptr || (ld.o * es) % 16 == 0);
   if (policy != kPlanAuto || vecs > kMaxVecs || !vec_ok) {
-    hipLaunchKernelGGL(apply_stream_kernel<DT>, dim3(static_cast<unsigned>(B)), dim3(kThreads), 0, stream,
+    hipLaunchKernelGGL((apply_stream_kernel<DT, kSample>), dim3(static_cast<unsigned>(B)), dim3(kThreads), 0, stream,
                        static_cast<const raw_t*>(logits), static_cast<const raw_t*>(p), k,
                        static_cast<const raw_t*>(min_p), static_cast<raw_t*>(out), static_cast<int>(V), ld,
-                       use_candidates);
+                       use_candidates, sa);
   } else if (vecs <= 1) {
-    launch_regs<DT, 1>(logits, p, k, min_p, out, B, V, ld, use_candidates, stream);
+    launch_regs<DT, 1, kSample>(logits, p, k, min_p, out, B, V, ld, use_candidates, sa, stream);
   } else if (vecs <= 2) {
-    launch_regs<DT, 2>(logits, p, k, min_p, out, B, V, ld, use_candidates, stream);
+    launch_regs<DT, 2, kSample>(logits, p, k, min_p, out, B, V, ld, use_candidates, sa, stream);
   } else if (vecs <= 4) {
-    launch_regs<DT, 4>(logits, p, k, min_p, out, B, V, ld, use_candidates, stream);
+    launch_regs<DT, 4, kSample>(logits, p, k, min_p, out, B, V, ld, use_candidates, sa, stream);
   } else if (vecs <= 8) {
-    launch_regs<DT, 8>(logits, p, k, min_p, out, B, V, ld, use_candidates, stream);
+    launch_regs<DT, 8, kSample>(logits, p, k, min_p, out, B, V, ld, use_candidates, sa, stream);
   } else if (vecs <= 12) {
-    launch_regs<DT, 12>(logits, p, k, min_p, out, B, V, ld, use_candidates, stream);
+    launch_regs<DT, 12, kSample>(logits, p, k, min_p, out, B, V, ld, use_candidates, sa, stream);
   } else if (vecs <= 16) {
-    launch_regs<DT, 16>(logits, p, k, min_p, out, B, V, ld, use_candidates, stream);
+    launch_regs<DT, 16, kSample>(logits, p, k, min_p, out, B, V, ld, use_candidates, sa, stream);
   } else if (vecs <= 19) {
-    launch_regs<DT, 19>(logits, p, k, min_p, out, B, V, ld, use_candidates, stream);
+    launch_regs<DT, 19, kSample>(logits, p, k, min_p, out, B, V, ld, use_candidates, sa, stream);
   } else {
-    launch_regs<DT, kMaxVecs>(logits, p, k, min_p, out, B, V, ld, use_candidates, stream);
+    launch_regs<DT, kMaxVecs, kSample>(logits, p, k, min_p, out, B, V, ld, use_candidates, sa, stream);
   }
   return hipGetLastError();
 }

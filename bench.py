@@ -18,6 +18,10 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1..5] [--
 per-row min_p drawn uniformly from [0.01, 0.2] to the chosen workload.
 --no-logits runs the pre-sorted workload without logits (the output is
 scattered through sorted_indices).
+--sample runs the filter followed by sampling (aclnnTopKTopPSampleV2
+"Subsequent processing", QSample with q drawn i.i.d. from Exp(1), eps 1e-6)
+and writes one index per row instead of the filtered logits; --sample-none
+uses the argmax mode instead.
 """
 
 import argparse
@@ -72,8 +76,8 @@ def kernel_source_digest():
 def measured_traffic(args):
     """Counter-measured HBM bytes per launch, or None when no counters were
     taken for this workload or the kernel sources changed since."""
-    if (args.workload != 3 or args.policy != 0 or args.copy_calibration or args.min_p
-            or not os.path.exists(TRAFFIC_PROFILE)):
+    if (args.workload != 3 or args.policy != 0 or args.copy_calibration or args.min_p or args.no_logits
+            or args.sample or args.sample_none or not os.path.exists(TRAFFIC_PROFILE)):
         return None
     text = open(TRAFFIC_PROFILE).read()
     m_bytes = re.search(r"traffic_bytes_per_launch:\s*(\d+)", text)
@@ -90,6 +94,14 @@ def dev(bits, dtype):
         return None
     iv, fv = TORCH_VIEW[dtype]
     return torch.from_numpy(np.ascontiguousarray(bits).view(getattr(np, iv))).cuda().view(getattr(torch, fv))
+
+
+def sample_bytes(wl, with_min_p, survivors, with_q):
+    """Minimal HBM bytes of one sampling call: read every logit once, read p
+    and k (and min_p), read q at each row's survivor ranks, write one int32
+    per row."""
+    s = wl.elem_bytes
+    return wl.B * (wl.V * s + s + 4 + (s if with_min_p else 0) + 4) + (4 * survivors if with_q else 0)
 
 
 def algorithmic_bytes(wl, with_min_p=False, with_logits=True):
@@ -109,9 +121,10 @@ def algorithmic_bytes(wl, with_min_p=False, with_logits=True):
     return total
 
 
-def cpu_baseline(wl, budget_s=12.0, min_p=None):
-    """The CPU oracle, as it stands, on the first rows of the same workload."""
-    from oracle import apply_top_k_top_p, apply_top_k_top_p_with_sorted
+def cpu_baseline(wl, budget_s=12.0, min_p=None, sample_q=None, sample_none=False):
+    """The CPU oracle, as it stands, on the first rows of the same workload
+    (its sampling stage too when the GPU samples)."""
+    from oracle import apply_top_k_top_p, apply_top_k_top_p_with_sorted, sample_top_k_top_p
 
     done = 0
     t0 = time.perf_counter()
@@ -119,7 +132,10 @@ def cpu_baseline(wl, budget_s=12.0, min_p=None):
         lo = done % wl.B
         r = slice(lo, min(wl.B, lo + 8))
         mp = None if min_p is None else min_p[r]
-        if wl.entry == "apply":
+        if sample_q is not None or sample_none:
+            sample_top_k_top_p(wl.logits[r], wl.dtype, wl.p[r], wl.k[r], mp,
+                               None if sample_q is None else sample_q[r], 1e-6)
+        elif wl.entry == "apply":
             apply_top_k_top_p(wl.logits[r], wl.dtype, wl.p[r], wl.k[r], keep_traces=False, min_p_bits=mp)
         else:
             apply_top_k_top_p_with_sorted(wl.sorted_value[r], wl.sorted_indices[r], wl.dtype, wl.p[r], wl.k[r],
@@ -148,6 +164,8 @@ def main():
     ap.add_argument("--policy", type=int, default=0, help="plan policy: 0 auto, 1 general, 2 registers")
     ap.add_argument("--min-p", action="store_true", help="add a per-row min_p in [0.01, 0.2] (the min-p stage)")
     ap.add_argument("--no-logits", action="store_true", help="pre-sorted workload without logits (scattered output)")
+    ap.add_argument("--sample", action="store_true", help="filter then sample one index per row (QSample)")
+    ap.add_argument("--sample-none", action="store_true", help="filter then take the argmax index per row")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time a plain device-to-device copy of the logits instead of the filter (the reference "
                          "kernel whose HBM counters scale the filter's)")
@@ -173,6 +191,17 @@ def main():
     k = torch.from_numpy(wl.k).cuda()
     mp_bits = min_p_for_workload(args.workload, wl.B, dt) if args.min_p else None
     mp = dev(mp_bits, dt)
+    sampling = args.sample or args.sample_none
+    if sampling and wl.entry != "apply":
+        print("--sample applies to the raw-logits workloads (1-4)", file=sys.stderr)
+        sys.exit(2)
+    q = None
+    q_host = None
+    if args.sample:
+        rng = np.random.default_rng(0x5A4D)
+        q_host = rng.exponential(1.0, size=(wl.B, wl.V)).astype(np.float32)
+        q = torch.from_numpy(q_host).cuda()
+    selected = torch.empty((wl.B,), dtype=torch.int32, device="cuda")
     sets = []
     for _ in range(max(1, args.sets)):
         if wl.entry == "apply":
@@ -187,6 +216,8 @@ def main():
         st = sets[i % len(sets)]
         if args.copy_calibration:
             st[1].copy_(st[0])
+        elif sampling:
+            tk.sample_top_k_top_p(st[0], p, k, mp, q, 1e-6, out=None, selected=selected)
         elif wl.entry == "apply":
             tk.apply_top_k_top_p(st[0], p, k, out=st[1], min_p=mp)
         else:
@@ -213,8 +244,17 @@ def main():
 
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     kernel_ms = ev0.elapsed_time(ev1) / args.steps
-    nbytes = (2 * wl.B * wl.V * wl.elem_bytes if args.copy_calibration
-              else algorithmic_bytes(wl, args.min_p, not args.no_logits))
+    if args.copy_calibration:
+        nbytes = 2 * wl.B * wl.V * wl.elem_bytes
+    elif sampling:
+        survivors = 0
+        if args.sample:  # q is read at each survivor's rank: count the survivors once (outside the timing)
+            ref = torch.empty_like(sets[0][0])
+            tk.apply_top_k_top_p(sets[0][0], p, k, out=ref, min_p=mp)
+            survivors = int((ref.float() != float("-inf")).sum().item())
+        nbytes = sample_bytes(wl, args.min_p, survivors, args.sample)
+    else:
+        nbytes = algorithmic_bytes(wl, args.min_p, not args.no_logits)
     achieved = nbytes / (kernel_ms * 1e-3) / 1e9
     rows_per_s = wl.B / (ms_per_step * 1e-3)
 
@@ -233,7 +273,9 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": WORKLOAD_TEXT[args.workload] + (", min-p U[0.01,0.2] per row" if args.min_p else "")
-                        + (", without logits" if args.no_logits and wl.entry == "with_sorted" else ""),
+                        + (", without logits" if args.no_logits and wl.entry == "with_sorted" else "")
+                        + (", then QSample (q ~ Exp(1), eps 1e-6), one index per row" if args.sample else "")
+                        + (", then argmax, one index per row" if args.sample_none else ""),
             "B": wl.B,
             "V": wl.V,
             "buffer_sets": len(sets),
@@ -256,7 +298,8 @@ def main():
         line["unit"] = "GB/s"
         line["config"]["workload"] = "torch copy_ of " + WORKLOAD_TEXT[args.workload]
     elif not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget, mp_bits)
+        line["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget, mp_bits,
+                                            None if q_host is None else q_host.astype(np.float64), args.sample_none)
     print(json.dumps(line), flush=True)
 
 

@@ -290,6 +290,37 @@ __device__ __forceinline__ void filter_row(const Tile& tile, const typename DT::
   gt.load(irow, 0, V);
   sel_reset(ss);
 
+  if constexpr (kSample) {
+    // argmax without the filtered row: the pick is the row's top position
+    // (the maximum always survives every stage), so no selection is needed
+    if (sa.q == nullptr && !wr) {
+      // per thread the last vector holding its maximum (later vectors hold
+      // higher indices), then the highest lane of it holding the row's
+      float best = -INFINITY;
+      vec_t bq = {0u, 0u, 0u, 0u};
+      int be0 = -1;
+      tile.for_each_vec_values([&](int i, const float (&x)[kPV]) {
+        float vm = x[0];
+#pragma unroll
+        for (int j = 1; j < kPV; ++j) vm = fmaxf(vm, x[j]);
+        if (vm >= best && vm > -INFINITY) {
+          best = vm;
+          bq = tile.vec_at(i, i * Tile::kSpan + static_cast<int>(threadIdx.x) * kPV);
+          be0 = i * Tile::kSpan + static_cast<int>(threadIdx.x) * kPV;
+        }
+      });
+      const float mrow = block_max_f32(best, sm);
+      int idx = -1;
+      if (be0 >= 0 && best == mrow) {
+#pragma unroll
+        for (int j = 0; j < kPV; ++j)
+          if (be0 + j < V && DT::value(lane_of<raw_t>(bq, j)) == mrow) idx = be0 + j;
+      }
+      idx = static_cast<int>(block_max_u32(static_cast<uint32_t>(idx + 1), sm)) - 1;
+      if (threadIdx.x == 0) sa.sel[b] = idx < 0 ? 0 : idx;
+      return;
+    }
+  }
   if (!row_filters(rp)) {  // nothing to filter
     if (wr) tile.store(orow, [](raw_t r, int) { return r; });
     if constexpr (kSample) sample_general<DT>(gt, 0u, 0u, S, sa, b);

@@ -207,6 +207,31 @@ topktopp_status sample_top_k_top_p(const void* logits, int dtype, int64_t B, int
                                    const int32_t* k, const void* min_p, const float* q, float eps, void* out,
                                    int32_t* selected, void* stream);
 
+/*
+ * top_k_top_p_sorted_survivors — the filter (as apply_top_k_top_p_min_p)
+ * returning the survivors themselves, in descending order, instead of the
+ * filtered row: the intermediate output of TKS (logitsSortMasked and
+ * logitsIdx, "Intermediate result output"), cut to the survivors. For row b
+ * and descending rank r < min(n_b, cap), with n_b the row's survivor count:
+ *   probs[b][r]    the survivor's probability of step 4 (the softmax over the
+ *                  top-k survivors, fp32), or skipped when probs is NULL;
+ *   indices[b][r]  its original index (int32);
+ * ranks n_b .. cap-1 hold probability 0 and index -1; counts[b] = n_b (which
+ * may exceed cap). Descending order is the reverse of the stable ascending
+ * order (equal values: higher index first). p, k and min_p may each be NULL.
+ *   cap     entries per output row, 1 <= cap <= 2^20 (else ERR_INVALID).
+ *   probs   [B, cap] fp32 device buffer, or NULL.
+ *   indices [B, cap] int32 device buffer.
+ *   counts  [B] int32 device buffer.
+ * Rows with more than 5120 survivors outside the candidate plan (the
+ * ranking's shared-memory capacity) report counts[b] and no entries.
+ * Errors as for apply_top_k_top_p_min_p; outputs may not overlap inputs or
+ * each other (ERR_INVALID).
+ */
+topktopp_status top_k_top_p_sorted_survivors(const void* logits, int dtype, int64_t B, int64_t V, const void* p,
+                                             const int32_t* k, const void* min_p, int64_t cap, float* probs,
+                                             int32_t* indices, int32_t* counts, void* stream);
+
 /* Text of the most recent error on the calling thread ("" if none); the
  * counterpart of aclGetRecentErrMsg (AKP §8). Valid until the next call on
  * the same thread. */

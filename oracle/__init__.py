@@ -9,10 +9,12 @@ from .topktopp_oracle import (  # noqa: F401
     OracleResult,
     RowTrace,
     SampleResult,
+    SurvivorsResult,
     apply_top_k_top_p,
     apply_top_k_top_p_with_sorted,
     filter_sorted_row,
     one_minus_p,
     sample_top_k_top_p,
+    sorted_survivors,
     widen_to_f64,
 )

@@ -345,3 +345,46 @@ def sample_top_k_top_p(logits_bits: np.ndarray, dtype: str, p_bits: Optional[np.
         scores.append(score)
         raw_scores.append(step4 / (qb + float(eps)))
     return SampleResult(selected, res, scores, raw_scores)
+
+
+@dataclass
+class SurvivorsResult:
+    """The survivors of each row in descending order (TKS intermediate output)."""
+
+    probs: np.ndarray  # float64 [B, cap]: step-4 probabilities, 0 after the survivors
+    indices: np.ndarray  # int64 [B, cap]: original indices, -1 after the survivors
+    counts: np.ndarray  # int64 [B]
+    filtered: OracleResult
+
+
+def sorted_survivors(logits_bits: np.ndarray, dtype: str, p_bits: Optional[np.ndarray] = None,
+                     k: Optional[np.ndarray] = None, min_p_bits: Optional[np.ndarray] = None, cap: int = 1,
+                     t_reading: str = "fp32") -> SurvivorsResult:
+    """TKS "Intermediate result output": logitsSortMasked and logitsIdx, the
+    filtered probabilities in descending order with their original indices,
+    cut to the survivors (the masked tail, zeros in TKS, is not listed).
+    The probabilities are those of step 4: the softmax over the top-k
+    survivors. Descending order is the reverse of the stable ascending sort."""
+    res = apply_top_k_top_p(logits_bits, dtype, p_bits, k, keep_traces=True, t_reading=t_reading,
+                            min_p_bits=min_p_bits)
+    B, V = np.asarray(logits_bits).shape
+    probs = np.zeros((B, cap), dtype=np.float64)
+    indices = np.full((B, cap), -1, dtype=np.int64)
+    counts = np.zeros(B, dtype=np.int64)
+    for b in range(B):
+        tr = res.traces[b]
+        masked = tr.top_k_mask | tr.top_p_mask
+        if tr.min_p_mask is not None:
+            masked = masked | tr.min_p_mask
+        desc = tr.sorted_indices[::-1]
+        kept_desc = ~masked[::-1]
+        n = int(kept_desc.sum())  # a prefix of the descending order
+        counts[b] = n
+        x = widen_to_f64(np.asarray(logits_bits)[b], dtype)[desc]
+        xk = np.where(tr.top_k_mask[::-1], -np.inf, x)
+        e = np.exp(xk - xk[0])
+        step4 = e / e.sum()
+        m = min(n, cap)
+        probs[b, :m] = step4[:m]
+        indices[b, :m] = desc[:m]
+    return SurvivorsResult(probs, indices, counts, res)

@@ -25,7 +25,10 @@ class HandCase:
     min_p: Optional[np.ndarray] = None  # bits [B], cases of min_p_cases.txt and sample_cases.txt
     q: Optional[np.ndarray] = None  # float64 [B, V] by descending rank (sample_cases.txt)
     eps: float = 0.0
-    expect_idx: Optional[np.ndarray] = None  # int64 [B] (sample_cases.txt)
+    expect_idx: Optional[np.ndarray] = None  # int64 [B] (sample_cases.txt) or [B, cap] (survivor_cases.txt)
+    cap: int = 0
+    expect_probs: Optional[np.ndarray] = None  # float64 [B, cap] (survivor_cases.txt)
+    expect_count: Optional[np.ndarray] = None  # int64 [B] (survivor_cases.txt)
 
 
 def _parse_values(tokens, dtype):
@@ -53,7 +56,7 @@ def load_hand_cases(path: Optional[str] = None) -> List[HandCase]:
             head, *rest = line.split()
             if head == "case":
                 cur = dict(name=rest[0], dtype=rest[1], x=[], p=None, k=None, min_p=None, expect=[], q=[],
-                           eps=0.0, expect_idx=None)
+                           eps=0.0, expect_idx=None, cap=0, idx_rows=[], prob_rows=[], counts=[])
                 cases.append(cur)
             elif head == "x":
                 cur["x"].append(_parse_values(rest, cur["dtype"]))
@@ -68,6 +71,13 @@ def load_hand_cases(path: Optional[str] = None) -> List[HandCase]:
                 cur["eps"] = float(rest[0])
             elif head == "expect_idx":
                 cur["expect_idx"] = np.array([int(v) for v in rest], dtype=np.int64)
+                cur["idx_rows"].append(cur["expect_idx"])
+            elif head == "cap":
+                cur["cap"] = int(rest[0])
+            elif head == "expect_probs":
+                cur["prob_rows"].append(np.array([float(v) for v in rest], dtype=np.float64))
+            elif head == "expect_count":
+                cur["counts"].append(int(rest[0]))
             elif head == "min_p":
                 cur["min_p"] = None if rest == ["none"] else _parse_values(rest, cur["dtype"])
             elif head == "k":
@@ -77,6 +87,9 @@ def load_hand_cases(path: Optional[str] = None) -> List[HandCase]:
     return [
         HandCase(c["name"], c["dtype"], np.stack(c["x"]), c["p"], c["k"],
                  np.stack(c["expect"]) if c["expect"] else None, c["min_p"],
-                 np.stack(c["q"]) if c["q"] else None, c["eps"], c["expect_idx"])
+                 np.stack(c["q"]) if c["q"] else None, c["eps"],
+                 np.stack(c["idx_rows"]) if c["cap"] else c["expect_idx"], c["cap"],
+                 np.stack(c["prob_rows"]) if c["prob_rows"] else None,
+                 np.array(c["counts"], dtype=np.int64) if c["counts"] else None)
         for c in cases
     ]

@@ -470,3 +470,79 @@ SAMPLE_CHECKS = [
     check_sample_bruteforce_tiny,
     check_sample_race_distribution,
 ]
+
+
+# ----------------------------------------------------- sorted survivors ---
+# Each check takes ``surv_fn(logits_bits, dtype, p_bits, k, min_p_bits, cap)
+# -> (probs [B, cap], indices [B, cap], counts [B])``. The facts used:
+# hand-derived cases (tests/golden/survivor_cases.txt); the brute-force
+# survivor sets (counting, the nucleus walk, the logit-space min-p rule)
+# ordered by sorting (value, index) pairs in descending order; and the
+# closed form that, without top-p and min-p, the listed probabilities are a
+# softmax over exactly the listed values (they sum to 1 and their ratios are
+# exp of the value differences).
+
+
+def check_survivor_hand_cases(surv_fn):
+    for case in load_hand_cases("survivor_cases.txt"):
+        probs, idx, cnt = surv_fn(case.x, case.dtype, case.p, case.k, case.min_p, case.cap)
+        assert np.array_equal(np.asarray(idx), case.expect_idx), (case.name, idx)
+        assert np.allclose(np.asarray(probs), case.expect_probs, atol=6e-5), (case.name, probs)
+        assert np.array_equal(np.asarray(cnt), case.expect_count), (case.name, cnt)
+
+
+def check_survivor_bruteforce_tiny(surv_fn, dtypes=("f32", "bf16"), n_rows=4, max_v=7):
+    from workloads.synth import f32_to_bits
+
+    seed = 1400
+    for dtype in dtypes:
+        for V in range(2, max_v + 1):
+            for kind in ("normal", "ties", "zeros"):
+                seed += 1
+                xb = random_rows(seed, n_rows, V, dtype, kind=kind, scale=1.5)
+                for b in range(n_rows):
+                    row = xb[b : b + 1]
+                    x = list(_vals(row[0], dtype))
+                    for kk in (None, 1, 2, V - 1):
+                        for pv in (None, 0.5, 0.9):
+                            for mpv in (None, 0.2):
+                                if kk is None and pv is None and mpv is None:
+                                    continue
+                                p_bits = None if pv is None else f32_to_bits(np.array([pv], np.float32), dtype)
+                                t = None if pv is None else _t32(p_bits[0], dtype)
+                                mp_bits = None if mpv is None else f32_to_bits(np.array([mpv], np.float32), dtype)
+                                mp = None if mpv is None else float(_vals(mp_bits, dtype)[0])
+                                keep_kp, amb1 = expected_keep_bruteforce(x, kk, t)
+                                keep_m, amb2 = minp_keep_logit_space(x, mp)
+                                if amb1 or amb2:
+                                    continue
+                                keep = keep_kp & keep_m
+                                order = [i for i in sorted(range(V), key=lambda i: (x[i], i), reverse=True) if keep[i]]
+                                cap = V + 1
+                                _, idx, cnt = surv_fn(row, dtype, p_bits, None if kk is None else np.array([kk], np.int32),
+                                                      mp_bits, cap)
+                                exp = order + [-1] * (cap - len(order))
+                                assert list(np.asarray(idx)[0]) == exp, (dtype, V, kind, b, kk, pv, mpv, x, idx)
+                                assert int(np.asarray(cnt)[0]) == len(order)
+
+
+def check_survivor_softmax_closed_form(surv_fn, dtype="f32", V=200, B=10):
+    rng = np.random.default_rng(47)
+    xb = random_rows(9100, B, V, dtype, kind="normal")
+    k = rng.integers(1, V - 1, size=B, endpoint=True).astype(np.int32)
+    probs, idx, cnt = (np.asarray(a) for a in surv_fn(xb, dtype, None, k, None, V))
+    vals = _vals(xb, dtype).reshape(B, V)
+    for b in range(B):
+        n = int(cnt[b])
+        assert abs(probs[b, :n].sum() - 1.0) <= 1e-9, b
+        v = vals[b, idx[b, :n]]
+        ratio = probs[b, :n] / probs[b, 0]
+        assert np.allclose(ratio, np.exp(v - v[0]), rtol=1e-9), b
+        assert np.all(np.diff(v) <= 0), b
+
+
+SURVIVOR_CHECKS = [
+    check_survivor_hand_cases,
+    check_survivor_softmax_closed_form,
+    check_survivor_bruteforce_tiny,
+]

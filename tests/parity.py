@@ -162,3 +162,46 @@ def compare_samples(g_sel, sample_result, tol=BAND_TOL):
             hard += 1
             details.append(dict(row=b, gpu=g, oracle=int(o)))
     return hard, soft, details
+
+
+def compare_survivors(g_probs, g_idx, g_cnt, surv_result, tol=BAND_TOL):
+    """Sorted-survivors rule, per row:
+      * the GPU's count equals the oracle's, or differs only by band positions
+        of top-p / min-p (which sit at the low end of the order);
+      * ranks below both counts (and the capacity) hold the same original
+        index, and probabilities within a relative ``tol`` (plus 1e-30);
+      * ranks past the GPU's count hold -1 and 0;
+      * a row with more than RANK_CAPACITY survivors may hold no entries.
+    Returns (hard mismatches, details)."""
+    hard, details = 0, []
+    cap = g_idx.shape[1]
+    for b, tr in enumerate(surv_result.filtered.traces):
+        n_o, n_g = int(surv_result.counts[b]), int(g_cnt[b])
+        masked = tr.top_k_mask | tr.top_p_mask
+        if tr.min_p_mask is not None:
+            masked = masked | tr.min_p_mask
+        V = len(tr.sorted_indices)
+        band = np.zeros(V, dtype=bool)
+        if tr.probs_sum32 is not None and tr.t is not None:
+            band |= np.abs(tr.probs_sum32.astype(np.float64) - np.float64(tr.t)) <= tol
+        if tr.min_p_ratio is not None:
+            band |= np.abs(tr.min_p_ratio - 1.0) <= tol
+        band &= ~tr.top_k_mask
+        nband = int(band.sum())
+        bad = abs(n_o - n_g) > nband
+        listed = min(n_g, cap)
+        if n_g > RANK_CAPACITY and (g_idx[b] == -1).all():
+            listed = 0  # beyond the ranking capacity: the count only
+        else:
+            m = min(n_o, n_g, cap)
+            bad |= not np.array_equal(g_idx[b, :m], surv_result.indices[b, :m])
+            if g_probs is not None:
+                o = surv_result.probs[b, :m]
+                bad |= not np.all(np.abs(g_probs[b, :m] - o) <= tol * o + 1e-30)
+        bad |= not (g_idx[b, listed:] == -1).all()
+        if g_probs is not None:
+            bad |= not (g_probs[b, listed:] == 0).all()
+        if bad:
+            hard += 1
+            details.append(dict(row=b, n_oracle=n_o, n_gpu=n_g, band=nband))
+    return hard, details

@@ -141,3 +141,16 @@ def test_sample_entry_point_checks(lib):
     assert f(FAKE, 0, 2, 8, None, None, None, None, 0.0, None, FAKE + 8, None) == INVALID  # selected inside logits
     assert "overlap" in tk.last_error()
     assert f(None, 1, 0, 8, None, None, None, None, 0.0, None, None, None) == 0  # empty
+
+
+def test_survivors_entry_point_checks(lib):
+    f = lib.top_k_top_p_sorted_survivors
+    o1, o2, o3 = FAKE + (1 << 36), FAKE + (1 << 37), FAKE + (1 << 38)
+    assert f(FAKE, 0, 2, 8, None, None, None, 4, o1, None, o3, None) == NULLPTR
+    assert "indices" in tk.last_error()
+    assert f(FAKE, 0, 2, 8, None, None, None, 4, o1, o2, None, None) == NULLPTR
+    assert f(FAKE, 0, 2, 8, None, None, None, 0, o1, o2, o3, None) == INVALID
+    assert "cap" in tk.last_error()
+    assert f(FAKE, 0, 2, 8, None, None, None, 4, o1, o1 + 8, o3, None) == INVALID  # probs and indices overlap
+    assert f(FAKE, 0, 2, 8, None, None, None, 4, None, FAKE + 4, o3, None) == INVALID  # indices inside logits
+    assert f(None, 1, 0, 8, None, None, None, 4, None, None, None, None) == 0

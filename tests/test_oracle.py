@@ -37,6 +37,18 @@ def test_oracle_sample_pins(check):
     check(oracle_sample)
 
 
+def oracle_survivors(x, dtype, p, k, min_p, cap):
+    from oracle import sorted_survivors
+
+    r = sorted_survivors(x, dtype, p, k, min_p, cap)
+    return r.probs, r.indices, r.counts
+
+
+@pytest.mark.parametrize("check", pins.SURVIVOR_CHECKS, ids=lambda c: c.__name__)
+def test_oracle_survivor_pins(check):
+    check(oracle_survivors)
+
+
 def test_min_p_absent_equals_before():
     """Without min-p the oracle's output is unchanged by the min-p code path."""
     xb = random_rows(88, 6, 200, "bf16", kind="ties")

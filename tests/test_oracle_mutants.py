@@ -126,6 +126,42 @@ def test_sample_mutant_is_caught(name):
     pytest.fail(f"mutant {name} passed every sampling pin")
 
 
+# Slips in the sorted-survivors output; its pins must catch each.
+SURVIVOR_MUTANTS = {
+    "survivors_ascending": ("        desc = tr.sorted_indices[::-1]\n        kept_desc = ~masked[::-1]\n        n = int",
+                            "        desc = tr.sorted_indices\n        kept_desc = ~masked\n        n = int"),
+    "survivors_renormalised_after_top_p": (
+        "        xk = np.where(tr.top_k_mask[::-1], -np.inf, x)\n        e = np.exp(xk - xk[0])\n"
+        "        step4 = e / e.sum()\n        m = min(n, cap)",
+        "        xk = np.where(masked[::-1], -np.inf, x)\n        e = np.exp(xk - xk[0])\n"
+        "        step4 = e / e.sum()\n        m = min(n, cap)"),
+    "survivors_ties_lower_index_first": ("        desc = tr.sorted_indices[::-1]\n        kept_desc = ~masked[::-1]\n        n = int",
+                                         "        desc = np.lexsort((tr.sorted_indices, -widen_to_f64(np.asarray(logits_bits)[b], dtype)[tr.sorted_indices]))\n        desc = tr.sorted_indices[desc]\n        kept_desc = ~masked[::-1]\n        n = int"),
+}
+
+SURVIVOR_CHECKS = [
+    pins.check_survivor_hand_cases,
+    pins.check_survivor_softmax_closed_form,
+    pins.check_survivor_bruteforce_tiny,
+]
+
+
+@pytest.mark.parametrize("name", sorted(SURVIVOR_MUTANTS))
+def test_survivor_mutant_is_caught(name):
+    mod = make_mutant(*SURVIVOR_MUTANTS[name])
+
+    def surv_fn(x, dtype, p, k, min_p, cap):
+        r = mod.sorted_survivors(x, dtype, p, k, min_p, cap)
+        return r.probs, r.indices, r.counts
+
+    for check in SURVIVOR_CHECKS:
+        try:
+            check(surv_fn)
+        except (AssertionError, IndexError, ValueError):
+            return
+    pytest.fail(f"mutant {name} passed every survivor pin")
+
+
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_mutant_is_caught(name):
     mod = make_mutant(*MUTANTS[name])

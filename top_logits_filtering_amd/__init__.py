@@ -10,4 +10,5 @@ from .binding import (  # noqa: F401
     load_library,
     sample_top_k_top_p,
     set_plan_policy,
+    top_k_top_p_sorted_survivors,
 )

@@ -25,6 +25,7 @@ EXPORTED_SYMBOLS = (
     "apply_top_k_top_p_with_sorted",
     "apply_top_k_top_p_with_sorted_ex",
     "sample_top_k_top_p",
+    "top_k_top_p_sorted_survivors",
     "topktopp_last_error",
     "topktopp_set_plan_policy",
 )
@@ -66,6 +67,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.apply_top_k_top_p_with_sorted_ex.restype = i32
     lib.sample_top_k_top_p.argtypes = [vp, i32, i64, i64, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp]
     lib.sample_top_k_top_p.restype = i32
+    lib.top_k_top_p_sorted_survivors.argtypes = [vp, i32, i64, i64, vp, vp, vp, i64, vp, vp, vp, vp]
+    lib.top_k_top_p_sorted_survivors.restype = i32
     lib.topktopp_last_error.argtypes = []
     lib.topktopp_last_error.restype = ctypes.c_char_p
     lib.topktopp_set_plan_policy.argtypes = [i32]
@@ -222,3 +225,25 @@ def sample_top_k_top_p(logits, p=None, k=None, min_p=None, q=None, eps=0.0, out=
     )
     _check(status)
     return selected
+
+
+def top_k_top_p_sorted_survivors(logits, p=None, k=None, min_p=None, cap=1024, with_probs=True, stream=None):
+    """The filter's survivors in descending order: (probs [B, cap] float32 or
+    None, indices [B, cap] int32, counts [B] int32). Ranks past a row's
+    survivors hold probability 0 and index -1."""
+    import torch
+
+    lib = load_library()
+    if logits.dim() != 2:
+        raise ValueError("logits must be 2-D [B, V]")
+    B, V = logits.shape
+    dev = logits.device
+    probs = torch.empty((B, cap), dtype=torch.float32, device=dev) if with_probs else None
+    indices = torch.empty((B, cap), dtype=torch.int32, device=dev)
+    counts = torch.empty((B,), dtype=torch.int32, device=dev)
+    status = lib.top_k_top_p_sorted_survivors(
+        _ptr(logits), _dtype_code(logits), B, V, _ptr(p), _ptr(k), _ptr(min_p), int(cap), _ptr(probs), _ptr(indices),
+        _ptr(counts), _stream(stream, dev)
+    )
+    _check(status)
+    return probs, indices, counts

@@ -197,9 +197,46 @@ topktopp_status sample_impl(const void* logits, int dtype, int64_t B, int64_t V,
     return check_launch(tkp::launch_fill_zero_i32(selected, B, st), "fill launch");
   }
   const tkp::RowStrides ld{V, V, 0, 0};
-  return check_launch(tkp::launch_sample(dtype, logits, p, k, min_p, q, V, eps, out, selected, B, V, ld,
-                                         g_policy.load(), st),
+  const tkp::SampleArgs sa{q, V, eps, selected, nullptr, nullptr, nullptr, 0};
+  return check_launch(tkp::launch_sample(dtype, logits, p, k, min_p, out, B, V, ld, g_policy.load(), st, sa),
                       "sample launch");
+}
+
+topktopp_status survivors_impl(const void* logits, int dtype, int64_t B, int64_t V, const void* p, const int32_t* k,
+                               const void* min_p, int64_t cap, float* probs, int32_t* indices, int32_t* counts,
+                               void* stream) {
+  g_last_error.clear();
+  if (B >= 0 && V >= 0 && (B == 0 || V == 0)) {  // empty: nothing is read or written, pointers may be NULL
+    if (!valid_dtype(dtype)) return fail(TOPKTOPP_ERR_INVALID, "dtype %d is not one of F32, F16, BF16", dtype);
+    return TOPKTOPP_OK;
+  }
+  if (logits == nullptr) return fail(TOPKTOPP_ERR_NULLPTR, "logits is NULL");
+  if (indices == nullptr) return fail(TOPKTOPP_ERR_NULLPTR, "indices is NULL");
+  if (counts == nullptr) return fail(TOPKTOPP_ERR_NULLPTR, "counts is NULL");
+  if (!valid_dtype(dtype)) return fail(TOPKTOPP_ERR_INVALID, "dtype %d is not one of F32, F16, BF16", dtype);
+  if (topktopp_status s = check_shape(B, V)) return s;
+  if (cap < 1 || cap > TOPKTOPP_MAX_V) return fail(TOPKTOPP_ERR_INVALID, "cap=%lld is outside [1, 2^20]", (long long)cap);
+  const size_t es = elem_size(dtype);
+  const size_t nx = static_cast<size_t>(B) * static_cast<size_t>(V) * es;
+  const size_t ncap = static_cast<size_t>(B) * static_cast<size_t>(cap) * 4;
+  const void* inputs[4] = {logits, p, k, min_p};
+  const size_t sizes[4] = {nx, static_cast<size_t>(B) * es, static_cast<size_t>(B) * 4, static_cast<size_t>(B) * es};
+  const void* outs[3] = {probs, indices, counts};
+  const size_t osz[3] = {ncap, ncap, static_cast<size_t>(B) * 4};
+  for (int o = 0; o < 3; ++o) {
+    for (int i = 0; i < 4; ++i)
+      if (overlaps(outs[o], osz[o], inputs[i], sizes[i])) return fail(TOPKTOPP_ERR_INVALID, "an output overlaps an input buffer");
+    for (int o2 = o + 1; o2 < 3; ++o2)
+      if (overlaps(outs[o], osz[o], outs[o2], osz[o2])) return fail(TOPKTOPP_ERR_INVALID, "two outputs overlap");
+  }
+  if (V == 1) return check_launch(tkp::launch_survivors_single(probs, indices, counts, B, cap,
+                                                              static_cast<hipStream_t>(stream)),
+                                  "survivors launch");
+  const tkp::RowStrides ld{V, V, 0, 0};
+  const tkp::SampleArgs sa{nullptr, V, 0.0f, nullptr, probs, indices, counts, cap};
+  return check_launch(tkp::launch_sample(dtype, logits, p, k, min_p, nullptr, B, V, ld, g_policy.load(),
+                                         static_cast<hipStream_t>(stream), sa),
+                      "survivors launch");
 }
 
 }  // namespace
@@ -210,6 +247,12 @@ topktopp_status sample_top_k_top_p(const void* logits, int dtype, int64_t B, int
                                    const int32_t* k, const void* min_p, const float* q, float eps, void* out,
                                    int32_t* selected, void* stream) {
   return sample_impl(logits, dtype, B, V, p, k, min_p, q, eps, out, selected, stream);
+}
+
+topktopp_status top_k_top_p_sorted_survivors(const void* logits, int dtype, int64_t B, int64_t V, const void* p,
+                                             const int32_t* k, const void* min_p, int64_t cap, float* probs,
+                                             int32_t* indices, int32_t* counts, void* stream) {
+  return survivors_impl(logits, dtype, B, V, p, k, min_p, cap, probs, indices, counts, stream);
 }
 
 topktopp_status apply_top_k_top_p(const void* logits, int dtype, int64_t B, int64_t V, const void* p,

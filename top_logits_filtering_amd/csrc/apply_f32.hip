@@ -10,11 +10,9 @@ hipError_t launch_apply_f32(const void* logits, const void* p, const int32_t* k,
   return launch_apply_t<F32T>(logits, p, k, min_p, out, B, V, ld, policy, stream);
 }
 
-hipError_t launch_sample_f32(const void* logits, const void* p, const int32_t* k, const void* min_p, const float* q,
-                          int64_t ld_q, float eps, void* out, int32_t* selected, int64_t B, int64_t V, RowStrides ld,
-                          int policy, hipStream_t stream) {
-  return launch_apply_t<F32T, true>(logits, p, k, min_p, out, B, V, ld, policy, stream,
-                                   SampleArgs{q, ld_q, eps, selected});
+hipError_t launch_sample_f32(const void* logits, const void* p, const int32_t* k, const void* min_p, void* out,
+                          int64_t B, int64_t V, RowStrides ld, int policy, hipStream_t stream, const SampleArgs& sa) {
+  return launch_apply_t<F32T, true>(logits, p, k, min_p, out, B, V, ld, policy, stream, sa);
 }
 
 }  // namespace tkp

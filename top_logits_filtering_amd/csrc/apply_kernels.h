@@ -166,9 +166,48 @@ __device__ __forceinline__ void filter_multipass(const Tile& tile, const RowPara
 // the survivors into shared memory when they fit (kCandCap), else the row's
 // pick is -1.
 template <class DT, class Tile>
-__device__ __forceinline__ void sample_general(const Tile& tile, uint32_t K, uint32_t I, ApplySmem& S,
-                                               const SampleArgs& sa, int b) {
+__device__ __forceinline__ void sample_general(const Tile& tile, uint32_t K, uint32_t I, const RowParams& rp,
+                                               ApplySmem& S, const SampleArgs& sa, int b) {
   RowSmem& sm = S.row;
+  if (wants_survivors(sa)) {
+    float mloc = -INFINITY;
+    uint32_t n = 0;
+    tile.for_each([&](auto raw, int idx) {
+      const uint32_t key = DT::key(raw);
+      mloc = fmaxf(mloc, DT::value(raw));
+      n += (key > K || (key == K && static_cast<uint32_t>(idx) >= I)) ? 1u : 0u;
+    });
+    const float m = block_max_f32(mloc, sm);
+    n = block_sum_u32(n, sm);
+    const uint32_t kmax = DT::key(DT::raw_of_value(m));
+    if (n <= static_cast<uint32_t>(kCandCap)) {
+      const double Z = survivors_z<DT>(tile, tile, rp, 0u, kmax, m, S.sel, sm, S.redd);
+      if (threadIdx.x == 0) S.ncand = 0;
+      lds_barrier();
+      tile.for_each([&](auto raw, int idx) {
+        const uint32_t key = DT::key(raw);
+        if (key > K || (key == K && static_cast<uint32_t>(idx) >= I)) {
+          const uint32_t at = atomicAdd(&S.ncand, 1u);
+          S.cel.raw[at] = raw;
+          S.cel.idx[at] = static_cast<uint32_t>(idx);
+        }
+      });
+      lds_barrier();
+      CandElems<DT> cs;
+      cs.load(S, static_cast<int>(n));
+      lds_barrier();  // the list below reuses the same shared memory
+      emit_survivors<DT>(cs, K, I, kmax, m, Z, sa, b, S.sel, reinterpret_cast<uint64_t*>(S.cel.raw));
+    } else {  // more survivors than the ranking holds: the count only
+      int32_t* irow = sa.indices + static_cast<size_t>(b) * sa.cap;
+      float* prow = sa.probs == nullptr ? nullptr : sa.probs + static_cast<size_t>(b) * sa.cap;
+      for (int64_t r = threadIdx.x; r < sa.cap; r += kThreads) {
+        irow[r] = -1;
+        if (prow != nullptr) prow[r] = 0.0f;
+      }
+      if (threadIdx.x == 0) sa.counts[b] = static_cast<int32_t>(n);
+    }
+    return;
+  }
   int32_t pick = -1;
   if (sa.q == nullptr) {
     uint32_t Kt, It;
@@ -203,7 +242,7 @@ __device__ __forceinline__ void sample_general(const Tile& tile, uint32_t K, uin
                               sa.eps, S.sel, reinterpret_cast<uint64_t*>(S.cel.raw), sm);
     }
   }
-  if (threadIdx.x == 0) sa.sel[b] = pick;
+  if (threadIdx.x == 0 && sa.sel != nullptr) sa.sel[b] = pick;
 }
 
 // Selection among at most one wave's worth of candidates (lane j of wave 0
@@ -293,7 +332,7 @@ __device__ __forceinline__ void filter_row(const Tile& tile, const typename DT::
   if constexpr (kSample) {
     // argmax without the filtered row: the pick is the row's top position
     // (the maximum always survives every stage), so no selection is needed
-    if (sa.q == nullptr && !wr) {
+    if (sa.q == nullptr && !wr && !wants_survivors(sa)) {
       // per thread the last vector holding its maximum (later vectors hold
       // higher indices), then the highest lane of it holding the row's
       float best = -INFINITY;
@@ -317,19 +356,19 @@ __device__ __forceinline__ void filter_row(const Tile& tile, const typename DT::
           if (be0 + j < V && DT::value(lane_of<raw_t>(bq, j)) == mrow) idx = be0 + j;
       }
       idx = static_cast<int>(block_max_u32(static_cast<uint32_t>(idx + 1), sm)) - 1;
-      if (threadIdx.x == 0) sa.sel[b] = idx < 0 ? 0 : idx;
+      if (threadIdx.x == 0 && sa.sel != nullptr) sa.sel[b] = idx < 0 ? 0 : idx;
       return;
     }
   }
   if (!row_filters(rp)) {  // nothing to filter
     if (wr) tile.store(orow, [](raw_t r, int) { return r; });
-    if constexpr (kSample) sample_general<DT>(gt, 0u, 0u, S, sa, b);
+    if constexpr (kSample) sample_general<DT>(gt, 0u, 0u, rp, S, sa, b);
     return;
   }
   if (!use_candidates) {
     uint32_t K, I;
     filter_multipass<DT>(gt, rp, V, S, orow, wr, K, I);
-    if constexpr (kSample) sample_general<DT>(gt, K, I, S, sa, b);
+    if constexpr (kSample) sample_general<DT>(gt, K, I, rp, S, sa, b);
     return;
   }
 
@@ -709,7 +748,10 @@ __device__ __forceinline__ void filter_row(const Tile& tile, const typename DT::
   if (!fallback && rp.mp_on) combine_min_p(min_p_key<DT>(cs, m, rp.minp, sm), K, I);
 
   if constexpr (kSample) {
-    if (!fallback) {  // every survivor is a candidate
+    if (!fallback && wants_survivors(sa)) {  // every survivor is a candidate
+      const double Z = survivors_z<DT>(cs, tile, rp, L, kmax, m, ss, sm, S.redd);
+      emit_survivors<DT>(cs, K, I, kmax, m, Z, sa, b, ss, reinterpret_cast<uint64_t*>(S.cel.raw));
+    } else if (!fallback) {  // every survivor is a candidate
       int32_t pick;
       if (sa.q == nullptr) {
         uint32_t Kt, It;
@@ -719,7 +761,7 @@ __device__ __forceinline__ void filter_row(const Tile& tile, const typename DT::
         pick = qsample_pick<DT>(cs, K, I, kmax, m, sa.q + static_cast<size_t>(b) * sa.ld_q, sa.eps, ss,
                                 reinterpret_cast<uint64_t*>(S.cel.raw), sm);
       }
-      if (threadIdx.x == 0) sa.sel[b] = pick;
+      if (threadIdx.x == 0 && sa.sel != nullptr) sa.sel[b] = pick;
     }
   }
 
@@ -736,7 +778,7 @@ __device__ __forceinline__ void filter_row(const Tile& tile, const typename DT::
     }
   } else {
     filter_multipass<DT>(gt, rp, V, S, orow, wr, K, I);
-    if constexpr (kSample) sample_general<DT>(gt, K, I, S, sa, b);
+    if constexpr (kSample) sample_general<DT>(gt, K, I, rp, S, sa, b);
   }
 }
 
@@ -790,7 +832,7 @@ void launch_regs(const void* logits, const void* p, const int32_t* k, const void
 template <class DT, bool kSample = false>
 hipError_t launch_apply_t(const void* logits, const void* p, const int32_t* k, const void* min_p, void* out,
                           int64_t B, int64_t V, RowStrides ld, int policy, hipStream_t stream,
-                          const SampleArgs& sa = SampleArgs{nullptr, 0, 0.0f, nullptr}) {
+                          const SampleArgs& sa = SampleArgs{nullptr, 0, 0.0f, nullptr, nullptr, nullptr, nullptr, 0}) {
   using raw_t = typename DT::raw_t;
   constexpr int span = kThreads * DT::kPerVec;
   const int64_t vecs = (V + span - 1) / span;

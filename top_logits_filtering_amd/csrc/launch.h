@@ -39,25 +39,38 @@ inline hipError_t launch_apply(int dtype, const void* logits, const void* p, con
   }
 }
 
-// Filter plus sampling (aclnnTopKTopPSampleV2 "Subsequent processing"): q
-// [B, ld_q] fp32 or NULL (None mode), out optional, selected [B] int32.
-hipError_t launch_sample_f32(const void* logits, const void* p, const int32_t* k, const void* min_p, const float* q,
-                             int64_t ld_q, float eps, void* out, int32_t* selected, int64_t B, int64_t V,
-                             RowStrides ld, int policy, hipStream_t stream);
-hipError_t launch_sample_f16(const void* logits, const void* p, const int32_t* k, const void* min_p, const float* q,
-                             int64_t ld_q, float eps, void* out, int32_t* selected, int64_t B, int64_t V,
-                             RowStrides ld, int policy, hipStream_t stream);
-hipError_t launch_sample_bf16(const void* logits, const void* p, const int32_t* k, const void* min_p, const float* q,
-                              int64_t ld_q, float eps, void* out, int32_t* selected, int64_t B, int64_t V,
-                              RowStrides ld, int policy, hipStream_t stream);
+// What follows the filter (aclnnTopKTopPSampleV2 "Subsequent processing"):
+// sampling into sel (q NULL: the argmax; else QSample with eps), or the
+// sorted survivors into probs / indices / counts (indices not NULL).
+struct SampleArgs {
+  const float* q;     // [B, ld_q] fp32, or NULL
+  int64_t ld_q;       // row stride of q in elements
+  float eps;
+  int32_t* sel;       // [B] selected original index (-1: survivors exceed the ranking capacity), or NULL
+  float* probs;       // [B, cap] survivors' probabilities in descending order, or NULL (sorted-survivors output)
+  int32_t* indices;   // [B, cap] their original indices
+  int32_t* counts;    // [B] survivors per row
+  int64_t cap;
+};
+
+// Filter plus the stage above; out (the filtered logits) may be NULL.
+hipError_t launch_sample_f32(const void* logits, const void* p, const int32_t* k, const void* min_p, void* out,
+                             int64_t B, int64_t V, RowStrides ld, int policy, hipStream_t stream,
+                             const SampleArgs& sa);
+hipError_t launch_sample_f16(const void* logits, const void* p, const int32_t* k, const void* min_p, void* out,
+                             int64_t B, int64_t V, RowStrides ld, int policy, hipStream_t stream,
+                             const SampleArgs& sa);
+hipError_t launch_sample_bf16(const void* logits, const void* p, const int32_t* k, const void* min_p, void* out,
+                              int64_t B, int64_t V, RowStrides ld, int policy, hipStream_t stream,
+                              const SampleArgs& sa);
 
 inline hipError_t launch_sample(int dtype, const void* logits, const void* p, const int32_t* k, const void* min_p,
-                                const float* q, int64_t ld_q, float eps, void* out, int32_t* selected, int64_t B,
-                                int64_t V, RowStrides ld, int policy, hipStream_t stream) {
+                                void* out, int64_t B, int64_t V, RowStrides ld, int policy, hipStream_t stream,
+                                const SampleArgs& sa) {
   switch (dtype) {
-    case 0: return launch_sample_f32(logits, p, k, min_p, q, ld_q, eps, out, selected, B, V, ld, policy, stream);
-    case 1: return launch_sample_f16(logits, p, k, min_p, q, ld_q, eps, out, selected, B, V, ld, policy, stream);
-    case 2: return launch_sample_bf16(logits, p, k, min_p, q, ld_q, eps, out, selected, B, V, ld, policy, stream);
+    case 0: return launch_sample_f32(logits, p, k, min_p, out, B, V, ld, policy, stream, sa);
+    case 1: return launch_sample_f16(logits, p, k, min_p, out, B, V, ld, policy, stream, sa);
+    case 2: return launch_sample_bf16(logits, p, k, min_p, out, B, V, ld, policy, stream, sa);
     default: return hipErrorInvalidValue;
   }
 }
@@ -65,6 +78,10 @@ inline hipError_t launch_sample(int dtype, const void* logits, const void* p, co
 // selected[b] = 0 for every row (rows of one element), as a kernel so that a
 // caller may capture the call in a graph.
 hipError_t launch_fill_zero_i32(int32_t* dst, int64_t n, hipStream_t stream);
+
+// Sorted survivors of rows of one element.
+hipError_t launch_survivors_single(float* probs, int32_t* indices, int32_t* counts, int64_t B, int64_t cap,
+                                   hipStream_t stream);
 
 hipError_t launch_with_sorted(int dtype, const void* sorted_value, const int32_t* sorted_indices, const void* p,
                               const int32_t* k, const void* min_p, const void* logits, void* out, int64_t B,

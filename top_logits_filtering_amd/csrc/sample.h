@@ -17,16 +17,13 @@
 // which stays small unless very many survivors share one bin.
 #pragma once
 
+#include "launch.h"
 #include "row_select.h"
 
 namespace tkp {
 
-struct SampleArgs {
-  const float* q;  // [B, ld_q] fp32, or NULL (None mode)
-  int64_t ld_q;    // row stride of q in elements
-  float eps;
-  int32_t* sel;    // [B] selected original index (-1: survivors exceed the ranking capacity)
-};
+
+__device__ __forceinline__ bool wants_survivors(const SampleArgs& sa) { return sa.indices != nullptr; }
 
 __device__ __forceinline__ uint64_t block_max_u64(uint64_t v, RowSmem& sm) {
   v = wave_reduce_u64(v, 0ull, [](uint64_t a, uint64_t b) { return a > b ? a : b; });
@@ -39,15 +36,14 @@ __device__ __forceinline__ uint64_t block_max_u64(uint64_t v, RowSmem& sm) {
   return r;
 }
 
-// The QSample pick among the survivors of `src` ((key, idx) >= (K, I)), all
-// of whose keys lie in [K, kmax]; `list` holds at least as many u64 entries
-// as there are survivors. Returns the winner's original index (uniform).
-// Every thread of the block must call it; the histograms are left zeroed.
-template <class DT, class Src>
-__device__ __forceinline__ int32_t qsample_pick(const Src& src, uint32_t K, uint32_t I, uint32_t kmax, float m,
-                                                const float* __restrict__ qrow, float eps, SelSmem& ss,
-                                                uint64_t* list, RowSmem& sm) {
-  constexpr float kLog2e = 1.4426950408889634f;
+// Ranks of the survivors of `src` ((key, idx) >= (K, I), keys in [K, kmax])
+// in descending (key, index) order: f(raw, idx, rank) for every survivor,
+// once. `list` holds at least as many u64 entries as there are survivors.
+// Returns the survivor count. Every thread of the block must call it; the
+// histograms are left zeroed.
+template <class DT, class Src, class F>
+__device__ __forceinline__ uint32_t for_each_ranked_survivor(const Src& src, uint32_t K, uint32_t I, uint32_t kmax,
+                                                             SelSmem& ss, uint64_t* list, F&& f) {
   const int shift = shift_for_range(kmax - K);
   auto survives = [&](uint32_t key, int idx) { return key > K || (key == K && static_cast<uint32_t>(idx) >= I); };
   // 1. survivors per bin
@@ -61,6 +57,7 @@ __device__ __forceinline__ int32_t qsample_pick(const Src& src, uint32_t K, uint
   const uint32_t c_t = ss.cnt[bin_t];
   const uint32_t incl = block_incl_scan_u32(c_t, ss.wtot32);
   ss.cnt[bin_t] = incl - c_t;
+  if (threadIdx.x == kThreads - 1) ss.bcnt = incl;  // the survivor count
   lds_barrier();
   // 3. survivors placed by bin (order inside a bin is arbitrary); kmx counts the bin's members
   src.for_each([&](auto raw, int idx) {
@@ -72,8 +69,7 @@ __device__ __forceinline__ int32_t qsample_pick(const Src& src, uint32_t K, uint
     }
   });
   lds_barrier();
-  // 4. rank = bin base + members of the bin above this survivor; score; pick
-  uint64_t best = 0;  // (monotone key of the score) << 32 | ~rank: the first maximum wins
+  // 4. rank = bin base + members of the bin above this survivor
   src.for_each([&](auto raw, int idx) {
     const uint32_t key = DT::key(raw);
     if (survives(key, idx)) {
@@ -82,37 +78,93 @@ __device__ __forceinline__ int32_t qsample_pick(const Src& src, uint32_t K, uint
       const uint64_t me = (static_cast<uint64_t>(key) << 32) | static_cast<uint32_t>(idx);
       uint32_t above = 0;
       for (uint32_t j = 0; j < nb; ++j) above += list[lo + j] > me ? 1u : 0u;
-      const uint32_t rank = lo + above;
-      const float e = __builtin_amdgcn_exp2f((DT::value(raw) - m) * kLog2e);
-      const float score = e / (qrow[rank] + eps);
-      const uint64_t packed = (static_cast<uint64_t>(F32T::key(__float_as_uint(score))) << 32) | (~rank);
-      best = packed > best ? packed : best;
+      f(raw, idx, lo + above);
     }
   });
-  best = block_max_u64(best, sm);
-  const uint32_t win_rank = ~static_cast<uint32_t>(best);
-  // the winner's index: the list entry at its rank is not known (order inside
-  // a bin is arbitrary), so the survivor holding that rank publishes it
-  src.for_each([&](auto raw, int idx) {
-    const uint32_t key = DT::key(raw);
-    if (survives(key, idx)) {
-      const uint32_t bin = (key - K) >> shift;
-      const uint32_t lo = ss.cnt[bin], nb = ss.kmx[bin];
-      if (win_rank >= lo && win_rank < lo + nb) {
-        const uint64_t me = (static_cast<uint64_t>(key) << 32) | static_cast<uint32_t>(idx);
-        uint32_t above = 0;
-        for (uint32_t j = 0; j < nb; ++j) above += list[lo + j] > me ? 1u : 0u;
-        if (lo + above == win_rank) ss.run_res = static_cast<uint32_t>(idx);
-      }
-    }
-  });
+  const uint32_t n = ss.bcnt;
   lds_barrier();
-  const int32_t win = static_cast<int32_t>(ss.run_res);
   // leave the histograms zeroed for later selections
   ss.cnt[threadIdx.x] = 0;
   ss.kmx[threadIdx.x] = 0;
   lds_barrier();
-  return win;
+  return n;
+}
+
+// The QSample pick among the survivors of `src`: the first maximum of
+// exp(x - m) / (q[rank] + eps). Returns the winner's original index (uniform).
+template <class DT, class Src>
+__device__ __forceinline__ int32_t qsample_pick(const Src& src, uint32_t K, uint32_t I, uint32_t kmax, float m,
+                                                const float* __restrict__ qrow, float eps, SelSmem& ss,
+                                                uint64_t* list, RowSmem& sm) {
+  constexpr float kLog2e = 1.4426950408889634f;
+  uint64_t best = 0;  // (monotone key of the score) << 32 | ~rank: the first maximum wins
+  uint32_t best_idx = 0;
+  for_each_ranked_survivor<DT>(src, K, I, kmax, ss, list, [&](auto raw, int idx, uint32_t rank) {
+    const float e = __builtin_amdgcn_exp2f((DT::value(raw) - m) * kLog2e);
+    const float score = e / (qrow[rank] + eps);
+    const uint64_t packed = (static_cast<uint64_t>(F32T::key(__float_as_uint(score))) << 32) | (~rank);
+    if (packed > best) {
+      best = packed;
+      best_idx = static_cast<uint32_t>(idx);
+    }
+  });
+  const uint64_t win = block_max_u64(best, sm);
+  if (best == win) ss.run_res = best_idx;  // exactly one survivor holds the winning rank
+  lds_barrier();
+  return static_cast<int32_t>(ss.run_res);
+}
+
+// Z of step 4 for the survivors' probabilities: the sum of exp(x - m) over
+// the top-k survivors (key >= the k-th largest key), or over the whole row
+// without top-k. `cand` holds every element with key >= lo (all top-k
+// survivors when k is on); `row` is the whole row.
+template <class DT, class Cand, class Row>
+__device__ __forceinline__ double survivors_z(const Cand& cand, const Row& row, const RowParams& rp, uint32_t lo,
+                                              uint32_t kmax, float m, SelSmem& ss, RowSmem& sm, double* redd) {
+  constexpr float kLog2e = 1.4426950408889634f;
+  double z = 0.0;
+  if (rp.k_on) {
+    const uint32_t Kk = kth_largest_key(
+        cand, rp.k, lo, kmax, [](auto raw, int) { return DT::key(raw); }, [](auto, int) { return true; }, ss);
+    cand.for_each([&](auto raw, int) {
+      if (DT::key(raw) >= Kk) z += static_cast<double>(__builtin_amdgcn_exp2f((DT::value(raw) - m) * kLog2e));
+    });
+  } else {
+    row.for_each([&](auto raw, int) {
+      z += static_cast<double>(__builtin_amdgcn_exp2f((DT::value(raw) - m) * kLog2e));
+    });
+  }
+  z = wave_sum_f64(z);
+  const int l = threadIdx.x & (kWave - 1);
+  if (l == 0) redd[threadIdx.x / kWave] = z;
+  lds_barrier();
+  const double r = wave_sum_f64(l < kWaves ? redd[l] : 0.0);
+  lds_barrier();
+  (void)sm;
+  return r;
+}
+
+// The sorted-survivors output of one row: probs[r] = exp(x - m) / Z and
+// indices[r] = the original index for descending ranks r < cap, then 0 and
+// -1 up to cap; counts = the survivor count.
+template <class DT, class Src>
+__device__ __forceinline__ void emit_survivors(const Src& src, uint32_t K, uint32_t I, uint32_t kmax, float m,
+                                               double Z, const SampleArgs& sa, int b, SelSmem& ss, uint64_t* list) {
+  constexpr float kLog2e = 1.4426950408889634f;
+  float* __restrict__ prow = sa.probs == nullptr ? nullptr : sa.probs + static_cast<size_t>(b) * sa.cap;
+  int32_t* __restrict__ irow = sa.indices + static_cast<size_t>(b) * sa.cap;
+  const float zinv = static_cast<float>(1.0 / Z);
+  const uint32_t n = for_each_ranked_survivor<DT>(src, K, I, kmax, ss, list, [&](auto raw, int idx, uint32_t rank) {
+    if (rank < sa.cap) {
+      irow[rank] = idx;
+      if (prow != nullptr) prow[rank] = __builtin_amdgcn_exp2f((DT::value(raw) - m) * kLog2e) * zinv;
+    }
+  });
+  for (int64_t r = static_cast<int64_t>(n) + threadIdx.x; r < sa.cap; r += kThreads) {
+    irow[r] = -1;
+    if (prow != nullptr) prow[r] = 0.0f;
+  }
+  if (threadIdx.x == 0) sa.counts[b] = static_cast<int32_t>(n);
 }
 
 }  // namespace tkp

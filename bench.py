@@ -21,7 +21,9 @@ scattered through sorted_indices).
 --sample runs the filter followed by sampling (aclnnTopKTopPSampleV2
 "Subsequent processing", QSample with q drawn i.i.d. from Exp(1), eps 1e-6)
 and writes one index per row instead of the filtered logits; --sample-none
-uses the argmax mode instead.
+uses the argmax mode instead. --survivors returns each row's survivors in
+descending order with their probabilities and original indices (capacity
+1024 per row) instead of the filtered logits.
 """
 
 import argparse
@@ -77,7 +79,7 @@ def measured_traffic(args):
     """Counter-measured HBM bytes per launch, or None when no counters were
     taken for this workload or the kernel sources changed since."""
     if (args.workload != 3 or args.policy != 0 or args.copy_calibration or args.min_p or args.no_logits
-            or args.sample or args.sample_none or not os.path.exists(TRAFFIC_PROFILE)):
+            or args.sample or args.sample_none or args.survivors or not os.path.exists(TRAFFIC_PROFILE)):
         return None
     text = open(TRAFFIC_PROFILE).read()
     m_bytes = re.search(r"traffic_bytes_per_launch:\s*(\d+)", text)
@@ -104,6 +106,14 @@ def sample_bytes(wl, with_min_p, survivors, with_q):
     return wl.B * (wl.V * s + s + 4 + (s if with_min_p else 0) + 4) + (4 * survivors if with_q else 0)
 
 
+def survivor_bytes(wl, with_min_p, cap):
+    """Minimal HBM bytes of one sorted-survivors call: read every logit once,
+    read p and k (and min_p), write cap probabilities and indices and one
+    count per row."""
+    s = wl.elem_bytes
+    return wl.B * (wl.V * s + s + 4 + (s if with_min_p else 0) + 8 * cap + 4)
+
+
 def algorithmic_bytes(wl, with_min_p=False, with_logits=True):
     """Minimal HBM bytes of one call: read every logit once, write every output
     once, read p and k (and min_p); the pre-sorted entry also reads at least
@@ -121,10 +131,11 @@ def algorithmic_bytes(wl, with_min_p=False, with_logits=True):
     return total
 
 
-def cpu_baseline(wl, budget_s=12.0, min_p=None, sample_q=None, sample_none=False):
+def cpu_baseline(wl, budget_s=12.0, min_p=None, sample_q=None, sample_none=False, survivors_cap=0):
     """The CPU oracle, as it stands, on the first rows of the same workload
-    (its sampling stage too when the GPU samples)."""
-    from oracle import apply_top_k_top_p, apply_top_k_top_p_with_sorted, sample_top_k_top_p
+    (its sampling stage or sorted-survivors output too when the GPU computes
+    them)."""
+    from oracle import apply_top_k_top_p, apply_top_k_top_p_with_sorted, sample_top_k_top_p, sorted_survivors
 
     done = 0
     t0 = time.perf_counter()
@@ -132,7 +143,9 @@ def cpu_baseline(wl, budget_s=12.0, min_p=None, sample_q=None, sample_none=False
         lo = done % wl.B
         r = slice(lo, min(wl.B, lo + 8))
         mp = None if min_p is None else min_p[r]
-        if sample_q is not None or sample_none:
+        if survivors_cap:
+            sorted_survivors(wl.logits[r], wl.dtype, wl.p[r], wl.k[r], mp, survivors_cap)
+        elif sample_q is not None or sample_none:
             sample_top_k_top_p(wl.logits[r], wl.dtype, wl.p[r], wl.k[r], mp,
                                None if sample_q is None else sample_q[r], 1e-6)
         elif wl.entry == "apply":
@@ -166,6 +179,8 @@ def main():
     ap.add_argument("--no-logits", action="store_true", help="pre-sorted workload without logits (scattered output)")
     ap.add_argument("--sample", action="store_true", help="filter then sample one index per row (QSample)")
     ap.add_argument("--sample-none", action="store_true", help="filter then take the argmax index per row")
+    ap.add_argument("--survivors", action="store_true",
+                    help="sorted survivors (probabilities, indices, counts; capacity 1024) instead of the filtered row")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time a plain device-to-device copy of the logits instead of the filter (the reference "
                          "kernel whose HBM counters scale the filter's)")
@@ -192,9 +207,15 @@ def main():
     mp_bits = min_p_for_workload(args.workload, wl.B, dt) if args.min_p else None
     mp = dev(mp_bits, dt)
     sampling = args.sample or args.sample_none
-    if sampling and wl.entry != "apply":
-        print("--sample applies to the raw-logits workloads (1-4)", file=sys.stderr)
+    if (sampling or args.survivors) and wl.entry != "apply":
+        print("--sample and --survivors apply to the raw-logits workloads (1-4)", file=sys.stderr)
         sys.exit(2)
+    cap = 1024
+    surv_out = None
+    if args.survivors:
+        surv_out = (torch.empty((wl.B, cap), dtype=torch.float32, device="cuda"),
+                    torch.empty((wl.B, cap), dtype=torch.int32, device="cuda"),
+                    torch.empty((wl.B,), dtype=torch.int32, device="cuda"))
     q = None
     q_host = None
     if args.sample:
@@ -218,6 +239,8 @@ def main():
             st[1].copy_(st[0])
         elif sampling:
             tk.sample_top_k_top_p(st[0], p, k, mp, q, 1e-6, out=None, selected=selected)
+        elif args.survivors:
+            tk.top_k_top_p_sorted_survivors(st[0], p, k, mp, cap=cap, out=surv_out)
         elif wl.entry == "apply":
             tk.apply_top_k_top_p(st[0], p, k, out=st[1], min_p=mp)
         else:
@@ -253,6 +276,8 @@ def main():
             tk.apply_top_k_top_p(sets[0][0], p, k, out=ref, min_p=mp)
             survivors = int((ref.float() != float("-inf")).sum().item())
         nbytes = sample_bytes(wl, args.min_p, survivors, args.sample)
+    elif args.survivors:
+        nbytes = survivor_bytes(wl, args.min_p, cap)
     else:
         nbytes = algorithmic_bytes(wl, args.min_p, not args.no_logits)
     achieved = nbytes / (kernel_ms * 1e-3) / 1e9
@@ -275,7 +300,9 @@ def main():
             "workload": WORKLOAD_TEXT[args.workload] + (", min-p U[0.01,0.2] per row" if args.min_p else "")
                         + (", without logits" if args.no_logits and wl.entry == "with_sorted" else "")
                         + (", then QSample (q ~ Exp(1), eps 1e-6), one index per row" if args.sample else "")
-                        + (", then argmax, one index per row" if args.sample_none else ""),
+                        + (", then argmax, one index per row" if args.sample_none else "")
+                        + (", sorted survivors (probabilities and indices, capacity 1024 per row)"
+                           if args.survivors else ""),
             "B": wl.B,
             "V": wl.V,
             "buffer_sets": len(sets),
@@ -299,7 +326,8 @@ def main():
         line["config"]["workload"] = "torch copy_ of " + WORKLOAD_TEXT[args.workload]
     elif not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget, mp_bits,
-                                            None if q_host is None else q_host.astype(np.float64), args.sample_none)
+                                            None if q_host is None else q_host.astype(np.float64), args.sample_none,
+                                            cap if args.survivors else 0)
     print(json.dumps(line), flush=True)
 
 

@@ -227,10 +227,12 @@ def sample_top_k_top_p(logits, p=None, k=None, min_p=None, q=None, eps=0.0, out=
     return selected
 
 
-def top_k_top_p_sorted_survivors(logits, p=None, k=None, min_p=None, cap=1024, with_probs=True, stream=None):
+def top_k_top_p_sorted_survivors(logits, p=None, k=None, min_p=None, cap=1024, with_probs=True, stream=None,
+                                 out=None):
     """The filter's survivors in descending order: (probs [B, cap] float32 or
     None, indices [B, cap] int32, counts [B] int32). Ranks past a row's
-    survivors hold probability 0 and index -1."""
+    survivors hold probability 0 and index -1. ``out`` may give the three
+    buffers (probs may be None); they are then filled and returned."""
     import torch
 
     lib = load_library()
@@ -238,9 +240,15 @@ def top_k_top_p_sorted_survivors(logits, p=None, k=None, min_p=None, cap=1024, w
         raise ValueError("logits must be 2-D [B, V]")
     B, V = logits.shape
     dev = logits.device
-    probs = torch.empty((B, cap), dtype=torch.float32, device=dev) if with_probs else None
-    indices = torch.empty((B, cap), dtype=torch.int32, device=dev)
-    counts = torch.empty((B,), dtype=torch.int32, device=dev)
+    if out is not None:
+        probs, indices, counts = out
+        if (tuple(indices.shape) != (B, cap) or tuple(counts.shape) != (B,)
+                or (probs is not None and tuple(probs.shape) != (B, cap))):
+            raise ValueError("out buffers must be probs [B, cap], indices [B, cap], counts [B]")
+    else:
+        probs = torch.empty((B, cap), dtype=torch.float32, device=dev) if with_probs else None
+        indices = torch.empty((B, cap), dtype=torch.int32, device=dev)
+        counts = torch.empty((B,), dtype=torch.int32, device=dev)
     status = lib.top_k_top_p_sorted_survivors(
         _ptr(logits), _dtype_code(logits), B, V, _ptr(p), _ptr(k), _ptr(min_p), int(cap), _ptr(probs), _ptr(indices),
         _ptr(counts), _stream(stream, dev)

@@ -247,3 +247,28 @@ def test_with_sorted_workload5_without_logits_sampled():
     _all_rows_properties(got, wl)
     with_logits = gpu_with_sorted(wl.sorted_value, wl.sorted_indices, wl.dtype, wl.p, wl.k, wl.logits)
     assert np.array_equal(got, with_logits)
+
+
+@pytest.mark.parametrize("dtype,V", [("bf16", 262144), ("f32", 262144), ("bf16", 262143)])
+def test_with_sorted_global_search_full_rows(dtype, V):
+    """Pre-sorted rows whose boundary search reads global memory: top-p
+    without k (the segmented two-level scan over the whole row), k beyond
+    the shared-memory copy of the top values, and a length that is not a
+    whole number of 16-byte vectors (one position per group)."""
+    need_gpu()
+    total = ParityReport()
+    seed = 1700 + V % 7
+    for kind in ("normal", "ties"):
+        seed += 1
+        xb = random_rows(seed, 3, V, dtype, kind=kind, scale=3.0)
+        idx, sv = stable_ascending_sort(xb, dtype)
+        for kv, pv in ((None, 0.5), (None, 0.99), (None, 0.02), (7000, 0.9), (200000, 0.999)):
+            k = None if kv is None else np.full(3, kv, np.int32)
+            p = f32_to_bits(np.full(3, pv, np.float32), dtype)
+            ref = oracle_sorted(sv, idx, dtype, p, k, logits_bits=xb)
+            for use_logits in (True, False):
+                got = gpu_with_sorted(sv, idx, dtype, p, k, xb if use_logits else None)
+                rep = compare(got, xb, ref, dtype)
+                assert rep.hard_mismatches == 0, (kind, kv, pv, use_logits, rep.details[:2])
+                total.merge(rep)
+    say(f"with_sorted global search {dtype} V={V}: {total}")

@@ -77,27 +77,95 @@ __device__ __forceinline__ int first_at_or_above(const Src& sv, int hi, uint32_t
   }
 }
 
-// Lowest sorted position F >= start whose mass strictly above is < thr.
-template <class DT, class Src>
-__device__ __forceinline__ int scan_boundary(const Src& sv, int start, int V, float m, uint64_t thr,
-                                             RowSmem& sm) {
-  int hi = V;
-  uint64_t base = 0;
-  for (;;) {
-    const int lo = max(start, hi - kThreads);
-    const int j = hi - 1 - static_cast<int>(threadIdx.x);
-    const bool valid = j >= lo;
-    const uint64_t e = valid ? mass_fx(DT::value(sv.at(j)), m) : 0;
-    uint64_t total;
-    const uint64_t excl = block_exscan_u64(e, sm, total);
-    const int cand = (valid && base + excl < thr) ? static_cast<int>(threadIdx.x) : -1;
-    const int tb = block_max_i32(cand, sm);
-    if (tb < 0) return min(hi, V - 1);  // only after a chunk whose lowest position survived
-    const int jb = hi - 1 - tb;
-    if (jb > lo || lo == start) return jb;
-    base += total;
-    hi = lo;
+// Largest u64 and largest int over the block in one exchange round.
+__device__ __forceinline__ void block_max_u64_i32(uint64_t a, int b, RowSmem& sm, uint64_t& amax, int& bmax) {
+  a = wave_reduce_u64(a, 0ull, [](uint64_t x, uint64_t y) { return x > y ? x : y; });
+  uint32_t bb = wave_max_u32(static_cast<uint32_t>(b + 1));
+  const int l = threadIdx.x & (kWave - 1);
+  if (l == 0) {
+    sm.redu[threadIdx.x / kWave] = a;
+    sm.redw[threadIdx.x / kWave] = bb;
   }
+  lds_barrier();
+  amax = wave_reduce_u64(l < kWaves ? sm.redu[l] : 0ull, 0ull, [](uint64_t x, uint64_t y) { return x > y ? x : y; });
+  bmax = static_cast<int>(wave_max_u32(l < kWaves ? sm.redw[l] : 0u)) - 1;
+  lds_barrier();
+}
+
+// Lowest sorted position F >= start whose mass strictly above is below
+// (1 - t) * Z, with Z the mass of positions [start, V), read from global
+// memory in two levels:
+//   1. each thread sums the mass of one contiguous segment of groups, thread 0
+//      taking the top segment (a group is one 16-byte vector when the row
+//      allows vector loads, else one position);
+//   2. an exclusive scan of the segment sums in thread order gives the mass
+//      above each segment and Z; F lies in the lowest segment whose mass above
+//      is below the threshold (every position under it has at least the
+//      threshold above);
+//   3. a block scan over that segment's positions (at most 1024 for
+//      V <= 2^20) finds F.
+// The masses are integers, so the result does not depend on how they are
+// grouped. Returns V - 1 when the threshold is zero (t >= 1).
+template <class DT>
+__device__ __forceinline__ int topp_boundary_global(const typename DT::raw_t* __restrict__ sv, int start, int V,
+                                                    float m, float t, RowSmem& sm) {
+  using raw_t = typename DT::raw_t;
+  constexpr int kPV = DT::kPerVec;
+  const int tid = static_cast<int>(threadIdx.x);
+  const bool vec = (V % kPV) == 0 && (reinterpret_cast<uintptr_t>(sv) & 15u) == 0;
+  const int G = vec ? kPV : 1;              // positions per group
+  const int gtop = (V - 1) / G;             // group of the top position
+  const int glo = start / G;                // group of `start`
+  const int L = (gtop - glo + kThreads) / kThreads;  // groups per segment
+  const int g0 = gtop - tid * L;            // this thread: groups g0 down to g0 - L + 1, not below glo
+  uint64_t s = 0;
+  if (vec) {
+    const __amdgpu_buffer_rsrc_t rs = row_rsrc(sv, V);
+    constexpr int kBatch = 4;  // loads in flight per thread
+    for (int u0 = 0; u0 < L; u0 += kBatch) {
+      vec_t q[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int g = g0 - u0 - u;
+        q[u] = (u0 + u < L && g >= glo)
+                   ? __builtin_amdgcn_raw_buffer_load_b128(rs, g * 16, 0, 0)
+                   : vec_t{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int g = g0 - u0 - u;
+        if (u0 + u < L && g >= glo) {
+#pragma unroll
+          for (int j = 0; j < kPV; ++j)
+            if (g * kPV + j >= start) s += mass_fx(DT::value(lane_of<raw_t>(q[u], j)), m);
+        }
+      }
+    }
+  } else {
+#pragma unroll 8
+    for (int u = 0; u < L; ++u) {
+      const int j = g0 - u;  // one position per group
+      if (j >= glo) s += mass_fx(DT::value(sv[j]), m);
+    }
+  }
+  uint64_t Z;
+  const uint64_t above = block_exscan_u64(s, sm, Z);
+  const uint64_t thr = topp_threshold(t, Z);
+  if (thr == 0) return V - 1;
+  // the mass above a segment grows with the thread index: the largest mass
+  // below the threshold is the one of the segment holding F
+  const bool hit = g0 >= glo && above < thr;
+  uint64_t base;
+  int ts;
+  block_max_u64_i32(hit ? above : 0ull, hit ? tid : -1, sm, base, ts);
+  const int ptop = min(V - 1, (gtop - ts * L) * G + G - 1);
+  const int pbot = max(start, (gtop - ts * L - L + 1) * G);
+  const int j = ptop - tid;
+  const bool valid = j >= pbot;
+  const uint64_t e = valid ? mass_fx(DT::value(sv[j]), m) : 0ull;
+  uint64_t total;
+  const uint64_t excl = block_exscan_u64(e, sm, total);
+  return ptop - block_max_i32(valid && base + excl < thr ? tid : -1, sm);
 }
 
 // Lowest sorted position j >= lo that survives min-p, given that the top
@@ -139,12 +207,7 @@ __device__ __forceinline__ SortedBoundary sorted_boundary(const Src& sv, const R
   if (rp.pmode == kPTopOnly) {
     F = V - 1;
   } else if (rp.pmode == kPBoundary) {
-    const float m = DT::value(sv.at(V - 1));
-    uint64_t z = 0;
-    for (int j = start + static_cast<int>(threadIdx.x); j < V; j += kThreads) z += mass_fx(DT::value(sv.at(j)), m);
-    const uint64_t Z = block_sum_u64(z, sm);
-    const uint64_t thr = topp_threshold(rp.t, Z);
-    F = (thr == 0) ? V - 1 : scan_boundary<DT>(sv, start, V, m, thr, sm);
+    F = topp_boundary_global<DT>(sv.g, start, V, DT::value(sv.at(V - 1)), rp.t, sm);
   }
   // min-p keeps a suffix of the sorted positions too: the tighter one wins
   if (rp.mp_on) F = first_min_p<DT>(sv, F, V, rp.minp, sm);

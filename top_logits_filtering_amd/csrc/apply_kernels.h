@@ -248,13 +248,15 @@ __device__ __forceinline__ void sample_general(const Tile& tile, uint32_t K, uin
 // Selection among at most one wave's worth of candidates (lane j of wave 0
 // holds candidate j): each candidate's rank in the descending (key, index)
 // order, which is the stable ascending order read from the top, and the
-// fixed-point mass strictly above it come from one sweep over the others;
-// the survivors are then a prefix of that order and (K, I) is the key and
-// index of the last one. Decisions match the histogram selection exactly:
-// the same masses and sums, in the same integer arithmetic. Wave 0 only;
-// the caller publishes the result.
+// fixed-point mass strictly above it come from one sweep over the others,
+// read as broadcasts from a table in shared memory (8 entries per round, so
+// their reads overlap); the survivors are then a prefix of that order and
+// (K, I) is the key and index of the last one. Decisions match the histogram
+// selection exactly: the same masses and sums, in the same integer
+// arithmetic. Wave 0 only; `tab` (64 entries) is free shared memory; the
+// caller publishes the result.
 template <class DT>
-__device__ __forceinline__ void select_small(const ApplySmem& S, int n, const RowParams& rp, float m,
+__device__ __forceinline__ void select_small(const ApplySmem& S, vec_t* tab, int n, const RowParams& rp, float m,
                                              uint64_t thr_ponly, bool top_only, uint32_t& K, uint32_t& I,
                                              bool& fallback) {
   fallback = n == 0;  // never: the row maximum is always a candidate
@@ -266,18 +268,31 @@ __device__ __forceinline__ void select_small(const ApplySmem& S, int n, const Ro
   const uint32_t key = has ? DT::key(static_cast<typename DT::raw_t>(raw)) : 0u;
   const uint64_t comp = has ? (static_cast<uint64_t>(key) << 32 | idx) : 0ull;
   const uint64_t mass = has ? mass_fx(DT::value(static_cast<typename DT::raw_t>(raw)), m) : 0ull;
+  if (has) tab[j] = vec_t{static_cast<uint32_t>(comp), static_cast<uint32_t>(comp >> 32), static_cast<uint32_t>(mass),
+                          static_cast<uint32_t>(mass >> 32)};
+  // one wave: its shared-memory accesses complete in order
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   uint32_t rank = 0;
   uint64_t above = 0;
-  for (int i = 0; i < n; ++i) {
-    const uint64_t ci = static_cast<uint64_t>(__builtin_amdgcn_readlane(static_cast<int>(comp >> 32), i)) << 32 |
-                        static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(comp), i));
-    const uint64_t mi = static_cast<uint64_t>(__builtin_amdgcn_readlane(static_cast<int>(mass >> 32), i)) << 32 |
-                        static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(mass), i));
+  auto visit = [&](const vec_t& e) {
+    const uint64_t ci = static_cast<uint64_t>(e.y) << 32 | e.x;
     if (ci > comp) {
       ++rank;
-      above += mi;
+      above += static_cast<uint64_t>(e.w) << 32 | e.z;
     }
+  };
+  constexpr int kRound = 8;
+  int i = 0;
+  for (; i + kRound <= n; i += kRound) {
+    vec_t e[kRound];
+#pragma unroll
+    for (int u = 0; u < kRound; ++u) e[u] = tab[i + u];
+#pragma unroll
+    for (int u = 0; u < kRound; ++u) visit(e[u]);
   }
+  for (; i < n; ++i) visit(tab[i]);
   uint32_t Kk = 0;
   if (rp.k_on) {
     const uint64_t at = __ballot(has && rank == rp.k - 1);
@@ -669,7 +684,8 @@ __device__ __forceinline__ void filter_row(const Tile& tile, const typename DT::
     if (threadIdx.x >= kWave) last_stores();
     if (threadIdx.x < kWave) {
       bool fb;
-      select_small<DT>(S, ncand, rp, m, thr, top_only, K, I, fb);
+      // the candidate vectors' list is no longer needed: its first entries hold the table
+      select_small<DT>(S, S.cvec, ncand, rp, m, thr, top_only, K, I, fb);
       if (threadIdx.x == 0) {
         S.sK = K;
         S.sI = I;

@@ -131,29 +131,42 @@ def algorithmic_bytes(wl, with_min_p=False, with_logits=True):
     return total
 
 
-def cpu_baseline(wl, budget_s=12.0, min_p=None, sample_q=None, sample_none=False, survivors_cap=0):
-    """The CPU oracle, as it stands, on the first rows of the same workload
-    (its sampling stage or sorted-survivors output too when the GPU computes
-    them)."""
+# The CPU oracle job of this run, set before worker processes are forked.
+_CPU_JOB = None
+
+
+def _oracle_chunk(lo):
+    """Runs the oracle, as it stands, on rows lo .. lo+7 of the workload (its
+    sampling stage or sorted-survivors output too when the GPU computes
+    them); returns the number of rows done."""
     from oracle import apply_top_k_top_p, apply_top_k_top_p_with_sorted, sample_top_k_top_p, sorted_survivors
 
+    wl, min_p, sample_q, sample_none, survivors_cap = _CPU_JOB
+    r = slice(lo, min(wl.B, lo + 8))
+    mp = None if min_p is None else min_p[r]
+    if survivors_cap:
+        sorted_survivors(wl.logits[r], wl.dtype, wl.p[r], wl.k[r], mp, survivors_cap)
+    elif sample_q is not None or sample_none:
+        sample_top_k_top_p(wl.logits[r], wl.dtype, wl.p[r], wl.k[r], mp,
+                           None if sample_q is None else sample_q[r], 1e-6)
+    elif wl.entry == "apply":
+        apply_top_k_top_p(wl.logits[r], wl.dtype, wl.p[r], wl.k[r], keep_traces=False, min_p_bits=mp)
+    else:
+        apply_top_k_top_p_with_sorted(wl.sorted_value[r], wl.sorted_indices[r], wl.dtype, wl.p[r], wl.k[r],
+                                      logits_bits=wl.logits[r], keep_traces=False, min_p_bits=mp)
+    return r.stop - r.start
+
+
+def cpu_baseline(wl, budget_s=12.0, min_p=None, sample_q=None, sample_none=False, survivors_cap=0):
+    """The CPU oracle on one thread, over the workload's rows in order (8 at a
+    time, wrapping), for about budget_s seconds. Also sets the job that
+    cpu_baseline_parallel runs."""
+    global _CPU_JOB
+    _CPU_JOB = (wl, min_p, sample_q, sample_none, survivors_cap)
     done = 0
     t0 = time.perf_counter()
     while (time.perf_counter() - t0) < budget_s:
-        lo = done % wl.B
-        r = slice(lo, min(wl.B, lo + 8))
-        mp = None if min_p is None else min_p[r]
-        if survivors_cap:
-            sorted_survivors(wl.logits[r], wl.dtype, wl.p[r], wl.k[r], mp, survivors_cap)
-        elif sample_q is not None or sample_none:
-            sample_top_k_top_p(wl.logits[r], wl.dtype, wl.p[r], wl.k[r], mp,
-                               None if sample_q is None else sample_q[r], 1e-6)
-        elif wl.entry == "apply":
-            apply_top_k_top_p(wl.logits[r], wl.dtype, wl.p[r], wl.k[r], keep_traces=False, min_p_bits=mp)
-        else:
-            apply_top_k_top_p_with_sorted(wl.sorted_value[r], wl.sorted_indices[r], wl.dtype, wl.p[r], wl.k[r],
-                                          logits_bits=wl.logits[r], keep_traces=False, min_p_bits=mp)
-        done += r.stop - r.start
+        done += _oracle_chunk(done % wl.B)
     dt = time.perf_counter() - t0
     return {
         "value": round(done / dt, 3),
@@ -162,6 +175,36 @@ def cpu_baseline(wl, budget_s=12.0, min_p=None, sample_q=None, sample_none=False
         "kind": "oracle",
         "sample": f"{done} rows (the workload's rows in order, wrapping after {wl.B}), numpy float64 oracle, "
                   f"one thread, {dt:.1f} s",
+    }
+
+
+def cpu_baseline_parallel(wl, rate1, budget_s=12.0):
+    """The same oracle job on every host core (at most 16: one GPU's share of
+    the host), one process per core over disjoint 8-row chunks, sized from the
+    one-thread rate to take about budget_s seconds. Must run before the GPU is
+    initialised: the workers are forked from this process."""
+    import multiprocessing as mp
+
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    cores = max(1, min(cores, 16))
+    chunks = max(cores, int(rate1 * cores * budget_s / 8))
+    starts = [(8 * i) % wl.B for i in range(chunks)]
+    ctx = mp.get_context("fork")
+    with ctx.Pool(cores) as pool:
+        pool.map(_oracle_chunk, starts[:cores])  # workers imported and warm
+        t0 = time.perf_counter()
+        done = sum(pool.map(_oracle_chunk, starts, chunksize=1))
+        dt = time.perf_counter() - t0
+    return {
+        "value": round(done / dt, 3),
+        "unit": "rows/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": f"{done} rows in 8-row chunks over {cores} worker processes (one per core), the same numpy "
+                  f"float64 oracle, {dt:.1f} s",
     }
 
 
@@ -181,6 +224,8 @@ def main():
     ap.add_argument("--sample-none", action="store_true", help="filter then take the argmax index per row")
     ap.add_argument("--survivors", action="store_true",
                     help="sorted survivors (probabilities, indices, counts; capacity 1024) instead of the filtered row")
+    ap.add_argument("--warm", action="store_true",
+                    help="also time back-to-back calls on one buffer set (warm caches), reported apart")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time a plain device-to-device copy of the logits instead of the filter (the reference "
                          "kernel whose HBM counters scale the filter's)")
@@ -192,35 +237,46 @@ def main():
               "single MI355X; run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
-    import torch
-
-    import top_logits_filtering_amd as tk
     from workloads.synth import make_workload, min_p_for_workload
 
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    tk.load_library()
-    tk.set_plan_policy(args.policy)
     wl = make_workload(args.workload)
     dt = wl.dtype
-    p = dev(wl.p, dt)
-    k = torch.from_numpy(wl.k).cuda()
     mp_bits = min_p_for_workload(args.workload, wl.B, dt) if args.min_p else None
-    mp = dev(mp_bits, dt)
     sampling = args.sample or args.sample_none
     if (sampling or args.survivors) and wl.entry != "apply":
         print("--sample and --survivors apply to the raw-logits workloads (1-4)", file=sys.stderr)
         sys.exit(2)
     cap = 1024
+    q_host = None
+    if args.sample:
+        rng = np.random.default_rng(0x5A4D)
+        q_host = rng.exponential(1.0, size=(wl.B, wl.V)).astype(np.float32)
+
+    # The CPU oracle first, before anything touches the GPU (its parallel leg
+    # forks worker processes).
+    baselines = None
+    if not (args.copy_calibration or args.no_cpu_baseline):
+        one = cpu_baseline(wl, args.cpu_budget, mp_bits, None if q_host is None else q_host.astype(np.float64),
+                           args.sample_none, cap if args.survivors else 0)
+        baselines = (one, cpu_baseline_parallel(wl, one["value"], args.cpu_budget))
+
+    import torch
+
+    import top_logits_filtering_amd as tk
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    tk.load_library()
+    tk.set_plan_policy(args.policy)
+    p = dev(wl.p, dt)
+    k = torch.from_numpy(wl.k).cuda()
+    mp = dev(mp_bits, dt)
     surv_out = None
     if args.survivors:
         surv_out = (torch.empty((wl.B, cap), dtype=torch.float32, device="cuda"),
                     torch.empty((wl.B, cap), dtype=torch.int32, device="cuda"),
                     torch.empty((wl.B,), dtype=torch.int32, device="cuda"))
     q = None
-    q_host = None
     if args.sample:
-        rng = np.random.default_rng(0x5A4D)
-        q_host = rng.exponential(1.0, size=(wl.B, wl.V)).astype(np.float32)
         q = torch.from_numpy(q_host).cuda()
     selected = torch.empty((wl.B,), dtype=torch.int32, device="cuda")
     sets = []
@@ -267,6 +323,32 @@ def main():
 
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     kernel_ms = ev0.elapsed_time(ev1) / args.steps
+
+    # Outside the timed region: each call between its own pair of events
+    # (rotating buffer sets), for the latency spread of a single call; with
+    # --warm also back-to-back calls on one buffer set (inputs partly cached).
+    n_single = 50
+    singles = []
+    for i in range(n_single):
+        a = torch.cuda.Event(enable_timing=True)
+        z = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        step(i)
+        z.record(stream)
+        z.synchronize()
+        singles.append(a.elapsed_time(z) * 1e3)
+    torch.cuda.synchronize()
+    warm_us = None
+    if args.warm:
+        wa = torch.cuda.Event(enable_timing=True)
+        wz = torch.cuda.Event(enable_timing=True)
+        wa.record(stream)
+        for _ in range(n_single):
+            step(0)
+        wz.record(stream)
+        torch.cuda.synchronize()
+        warm_us = round(wa.elapsed_time(wz) * 1e3 / n_single, 3)
+    p10, p50, p90 = np.percentile(np.array(singles), [10, 50, 90])
     if args.copy_calibration:
         nbytes = 2 * wl.B * wl.V * wl.elem_bytes
     elif sampling:
@@ -319,15 +401,20 @@ def main():
             "algorithmic_bytes_per_launch": nbytes,
         },
     }
+    line["latency"] = {
+        "per_call_us": {"p10": round(float(p10), 3), "median": round(float(p50), 3), "p90": round(float(p90), 3),
+                        "calls": n_single},
+        "warm_same_buffer_us": warm_us,
+        "note": "per_call_us: one call between its own events, rotating buffer sets; warm_same_buffer_us "
+                "(--warm): back-to-back calls on one buffer set, inputs partly cached; both outside the timed region",
+    }
     if args.copy_calibration:
         line["metric"] = "device copy of the logits (HBM counter calibration)"
         line["value"] = round(nbytes / (ms_per_step * 1e-3) / 1e9, 1)
         line["unit"] = "GB/s"
         line["config"]["workload"] = "torch copy_ of " + WORKLOAD_TEXT[args.workload]
-    elif not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget, mp_bits,
-                                            None if q_host is None else q_host.astype(np.float64), args.sample_none,
-                                            cap if args.survivors else 0)
+    elif baselines is not None:
+        line["cpu_baseline"], line["cpu_baseline_parallel"] = baselines
     print(json.dumps(line), flush=True)
 
 

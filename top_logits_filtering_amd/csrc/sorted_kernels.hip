@@ -26,8 +26,12 @@
 // Each row is split into slices handled by separate blocks; every block
 // repeats the (cheap) boundary search, so no block waits on another and no
 // global scratch is needed. The logits slice is loaded into registers before
-// the boundary search so its latency overlaps that search.
+// the boundary search so its latency overlaps that search. Without k the
+// search scans the whole sorted row (Z needs every mass); that scan is bound
+// by the vector ALUs (one exp2 per distinct value), so fewer blocks share a
+// row then, each taking several slices.
 
+#include <algorithm>
 #include <type_traits>
 
 #include "launch.h"
@@ -106,7 +110,7 @@ __device__ __forceinline__ void block_max_u64_i32(uint64_t a, int b, RowSmem& sm
 //      V <= 2^20) finds F.
 // The masses are integers, so the result does not depend on how they are
 // grouped. Returns V - 1 when the threshold is zero (t >= 1).
-template <class DT>
+template <class DT, int kBatch>
 __device__ __forceinline__ int topp_boundary_global(const typename DT::raw_t* __restrict__ sv, int start, int V,
                                                     float m, float t, RowSmem& sm) {
   using raw_t = typename DT::raw_t;
@@ -119,9 +123,19 @@ __device__ __forceinline__ int topp_boundary_global(const typename DT::raw_t* __
   const int L = (gtop - glo + kThreads) / kThreads;  // groups per segment
   const int g0 = gtop - tid * L;            // this thread: groups g0 down to g0 - L + 1, not below glo
   uint64_t s = 0;
+  // the mass of a run of equal values is computed once per run (sorted rows
+  // of 16-bit values are mostly long runs); no raw value equals ~0u here
+  uint32_t prev = 0xFFFFFFFFu;
+  uint64_t pe = 0;
+  auto add = [&](raw_t r) {
+    if (static_cast<uint32_t>(r) != prev) {
+      pe = mass_fx(DT::value(r), m);
+      prev = static_cast<uint32_t>(r);
+    }
+    s += pe;
+  };
   if (vec) {
     const __amdgpu_buffer_rsrc_t rs = row_rsrc(sv, V);
-    constexpr int kBatch = 4;  // loads in flight per thread
     for (int u0 = 0; u0 < L; u0 += kBatch) {
       vec_t q[kBatch];
 #pragma unroll
@@ -137,7 +151,7 @@ __device__ __forceinline__ int topp_boundary_global(const typename DT::raw_t* __
         if (u0 + u < L && g >= glo) {
 #pragma unroll
           for (int j = 0; j < kPV; ++j)
-            if (g * kPV + j >= start) s += mass_fx(DT::value(lane_of<raw_t>(q[u], j)), m);
+            if (g * kPV + j >= start) add(lane_of<raw_t>(q[u], j));
         }
       }
     }
@@ -145,7 +159,7 @@ __device__ __forceinline__ int topp_boundary_global(const typename DT::raw_t* __
 #pragma unroll 8
     for (int u = 0; u < L; ++u) {
       const int j = g0 - u;  // one position per group
-      if (j >= glo) s += mass_fx(DT::value(sv[j]), m);
+      if (j >= glo) add(sv[j]);
     }
   }
   uint64_t Z;
@@ -193,7 +207,7 @@ struct SortedBoundary {
   int a;        // first sorted position holding key KF (positions a..F-1 are masked)
 };
 
-template <class DT, class Src>
+template <class DT, int kScanBatch, class Src>
 __device__ __forceinline__ SortedBoundary sorted_boundary(const Src& sv, const RowParams& rp, int V,
                                                           RowSmem& sm) {
   int start = 0;
@@ -207,7 +221,7 @@ __device__ __forceinline__ SortedBoundary sorted_boundary(const Src& sv, const R
   if (rp.pmode == kPTopOnly) {
     F = V - 1;
   } else if (rp.pmode == kPBoundary) {
-    F = topp_boundary_global<DT>(sv.g, start, V, DT::value(sv.at(V - 1)), rp.t, sm);
+    F = topp_boundary_global<DT, kScanBatch>(sv.g, start, V, DT::value(sv.at(V - 1)), rp.t, sm);
   }
   // min-p keeps a suffix of the sorted positions too: the tighter one wins
   if (rp.mp_on) F = first_min_p<DT>(sv, F, V, rp.minp, sm);
@@ -324,12 +338,12 @@ __device__ __forceinline__ bool boundary_from_copy(const typename DT::raw_t* top
 constexpr int kSortedVecs = 8;  // logits slice held in registers: 8 vectors per thread
 constexpr int kMaxSliceWords = (kThreads * kSortedVecs * 8) / 32;
 
-template <class DT, bool kRegs>
+template <class DT, bool kRegs, bool kNoK>
 __global__ __launch_bounds__(kThreads, 8) void sorted_logits_kernel(
     const typename DT::raw_t* __restrict__ sorted_value, const int32_t* __restrict__ sorted_indices,
     const typename DT::raw_t* __restrict__ p, const int32_t* __restrict__ k,
     const typename DT::raw_t* __restrict__ min_p, const typename DT::raw_t* __restrict__ logits,
-    typename DT::raw_t* __restrict__ out, int V, int S, RowStrides ld) {
+    typename DT::raw_t* __restrict__ out, int V, int S, RowStrides ld, int blocks_per_row) {
   using raw_t = typename DT::raw_t;
   using Tile = std::conditional_t<kRegs, RegTile<DT, kSortedVecs>, GlobalTile<DT>>;
   constexpr int kCap = RegTile<DT, kSortedVecs>::kCapacity;
@@ -337,10 +351,17 @@ __global__ __launch_bounds__(kThreads, 8) void sorted_logits_kernel(
   __shared__ uint32_t ties[kMaxSliceWords];
   __shared__ __align__(16) raw_t top[kSortedPrefetch];
 
-  const int b = blockIdx.x / S;
-  const int s = blockIdx.x - b * S;
-  const int v0 = s * kCap;
-  const int len = min(kCap, V - v0);
+  // Without k (kNoK) no row can use the copy of the top values, and every
+  // block of a row would scan the whole sorted row for Z: then Sb blocks
+  // share the row's S slices (Sb = blocks_per_row, chosen so the batch still
+  // fills the device), each taking its own run of slices one after another.
+  const int Sb = kNoK ? blocks_per_row : S;
+  const int b = static_cast<int>(blockIdx.x) / Sb;
+  const int s = static_cast<int>(blockIdx.x) - b * Sb;
+  const int s_lo = kNoK ? (s * S) / Sb : s;
+  const int s_hi = kNoK ? ((s + 1) * S) / Sb : s + 1;
+  int v0 = s_lo * kCap;
+  int len = min(kCap, V - v0);
   const raw_t* __restrict__ sv = sorted_value + static_cast<size_t>(b) * static_cast<size_t>(ld.sv);
 
   // p[b] and k[b], the top sorted values the boundary search reads, then the
@@ -349,30 +370,52 @@ __global__ __launch_bounds__(kThreads, 8) void sorted_logits_kernel(
   const RowParamsRaw<DT> rpr = fetch_row_params<DT>(p, k, min_p, b);
   const int R = min(V, kSortedPrefetch);
   raw_t pre[kPre];
-  prefetch_top<DT>(sv, V, R, pre);
+  if constexpr (!kNoK) prefetch_top<DT>(sv, V, R, pre);
   __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the slice's
   Tile tile;
-  tile.load(logits + static_cast<size_t>(b) * static_cast<size_t>(ld.x), v0, len);
+  if constexpr (!kNoK) tile.load(logits + static_cast<size_t>(b) * static_cast<size_t>(ld.x), v0, len);
   const RowParams rp = decode_row_params<DT>(rpr, V);
+  if constexpr (!kNoK) {
 #pragma unroll
-  for (int u = 0; u < kPre; ++u) top[u * kThreads + threadIdx.x] = pre[u];  // entries past R: zero, unused
+    for (int u = 0; u < kPre; ++u) top[u * kThreads + threadIdx.x] = pre[u];  // entries past R: zero, unused
+  }
   lds_barrier();
 
   raw_t* __restrict__ orow = out + static_cast<size_t>(b) * static_cast<size_t>(ld.o);
+  const raw_t* __restrict__ xrow = logits + static_cast<size_t>(b) * static_cast<size_t>(ld.x);
   if (!row_filters(rp)) {
-    tile.store(orow, [](raw_t r, int) { return r; });
+    if constexpr (kNoK) {
+      for (int ss = s_lo; ss < s_hi; ++ss) {
+        v0 = ss * kCap;
+        len = min(kCap, V - v0);
+        tile.load(xrow, v0, len);
+        tile.store(orow, [](raw_t r, int) { return r; });
+      }
+    } else {
+      tile.store(orow, [](raw_t r, int) { return r; });
+    }
     return;
   }
   SortedBoundary bd;
-  if (boundary_from_copy<DT>(top, R, V, rp))
+  if constexpr (kNoK) {
+    bd = sorted_boundary<DT, 8>(SortedSrcGlobal<DT>{sv}, rp, V, sm);
+  } else if (boundary_from_copy<DT>(top, R, V, rp)) {
     bd = sorted_boundary_copy<DT>(top, R, V, rp, sm);
-  else
-    bd = sorted_boundary<DT>(SortedSrcGlobal<DT>{sv}, rp, V, sm);
+  } else {
+    bd = sorted_boundary<DT, 4>(SortedSrcGlobal<DT>{sv}, rp, V, sm);
+  }
 
+  const int32_t* __restrict__ si = sorted_indices + static_cast<size_t>(b) * static_cast<size_t>(ld.si);
+  for (int ss = s_lo; ss < s_hi; ++ss) {
+  if constexpr (kNoK) {
+    v0 = ss * kCap;
+    len = min(kCap, V - v0);
+    tile.load(xrow, v0, len);
+    if (ss > s_lo) lds_barrier();  // the previous slice's bitmap reads are done
+  }
   const int words = (len + 31) / 32;
   for (int i = threadIdx.x; i < words; i += kThreads) ties[i] = 0;
   lds_barrier();
-  const int32_t* __restrict__ si = sorted_indices + static_cast<size_t>(b) * static_cast<size_t>(ld.si);
   for (int j = bd.a + static_cast<int>(threadIdx.x); j < bd.F; j += kThreads) {
     const int v = si[j] - v0;
     if (v >= 0 && v < len) atomicOr(&ties[v >> 5], 1u << (v & 31));
@@ -406,6 +449,7 @@ __global__ __launch_bounds__(kThreads, 8) void sorted_logits_kernel(
       }
       return keep ? r : DT::kNegInf;
     });
+  }
   }
 }
 
@@ -473,7 +517,7 @@ __global__ __launch_bounds__(kThreads) void sorted_scatter_kernel(
   lds_barrier();  // the copy is in place (this barrier does not wait for the stores)
 
   const int F = boundary_from_copy<DT>(top, R, V, rp) ? sorted_boundary_copy<DT>(top, R, V, rp, sm).F
-                                                      : sorted_boundary<DT>(SortedSrcGlobal<DT>{sv}, rp, V, sm).F;
+                                                      : sorted_boundary<DT, 4>(SortedSrcGlobal<DT>{sv}, rp, V, sm).F;
   // The survivors, 8 per thread per round with every load of a round in
   // flight together (bounded buffer loads: positions past V read as zero).
   // The first round's loads are issued before the wait for the -inf stores,
@@ -523,16 +567,24 @@ static hipError_t launch_sorted_t(const void* sorted_value, const int32_t* sorte
     const bool vec_ok = (V % DT::kPerVec) == 0 && (reinterpret_cast<uintptr_t>(logits) & 15u) == 0 &&
                         (reinterpret_cast<uintptr_t>(out) & 15u) == 0 && (ld.x * es) % 16 == 0 &&
                         (ld.o * es) % 16 == 0;
-    if (vec_ok)
-      hipLaunchKernelGGL((sorted_logits_kernel<DT, true>), dim3(static_cast<unsigned>(B * S)), dim3(kThreads), 0,
-                         stream, static_cast<const raw_t*>(sorted_value), sorted_indices,
-                         static_cast<const raw_t*>(p), k, static_cast<const raw_t*>(min_p),
-                         static_cast<const raw_t*>(logits), static_cast<raw_t*>(out), static_cast<int>(V), S, ld);
+    // without k: blocks per row so that the batch still fills the 256 CUs
+    const int Sb = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(S, 256 / std::max<int64_t>(B, 1))));
+    auto go = [&](auto kernel, int64_t grid) {
+      hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, stream,
+                         static_cast<const raw_t*>(sorted_value), sorted_indices, static_cast<const raw_t*>(p), k,
+                         static_cast<const raw_t*>(min_p), static_cast<const raw_t*>(logits), static_cast<raw_t*>(out),
+                         static_cast<int>(V), S, ld, Sb);
+    };
+    // without k no row can use the copy of the top values: no copy, and the
+    // slices are read after the scan over the sorted row
+    if (vec_ok && k == nullptr)
+      go(sorted_logits_kernel<DT, true, true>, B * Sb);
+    else if (vec_ok)
+      go(sorted_logits_kernel<DT, true, false>, B * S);
+    else if (k == nullptr)
+      go(sorted_logits_kernel<DT, false, true>, B * Sb);
     else
-      hipLaunchKernelGGL((sorted_logits_kernel<DT, false>), dim3(static_cast<unsigned>(B * S)), dim3(kThreads), 0,
-                         stream, static_cast<const raw_t*>(sorted_value), sorted_indices,
-                         static_cast<const raw_t*>(p), k, static_cast<const raw_t*>(min_p),
-                         static_cast<const raw_t*>(logits), static_cast<raw_t*>(out), static_cast<int>(V), S, ld);
+      go(sorted_logits_kernel<DT, false, false>, B * S);
   } else {
     const int S = static_cast<int>((V + kScatterSlice - 1) / kScatterSlice);
     hipLaunchKernelGGL(sorted_scatter_kernel<DT>, dim3(static_cast<unsigned>(B * S)), dim3(kThreads), 0, stream,

@@ -1,0 +1,85 @@
+"""The longest rows the library accepts (V = 2^20, and 2^20 - 1 for a ragged
+tail) on every entry point, against the CPU oracle (needs an MI355X). Rows
+this long are streamed from global memory: they exceed a block's register
+tile, and the pre-sorted kernels split them into 16 slices."""
+
+import numpy as np
+import pytest
+
+from oracle import apply_top_k_top_p as oracle_apply
+from oracle import apply_top_k_top_p_with_sorted as oracle_sorted
+from oracle import sample_top_k_top_p as oracle_sample
+from oracle import sorted_survivors as oracle_survivors
+from tests.gpu_util import gpu_apply, gpu_with_sorted, k_dev, need_gpu, say, to_dev
+from tests.parity import ParityReport, compare, compare_samples, compare_survivors
+from workloads.synth import f32_to_bits, random_rows, stable_ascending_sort
+
+pytestmark = pytest.mark.gpu
+
+V_MAX = 1 << 20
+
+
+def _params(dtype, B):
+    k = np.array([1, 3000, 0], np.int32)[:B]
+    p = f32_to_bits(np.array([0.9, 0.5, 0.99], np.float32)[:B], dtype)
+    mp = f32_to_bits(np.array([0.05, 0.2, 0.01], np.float32)[:B], dtype)
+    return k, p, mp
+
+
+@pytest.mark.parametrize("dtype,V", [("bf16", V_MAX), ("f32", V_MAX), ("f16", V_MAX - 1)])
+def test_apply_max_rows(dtype, V):
+    need_gpu()
+    B = 3
+    total = ParityReport()
+    for kind in ("normal", "ties"):
+        xb = random_rows(2100 + V % 5, B, V, dtype, kind=kind, scale=3.0)
+        k, p, mp = _params(dtype, B)
+        for pp, kk, mm in ((p, k, None), (None, k, None), (p, None, None), (p, k, mp)):
+            got = gpu_apply(xb, dtype, pp, kk, mm)
+            ref = oracle_apply(xb, dtype, pp, kk, min_p_bits=mm)
+            rep = compare(got, xb, ref, dtype)
+            assert rep.hard_mismatches == 0, (kind, pp is None, kk is None, mm is None, rep.details[:2])
+            total.merge(rep)
+    say(f"apply {dtype} V={V}: {total}")
+
+
+@pytest.mark.parametrize("dtype,V", [("bf16", V_MAX), ("f32", V_MAX - 1)])
+def test_with_sorted_max_rows(dtype, V):
+    need_gpu()
+    B = 3
+    total = ParityReport()
+    xb = random_rows(2200 + V % 5, B, V, dtype, kind="ties", scale=3.0)
+    idx, sv = stable_ascending_sort(xb, dtype)
+    k, p, mp = _params(dtype, B)
+    for pp, kk, mm in ((p, k, None), (None, k, None), (p, None, None), (p, k, mp)):
+        ref = oracle_sorted(sv, idx, dtype, pp, kk, logits_bits=xb, min_p_bits=mm)
+        for use_logits in (True, False):
+            got = gpu_with_sorted(sv, idx, dtype, pp, kk, xb if use_logits else None, min_p=mm)
+            rep = compare(got, xb, ref, dtype)
+            assert rep.hard_mismatches == 0, (pp is None, kk is None, mm is None, use_logits, rep.details[:2])
+            total.merge(rep)
+    say(f"with_sorted {dtype} V={V}: {total}")
+
+
+def test_sample_and_survivors_max_rows():
+    need_gpu()
+    import torch
+    import top_logits_filtering_amd as tk
+
+    dtype, V, B = "bf16", V_MAX, 3
+    xb = random_rows(2300, B, V, dtype, kind="gumbel", scale=4.0)
+    k, p, _ = _params(dtype, B)
+    q = np.random.default_rng(2301).exponential(1.0, size=(B, V)).astype(np.float32)
+    qd = torch.from_numpy(q).cuda()
+    for qq, qh in ((None, None), (qd, q)):
+        sel = tk.sample_top_k_top_p(to_dev(xb, dtype), to_dev(p, dtype), k_dev(k), None, qq, 1e-6)
+        torch.cuda.synchronize()
+        ref = oracle_sample(xb, dtype, p, k, None, None if qh is None else qh.astype(np.float64), 1e-6)
+        h, _, det = compare_samples(sel.cpu().numpy(), ref)
+        assert h == 0, (qq is None, det[:3])
+    pr, ix, cnt = tk.top_k_top_p_sorted_survivors(to_dev(xb, dtype), to_dev(p, dtype), k_dev(k), None, cap=512)
+    torch.cuda.synchronize()
+    ref = oracle_survivors(xb, dtype, p, k, None, 512)
+    h, det = compare_survivors(pr.cpu().numpy().astype(np.float64), ix.cpu().numpy(), cnt.cpu().numpy(), ref)
+    assert h == 0, det[:3]
+    say("sample and survivors bf16 V=2^20: ok")

@@ -83,3 +83,27 @@ def test_sample_and_survivors_max_rows():
     h, det = compare_survivors(pr.cpu().numpy().astype(np.float64), ix.cpu().numpy(), cnt.cpu().numpy(), ref)
     assert h == 0, det[:3]
     say("sample and survivors bf16 V=2^20: ok")
+
+
+def test_many_short_rows():
+    """More rows than one grid dimension of 65535 blocks would hold: one block
+    per row (or per slice) over 70000 rows of 96 values, sampled rows against
+    the oracle and properties on every row."""
+    need_gpu()
+    dtype, B, V = "bf16", 70000, 96
+    xb = random_rows(2400, B, V, dtype, kind="ties", scale=2.0)
+    rng = np.random.default_rng(2401)
+    k = rng.integers(0, V + 2, size=B).astype(np.int32)
+    p = f32_to_bits(rng.uniform(0.1, 1.0, size=B).astype(np.float32), dtype)
+    got = gpu_apply(xb, dtype, p, k)
+    rows = np.unique(np.concatenate([[0, 1, 65534, 65535, 65536, B - 1], rng.choice(B, 40, replace=False)]))
+    ref = oracle_apply(xb[rows], dtype, p[rows], k[rows])
+    rep = compare(got[rows], xb[rows], ref, dtype)
+    assert rep.hard_mismatches == 0, rep.details[:2]
+    neg = 0xFF80
+    assert np.all((got == xb) | (got == neg)), "values other than input bits or -inf"
+    assert (got != neg).any(axis=1).all(), "a row lost every position"
+    idx, sv = stable_ascending_sort(xb[:20000], dtype)
+    got_s = gpu_with_sorted(sv, idx, dtype, p[:20000], k[:20000], xb[:20000])
+    assert np.array_equal(got_s, got[:20000]), "pre-sorted entry differs from the sorting entry"
+    say(f"{B} rows of {V}: {rep}")

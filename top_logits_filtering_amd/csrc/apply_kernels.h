@@ -57,6 +57,7 @@ constexpr int kMaxVecs = 20;
 constexpr int kCandVecCap = 2048;  // candidate vectors kept in shared memory
 constexpr int kStreamVmSlots = 32;  // streamed rows: vector maxima kept for this many layers
 constexpr int kCandPerThread = 5;
+constexpr int kRegFallbackVecs = 4;  // register tiles of up to this many vectors run the fallback in registers
 constexpr int kCandCap = kCandPerThread * kThreads;  // candidate elements kept in shared memory
 
 // When the -inf stores of a register tile are issued, as cumulative shares (in
@@ -765,7 +766,9 @@ __device__ __forceinline__ void filter_row(const Tile& tile, const typename DT::
 
   if constexpr (kSample) {
     if (!fallback && wants_survivors(sa)) {  // every survivor is a candidate
-      const double Z = survivors_z<DT>(cs, tile, rp, L, kmax, m, ss, sm, S.redd);
+      // (rows without k sum the whole row re-read from global memory: keeping
+      // the register tile live through the ranking below would spill it)
+      const double Z = survivors_z<DT>(cs, gt, rp, L, kmax, m, ss, sm, S.redd);
       emit_survivors<DT>(cs, K, I, kmax, m, Z, sa, b, ss, reinterpret_cast<uint64_t*>(S.cel.raw));
     } else if (!fallback) {  // every survivor is a candidate
       int32_t pick;
@@ -792,6 +795,12 @@ __device__ __forceinline__ void filter_row(const Tile& tile, const typename DT::
         if (key > K || (key == K && static_cast<uint32_t>(idx) >= I)) orow[idx] = raw;
       });
     }
+  } else if constexpr (Tile::kRegisters && Tile::kVecs <= kRegFallbackVecs) {
+    // short register rows run the multi-pass plan over the registers: each
+    // traversal then costs no memory latency (longer rows re-read global
+    // memory, which keeps the unrolled code of their kernels small)
+    filter_multipass<DT>(tile, rp, V, S, orow, wr, K, I);
+    if constexpr (kSample) sample_general<DT>(tile, K, I, rp, S, sa, b);
   } else {
     filter_multipass<DT>(gt, rp, V, S, orow, wr, K, I);
     if constexpr (kSample) sample_general<DT>(gt, K, I, rp, S, sa, b);

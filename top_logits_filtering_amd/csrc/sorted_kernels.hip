@@ -402,7 +402,10 @@ __global__ __launch_bounds__(kThreads, 8) void sorted_logits_kernel(
   } else if (boundary_from_copy<DT>(top, R, V, rp)) {
     bd = sorted_boundary_copy<DT>(top, R, V, rp, sm);
   } else {
-    bd = sorted_boundary<DT, 4>(SortedSrcGlobal<DT>{sv}, rp, V, sm);
+    // the slice tile is live beside the scan: fp16, whose conversions take
+    // more registers, keeps one load fewer in flight so nothing spills
+    constexpr int kScan = std::is_same_v<DT, F16T> && kRegs ? 3 : 4;
+    bd = sorted_boundary<DT, kScan>(SortedSrcGlobal<DT>{sv}, rp, V, sm);
   }
 
   const int32_t* __restrict__ si = sorted_indices + static_cast<size_t>(b) * static_cast<size_t>(ld.si);

@@ -154,3 +154,19 @@ def test_survivors_entry_point_checks(lib):
     assert f(FAKE, 0, 2, 8, None, None, None, 4, o1, o1 + 8, o3, None) == INVALID  # probs and indices overlap
     assert f(FAKE, 0, 2, 8, None, None, None, 4, None, FAKE + 4, o3, None) == INVALID  # indices inside logits
     assert f(None, 1, 0, 8, None, None, None, 4, None, None, None, None) == 0
+
+
+def test_build_rejects_spilling_kernels():
+    """The build reads the compiler's resource report and fails on any kernel
+    that uses scratch (a register spill)."""
+    from top_logits_filtering_amd.build import _spills
+
+    report = "\n".join([
+        "a.hip:1:1: remark: Function Name: _ZN3tkp4goodE [-Rpass-analysis=kernel-resource-usage]",
+        "a.hip:1:1: remark:     VGPRs: 64 [-Rpass-analysis=kernel-resource-usage]",
+        "a.hip:1:1: remark:     ScratchSize [bytes/lane]: 0 [-Rpass-analysis=kernel-resource-usage]",
+        "a.hip:9:1: remark: Function Name: _ZN3tkp5spillE [-Rpass-analysis=kernel-resource-usage]",
+        "a.hip:9:1: remark:     ScratchSize [bytes/lane]: 12 [-Rpass-analysis=kernel-resource-usage]",
+    ])
+    assert _spills(report) == [("_ZN3tkp5spillE", 12)]
+    assert _spills(report.replace(": 12 ", ": 0 ")) == []

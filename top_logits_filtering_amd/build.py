@@ -8,6 +8,7 @@ file as ``libtopktopp.so``; object files go to ``_build/``.
 from __future__ import annotations
 
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -45,16 +46,41 @@ def _hipcc() -> str:
     return path
 
 
+# Every kernel must fit its registers: a spill goes to scratch memory, whose
+# accesses wait behind the row loads in flight. The compiler's resource report
+# is read after each compile and any kernel with scratch fails the build.
+RESOURCE_FLAG = "-Rpass-analysis=kernel-resource-usage"
+
+
+def _spills(report: str) -> list:
+    """(kernel, bytes per lane) for every kernel of a resource report that uses scratch."""
+    found, name = [], None
+    for line in report.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+            continue
+        m = re.search(r"ScratchSize \[bytes/lane\]: (\d+)", line)
+        if m and name is not None and int(m.group(1)) > 0:
+            found.append((name, int(m.group(1))))
+    return found
+
+
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [_hipcc(), *COMMON_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [_hipcc(), *COMMON_FLAGS, RESOURCE_FLAG, "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     noise = "not a recognized feature for this target"
-    msg = "\n".join(l for l in (res.stdout + res.stderr).splitlines() if noise not in l)
+    lines = [l for l in (res.stdout + res.stderr).splitlines() if noise not in l]
+    msg = "\n".join(l for l in lines if RESOURCE_FLAG not in l)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{msg}")
+    spills = _spills("\n".join(lines))
+    if spills:
+        raise RuntimeError(f"kernels in {src} spill registers to scratch: " +
+                           ", ".join(f"{n} ({b} B/lane)" for n, b in spills))
     if verbose and msg.strip():
         print(msg, flush=True)
     return obj

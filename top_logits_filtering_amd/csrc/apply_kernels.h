@@ -867,7 +867,10 @@ hipError_t launch_apply_t(const void* logits, const void* p, const int32_t* k, c
   const bool vec_ok = (V % DT::kPerVec) == 0 && (reinterpret_cast<uintptr_t>(logits) & 15u) == 0 &&
                       (reinterpret_cast<uintptr_t>(out) & 15u) == 0 && (ld.x * es) % 16 == 0 &&
                       (out == nullptr || (ld.o * es) % 16 == 0);
-  if (policy != kPlanAuto || vecs > kMaxVecs || !vec_ok) {
+  // the sampling kernels hold at most 19 vectors per thread in registers
+  // (20 would spill in fp16); longer rows are streamed
+  constexpr int64_t max_vecs = kSample ? 19 : kMaxVecs;
+  if (policy != kPlanAuto || vecs > max_vecs || !vec_ok) {
     hipLaunchKernelGGL((apply_stream_kernel<DT, kSample>), dim3(static_cast<unsigned>(B)), dim3(kThreads), 0, stream,
                        static_cast<const raw_t*>(logits), static_cast<const raw_t*>(p), k,
                        static_cast<const raw_t*>(min_p), static_cast<raw_t*>(out), static_cast<int>(V), ld,
@@ -886,7 +889,7 @@ hipError_t launch_apply_t(const void* logits, const void* p, const int32_t* k, c
     launch_regs<DT, 16, kSample>(logits, p, k, min_p, out, B, V, ld, use_candidates, sa, stream);
   } else if (vecs <= 19) {
     launch_regs<DT, 19, kSample>(logits, p, k, min_p, out, B, V, ld, use_candidates, sa, stream);
-  } else {
+  } else if constexpr (!kSample) {
     launch_regs<DT, kMaxVecs, kSample>(logits, p, k, min_p, out, B, V, ld, use_candidates, sa, stream);
   }
   return hipGetLastError();

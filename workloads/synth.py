@@ -97,7 +97,7 @@ def _param_rng(seed: int) -> np.random.Generator:
     return np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, PARAM_STREAM])))
 
 
-CONFIGS = {
+WORKLOAD_SPECS = {
     1: dict(name="joint_fp32_B4_V1000", entry="apply", dtype="f32", B=4, V=1000),
     2: dict(name="spikes_fp16_B64_V32000", entry="apply", dtype="f16", B=64, V=32000),
     3: dict(name="mixed_bf16_B256_V151936", entry="apply", dtype="bf16", B=256, V=151936),
@@ -135,7 +135,7 @@ def make_workload(c: int, rows: Optional[Sequence[int]] = None, timed_modes: boo
     positions). :func:`split_modes` rebuilds the same rows as three calls with
     truly absent p or k.
     """
-    cfg = CONFIGS[c]
+    cfg = WORKLOAD_SPECS[c]
     B, V, dtype = cfg["B"], cfg["V"], cfg["dtype"]
     seed = SEED_BASE + c
     prng = _param_rng(seed)

@@ -6,7 +6,7 @@ path can take their inputs from it.
 """
 
 from .synth import (  # noqa: F401
-    CONFIGS,
+    WORKLOAD_SPECS,
     Workload,
     bf16_bits_from_f32,
     bits_to_f32,

@@ -61,6 +61,11 @@ def compare_row(g_row, x_row, trace, dtype, tol=BAND_TOL, row_id=None) -> Parity
     is_x = gs == xs
     mask_m = trace.min_p_mask if trace.min_p_mask is not None else np.zeros(V, dtype=bool)
     o_masked = trace.top_k_mask | trace.top_p_mask | mask_m
+    # min-p's own decision, probability below the threshold: the oracle's
+    # trace also marks every position top-p masked (their probability is set
+    # aside), but those are top-p's decisions, and inside top-p's band the GPU
+    # may keep them
+    own_m = mask_m if trace.min_p_ratio is None else (trace.min_p_ratio < 1.0)
     band_p = np.zeros(V, dtype=bool)
     if trace.probs_sum32 is not None and trace.t is not None:
         band_p = np.abs(trace.probs_sum32.astype(np.float64) - np.float64(trace.t)) <= tol
@@ -73,8 +78,8 @@ def compare_row(g_row, x_row, trace, dtype, tol=BAND_TOL, row_id=None) -> Parity
     ambiguous_val = xs == neg  # input already -inf: kept and masked look the same
     # a stage forces a mask where it masks outside its band, and allows a keep
     # where it keeps or is inside its band
-    must_mask = trace.top_k_mask | (trace.top_p_mask & ~band_p) | (mask_m & ~band_m)
-    must_keep = ~trace.top_k_mask & ~(trace.top_p_mask | band_p) & ~(mask_m | band_m)
+    must_mask = trace.top_k_mask | (trace.top_p_mask & ~band_p) | (own_m & ~band_m)
+    must_keep = ~trace.top_k_mask & ~(trace.top_p_mask | band_p) & ~(own_m | band_m)
     bad = ~(is_neg | is_x)  # rule 4
     bad |= must_mask & ~is_neg  # rules 1 and 3
     bad |= must_keep & ~is_x  # rule 2

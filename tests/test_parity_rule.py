@@ -76,3 +76,29 @@ def test_sample_rule():
     # a masked position (the row's minimum) is never an allowed pick
     bad[0] = int(res.filtered.traces[0].sorted_indices[0])
     assert compare_samples(bad, res)[0] == 1
+
+
+def test_top_p_band_position_with_min_p():
+    """With min-p on, a position top-p masks inside its band may still be kept:
+    the oracle's min-p trace also marks the positions top-p masked, but those
+    are top-p's decisions. A long row of equal values puts several positions in
+    the top-p band (each holds 1/V < 1e-5 of the mass)."""
+    dtype, V = "bf16", 200000
+    xb = np.zeros((1, V), dtype=np.uint16)  # every value +0.0
+    p = f32_to_bits(np.array([0.026], np.float32), dtype)
+    mp = f32_to_bits(np.array([1e-3], np.float32), dtype)
+    ref = apply_top_k_top_p(xb, dtype, p, None, min_p_bits=mp)
+    tr = ref.traces[0]
+    band = np.abs(tr.probs_sum32.astype(np.float64) - float(tr.t)) <= 1e-5
+    masked_band = np.nonzero(band & tr.top_p_mask)[0]
+    assert len(masked_band) > 0
+    g = ref.out.copy()
+    j = int(masked_band[-1])  # the band position just below the survivors: kept on the "GPU"
+    g[0, tr.sorted_indices[j]] = xb[0, tr.sorted_indices[j]]
+    rep = compare(g, xb, ref, dtype)
+    assert rep.hard_mismatches == 0 and rep.band_mismatches == 1
+    # outside the band the same change is still an error
+    g = ref.out.copy()
+    far = int(np.nonzero(tr.top_p_mask & ~band)[0][-1])
+    g[0, tr.sorted_indices[far]] = xb[0, tr.sorted_indices[far]]
+    assert compare(g, xb, ref, dtype).hard_mismatches >= 1

@@ -1,0 +1,81 @@
+"""A seeded sweep over random shapes, dtypes, value kinds, parameter mixes,
+plan policies and every entry point, each case against the CPU oracle (needs
+an MI355X). Row lengths are drawn from three ranges (short rows, rows held in
+registers, streamed rows), so the cases cross every plan's branch points."""
+
+import numpy as np
+import pytest
+
+from oracle import apply_top_k_top_p as o_apply
+from oracle import apply_top_k_top_p_with_sorted as o_sorted
+from oracle import sample_top_k_top_p as o_sample
+from oracle import sorted_survivors as o_surv
+from tests.gpu_util import gpu_apply, gpu_with_sorted, k_dev, need_gpu, say, to_dev
+from tests.parity import compare, compare_samples, compare_survivors
+from workloads.synth import random_min_p, random_params, random_rows, stable_ascending_sort
+
+pytestmark = pytest.mark.gpu
+
+KINDS = ("normal", "ties", "gumbel", "spikes", "const", "zeros")
+
+
+def _case(rng):
+    dtype = str(rng.choice(["f32", "f16", "bf16"]))
+    band = int(rng.integers(0, 3))
+    V = int([rng.integers(2, 300), rng.integers(300, 20000), rng.integers(20000, 300000)][band])
+    B = int(rng.integers(1, 5))
+    kind = str(rng.choice(KINDS))
+    seed = int(rng.integers(1, 1 << 30))
+    xb = random_rows(seed, B, V, dtype, kind=kind, scale=float(rng.choice([0.5, 2.0, 4.0])))
+    k, p = random_params(seed, B, V, dtype, k_lo=-1, k_hi=min(V + 2, 5000))
+    mp = random_min_p(seed, B, dtype, specials=True) if rng.random() < 0.4 else None
+    pp = p if rng.random() < 0.8 else None
+    kk = k if (pp is None or rng.random() < 0.7) else None
+    return dtype, B, V, kind, seed, xb, kk, pp, mp
+
+
+@pytest.mark.parametrize("sweep_seed", [101, 202])
+def test_random_sweep(sweep_seed):
+    need_gpu()
+    import torch
+    import top_logits_filtering_amd as tk
+
+    rng = np.random.default_rng(sweep_seed)
+    counts = {}
+    try:
+        for _ in range(1500):
+            dtype, B, V, kind, seed, xb, kk, pp, mp = _case(rng)
+            policy = int(rng.choice([0, 0, 0, 1, 2]))
+            tk.set_plan_policy(policy)
+            entry = str(rng.choice(["apply", "sorted", "sample", "survivors"]))
+            tag = (entry, dtype, B, V, kind, seed, policy, pp is not None, kk is not None, mp is not None)
+            if entry == "apply":
+                got = gpu_apply(xb, dtype, pp, kk, mp)
+                rep = compare(got, xb, o_apply(xb, dtype, pp, kk, min_p_bits=mp), dtype)
+                assert rep.hard_mismatches == 0, (tag, rep.details[:2])
+            elif entry == "sorted":
+                idx, sv = stable_ascending_sort(xb, dtype)
+                logits = xb if rng.random() < 0.7 else None
+                got = gpu_with_sorted(sv, idx, dtype, pp, kk, logits, min_p=mp)
+                rep = compare(got, xb, o_sorted(sv, idx, dtype, pp, kk, logits_bits=xb, min_p_bits=mp), dtype)
+                assert rep.hard_mismatches == 0, (tag, rep.details[:2])
+            elif entry == "sample":
+                q = rng.exponential(1.0, size=(B, V)).astype(np.float32) if rng.random() < 0.7 else None
+                sel = tk.sample_top_k_top_p(to_dev(xb, dtype), to_dev(pp, dtype), k_dev(kk), to_dev(mp, dtype),
+                                            None if q is None else torch.from_numpy(q).cuda(), 1e-6)
+                torch.cuda.synchronize()
+                ref = o_sample(xb, dtype, pp, kk, mp, None if q is None else q.astype(np.float64), 1e-6)
+                h, _, det = compare_samples(sel.cpu().numpy(), ref)
+                assert h == 0, (tag, det[:2])
+            else:
+                cap = int(rng.choice([1, 64, 1024]))
+                pr, ix, cnt = tk.top_k_top_p_sorted_survivors(to_dev(xb, dtype), to_dev(pp, dtype), k_dev(kk),
+                                                              to_dev(mp, dtype), cap=cap)
+                torch.cuda.synchronize()
+                h, det = compare_survivors(pr.cpu().numpy().astype(np.float64), ix.cpu().numpy(), cnt.cpu().numpy(),
+                                           o_surv(xb, dtype, pp, kk, mp, cap))
+                assert h == 0, (tag, det[:2])
+            counts[entry] = counts.get(entry, 0) + 1
+    finally:
+        tk.set_plan_policy(0)
+    say(f"random sweep {sweep_seed}: {counts}")

@@ -183,7 +183,7 @@ struct RegTile {
 
   // f(i, x) for every vector slot of this thread, x[] holding the values as
   // fp32 with invalid slots (past the row end) set to -inf.
-  template <class F>
+  template <int kB = 0, class F>  // (kB: the streamed tile's batch size; registers need none)
   __device__ __forceinline__ void for_each_vec_values(F&& f) const {
     const int tid = fresh_tid();
 #pragma unroll
@@ -321,7 +321,8 @@ struct GlobalTile {
     return read(e0);
   }
 
-  template <class F>
+  // kB: vector layers per batch (two batches in flight)
+  template <int kB = kBatch, class F>
   __device__ __forceinline__ void for_each_vec_values(F&& f) const {
     if (vec_ok) {
       // two batches in flight: the next batch is requested before the
@@ -330,16 +331,16 @@ struct GlobalTile {
       const __amdgpu_buffer_rsrc_t rs = row_rsrc(src, len);
       const int tid = static_cast<int>(threadIdx.x);
       const int layers = (len + kSpan - 1) / kSpan;
-      vec_t qa[kBatch], qb[kBatch];
-      auto request = [&](vec_t(&q)[kBatch], int l0) {
+      vec_t qa[kB], qb[kB];
+      auto request = [&](vec_t(&q)[kB], int l0) {
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u)
+        for (int u = 0; u < kB; ++u)
           q[u] = __builtin_amdgcn_raw_buffer_load_b128(
               rs, ((l0 + u) * kSpan + tid * kPV) * static_cast<int>(sizeof(raw_t)), 0, kLoadPolicy);
       };
-      auto consume = [&](const vec_t(&q)[kBatch], int l0) {
+      auto consume = [&](const vec_t(&q)[kB], int l0) {
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
+        for (int u = 0; u < kB; ++u) {
           const int e0 = (l0 + u) * kSpan + tid * kPV;
           if (l0 + u < layers) {  // uniform: the layer exists
             float x[kPV];
@@ -350,11 +351,11 @@ struct GlobalTile {
         }
       };
       request(qa, 0);
-      for (int l0 = 0; l0 < layers; l0 += 2 * kBatch) {
-        request(qb, l0 + kBatch);
+      for (int l0 = 0; l0 < layers; l0 += 2 * kB) {
+        request(qb, l0 + kB);
         consume(qa, l0);
-        request(qa, l0 + 2 * kBatch);
-        consume(qb, l0 + kBatch);
+        request(qa, l0 + 2 * kB);
+        consume(qb, l0 + kB);
       }
       return;
     }

@@ -117,7 +117,7 @@ __device__ __forceinline__ int32_t qsample_pick(const Src& src, uint32_t K, uint
 // Z of step 4 for the survivors' probabilities: the sum of exp(x - m) over
 // the top-k survivors (key >= the k-th largest key), or over the whole row
 // without top-k. `cand` holds every element with key >= lo (all top-k
-// survivors when k is on); `row` is the whole row.
+// survivors when k is on); `row` is the whole row, read from global memory.
 template <class DT, class Cand, class Row>
 __device__ __forceinline__ double survivors_z(const Cand& cand, const Row& row, const RowParams& rp, uint32_t lo,
                                               uint32_t kmax, float m, SelSmem& ss, RowSmem& sm, double* redd) {
@@ -129,9 +129,12 @@ __device__ __forceinline__ double survivors_z(const Cand& cand, const Row& row, 
     cand.for_each([&](auto raw, int) {
       if (DT::key(raw) >= Kk) z += static_cast<double>(__builtin_amdgcn_exp2f((DT::value(raw) - m) * kLog2e));
     });
-  } else {
-    row.for_each([&](auto raw, int) {
-      z += static_cast<double>(__builtin_amdgcn_exp2f((DT::value(raw) - m) * kLog2e));
+  } else {  // the whole row, 4 vector loads in flight (more spill in the fp32 kernels); elements past the row read as -inf
+    row.template for_each_vec_values<2>([&](int, const float (&x)[DT::kPerVec]) {
+      float zv = 0.0f;
+#pragma unroll
+      for (int j = 0; j < DT::kPerVec; ++j) zv += __builtin_amdgcn_exp2f((x[j] - m) * kLog2e);
+      z += static_cast<double>(zv);
     });
   }
   z = wave_sum_f64(z);

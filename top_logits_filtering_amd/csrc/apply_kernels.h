@@ -57,6 +57,10 @@ constexpr int kMaxVecs = 20;
 constexpr int kCandVecCap = 2048;  // candidate vectors kept in shared memory
 constexpr int kStreamVmSlots = 32;  // streamed rows: vector maxima kept for this many layers
 constexpr int kCandPerThread = 5;
+// streamed rows: flags on a listed candidate's start (< 2^20) when its
+// thread kept the vector in shared memory, and in which of its two entries
+constexpr uint32_t kCe0Listed = 0x80000000u;
+constexpr uint32_t kCe0Second = 0x40000000u;
 constexpr int kRegFallbackVecs = 4;  // register tiles of up to this many vectors run the fallback in registers
 constexpr int kCandCap = kCandPerThread * kThreads;  // candidate elements kept in shared memory
 
@@ -396,6 +400,12 @@ __device__ __forceinline__ void filter_row(const Tile& tile, const typename DT::
   // 16-bit upper bounds of each register vector's maximum go to shared
   // memory, two per word, so the compaction below need not revisit the data
   uint32_t vm_even = 0;
+  // streamed rows: the thread's two vectors of largest maximum are kept in
+  // shared memory (candidate list entries 2*tid and 2*tid+1, unused until the
+  // compaction), so the compaction need not fetch them again; they hold most
+  // of a row's candidates. keep_l0/keep_l1: layer held by each entry;
+  // keep_top: the entry holding the largest
+  int keep_l0 = -1, keep_l1 = -1, keep_top = 0;
   tile.for_each_vec_values([&](int i, const float (&x)[kPV]) {
     // the -inf store of this slot goes out as soon as its data is in (the
     // output does not depend on it): stores then drain alongside the loads
@@ -416,6 +426,20 @@ __device__ __forceinline__ void filter_row(const Tile& tile, const typename DT::
       }
     } else {
       if (i < kStreamVmSlots) S.vmh[i][threadIdx.x] = static_cast<uint16_t>(DT::ub16(vm));
+      // the new vector replaces the second largest kept one (lanes past the
+      // row end hold -inf here and are never compacted)
+      if (vm > M2) {
+        vec_t q;
+#pragma unroll
+        for (int j = 0; j < kPV; ++j) set_lane<raw_t>(q, j, DT::raw_of_value(x[j]));
+        const int slot = keep_top ^ 1;
+        S.cvec[2 * threadIdx.x + slot] = q;
+        if (slot == 0)
+          keep_l0 = i;
+        else
+          keep_l1 = i;
+        if (vm > M1) keep_top = slot;
+      }
     }
     M2 = fmaxf(M2, fminf(M1, vm));
     M1 = fmaxf(M1, vm);
@@ -580,7 +604,11 @@ __device__ __forceinline__ void filter_row(const Tile& tile, const typename DT::
       while (mine != 0) {
         const int i = __ffs(mine) - 1;
         mine &= mine - 1;
-        if (pos < static_cast<uint32_t>(kCandVecCap)) S.ce0[pos] = static_cast<uint32_t>(i * Tile::kSpan + tid * kPV);
+        if (pos < static_cast<uint32_t>(kCandVecCap)) {
+          // a kept vector is flagged with its entry, instead of being fetched again
+          const uint32_t kept = i == keep_l0 ? kCe0Listed : i == keep_l1 ? kCe0Listed | kCe0Second : 0u;
+          S.ce0[pos] = static_cast<uint32_t>(i * Tile::kSpan + tid * kPV) | kept;
+        }
         ++pos;
       }
     } else {
@@ -615,11 +643,16 @@ __device__ __forceinline__ void filter_row(const Tile& tile, const typename DT::
         qs[r] = vec_t{0u, 0u, 0u, 0u};
         e0s[r] = V;  // past the row: no element of an unused slot passes
         if (vi < static_cast<int>(nvec)) {
-          e0s[r] = static_cast<int>(S.ce0[vi]);
-          if constexpr (Tile::kRegisters)
+          const uint32_t ce = S.ce0[vi];
+          e0s[r] = static_cast<int>(ce & ~(kCe0Listed | kCe0Second));
+          if constexpr (Tile::kRegisters) {
             qs[r] = S.cvec[vi];
-          else
+          } else if (ce & kCe0Listed) {  // kept by its thread: entry 2*owner (+1)
+            const int owner = (e0s[r] % Tile::kSpan) / kPV;
+            qs[r] = S.cvec[2 * owner + ((ce & kCe0Second) ? 1 : 0)];
+          } else {
             qs[r] = tile.gather(e0s[r]);
+          }
         }
       }
 #pragma unroll

@@ -489,13 +489,14 @@ __device__ __forceinline__ void filter_row(const Tile& tile, const typename DT::
   block_max_f32_min_u32(M1s, klo, sm, m, klo);
   const uint32_t kmax = DT::key(DT::raw_of_value(m));
   uint64_t thr = 0;
+  double z_row = 0.0;  // top-p-only rows: sum of exp(x - m) over the whole row
   if (ponly) {
     const float r = S.run[threadIdx.x];
     const double zt = (r > -INFINITY) ? static_cast<double>(S.acc[threadIdx.x]) *
                                             static_cast<double>(__builtin_amdgcn_exp2f((r - m) * kLog2e))
                                       : 0.0;
-    const double Z = block_sum_f64(zt, S.redd);  // >= 1: the maximum contributes exp(0)
-    thr = topp_threshold(rp.t, static_cast<uint64_t>(Z * 8796093022208.0));  // Z * 2^43
+    z_row = block_sum_f64(zt, S.redd);  // >= 1: the maximum contributes exp(0)
+    thr = topp_threshold(rp.t, static_cast<uint64_t>(z_row * 8796093022208.0));  // Z * 2^43
   }
 
   if constexpr (Tile::kRegisters)
@@ -799,9 +800,10 @@ __device__ __forceinline__ void filter_row(const Tile& tile, const typename DT::
 
   if constexpr (kSample) {
     if (!fallback && wants_survivors(sa)) {  // every survivor is a candidate
-      // (rows without k sum the whole row re-read from global memory: keeping
-      // the register tile live through the ranking below would spill it)
-      const double Z = survivors_z<DT>(cs, gt, rp, L, kmax, m, ss, sm, S.redd);
+      // (top-p-only rows reuse the row sum of step 3; other rows without k
+      // sum the whole row re-read from global memory: keeping the register
+      // tile live through the ranking below would spill it)
+      const double Z = ponly ? z_row : survivors_z<DT>(cs, gt, rp, L, kmax, m, ss, sm, S.redd);
       emit_survivors<DT>(cs, K, I, kmax, m, Z, sa, b, ss, reinterpret_cast<uint64_t*>(S.cel.raw));
     } else if (!fallback) {  // every survivor is a candidate
       int32_t pick;

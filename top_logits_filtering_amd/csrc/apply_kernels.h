@@ -154,10 +154,10 @@ __device__ __forceinline__ double block_sum_f64(double v, double* red) {
 template <class DT, class Tile>
 __device__ __forceinline__ void filter_multipass(const Tile& tile, const RowParams& rp, int V, ApplySmem& S,
                                                  typename DT::raw_t* __restrict__ orow, bool wr, uint32_t& K,
-                                                 uint32_t& I) {
+                                                 uint32_t& I, const RowKnown& known = RowKnown{}) {
   using raw_t = typename DT::raw_t;
   lds_barrier();  // histograms cleared (sel_reset) before the first pass
-  solve_row<DT>(tile, rp, V, S.row, S.sel, K, I);
+  solve_row<DT>(tile, rp, V, S.row, S.sel, K, I, known);
   if (wr) {
     tile.store(orow, [K, I](raw_t r, int idx) {
       const uint32_t key = DT::key(r);
@@ -834,10 +834,10 @@ __device__ __forceinline__ void filter_row(const Tile& tile, const typename DT::
     // short register rows run the multi-pass plan over the registers: each
     // traversal then costs no memory latency (longer rows re-read global
     // memory, which keeps the unrolled code of their kernels small)
-    filter_multipass<DT>(tile, rp, V, S, orow, wr, K, I);
+    filter_multipass<DT>(tile, rp, V, S, orow, wr, K, I, RowKnown{true, m, ponly ? thr : 0});
     if constexpr (kSample) sample_general<DT>(tile, K, I, rp, S, sa, b);
   } else {
-    filter_multipass<DT>(gt, rp, V, S, orow, wr, K, I);
+    filter_multipass<DT>(gt, rp, V, S, orow, wr, K, I, RowKnown{true, m, ponly ? thr : 0});
     if constexpr (kSample) sample_general<DT>(gt, K, I, rp, S, sa, b);
   }
 }

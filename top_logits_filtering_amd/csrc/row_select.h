@@ -451,7 +451,7 @@ __device__ __forceinline__ void top_position(const Src& src, RowSmem& sm, uint32
 // the mass of those elements) is the fixed-point threshold (1 - t) * Z and m
 // the row maximum. Gives (Kp, Ip): survivors are key > Kp, or key == Kp with
 // idx >= Ip.
-template <class DT, class Src>
+template <class DT, bool kWholeRow = false, class Src>
 __device__ __forceinline__ void topp_boundary(const Src& src, uint32_t lo, uint32_t hi, float m, uint64_t thr,
                                               int V, SelSmem& ss, uint32_t& Kp, uint32_t& Ip) {
   uint64_t acc = 0;  // mass strictly above the current range
@@ -459,17 +459,24 @@ __device__ __forceinline__ void topp_boundary(const Src& src, uint32_t lo, uint3
   uint64_t bmass = 0;
   for (;;) {
     const int shift = shift_for_range(hi - lo);
+    // The keys present in each bin narrow the next pass, and end the search
+    // when the picked bin holds one key. Passes over a whole row of 16-bit
+    // keys skip that: a bin then spans at most 64 keys, which the next pass
+    // resolves exactly either way, and two atomics per element are saved
+    // (candidate lists hold a few elements per thread, where the pass that
+    // a one-key bin saves is worth more).
+    const bool ranges = shift != 0 && (DT::kKeyBits == 32 || !kWholeRow);
     src.for_each([&](auto raw, int) {
       const uint32_t key = DT::key(raw);
       if (key >= lo && key <= hi) {
         const uint32_t bin = (key - lo) >> shift;
         atomicAdd(&ss.mass[bin], mass_fx(DT::value(raw), m));
         atomicAdd(&ss.cnt[bin], 1u);
-        if (shift != 0) sel_note_key(ss, bin, key);
+        if (ranges) sel_note_key(ss, bin, key);
       }
     });
     lds_barrier();
-    if (shift == 0)
+    if (!ranges)
       sel_pick_mass(ss, thr - acc);
     else
       sel_pick_mass<false, true>(ss, thr - acc);
@@ -480,10 +487,10 @@ __device__ __forceinline__ void topp_boundary(const Src& src, uint32_t lo, uint3
       lo += static_cast<uint32_t>(ss.bin);
       break;
     }
-    if (cnt != 0) {  // the keys present in the bin (it holds the boundary)
+    if (ranges && cnt != 0) {  // the keys present in the bin (it holds the boundary)
       lo = ss.bkmin;
       hi = ss.bkmax;
-    } else {  // not reached with 1 <= thr <= the range's mass: the bin's whole span
+    } else {  // the bin's whole span
       lo += static_cast<uint32_t>(ss.bin) << shift;
       hi = (hi - lo > (1u << shift) - 1u) ? lo + ((1u << shift) - 1u) : hi;
     }
@@ -541,9 +548,17 @@ __device__ __forceinline__ void combine_min_p(uint32_t Kmp, uint32_t& K, uint32_
 
 // Full threshold pair (K, I) of a row, every statistic computed from `src`,
 // which holds all V elements of the row.
+// What a caller already knows of a row: its maximum (m_ok), and for rows with
+// top-p but no top-k the top-p threshold in 2^-43 units (thr != 0).
+struct RowKnown {
+  bool m_ok = false;
+  float m = 0.0f;
+  uint64_t thr = 0;
+};
+
 template <class DT, class Src>
 __device__ __forceinline__ void solve_row_kp(const Src& src, const RowParams& rp, int V, RowSmem& sm, SelSmem& ss,
-                                             uint32_t& K, uint32_t& I) {
+                                             uint32_t& K, uint32_t& I, const RowKnown& known) {
   K = 0;
   I = 0;
   if (!rp.k_on && rp.pmode == kPNone) return;
@@ -561,30 +576,40 @@ __device__ __forceinline__ void solve_row_kp(const Src& src, const RowParams& rp
     top_position<DT>(src, sm, K, I);
     return;
   }
-  float mloc = -INFINITY;
-  src.for_each([&](auto raw, int) { mloc = fmaxf(mloc, DT::value(raw)); });
-  const float m = block_max_f32(mloc, sm);
-  uint64_t zloc = 0;
-  src.for_each([&](auto raw, int) {
-    if (DT::key(raw) >= Kk) zloc += mass_fx(DT::value(raw), m);
-  });
-  const uint64_t Z = block_sum_u64(zloc, sm);
-  const uint64_t thr = topp_threshold(rp.t, Z);
+  float m;
+  uint64_t thr;
+  if (known.thr != 0 && !rp.k_on) {  // the row maximum and threshold were formed already
+    m = known.m;
+    thr = known.thr;
+  } else {
+    float mloc = -INFINITY;
+    src.for_each([&](auto raw, int) { mloc = fmaxf(mloc, DT::value(raw)); });
+    m = block_max_f32(mloc, sm);
+    uint64_t zloc = 0;
+    src.for_each([&](auto raw, int) {
+      if (DT::key(raw) >= Kk) zloc += mass_fx(DT::value(raw), m);
+    });
+    const uint64_t Z = block_sum_u64(zloc, sm);
+    thr = topp_threshold(rp.t, Z);
+  }
   if (thr == 0) {
     top_position<DT>(src, sm, K, I);
     return;
   }
-  topp_boundary<DT>(src, Kk, kKeyMax, m, thr, V, ss, K, I);
+  topp_boundary<DT, true>(src, Kk, kKeyMax, m, thr, V, ss, K, I);
 }
 
 template <class DT, class Src>
 __device__ __forceinline__ void solve_row(const Src& src, const RowParams& rp, int V, RowSmem& sm, SelSmem& ss,
-                                          uint32_t& K, uint32_t& I) {
-  solve_row_kp<DT>(src, rp, V, sm, ss, K, I);
+                                          uint32_t& K, uint32_t& I, const RowKnown& known = RowKnown{}) {
+  solve_row_kp<DT>(src, rp, V, sm, ss, K, I, known);
   if (rp.mp_on) {
-    float mloc = -INFINITY;
-    src.for_each([&](auto raw, int) { mloc = fmaxf(mloc, DT::value(raw)); });
-    const float m = block_max_f32(mloc, sm);
+    float m = known.m;
+    if (!known.m_ok) {
+      float mloc = -INFINITY;
+      src.for_each([&](auto raw, int) { mloc = fmaxf(mloc, DT::value(raw)); });
+      m = block_max_f32(mloc, sm);
+    }
     combine_min_p(min_p_key<DT>(src, m, rp.minp, sm), K, I);
   }
 }

@@ -888,6 +888,38 @@ void launch_regs(const void* logits, const void* p, const int32_t* k, const void
                      use_candidates, sa);
 }
 
+// The argmax of streamed rows when neither the filtered row, q nor the
+// survivors are asked for: the row maximum survives every stage, so the pick
+// is the top position of the stable order (the highest index holding the
+// maximum; -0 and +0 tie). Only a block reduction is kept in shared memory,
+// so two blocks share a compute unit and one row's loads overlap another's
+// reductions.
+template <class DT>
+__global__ __launch_bounds__(kThreads, 2) void argmax_stream_kernel(const typename DT::raw_t* __restrict__ logits,
+                                                                     int V, int64_t ld_x, int32_t* __restrict__ sel) {
+  __shared__ RowSmem sm;
+  constexpr int kPV = DT::kPerVec;
+  const int b = blockIdx.x;
+  GlobalTile<DT> gt;
+  gt.load(logits + static_cast<size_t>(b) * static_cast<size_t>(ld_x), 0, V);
+  float best = -INFINITY;
+  int bidx = -1;  // a thread's elements come in ascending index order: ">=" keeps the last maximum
+  gt.template for_each_vec_values<4>([&](int i, const float (&x)[kPV]) {
+    const int e0 = i * GlobalTile<DT>::kSpan + static_cast<int>(threadIdx.x) * kPV;
+#pragma unroll
+    for (int j = 0; j < kPV; ++j) {
+      if (x[j] >= best && x[j] > -INFINITY) {
+        best = x[j];
+        bidx = e0 + j;
+      }
+    }
+  });
+  const float mrow = block_max_f32(best, sm);
+  const int idx = (bidx >= 0 && best == mrow) ? bidx : -1;
+  const int top = static_cast<int>(block_max_u32(static_cast<uint32_t>(idx + 1), sm)) - 1;
+  if (threadIdx.x == 0) sel[b] = top < 0 ? 0 : top;
+}
+
 // kSample: the sampling stage (sa), and out may be NULL; otherwise sa is unused.
 template <class DT, bool kSample = false>
 hipError_t launch_apply_t(const void* logits, const void* p, const int32_t* k, const void* min_p, void* out,
@@ -906,6 +938,14 @@ hipError_t launch_apply_t(const void* logits, const void* p, const int32_t* k, c
   // (20 would spill in fp16); longer rows are streamed
   constexpr int64_t max_vecs = kSample ? 19 : kMaxVecs;
   if (policy != kPlanAuto || vecs > max_vecs || !vec_ok) {
+    if constexpr (kSample) {
+      if (sa.q == nullptr && out == nullptr && sa.indices == nullptr) {
+        if (sa.sel != nullptr)
+          hipLaunchKernelGGL((argmax_stream_kernel<DT>), dim3(static_cast<unsigned>(B)), dim3(kThreads), 0, stream,
+                             static_cast<const raw_t*>(logits), static_cast<int>(V), ld.x, sa.sel);
+        return hipGetLastError();
+      }
+    }
     hipLaunchKernelGGL((apply_stream_kernel<DT, kSample>), dim3(static_cast<unsigned>(B)), dim3(kThreads), 0, stream,
                        static_cast<const raw_t*>(logits), static_cast<const raw_t*>(p), k,
                        static_cast<const raw_t*>(min_p), static_cast<raw_t*>(out), static_cast<int>(V), ld,

@@ -68,6 +68,20 @@ def gpu_with_sorted(sv, si, dtype, p=None, k=None, logits=None, min_p=None):
     return from_dev(out, dtype)
 
 
+# NaN patterns the filter never writes: they mark padding that must stay untouched
+SENTINEL = {"f32": 0x7FC00001, "f16": 0x7E01, "bf16": 0x7FC1}
+
+
+def padded_dev(bits, dtype, ld, fill):
+    """A [B, ld] device buffer holding bits in its first V columns (fill in
+    the rest), and its [B, V] row-strided view."""
+    B, V = bits.shape
+    full = np.full((B, ld), fill, dtype=bits.dtype)
+    full[:, :V] = bits
+    t = to_dev(full, dtype)
+    return t, t[:, :V]
+
+
 def say(*a):
     print(*a, flush=True)
     sys.stdout.flush()

@@ -33,16 +33,27 @@ class ParityReport:
     band_positions: int = 0
     band_mismatches: int = 0
     hard_mismatches: int = 0
+    # the same split by stage: top-p band and min-p band (a position may be in both)
+    band_positions_p: int = 0
+    band_mismatches_p: int = 0
+    band_positions_m: int = 0
+    band_mismatches_m: int = 0
     details: list = field(default_factory=list)
 
+    COUNTS = ("rows", "positions", "band_positions", "band_mismatches", "hard_mismatches", "band_positions_p",
+              "band_mismatches_p", "band_positions_m", "band_mismatches_m")
+
     def merge(self, other: "ParityReport"):
-        self.rows += other.rows
-        self.positions += other.positions
-        self.band_positions += other.band_positions
-        self.band_mismatches += other.band_mismatches
-        self.hard_mismatches += other.hard_mismatches
+        for name in self.COUNTS:
+            setattr(self, name, getattr(self, name) + getattr(other, name))
         self.details.extend(other.details)
         return self
+
+    def summary(self) -> dict:
+        """The counts as a dict, with the first few mismatch details."""
+        d = {name: getattr(self, name) for name in self.COUNTS}
+        d["details"] = self.details[:3]
+        return d
 
     def __str__(self):
         return (f"rows={self.rows} positions={self.positions} band={self.band_positions} "
@@ -74,6 +85,9 @@ def compare_row(g_row, x_row, trace, dtype, tol=BAND_TOL, row_id=None) -> Parity
     if trace.min_p_ratio is not None:
         band_m = np.abs(trace.min_p_ratio - 1.0) <= tol
         band_m[V - 1] = False
+    # top-k decisions are exact: a position top-k masks is never a band position
+    band_p &= ~trace.top_k_mask
+    band_m &= ~trace.top_k_mask
     band = band_p | band_m
     ambiguous_val = xs == neg  # input already -inf: kept and masked look the same
     # a stage forces a mask where it masks outside its band, and allows a keep
@@ -94,7 +108,12 @@ def compare_row(g_row, x_row, trace, dtype, tol=BAND_TOL, row_id=None) -> Parity
     rep.hard_mismatches = n_bad
     rep.band_positions = int(band.sum())
     g_masked = is_neg & ~ambiguous_val
-    rep.band_mismatches = int((band & (g_masked != (o_masked & ~ambiguous_val))).sum())
+    differs = g_masked != (o_masked & ~ambiguous_val)
+    rep.band_mismatches = int((band & differs).sum())
+    rep.band_positions_p = int(band_p.sum())
+    rep.band_mismatches_p = int((band_p & differs).sum())
+    rep.band_positions_m = int(band_m.sum())
+    rep.band_mismatches_m = int((band_m & differs).sum())
     if n_bad:
         js = np.nonzero(bad)[0][:5]
         rep.details.append(dict(row=row_id, sorted_positions=js.tolist(), orig=perm[js].tolist(),

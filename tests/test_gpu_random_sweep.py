@@ -1,7 +1,10 @@
 """A seeded sweep over random shapes, dtypes, value kinds, parameter mixes,
 plan policies and every entry point, each case against the CPU oracle (needs
 an MI355X). Row lengths are drawn from three ranges (short rows, rows held in
-registers, streamed rows), so the cases cross every plan's branch points."""
+registers, streamed rows), so the cases cross every plan's branch points.
+About a third of the filter cases pass row-strided views (each operand in a
+buffer padded by 1-70 elements per row, so most row strides are not a
+multiple of 16 bytes), and the padding must stay untouched."""
 
 import numpy as np
 import pytest
@@ -10,7 +13,7 @@ from oracle import apply_top_k_top_p as o_apply
 from oracle import apply_top_k_top_p_with_sorted as o_sorted
 from oracle import sample_top_k_top_p as o_sample
 from oracle import sorted_survivors as o_surv
-from tests.gpu_util import gpu_apply, gpu_with_sorted, k_dev, need_gpu, say, to_dev
+from tests.gpu_util import SENTINEL, from_dev, gpu_apply, gpu_with_sorted, k_dev, need_gpu, padded_dev, say, to_dev
 from tests.parity import compare, compare_samples, compare_survivors
 from workloads.synth import random_min_p, random_params, random_rows, stable_ascending_sort
 
@@ -34,6 +37,41 @@ def _case(rng):
     return dtype, B, V, kind, seed, xb, kk, pp, mp
 
 
+def strided_apply(xb, dtype, p, k, mp, pads):
+    """The filter on row-strided views of padded buffers; returns the [B, V]
+    result after checking that the padding is untouched."""
+    import torch
+    import top_logits_filtering_amd as tk
+
+    B, V = xb.shape
+    _, xv = padded_dev(xb, dtype, V + pads[0], SENTINEL[dtype])
+    obuf, ov = padded_dev(np.zeros_like(xb), dtype, V + pads[1], SENTINEL[dtype])
+    tk.apply_top_k_top_p(xv, to_dev(p, dtype), k_dev(k), out=ov, min_p=to_dev(mp, dtype))
+    torch.cuda.synchronize()
+    got = from_dev(obuf, dtype)
+    assert (got[:, V:] == SENTINEL[dtype]).all(), "padding was written"
+    return np.ascontiguousarray(got[:, :V])
+
+
+def strided_sorted(sv, idx, dtype, p, k, logits, mp, pads):
+    """The pre-sorted entry on row-strided views of padded buffers."""
+    import torch
+    import top_logits_filtering_amd as tk
+
+    B, V = sv.shape
+    _, svv = padded_dev(sv, dtype, V + pads[0], SENTINEL[dtype])
+    ibuf = torch.from_numpy(np.full((B, V + pads[1]), -7, np.int32)).cuda()
+    ibuf[:, :V] = k_dev(idx)
+    xv = None if logits is None else padded_dev(logits, dtype, V + pads[2], SENTINEL[dtype])[1]
+    obuf, ov = padded_dev(np.zeros_like(sv), dtype, V + pads[3], SENTINEL[dtype])
+    tk.apply_top_k_top_p_with_sorted(svv, ibuf[:, :V], to_dev(p, dtype), k_dev(k), xv, out=ov,
+                                     min_p=to_dev(mp, dtype))
+    torch.cuda.synchronize()
+    got = from_dev(obuf, dtype)
+    assert (got[:, V:] == SENTINEL[dtype]).all(), "padding was written"
+    return np.ascontiguousarray(got[:, :V])
+
+
 @pytest.mark.parametrize("sweep_seed", [101, 202])
 def test_random_sweep(sweep_seed):
     need_gpu()
@@ -49,14 +87,23 @@ def test_random_sweep(sweep_seed):
             tk.set_plan_policy(policy)
             entry = str(rng.choice(["apply", "sorted", "sample", "survivors"]))
             tag = (entry, dtype, B, V, kind, seed, policy, pp is not None, kk is not None, mp is not None)
+            strided = entry in ("apply", "sorted") and rng.random() < 0.35
+            pads = [int(v) for v in rng.integers(1, 71, size=4)] if strided else None
+            tag = tag + (pads,)
             if entry == "apply":
-                got = gpu_apply(xb, dtype, pp, kk, mp)
+                if strided:
+                    got = strided_apply(xb, dtype, pp, kk, mp, pads)
+                else:
+                    got = gpu_apply(xb, dtype, pp, kk, mp)
                 rep = compare(got, xb, o_apply(xb, dtype, pp, kk, min_p_bits=mp), dtype)
                 assert rep.hard_mismatches == 0, (tag, rep.details[:2])
             elif entry == "sorted":
                 idx, sv = stable_ascending_sort(xb, dtype)
                 logits = xb if rng.random() < 0.7 else None
-                got = gpu_with_sorted(sv, idx, dtype, pp, kk, logits, min_p=mp)
+                if strided:
+                    got = strided_sorted(sv, idx, dtype, pp, kk, logits, mp, pads)
+                else:
+                    got = gpu_with_sorted(sv, idx, dtype, pp, kk, logits, min_p=mp)
                 rep = compare(got, xb, o_sorted(sv, idx, dtype, pp, kk, logits_bits=xb, min_p_bits=mp), dtype)
                 assert rep.hard_mismatches == 0, (tag, rep.details[:2])
             elif entry == "sample":

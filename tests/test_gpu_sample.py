@@ -5,7 +5,6 @@ processing" of Ascend's aclnnTopKTopPSampleV2 page)."""
 import numpy as np
 import pytest
 
-from oracle import apply_top_k_top_p as oracle_apply
 from oracle import sample_top_k_top_p as oracle_sample
 from tests.golden_io import load_hand_cases
 from tests.gpu_util import from_dev, k_dev, need_gpu, say, to_dev
@@ -114,15 +113,3 @@ def test_sample_large_survivor_sets(policy):
     assert np.array_equal(none, oracle_sample(xb, dtype, p, None, None, None).selected)
 
 
-def test_sample_workload3_sampled(policy):
-    """The timed shape with QSample and min-p, sampled rows against the oracle."""
-    wl = make_workload(3)
-    mp = f32_to_bits(np.full(wl.B, 0.05, np.float32), wl.dtype)
-    q = _q(99, wl.B, wl.V)
-    got, _ = gpu_sample(wl.logits, wl.dtype, wl.p, wl.k, mp, q, 1e-6)
-    rows = np.array([0, 1, 2, 3, 4, 5, 128, 129, 130, wl.B - 1])
-    ref = oracle_sample(wl.logits[rows], wl.dtype, wl.p[rows], wl.k[rows], mp[rows], q[rows].astype(np.float64), 1e-6)
-    h, s_, det = compare_samples(got[rows], ref)
-    say(f"workload 3 sampled ({policy}): near-tie picks {s_}")
-    assert h == 0, det[:3]
-    assert (got >= 0).all() and (got < wl.V).all()

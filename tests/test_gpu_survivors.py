@@ -8,7 +8,7 @@ from oracle import sorted_survivors as oracle_survivors
 from tests.golden_io import load_hand_cases
 from tests.gpu_util import k_dev, need_gpu, say, to_dev
 from tests.parity import compare_survivors
-from workloads.synth import f32_to_bits, make_workload, random_min_p, random_params, random_rows
+from workloads.synth import random_min_p, random_params, random_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -62,13 +62,3 @@ def test_survivors_random_rows(dtype, policy):
     say(f"survivors {dtype}/{policy}: ok")
 
 
-def test_survivors_indices_only_and_workload3(policy):
-    """The timed shape; indices without probabilities match those with them."""
-    wl = make_workload(3)
-    pr, idx, cnt = gpu_survivors(wl.logits, wl.dtype, wl.p, wl.k, None, 1024)
-    _, idx2, cnt2 = gpu_survivors(wl.logits, wl.dtype, wl.p, wl.k, None, 1024, with_probs=False)
-    assert np.array_equal(idx, idx2) and np.array_equal(cnt, cnt2)
-    rows = np.array([0, 1, 2, 3, 4, 5, 200, 201, 202, wl.B - 1])
-    ref = oracle_survivors(wl.logits[rows], wl.dtype, wl.p[rows], wl.k[rows], None, 1024)
-    h, det = compare_survivors(pr[rows], idx[rows], cnt[rows], ref)
-    assert h == 0, det[:3]

@@ -102,3 +102,29 @@ def test_top_p_band_position_with_min_p():
     far = int(np.nonzero(tr.top_p_mask & ~band)[0][-1])
     g[0, tr.sorted_indices[far]] = xb[0, tr.sorted_indices[far]]
     assert compare(g, xb, ref, dtype).hard_mismatches >= 1
+
+
+def test_worker_pool_on_oracle_outputs(tmp_path):
+    """The whole-batch harness (tests/parity_pool.py) on the CPU: the
+    oracle's own outputs for workloads 1 and 2 pass on every row, and a
+    survivor dropped from one row is caught in that row."""
+    from tests.parity_pool import run_batch
+    from workloads.synth import make_workload
+
+    for c, rows_per_job in ((1, 1), (2, 16)):
+        wl = make_workload(c)
+        ref = apply_top_k_top_p(wl.logits, wl.dtype, wl.p, wl.k, keep_traces=False).out
+        good = str(tmp_path / f"good{c}.npy")
+        np.save(good, ref)
+        bad_out = ref.copy()
+        b = wl.B - 1
+        top = int(np.nonzero(bad_out[b] != NEG_INF_WORD[wl.dtype])[0][-1])
+        bad_out[b, top] = NEG_INF_WORD[wl.dtype]
+        bad = str(tmp_path / f"bad{c}.npy")
+        np.save(bad, bad_out)
+        res = run_batch(dict(kind="apply", config=c, outs={"good": good, "bad": bad}, r5=(c == 2)), wl.B,
+                        rows_per_job)
+        assert res["good"]["rows"] == wl.B and res["good"]["hard_mismatches"] == 0
+        assert res["bad"]["hard_mismatches"] >= 1 and res["bad"]["details"][0]["row"] == b
+        if c == 2:
+            assert 0 <= res["r5_rows_changed"] <= wl.B

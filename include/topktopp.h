@@ -71,6 +71,10 @@ typedef enum {
  * operator, aclnnTopKTopPSampleV2, states for its vocabulary size). */
 #define TOPKTOPP_MAX_V (1 << 20)
 
+/* Largest supported number of rows, 2^31 - 1. Batches of more than 2^21
+ * rows are launched in row chunks. */
+#define TOPKTOPP_MAX_B 0x7FFFFFFFLL
+
 /* Largest row stride accepted by the _ex entry points, in elements (2^31). */
 #define TOPKTOPP_MAX_LD (1LL << 31)
 
@@ -83,13 +87,14 @@ typedef enum {
  *   dtype   one of topktopp_dtype.
  *   B, V    rows and row length; B == 0 or V == 0 is a successful no-op
  *           (every pointer may then be NULL; only dtype is checked);
- *           V == 1 copies logits to out (AKP §6.1); V <= TOPKTOPP_MAX_V.
+ *           V == 1 copies logits to out (AKP §6.1); V <= TOPKTOPP_MAX_V,
+ *           B <= TOPKTOPP_MAX_B.
  *   p       [B] device buffer of `dtype` values, or NULL for no top-p.
  *   k       [B] device buffer of int32, or NULL for no top-k.
  *   out     [B, V] device buffer of `dtype`, written completely.
  *   stream  hipStream_t to enqueue on, or NULL.
  */
-topktopp_status apply_top_k_top_p(const void* logits, int dtype, int64_t B, int64_t V,
+topktopp_status apply_top_k_top_p(const void* logits, topktopp_dtype dtype, int64_t B, int64_t V,
                                   const void* p, const int32_t* k, void* out, void* stream);
 
 /*
@@ -109,7 +114,7 @@ topktopp_status apply_top_k_top_p(const void* logits, int dtype, int64_t B, int6
  * Sortedness and the permutation are the caller's contract and are not checked.
  */
 topktopp_status apply_top_k_top_p_with_sorted(const void* sorted_value, const int32_t* sorted_indices,
-                                              int dtype, int64_t B, int64_t V, const void* p,
+                                              topktopp_dtype dtype, int64_t B, int64_t V, const void* p,
                                               const int32_t* k, const void* logits, void* out,
                                               void* stream);
 
@@ -135,7 +140,7 @@ topktopp_status apply_top_k_top_p_with_sorted(const void* sorted_value, const in
  * ratio lies within a relative 1e-5 of min_p[b] can be decided differently
  * from an exact evaluation.
  */
-topktopp_status apply_top_k_top_p_min_p(const void* logits, int dtype, int64_t B, int64_t V,
+topktopp_status apply_top_k_top_p_min_p(const void* logits, topktopp_dtype dtype, int64_t B, int64_t V,
                                         const void* p, const int32_t* k, const void* min_p, void* out,
                                         void* stream);
 
@@ -147,7 +152,7 @@ topktopp_status apply_top_k_top_p_min_p(const void* logits, int dtype, int64_t B
  *           NULL, but not all three.
  */
 topktopp_status apply_top_k_top_p_min_p_with_sorted(const void* sorted_value, const int32_t* sorted_indices,
-                                                    int dtype, int64_t B, int64_t V, const void* p,
+                                                    topktopp_dtype dtype, int64_t B, int64_t V, const void* p,
                                                     const int32_t* k, const void* min_p, const void* logits,
                                                     void* out, void* stream);
 
@@ -161,7 +166,7 @@ topktopp_status apply_top_k_top_p_min_p_with_sorted(const void* sorted_value, co
  * inputs must not overlap. Positions between V and the stride are neither
  * read nor written. Other arguments as for apply_top_k_top_p_min_p.
  */
-topktopp_status apply_top_k_top_p_ex(const void* logits, int64_t ld_logits, int dtype, int64_t B, int64_t V,
+topktopp_status apply_top_k_top_p_ex(const void* logits, int64_t ld_logits, topktopp_dtype dtype, int64_t B, int64_t V,
                                      const void* p, const int32_t* k, const void* min_p, void* out,
                                      int64_t ld_out, void* stream);
 
@@ -172,7 +177,7 @@ topktopp_status apply_top_k_top_p_ex(const void* logits, int64_t ld_logits, int 
  */
 topktopp_status apply_top_k_top_p_with_sorted_ex(const void* sorted_value, int64_t ld_sorted_value,
                                                  const int32_t* sorted_indices, int64_t ld_sorted_indices,
-                                                 int dtype, int64_t B, int64_t V, const void* p,
+                                                 topktopp_dtype dtype, int64_t B, int64_t V, const void* p,
                                                  const int32_t* k, const void* min_p, const void* logits,
                                                  int64_t ld_logits, void* out, int64_t ld_out, void* stream);
 
@@ -196,14 +201,13 @@ topktopp_status apply_top_k_top_p_with_sorted_ex(const void* sorted_value, int64
  *   eps      added to q; finite and >= 0 (the pages give it no value).
  *   out      [B, V] device buffer for the filtered logits, or NULL to skip
  *            them (then the row is only read, not written).
- *   selected [B] int32 device buffer, written completely. In QSample a row
- *            whose survivors exceed 5120 positions outside the candidate plan
- *            (the ranking's shared-memory capacity) gets -1.
+ *   selected [B] int32 device buffer, written completely, with an index in
+ *            [0, V) for every row, whatever its number of survivors.
  * Errors as for apply_top_k_top_p_min_p; selected NULL is ERR_NULLPTR, a
  * negative or non-finite eps ERR_INVALID, and out or selected overlapping
  * another buffer ERR_INVALID.
  */
-topktopp_status sample_top_k_top_p(const void* logits, int dtype, int64_t B, int64_t V, const void* p,
+topktopp_status sample_top_k_top_p(const void* logits, topktopp_dtype dtype, int64_t B, int64_t V, const void* p,
                                    const int32_t* k, const void* min_p, const float* q, float eps, void* out,
                                    int32_t* selected, void* stream);
 
@@ -223,12 +227,11 @@ topktopp_status sample_top_k_top_p(const void* logits, int dtype, int64_t B, int
  *   probs   [B, cap] fp32 device buffer, or NULL.
  *   indices [B, cap] int32 device buffer.
  *   counts  [B] int32 device buffer.
- * Rows with more than 5120 survivors outside the candidate plan (the
- * ranking's shared-memory capacity) report counts[b] and no entries.
+ * Every row lists min(n_b, cap) survivors, whatever n_b is (up to V).
  * Errors as for apply_top_k_top_p_min_p; outputs may not overlap inputs or
  * each other (ERR_INVALID).
  */
-topktopp_status top_k_top_p_sorted_survivors(const void* logits, int dtype, int64_t B, int64_t V, const void* p,
+topktopp_status top_k_top_p_sorted_survivors(const void* logits, topktopp_dtype dtype, int64_t B, int64_t V, const void* p,
                                              const int32_t* k, const void* min_p, int64_t cap, float* probs,
                                              int32_t* indices, int32_t* counts, void* stream);
 

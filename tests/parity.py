@@ -131,37 +131,18 @@ def compare(g, x_bits, oracle_result, dtype, tol=BAND_TOL, row_ids=None) -> Pari
     return rep
 
 
-# QSample ranks at most this many survivors per row on the GPU; a row with
-# more may be reported as -1 there.
-RANK_CAPACITY = 5120
-
-
 def compare_samples(g_sel, sample_result, tol=BAND_TOL):
     """Sampling rule: per row the GPU's pick equals the oracle's, unless the
     row is a near tie: the GPU's pick must then be an oracle survivor or a
     band position of top-p or min-p (kept or masked on the GPU within the
     tolerance), and its score (probability over q + eps, at its descending
     rank) must be within a relative ``tol`` of the best oracle survivor's.
-    A QSample pick of -1 is accepted only for a row that may have more than
-    RANK_CAPACITY survivors (its oracle survivors plus its band positions).
     Returns (hard mismatches, near-tie mismatches, details)."""
     hard, soft, details = 0, 0, []
     for b, (o, tr) in enumerate(zip(sample_result.selected, sample_result.filtered.traces)):
         g = int(g_sel[b])
         if g == int(o):
             continue
-        if g == -1 and sample_result.scores[b] is not None:
-            masked = tr.top_k_mask | tr.top_p_mask
-            if tr.min_p_mask is not None:
-                masked = masked | tr.min_p_mask
-            V = len(tr.sorted_indices)
-            band = np.zeros(V, dtype=bool)
-            if tr.probs_sum32 is not None and tr.t is not None:
-                band |= np.abs(tr.probs_sum32.astype(np.float64) - np.float64(tr.t)) <= tol
-            if tr.min_p_ratio is not None:
-                band |= np.abs(tr.min_p_ratio - 1.0) <= tol
-            if int((~masked | (band & ~tr.top_k_mask)).sum()) > RANK_CAPACITY:
-                continue
         sc = sample_result.scores[b]
         raw = sample_result.raw_scores[b]
         ok = False
@@ -194,8 +175,7 @@ def compare_survivors(g_probs, g_idx, g_cnt, surv_result, tol=BAND_TOL):
         of top-p / min-p (which sit at the low end of the order);
       * ranks below both counts (and the capacity) hold the same original
         index, and probabilities within a relative ``tol`` (plus 1e-30);
-      * ranks past the GPU's count hold -1 and 0;
-      * a row with more than RANK_CAPACITY survivors may hold no entries.
+      * ranks past the GPU's count hold -1 and 0.
     Returns (hard mismatches, details)."""
     hard, details = 0, []
     cap = g_idx.shape[1]
@@ -214,14 +194,11 @@ def compare_survivors(g_probs, g_idx, g_cnt, surv_result, tol=BAND_TOL):
         nband = int(band.sum())
         bad = abs(n_o - n_g) > nband
         listed = min(n_g, cap)
-        if n_g > RANK_CAPACITY and (g_idx[b] == -1).all():
-            listed = 0  # beyond the ranking capacity: the count only
-        else:
-            m = min(n_o, n_g, cap)
-            bad |= not np.array_equal(g_idx[b, :m], surv_result.indices[b, :m])
-            if g_probs is not None:
-                o = surv_result.probs[b, :m]
-                bad |= not np.all(np.abs(g_probs[b, :m] - o) <= tol * o + 1e-30)
+        m = min(n_o, n_g, cap)
+        bad |= not np.array_equal(g_idx[b, :m], surv_result.indices[b, :m])
+        if g_probs is not None:
+            o = surv_result.probs[b, :m]
+            bad |= not np.all(np.abs(g_probs[b, :m] - o) <= tol * o + 1e-30)
         bad |= not (g_idx[b, listed:] == -1).all()
         if g_probs is not None:
             bad |= not (g_probs[b, listed:] == 0).all()

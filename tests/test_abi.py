@@ -76,6 +76,14 @@ def test_invalid_dtype_and_shape(lib):
     assert f(FAKE, 0, 2, -8, FAKE, None, out, None) == INVALID
     assert f(FAKE, 2, 2, (1 << 20) + 1, FAKE, None, out, None) == INVALID
     assert "maximum" in tk.last_error()
+    assert f(FAKE, 0, 1 << 31, 8, FAKE, None, out, None) == INVALID  # more rows than 2^31 - 1
+    assert "rows" in tk.last_error()
+    g = lib.apply_top_k_top_p_with_sorted
+    assert g(FAKE, FAKE, 0, 1 << 31, 8, FAKE, None, None, out, None) == INVALID
+    h = lib.sample_top_k_top_p
+    assert h(FAKE, 0, 1 << 31, 8, None, None, None, None, 0.0, None, out, None) == INVALID
+    s = lib.top_k_top_p_sorted_survivors
+    assert s(FAKE, 0, 1 << 31, 8, None, None, None, 4, None, out, out + (1 << 20), None) == INVALID
 
 
 def test_overlap_rejected(lib):

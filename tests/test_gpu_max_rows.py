@@ -107,3 +107,50 @@ def test_many_short_rows():
     got_s = gpu_with_sorted(sv, idx, dtype, p[:20000], k[:20000], xb[:20000])
     assert np.array_equal(got_s, got[:20000]), "pre-sorted entry differs from the sorting entry"
     say(f"{B} rows of {V}: {rep}")
+
+
+def test_rows_beyond_one_launch():
+    """2^21 + 3 rows of two values: one launch takes at most 2^21 rows, so
+    the batch is launched in two chunks. Every row is checked against the
+    result the filter must give for k = 1 (the maximum and its ties), on the
+    sorting entry, the pre-sorted entry, both sampling modes and the sorted
+    survivors; rows around the chunk boundary also against the oracle."""
+    torch = need_gpu()
+    import top_logits_filtering_amd as tk
+
+    dtype, B, V = "f32", (1 << 21) + 3, 2
+    rng = np.random.default_rng(2500)
+    vals = np.round(rng.normal(0.0, 2.0, size=(B, V)), 1).astype(np.float32)  # some rows tie
+    xb = vals.view(np.uint32)
+    k = np.ones(B, np.int32)
+    p = f32_to_bits(np.full(B, 0.5, np.float32), dtype)
+    mx = vals.max(axis=1, keepdims=True)
+    keep = vals == mx
+    expect = np.where(keep, xb, np.uint32(0xFF800000))
+    top = np.where(keep[:, 1], 1, 0)  # the maximum with the highest index
+    got = gpu_apply(xb, dtype, None, k)
+    assert np.array_equal(got, expect)
+    rows = np.array([0, (1 << 21) - 2, (1 << 21) - 1, 1 << 21, (1 << 21) + 1, B - 1])
+    rep = compare(got[rows], xb[rows], oracle_apply(xb[rows], dtype, p[rows], k[rows]), dtype)
+    assert rep.hard_mismatches == 0, rep.details
+    got_pk = gpu_apply(xb, dtype, p, k)
+    rep = compare(got_pk[rows], xb[rows], oracle_apply(xb[rows], dtype, p[rows], k[rows]), dtype)
+    assert rep.hard_mismatches == 0, rep.details
+    idx, sv = stable_ascending_sort(xb, dtype)
+    for logits in (xb, None):
+        got_s = gpu_with_sorted(sv, idx, dtype, None, k, logits)
+        assert np.array_equal(got_s, expect)
+    x = to_dev(xb, dtype)
+    q = torch.ones((B, V), dtype=torch.float32, device="cuda")
+    for qq in (None, q):
+        sel = tk.sample_top_k_top_p(x, None, k_dev(k), None, qq, 0.0)
+        torch.cuda.synchronize()
+        assert np.array_equal(sel.cpu().numpy(), top)
+    pr, ix, cnt = tk.top_k_top_p_sorted_survivors(x, None, k_dev(k), None, cap=2)
+    torch.cuda.synchronize()
+    n = keep.sum(axis=1)
+    assert np.array_equal(cnt.cpu().numpy(), n)
+    ix = ix.cpu().numpy()
+    assert np.array_equal(ix[:, 0], top)
+    assert np.array_equal(ix[:, 1], np.where(n == 2, 0, -1))
+    say(f"{B} rows of {V} in two launches: ok")

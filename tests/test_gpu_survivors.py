@@ -8,7 +8,7 @@ from oracle import sorted_survivors as oracle_survivors
 from tests.golden_io import load_hand_cases
 from tests.gpu_util import k_dev, need_gpu, say, to_dev
 from tests.parity import compare_survivors
-from workloads.synth import random_min_p, random_params, random_rows
+from workloads.synth import f32_to_bits, random_min_p, random_params, random_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -62,3 +62,21 @@ def test_survivors_random_rows(dtype, policy):
     say(f"survivors {dtype}/{policy}: ok")
 
 
+
+
+def test_survivors_large_sets(policy):
+    """Rows that keep tens of thousands of survivors (nearly flat and constant
+    rows, p near 1, no top-k): every listed index, probability and count
+    against the oracle, with a capacity below and above the count."""
+    cases = [("bf16", 40000, "normal", [0.99, 0.5]), ("f32", 40000, "const", [0.99, 0.3]),
+             ("bf16", 151936, "normal", [0.99])]
+    for dtype, V, kind, ps in cases:
+        B = len(ps)
+        xb = random_rows(91 + V, B, V, dtype, kind=kind, scale=0.05)
+        p = f32_to_bits(np.array(ps, np.float32), dtype)
+        for cap in (5000, V):
+            pr, idx, cnt = gpu_survivors(xb, dtype, p, None, None, cap)
+            ref = oracle_survivors(xb, dtype, p, None, None, cap)
+            h, det = compare_survivors(pr, idx, cnt, ref)
+            assert h == 0, (dtype, V, kind, cap, det[:3])
+        say(f"survivors large sets {dtype} V={V} {kind} ({policy}): counts {ref.counts.tolist()}")

@@ -43,8 +43,8 @@ topktopp_status check_shape(int64_t B, int64_t V) {
   if (B < 0 || V < 0) return fail(TOPKTOPP_ERR_INVALID, "shape [%lld, %lld] has a negative extent", (long long)B, (long long)V);
   if (V > TOPKTOPP_MAX_V)
     return fail(TOPKTOPP_ERR_INVALID, "row length V=%lld exceeds the supported maximum %d", (long long)V, TOPKTOPP_MAX_V);
-  if (B > 0x7FFFFFFFLL / 64)
-    return fail(TOPKTOPP_ERR_INVALID, "B=%lld rows exceeds the launch limit", (long long)B);
+  if (B > TOPKTOPP_MAX_B)
+    return fail(TOPKTOPP_ERR_INVALID, "B=%lld rows exceeds the supported maximum 2^31-1", (long long)B);
   return TOPKTOPP_OK;
 }
 
@@ -243,35 +243,35 @@ topktopp_status survivors_impl(const void* logits, int dtype, int64_t B, int64_t
 
 extern "C" {
 
-topktopp_status sample_top_k_top_p(const void* logits, int dtype, int64_t B, int64_t V, const void* p,
+topktopp_status sample_top_k_top_p(const void* logits, topktopp_dtype dtype, int64_t B, int64_t V, const void* p,
                                    const int32_t* k, const void* min_p, const float* q, float eps, void* out,
                                    int32_t* selected, void* stream) {
   return sample_impl(logits, dtype, B, V, p, k, min_p, q, eps, out, selected, stream);
 }
 
-topktopp_status top_k_top_p_sorted_survivors(const void* logits, int dtype, int64_t B, int64_t V, const void* p,
+topktopp_status top_k_top_p_sorted_survivors(const void* logits, topktopp_dtype dtype, int64_t B, int64_t V, const void* p,
                                              const int32_t* k, const void* min_p, int64_t cap, float* probs,
                                              int32_t* indices, int32_t* counts, void* stream) {
   return survivors_impl(logits, dtype, B, V, p, k, min_p, cap, probs, indices, counts, stream);
 }
 
-topktopp_status apply_top_k_top_p(const void* logits, int dtype, int64_t B, int64_t V, const void* p,
+topktopp_status apply_top_k_top_p(const void* logits, topktopp_dtype dtype, int64_t B, int64_t V, const void* p,
                                   const int32_t* k, void* out, void* stream) {
   return apply_impl(logits, V, dtype, B, V, p, k, nullptr, false, out, V, stream);
 }
 
-topktopp_status apply_top_k_top_p_min_p(const void* logits, int dtype, int64_t B, int64_t V, const void* p,
+topktopp_status apply_top_k_top_p_min_p(const void* logits, topktopp_dtype dtype, int64_t B, int64_t V, const void* p,
                                         const int32_t* k, const void* min_p, void* out, void* stream) {
   return apply_impl(logits, V, dtype, B, V, p, k, min_p, true, out, V, stream);
 }
 
-topktopp_status apply_top_k_top_p_ex(const void* logits, int64_t ld_logits, int dtype, int64_t B, int64_t V,
+topktopp_status apply_top_k_top_p_ex(const void* logits, int64_t ld_logits, topktopp_dtype dtype, int64_t B, int64_t V,
                                      const void* p, const int32_t* k, const void* min_p, void* out, int64_t ld_out,
                                      void* stream) {
   return apply_impl(logits, ld_logits, dtype, B, V, p, k, min_p, true, out, ld_out, stream);
 }
 
-topktopp_status apply_top_k_top_p_with_sorted(const void* sorted_value, const int32_t* sorted_indices, int dtype,
+topktopp_status apply_top_k_top_p_with_sorted(const void* sorted_value, const int32_t* sorted_indices, topktopp_dtype dtype,
                                               int64_t B, int64_t V, const void* p, const int32_t* k,
                                               const void* logits, void* out, void* stream) {
   return with_sorted_impl(sorted_value, V, sorted_indices, V, dtype, B, V, p, k, nullptr, false, logits, V, out, V,
@@ -279,7 +279,7 @@ topktopp_status apply_top_k_top_p_with_sorted(const void* sorted_value, const in
 }
 
 topktopp_status apply_top_k_top_p_min_p_with_sorted(const void* sorted_value, const int32_t* sorted_indices,
-                                                    int dtype, int64_t B, int64_t V, const void* p,
+                                                    topktopp_dtype dtype, int64_t B, int64_t V, const void* p,
                                                     const int32_t* k, const void* min_p, const void* logits,
                                                     void* out, void* stream) {
   return with_sorted_impl(sorted_value, V, sorted_indices, V, dtype, B, V, p, k, min_p, true, logits, V, out, V,
@@ -287,7 +287,7 @@ topktopp_status apply_top_k_top_p_min_p_with_sorted(const void* sorted_value, co
 }
 
 topktopp_status apply_top_k_top_p_with_sorted_ex(const void* sorted_value, int64_t ld_sorted_value,
-                                                 const int32_t* sorted_indices, int64_t ld_sorted_indices, int dtype,
+                                                 const int32_t* sorted_indices, int64_t ld_sorted_indices, topktopp_dtype dtype,
                                                  int64_t B, int64_t V, const void* p, const int32_t* k,
                                                  const void* min_p, const void* logits, int64_t ld_logits, void* out,
                                                  int64_t ld_out, void* stream) {

@@ -167,87 +167,65 @@ __device__ __forceinline__ void filter_multipass(const Tile& tile, const RowPara
 }
 
 // Sampling for a row whose survivors ((key, idx) >= (K, I)) are not in a
-// candidate list: None mode from the row's top position; QSample gathers
-// the survivors into shared memory when they fit (kCandCap), else the row's
-// pick is -1.
+// candidate list: None mode from the row's top position; QSample and the
+// sorted survivors rank the survivors in chunks (sample.h), any number of
+// them, re-reading the row on each pass.
 template <class DT, class Tile>
 __device__ __forceinline__ void sample_general(const Tile& tile, uint32_t K, uint32_t I, const RowParams& rp,
-                                               ApplySmem& S, const SampleArgs& sa, int b) {
+                                               ApplySmem& S, const SampleArgs& sa, int b, int V) {
+  constexpr float kLog2e = 1.4426950408889634f;
   RowSmem& sm = S.row;
-  if (wants_survivors(sa)) {
-    float mloc = -INFINITY;
-    uint32_t n = 0;
-    tile.for_each([&](auto raw, int idx) {
-      const uint32_t key = DT::key(raw);
-      mloc = fmaxf(mloc, DT::value(raw));
-      n += (key > K || (key == K && static_cast<uint32_t>(idx) >= I)) ? 1u : 0u;
-    });
-    const float m = block_max_f32(mloc, sm);
-    n = block_sum_u32(n, sm);
-    const uint32_t kmax = DT::key(DT::raw_of_value(m));
-    if (n <= static_cast<uint32_t>(kCandCap)) {
-      const double Z = survivors_z<DT>(tile, tile, rp, 0u, kmax, m, S.sel, sm, S.redd);
-      if (threadIdx.x == 0) S.ncand = 0;
-      lds_barrier();
-      tile.for_each([&](auto raw, int idx) {
-        const uint32_t key = DT::key(raw);
-        if (key > K || (key == K && static_cast<uint32_t>(idx) >= I)) {
-          const uint32_t at = atomicAdd(&S.ncand, 1u);
-          S.cel.raw[at] = raw;
-          S.cel.idx[at] = static_cast<uint32_t>(idx);
-        }
-      });
-      lds_barrier();
-      CandElems<DT> cs;
-      cs.load(S, static_cast<int>(n));
-      lds_barrier();  // the list below reuses the same shared memory
-      emit_survivors<DT>(cs, K, I, kmax, m, Z, sa, b, S.sel, reinterpret_cast<uint64_t*>(S.cel.raw));
-    } else {  // more survivors than the ranking holds: the count only
-      int32_t* irow = sa.indices + static_cast<size_t>(b) * sa.cap;
-      float* prow = sa.probs == nullptr ? nullptr : sa.probs + static_cast<size_t>(b) * sa.cap;
-      for (int64_t r = threadIdx.x; r < sa.cap; r += kThreads) {
-        irow[r] = -1;
-        if (prow != nullptr) prow[r] = 0.0f;
-      }
-      if (threadIdx.x == 0) sa.counts[b] = static_cast<int32_t>(n);
-    }
-    return;
-  }
-  int32_t pick = -1;
-  if (sa.q == nullptr) {
+  if (sa.q == nullptr && !wants_survivors(sa)) {
     uint32_t Kt, It;
     top_position<DT>(tile, sm, Kt, It);
-    pick = static_cast<int32_t>(It);
-  } else {
-    float mloc = -INFINITY;
-    uint32_t n = 0;
-    tile.for_each([&](auto raw, int idx) {
-      const uint32_t key = DT::key(raw);
-      mloc = fmaxf(mloc, DT::value(raw));
-      n += (key > K || (key == K && static_cast<uint32_t>(idx) >= I)) ? 1u : 0u;
-    });
-    const float m = block_max_f32(mloc, sm);
-    n = block_sum_u32(n, sm);
-    if (n <= static_cast<uint32_t>(kCandCap)) {
-      if (threadIdx.x == 0) S.ncand = 0;
-      lds_barrier();
-      tile.for_each([&](auto raw, int idx) {
-        const uint32_t key = DT::key(raw);
-        if (key > K || (key == K && static_cast<uint32_t>(idx) >= I)) {
-          const uint32_t at = atomicAdd(&S.ncand, 1u);
-          S.cel.raw[at] = raw;
-          S.cel.idx[at] = static_cast<uint32_t>(idx);
-        }
-      });
-      lds_barrier();
-      CandElems<DT> cs;
-      cs.load(S, static_cast<int>(n));
-      lds_barrier();  // the list below reuses the same shared memory
-      pick = qsample_pick<DT>(cs, K, I, DT::key(DT::raw_of_value(m)), m, sa.q + static_cast<size_t>(b) * sa.ld_q,
-                              sa.eps, S.sel, reinterpret_cast<uint64_t*>(S.cel.raw), sm);
-    }
+    if (threadIdx.x == 0 && sa.sel != nullptr) sa.sel[b] = static_cast<int32_t>(It);
+    return;
   }
-  if (threadIdx.x == 0 && sa.sel != nullptr) sa.sel[b] = pick;
+  float mloc = -INFINITY;
+  uint32_t n = 0;
+  tile.for_each([&](auto raw, int idx) {
+    const uint32_t key = DT::key(raw);
+    mloc = fmaxf(mloc, DT::value(raw));
+    n += (key > K || (key == K && static_cast<uint32_t>(idx) >= I)) ? 1u : 0u;
+  });
+  const float m = block_max_f32(mloc, sm);
+  n = block_sum_u32(n, sm);
+  const uint32_t kmax = DT::key(DT::raw_of_value(m));
+  uint64_t* list = reinterpret_cast<uint64_t*>(S.cel.raw);
+  if (wants_survivors(sa)) {
+    const double Z = survivors_z<DT>(tile, tile, rp, 0u, kmax, m, S.sel, sm, S.redd);
+    const float zinv = static_cast<float>(1.0 / Z);
+    int32_t* __restrict__ irow = sa.indices + static_cast<size_t>(b) * sa.cap;
+    float* __restrict__ prow = sa.probs == nullptr ? nullptr : sa.probs + static_cast<size_t>(b) * sa.cap;
+    const uint32_t limit = static_cast<int64_t>(n) < sa.cap ? n : static_cast<uint32_t>(sa.cap);
+    for_each_ranked_survivor_chunked<DT>(tile, K, I, kmax, n, limit, V, S.sel, list,
+                                         [&](float x, int idx, uint32_t rank) {
+                                           irow[rank] = idx;
+                                           if (prow != nullptr) prow[rank] = __builtin_amdgcn_exp2f((x - m) * kLog2e) * zinv;
+                                         });
+    for (int64_t r = static_cast<int64_t>(n) + threadIdx.x; r < sa.cap; r += kThreads) {
+      irow[r] = -1;
+      if (prow != nullptr) prow[r] = 0.0f;
+    }
+    if (threadIdx.x == 0) sa.counts[b] = static_cast<int32_t>(n);
+    return;
+  }
+  // QSample: the first maximum of exp(x - m) / (q[rank] + eps), as qsample_pick
+  const float* __restrict__ qrow = sa.q + static_cast<size_t>(b) * sa.ld_q;
+  uint64_t best = 0;  // (monotone key of the score) << 32 | ~rank
+  uint32_t best_idx = 0;
+  for_each_ranked_survivor_chunked<DT>(tile, K, I, kmax, n, n, V, S.sel, list, [&](float x, int idx, uint32_t rank) {
+    const float score = __builtin_amdgcn_exp2f((x - m) * kLog2e) / (qrow[rank] + sa.eps);
+    const uint64_t packed = (static_cast<uint64_t>(F32T::key(__float_as_uint(score))) << 32) | (~rank);
+    if (packed > best) {
+      best = packed;
+      best_idx = static_cast<uint32_t>(idx);
+    }
+  });
+  const uint64_t win = block_max_u64(best, sm);
+  if (best == win) S.sel.run_res = best_idx;  // exactly one survivor holds the winning rank
+  lds_barrier();
+  if (threadIdx.x == 0 && sa.sel != nullptr) sa.sel[b] = static_cast<int32_t>(S.sel.run_res);
 }
 
 // Selection among at most one wave's worth of candidates (lane j of wave 0
@@ -332,66 +310,18 @@ __device__ __forceinline__ void select_small(const ApplySmem& S, vec_t* tab, int
   I = static_cast<uint32_t>(last);
 }
 
-// `tile` holds the row (registers or global); `irow` is the same row in
-// global memory, re-read by the multi-pass fallback. kSample adds the
-// sampling stage (sample.h) and makes the row's output optional (wr).
+// The candidate plan (steps 1-7 above) for a row with something to filter.
+// Returns true when the row fell back to the multi-pass plan over the row in
+// global memory, whose survivors the sampling stage then takes from there;
+// otherwise the plan has done the sampling stage itself. K, I: the result.
 template <class DT, bool kSample, class Tile>
-__device__ __forceinline__ void filter_row(const Tile& tile, const typename DT::raw_t* __restrict__ irow, int V,
-                                           const RowParams& rp, bool use_candidates, ApplySmem& S,
-                                           typename DT::raw_t* __restrict__ orow, bool wr_out,
-                                           const SampleArgs& sa, int b) {
-  const bool wr = kSample ? wr_out : true;
+__device__ __forceinline__ bool candidate_plan(const Tile& tile, const GlobalTile<DT>& gt, int V, const RowParams& rp,
+                                               ApplySmem& S, typename DT::raw_t* __restrict__ orow, bool wr,
+                                               const SampleArgs& sa, int b, uint32_t& K, uint32_t& I) {
   using raw_t = typename DT::raw_t;
   constexpr int kPV = DT::kPerVec;
   RowSmem& sm = S.row;
   SelSmem& ss = S.sel;
-  GlobalTile<DT> gt;
-  gt.load(irow, 0, V);
-  sel_reset(ss);
-
-  if constexpr (kSample) {
-    // argmax without the filtered row: the pick is the row's top position
-    // (the maximum always survives every stage), so no selection is needed
-    if (sa.q == nullptr && !wr && !wants_survivors(sa)) {
-      // per thread the last vector holding its maximum (later vectors hold
-      // higher indices), then the highest lane of it holding the row's
-      float best = -INFINITY;
-      vec_t bq = {0u, 0u, 0u, 0u};
-      int be0 = -1;
-      tile.for_each_vec_values([&](int i, const float (&x)[kPV]) {
-        float vm = x[0];
-#pragma unroll
-        for (int j = 1; j < kPV; ++j) vm = fmaxf(vm, x[j]);
-        if (vm >= best && vm > -INFINITY) {
-          best = vm;
-          bq = tile.vec_at(i, i * Tile::kSpan + static_cast<int>(threadIdx.x) * kPV);
-          be0 = i * Tile::kSpan + static_cast<int>(threadIdx.x) * kPV;
-        }
-      });
-      const float mrow = block_max_f32(best, sm);
-      int idx = -1;
-      if (be0 >= 0 && best == mrow) {
-#pragma unroll
-        for (int j = 0; j < kPV; ++j)
-          if (be0 + j < V && DT::value(lane_of<raw_t>(bq, j)) == mrow) idx = be0 + j;
-      }
-      idx = static_cast<int>(block_max_u32(static_cast<uint32_t>(idx + 1), sm)) - 1;
-      if (threadIdx.x == 0 && sa.sel != nullptr) sa.sel[b] = idx < 0 ? 0 : idx;
-      return;
-    }
-  }
-  if (!row_filters(rp)) {  // nothing to filter
-    if (wr) tile.store(orow, [](raw_t r, int) { return r; });
-    if constexpr (kSample) sample_general<DT>(gt, 0u, 0u, rp, S, sa, b);
-    return;
-  }
-  if (!use_candidates) {
-    uint32_t K, I;
-    filter_multipass<DT>(gt, rp, V, S, orow, wr, K, I);
-    if constexpr (kSample) sample_general<DT>(gt, K, I, rp, S, sa, b);
-    return;
-  }
-
   // 1. per-thread statistics
   const bool ponly = rp.pmode == kPBoundary && !rp.k_on;
   constexpr float kLog2e = 1.4426950408889634f;
@@ -714,7 +644,8 @@ __device__ __forceinline__ void filter_row(const Tile& tile, const typename DT::
   // 6. exact selection on the candidates (all elements with key in [L, kmax])
   CandElems<DT> cs;
   cs.load(S, fallback ? 0 : ncand);
-  uint32_t K = 0, I = 0;
+  K = 0;
+  I = 0;
   if (small) {
     if (threadIdx.x >= kWave) last_stores();
     if (threadIdx.x < kWave) {
@@ -835,11 +766,76 @@ __device__ __forceinline__ void filter_row(const Tile& tile, const typename DT::
     // traversal then costs no memory latency (longer rows re-read global
     // memory, which keeps the unrolled code of their kernels small)
     filter_multipass<DT>(tile, rp, V, S, orow, wr, K, I, RowKnown{true, m, ponly ? thr : 0});
-    if constexpr (kSample) sample_general<DT>(tile, K, I, rp, S, sa, b);
+    if constexpr (kSample) sample_general<DT>(tile, K, I, rp, S, sa, b, V);
   } else {
     filter_multipass<DT>(gt, rp, V, S, orow, wr, K, I, RowKnown{true, m, ponly ? thr : 0});
-    if constexpr (kSample) sample_general<DT>(gt, K, I, rp, S, sa, b);
+    return true;
   }
+  return false;
+}
+
+
+// `tile` holds the row (registers or global); `irow` is the same row in
+// global memory, re-read by the multi-pass fallback. kSample adds the
+// sampling stage (sample.h) and makes the row's output optional (wr).
+template <class DT, bool kSample, class Tile>
+__device__ __forceinline__ void filter_row(const Tile& tile, const typename DT::raw_t* __restrict__ irow, int V,
+                                           const RowParams& rp, bool use_candidates, ApplySmem& S,
+                                           typename DT::raw_t* __restrict__ orow, bool wr_out,
+                                           const SampleArgs& sa, int b) {
+  const bool wr = kSample ? wr_out : true;
+  using raw_t = typename DT::raw_t;
+  constexpr int kPV = DT::kPerVec;
+  RowSmem& sm = S.row;
+  SelSmem& ss = S.sel;
+  GlobalTile<DT> gt;
+  gt.load(irow, 0, V);
+  sel_reset(ss);
+
+  if constexpr (kSample) {
+    // argmax without the filtered row: the pick is the row's top position
+    // (the maximum always survives every stage), so no selection is needed
+    if (sa.q == nullptr && !wr && !wants_survivors(sa)) {
+      // per thread the last vector holding its maximum (later vectors hold
+      // higher indices), then the highest lane of it holding the row's
+      float best = -INFINITY;
+      vec_t bq = {0u, 0u, 0u, 0u};
+      int be0 = -1;
+      tile.for_each_vec_values([&](int i, const float (&x)[kPV]) {
+        float vm = x[0];
+#pragma unroll
+        for (int j = 1; j < kPV; ++j) vm = fmaxf(vm, x[j]);
+        if (vm >= best && vm > -INFINITY) {
+          best = vm;
+          bq = tile.vec_at(i, i * Tile::kSpan + static_cast<int>(threadIdx.x) * kPV);
+          be0 = i * Tile::kSpan + static_cast<int>(threadIdx.x) * kPV;
+        }
+      });
+      const float mrow = block_max_f32(best, sm);
+      int idx = -1;
+      if (be0 >= 0 && best == mrow) {
+#pragma unroll
+        for (int j = 0; j < kPV; ++j)
+          if (be0 + j < V && DT::value(lane_of<raw_t>(bq, j)) == mrow) idx = be0 + j;
+      }
+      idx = static_cast<int>(block_max_u32(static_cast<uint32_t>(idx + 1), sm)) - 1;
+      if (threadIdx.x == 0 && sa.sel != nullptr) sa.sel[b] = idx < 0 ? 0 : idx;
+      return;
+    }
+  }
+  uint32_t K = 0, I = 0;
+  bool general = true;  // the survivors are (key, idx) >= (K, I) of the whole row, re-read from global memory
+  if (!row_filters(rp)) {  // nothing to filter
+    if (wr) tile.store(orow, [](raw_t r, int) { return r; });
+  } else if (!use_candidates) {
+    filter_multipass<DT>(gt, rp, V, S, orow, wr, K, I);
+  } else {
+    general = candidate_plan<DT, kSample>(tile, gt, V, rp, S, orow, wr, sa, b, K, I);
+  }
+  // one place for the general sampling path: each inlined copy of it costs
+  // registers in the kernels whose row is held in registers
+  if constexpr (kSample)
+    if (general) sample_general<DT>(gt, K, I, rp, S, sa, b, V);
 }
 
 template <class DT, int NVEC, bool kSample>
@@ -921,10 +917,11 @@ __global__ __launch_bounds__(kThreads, 2) void argmax_stream_kernel(const typena
 }
 
 // kSample: the sampling stage (sa), and out may be NULL; otherwise sa is unused.
-template <class DT, bool kSample = false>
-hipError_t launch_apply_t(const void* logits, const void* p, const int32_t* k, const void* min_p, void* out,
-                          int64_t B, int64_t V, RowStrides ld, int policy, hipStream_t stream,
-                          const SampleArgs& sa = SampleArgs{nullptr, 0, 0.0f, nullptr, nullptr, nullptr, nullptr, 0}) {
+// Rows [0, B) in one launch of one block per row (B <= kMaxLaunchBlocks).
+template <class DT, bool kSample>
+hipError_t launch_apply_rows(const void* logits, const void* p, const int32_t* k, const void* min_p, void* out,
+                             int64_t B, int64_t V, RowStrides ld, int policy, hipStream_t stream,
+                             const SampleArgs& sa) {
   using raw_t = typename DT::raw_t;
   constexpr int span = kThreads * DT::kPerVec;
   const int64_t vecs = (V + span - 1) / span;
@@ -968,6 +965,31 @@ hipError_t launch_apply_t(const void* logits, const void* p, const int32_t* k, c
     launch_regs<DT, kMaxVecs, kSample>(logits, p, k, min_p, out, B, V, ld, use_candidates, sa, stream);
   }
   return hipGetLastError();
+}
+
+// Any number of rows: launches of at most kMaxLaunchBlocks rows each, every
+// pointer advanced to the launch's first row (the kernels index rows by
+// block only).
+template <class DT, bool kSample = false>
+hipError_t launch_apply_t(const void* logits, const void* p, const int32_t* k, const void* min_p, void* out,
+                          int64_t B, int64_t V, RowStrides ld, int policy, hipStream_t stream,
+                          const SampleArgs& sa = SampleArgs{nullptr, 0, 0.0f, nullptr, nullptr, nullptr, nullptr, 0}) {
+  using raw_t = typename DT::raw_t;
+  for (int64_t r0 = 0; r0 < B; r0 += kMaxLaunchBlocks) {
+    const int64_t nb = B - r0 < kMaxLaunchBlocks ? B - r0 : kMaxLaunchBlocks;
+    SampleArgs s = sa;
+    if (s.q != nullptr) s.q += r0 * s.ld_q;
+    if (s.sel != nullptr) s.sel += r0;
+    if (s.probs != nullptr) s.probs += r0 * s.cap;
+    if (s.indices != nullptr) s.indices += r0 * s.cap;
+    if (s.counts != nullptr) s.counts += r0;
+    const hipError_t e = launch_apply_rows<DT, kSample>(
+        static_cast<const raw_t*>(logits) + r0 * ld.x, p == nullptr ? nullptr : static_cast<const raw_t*>(p) + r0,
+        k == nullptr ? nullptr : k + r0, min_p == nullptr ? nullptr : static_cast<const raw_t*>(min_p) + r0,
+        out == nullptr ? nullptr : static_cast<raw_t*>(out) + r0 * ld.o, nb, V, ld, policy, stream, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace tkp

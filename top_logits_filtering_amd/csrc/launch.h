@@ -7,6 +7,10 @@
 
 namespace tkp {
 
+// Blocks per launch at most: 2^21 blocks of 1024 threads keep a grid below
+// 2^32 work-items. Larger batches are launched in row chunks.
+constexpr int64_t kMaxLaunchBlocks = int64_t{1} << 21;
+
 // 0: candidate plan, row in registers when it fits; 1: multi-pass plan only,
 // row re-read from global memory; 2: candidate plan with the row re-read from
 // global memory even when it would fit in registers.
@@ -46,7 +50,7 @@ struct SampleArgs {
   const float* q;     // [B, ld_q] fp32, or NULL
   int64_t ld_q;       // row stride of q in elements
   float eps;
-  int32_t* sel;       // [B] selected original index (-1: survivors exceed the ranking capacity), or NULL
+  int32_t* sel;       // [B] selected original index, or NULL
   float* probs;       // [B, cap] survivors' probabilities in descending order, or NULL (sorted-survivors output)
   int32_t* indices;   // [B, cap] their original indices
   int32_t* counts;    // [B] survivors per row

@@ -336,13 +336,19 @@ __device__ __forceinline__ void sel_pick_joint(SelSmem& ss, uint32_t k, float t)
 
 // k-th largest (1-based, with multiplicity) of keyfn(raw, idx) over the
 // elements with pred(raw, idx), given that all of them lie in [lo, hi].
-// Every thread of the block must call it.
+// Every thread of the block must call it. With rem, *rem receives the rank
+// of the k-th largest among the elements equal to it (k minus the count of
+// larger ones), the same in every thread.
 template <class Src, class KeyFn, class Pred>
 __device__ __forceinline__ uint32_t kth_largest_key(const Src& src, uint32_t k, uint32_t lo, uint32_t hi,
-                                                    KeyFn keyfn, Pred pred, SelSmem& ss) {
+                                                    KeyFn keyfn, Pred pred, SelSmem& ss,
+                                                    uint32_t* rem = nullptr) {
   for (;;) {
     const uint32_t range = hi - lo;
-    if (range == 0) return lo;
+    if (range == 0) {
+      if (rem != nullptr) *rem = k;
+      return lo;
+    }
     const int shift = shift_for_range(range);
     if (shift == 0) {  // one key per bin: this pass settles it
       src.for_each([&](auto raw, int idx) {
@@ -351,6 +357,7 @@ __device__ __forceinline__ uint32_t kth_largest_key(const Src& src, uint32_t k, 
       });
       lds_barrier();
       sel_pick_count(ss, k);
+      if (rem != nullptr) *rem = k - ss.above;
       return lo + static_cast<uint32_t>(ss.bin);
     }
     src.for_each([&](auto raw, int idx) {

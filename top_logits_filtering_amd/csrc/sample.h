@@ -90,6 +90,124 @@ __device__ __forceinline__ uint32_t for_each_ranked_survivor(const Src& src, uin
   return n;
 }
 
+// Survivors ranked in chunks, for any number of them: the list in shared
+// memory holds kRankChunk entries, and a row may keep up to 2^20 survivors.
+// Chunks are taken in descending (key, index) order. Each chunk's lowest
+// entry is the want-th largest survivor below the previous chunk, found by
+// the radix selection of row_select.h (the key, then the index among the
+// survivors holding that key: indices are distinct, so the chunk has exactly
+// want members). Its members are gathered into the list and sorted there by a
+// bitonic network, descending, so the member at list position j has rank
+// base + j. A row with at most kRankChunk survivors takes one chunk and no
+// selection.
+constexpr int kRankChunk = 4096;
+static_assert((kRankChunk & (kRankChunk - 1)) == 0 && kRankChunk >= 2 * kThreads,
+              "the bitonic network takes a power of two, two pairs or more per thread");
+
+// Sorts list[0, kRankChunk) descending. Pair i (i < kRankChunk / 2) joins
+// positions a and a + j, a = i with a zero bit inserted at j's bit; thread t
+// takes pairs t, t + 1024, ... A stage with j <= 64 keeps the pairs of each
+// wave's lanes inside 128 positions of their own, so between two such stages
+// only the wave's own ordering of its shared-memory accesses is needed.
+__device__ __forceinline__ void bitonic_sort_desc(uint64_t* list) {
+  constexpr int kPairs = kRankChunk / 2;
+  for (int k = 2; k <= kRankChunk; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = threadIdx.x; i < kPairs; i += kThreads) {
+        const int a = ((i & ~(j - 1)) << 1) | (i & (j - 1));
+        const int c = a + j;
+        const uint64_t x = list[a], y = list[c];
+        // blocks whose k bit is clear end descending, the others ascending;
+        // the last stage (k = kRankChunk) leaves the whole list descending
+        const bool desc = (a & k) == 0;
+        if (desc ? (x < y) : (x > y)) {
+          list[a] = y;
+          list[c] = x;
+        }
+      }
+      // the next stage: j / 2, or the first of the next k (j = k); a stage
+      // whose pairs span waves must see, and be seen by, every wave
+      const int jn = j > 1 ? (j >> 1) : k;
+      if (j > kWave || jn > kWave) {
+        lds_barrier();
+      } else {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      }
+    }
+  }
+  lds_barrier();
+}
+
+// Calls f(value, idx, rank) for every survivor of `src` ((key, idx) >= (K, I),
+// keys in [K, kmax]) whose descending rank is below limit; n is the survivor
+// count (limit <= n). `list` holds kRankChunk u64 entries of free shared
+// memory. Every thread of the block must call it; the histograms stay zeroed.
+template <class DT, class Src, class F>
+__device__ __forceinline__ void for_each_ranked_survivor_chunked(const Src& src, uint32_t K, uint32_t I,
+                                                                 uint32_t kmax, uint32_t n, uint32_t limit, int V,
+                                                                 SelSmem& ss, uint64_t* list, F&& f) {
+  auto survives = [K, I](uint32_t key, uint32_t idx) { return key > K || (key == K && idx >= I); };
+  // the survivors not yet ranked have (key, idx) <= (hk, hidx)
+  uint32_t hk = kmax, hidx = 0xFFFFFFFFu;
+  uint32_t base = 0;
+  while (base < limit) {  // uniform; every chunk takes at least one survivor
+    const uint32_t rem = n - base;
+    const uint32_t want = rem < static_cast<uint32_t>(kRankChunk) ? rem : static_cast<uint32_t>(kRankChunk);
+    auto pending = [&](uint32_t key, uint32_t idx) {
+      return survives(key, idx) && (key < hk || (key == hk && idx <= hidx));
+    };
+    // the chunk's lowest member (tk, tidx)
+    uint32_t tk = K, tidx = 0;
+    if (rem > static_cast<uint32_t>(kRankChunk)) {
+      uint32_t r = 0;
+      tk = kth_largest_key(
+          src, want, K, hk, [](auto raw, int) { return DT::key(raw); },
+          [&](auto raw, int idx) { return pending(DT::key(raw), static_cast<uint32_t>(idx)); }, ss, &r);
+      tidx = kth_largest_key(
+          src, r, 0u, static_cast<uint32_t>(V - 1), [](auto, int idx) { return static_cast<uint32_t>(idx); },
+          [&](auto raw, int idx) {
+            const uint32_t key = DT::key(raw);
+            return key == tk && pending(key, static_cast<uint32_t>(idx));
+          },
+          ss);
+    }
+    // gather the chunk: (key, index + 1) descending is (key, index) descending,
+    // and the padding (0) sorts after every member
+    for (int e = threadIdx.x; e < kRankChunk; e += kThreads) list[e] = 0ull;
+    if (threadIdx.x == 0) ss.run_n = 0;
+    lds_barrier();
+    src.for_each([&](auto raw, int idx) {
+      const uint32_t key = DT::key(raw);
+      const uint32_t u = static_cast<uint32_t>(idx);
+      if (pending(key, u) && (key > tk || (key == tk && u >= tidx))) {
+        const uint32_t at = atomicAdd(&ss.run_n, 1u);
+        if (at < static_cast<uint32_t>(kRankChunk)) list[at] = (static_cast<uint64_t>(key) << 32) | (u + 1u);
+      }
+    });
+    lds_barrier();
+    bitonic_sort_desc(list);
+    for (uint32_t j = threadIdx.x; j < want && base + j < limit; j += kThreads) {
+      const uint64_t e = list[j];
+      const uint32_t key = static_cast<uint32_t>(e >> 32);
+      f(DT::value(DT::raw_of_key(key)), static_cast<int>(static_cast<uint32_t>(e) - 1u), base + j);
+    }
+    base += want;
+    // the next chunk lies strictly below (tk, tidx)
+    if (tidx > 0) {
+      hk = tk;
+      hidx = tidx - 1;
+    } else {
+      hk = tk - 1;
+      hidx = 0xFFFFFFFFu;
+    }
+    lds_barrier();  // the list is refilled by the next chunk
+  }
+  if (threadIdx.x == 0) ss.run_n = 0;
+  lds_barrier();
+}
+
 // The QSample pick among the survivors of `src`: the first maximum of
 // exp(x - m) / (q[rank] + eps). Returns the winner's original index (uniform).
 template <class DT, class Src>

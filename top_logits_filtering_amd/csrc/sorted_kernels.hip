@@ -558,10 +558,11 @@ __global__ __launch_bounds__(kThreads) void sorted_scatter_kernel(
   }
 }
 
+// Rows [0, B) in one launch (B times the blocks per row <= kMaxLaunchBlocks).
 template <class DT>
-static hipError_t launch_sorted_t(const void* sorted_value, const int32_t* sorted_indices, const void* p,
-                                  const int32_t* k, const void* min_p, const void* logits, void* out, int64_t B,
-                                  int64_t V, RowStrides ld, hipStream_t stream) {
+static hipError_t launch_sorted_rows(const void* sorted_value, const int32_t* sorted_indices, const void* p,
+                                     const int32_t* k, const void* min_p, const void* logits, void* out, int64_t B,
+                                     int64_t V, RowStrides ld, hipStream_t stream) {
   using raw_t = typename DT::raw_t;
   if (logits != nullptr) {
     constexpr int cap = RegTile<DT, kSortedVecs>::kCapacity;
@@ -595,6 +596,34 @@ static hipError_t launch_sorted_t(const void* sorted_value, const int32_t* sorte
                        static_cast<const raw_t*>(min_p), static_cast<raw_t*>(out), static_cast<int>(V), S, ld);
   }
   return hipGetLastError();
+}
+
+// Blocks per row of the launches above (at most: rows without k may take fewer).
+template <class DT>
+static int64_t sorted_blocks_per_row(int64_t V, bool with_logits) {
+  constexpr int64_t cap = RegTile<DT, kSortedVecs>::kCapacity;
+  return with_logits ? (V + cap - 1) / cap : (V + kScatterSlice - 1) / kScatterSlice;
+}
+
+// Any number of rows: launches of at most kMaxLaunchBlocks blocks each, every
+// pointer advanced to the launch's first row.
+template <class DT>
+static hipError_t launch_sorted_t(const void* sorted_value, const int32_t* sorted_indices, const void* p,
+                                  const int32_t* k, const void* min_p, const void* logits, void* out, int64_t B,
+                                  int64_t V, RowStrides ld, hipStream_t stream) {
+  using raw_t = typename DT::raw_t;
+  const int64_t rows = kMaxLaunchBlocks / sorted_blocks_per_row<DT>(V, logits != nullptr);
+  for (int64_t r0 = 0; r0 < B; r0 += rows) {
+    const int64_t nb = B - r0 < rows ? B - r0 : rows;
+    const hipError_t e = launch_sorted_rows<DT>(
+        static_cast<const raw_t*>(sorted_value) + r0 * ld.sv, sorted_indices + r0 * ld.si,
+        p == nullptr ? nullptr : static_cast<const raw_t*>(p) + r0, k == nullptr ? nullptr : k + r0,
+        min_p == nullptr ? nullptr : static_cast<const raw_t*>(min_p) + r0,
+        logits == nullptr ? nullptr : static_cast<const raw_t*>(logits) + r0 * ld.x, static_cast<raw_t*>(out) + r0 * ld.o,
+        nb, V, ld, stream);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_with_sorted(int dtype, const void* sorted_value, const int32_t* sorted_indices, const void* p,

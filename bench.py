@@ -157,6 +157,18 @@ def _oracle_chunk(lo):
     return r.stop - r.start
 
 
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or "unknown"."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(wl, budget_s=12.0, min_p=None, sample_q=None, sample_none=False, survivors_cap=0):
     """The CPU oracle on one thread, over the workload's rows in order (8 at a
     time, wrapping), for about budget_s seconds. Also sets the job that
@@ -173,8 +185,9 @@ def cpu_baseline(wl, budget_s=12.0, min_p=None, sample_q=None, sample_none=False
         "unit": "rows/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": f"{done} rows (the workload's rows in order, wrapping after {wl.B}), numpy float64 oracle, "
-                  f"one thread, {dt:.1f} s",
+        "sample": f"{done} rows (the workload's rows in order, wrapping after {wl.B}), the C++17 oracle "
+                  f"(double-precision softmax, std::stable_sort ranking), one thread, {dt:.1f} s",
+        "cpu": cpu_model(),
     }
 
 
@@ -203,8 +216,9 @@ def cpu_baseline_parallel(wl, rate1, budget_s=12.0):
         "unit": "rows/s",
         "cores": cores,
         "kind": "oracle",
-        "sample": f"{done} rows in 8-row chunks over {cores} worker processes (one per core), the same numpy "
-                  f"float64 oracle, {dt:.1f} s",
+        "sample": f"{done} rows in 8-row chunks over {cores} worker processes (one per core), the same C++17 "
+                  f"oracle, {dt:.1f} s",
+        "cpu": cpu_model(),
     }
 
 

@@ -161,3 +161,41 @@ def test_t_readings_report():
         for dtype in ("bf16", "f16"):
             pb = f32_to_bits(np.array([pv], np.float32), dtype)[0]
             assert one_minus_p(pb, dtype, "fp32") == one_minus_p(pb, dtype, "dtype")
+
+
+def test_t_reading_dtype_hand_rounded():
+    """The other reading of step 6 (1 - p rounded to p's dtype, AKP §2 step 6
+    with p in the logits dtype, §3) against values rounded by hand. Both
+    readings agree for p >= 0.5 (above); below 0.5, 1 - p needs one bit more
+    than the dtype holds:
+      bf16 0x3E9B = 0.302734375: 1 - p = 0.697265625 = 178.5 * 2^-8, a tie,
+        rounds to even 178 * 2^-8 = 0.6953125;
+      bf16 0x3DCD = 0.10009765625: 1 - p = 0.89990234375 = 230.375 * 2^-8
+        rounds to 230 * 2^-8 = 0.8984375;
+      fp16 0x34CD = 1229 * 2^-12: 1 - p = 2867 * 2^-12 = 1433.5 * 2^-11, a tie,
+        rounds to even 1434 * 2^-11 = 0.7001953125;
+      fp16 0x2E66 = 1638 * 2^-14: 1 - p = 14746 * 2^-14 = 1843.25 * 2^-11
+        rounds to 1843 * 2^-11 = 0.89990234375."""
+    from oracle import one_minus_p
+
+    cases = [("bf16", 0x3E9B, 0.697265625, 0.6953125), ("bf16", 0x3DCD, 0.89990234375, 0.8984375),
+             ("f16", 0x34CD, 0.699951171875, 0.7001953125), ("f16", 0x2E66, 0.9000244140625, 0.89990234375)]
+    for dtype, bits, t32, tdt in cases:
+        assert one_minus_p(bits, dtype, "fp32") == np.float32(t32), (dtype, hex(bits))
+        assert one_minus_p(bits, dtype, "dtype") == np.float32(tdt), (dtype, hex(bits))
+
+
+def test_t_reading_changes_mask_on_flat_row():
+    """A row of 1000 equal values has cumulative probabilities (j + 1) / 1000,
+    and ties survive from the highest index down. bf16 p = 0x3E9B: the fp32
+    reading t = 0.697265625 masks ranks with j + 1 <= 697 and keeps the 303
+    highest indices; the dtype reading t = 0.6953125 keeps 305. fp16 p =
+    0x34CD: t = 0.699951171875 keeps 301, the dtype reading 0.7001953125
+    keeps 300."""
+    for dtype, pbits, keep32, keepdt in (("bf16", 0x3E9B, 303, 305), ("f16", 0x34CD, 301, 300)):
+        x = np.zeros((1, 1000), np.uint16)  # +0.0 in both dtypes
+        p = np.array([pbits], np.uint16)
+        for reading, keep in (("fp32", keep32), ("dtype", keepdt)):
+            out = apply_top_k_top_p(x, dtype, p, None, keep_traces=False, t_reading=reading).out[0]
+            kept = np.nonzero(out == 0)[0]
+            assert np.array_equal(kept, np.arange(1000 - keep, 1000)), (dtype, reading, len(kept))

@@ -17,7 +17,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1..5] [--
 --min-p adds the min-p stage (aclnnTopKTopPSampleV2, "minP sampling") with a
 per-row min_p drawn uniformly from [0.01, 0.2] to the chosen workload.
 --no-logits runs the pre-sorted workload without logits (the output is
-scattered through sorted_indices).
+scattered through sorted_indices). --p-only passes no k (top-p alone).
 --sample runs the filter followed by sampling (aclnnTopKTopPSampleV2
 "Subsequent processing", QSample with q drawn i.i.d. from Exp(1), eps 1e-6)
 and writes one index per row instead of the filtered logits; --sample-none
@@ -114,15 +114,16 @@ def survivor_bytes(wl, with_min_p, cap):
     return wl.B * (wl.V * s + s + 4 + (s if with_min_p else 0) + 8 * cap + 4)
 
 
-def algorithmic_bytes(wl, with_min_p=False, with_logits=True):
+def algorithmic_bytes(wl, with_min_p=False, with_logits=True, with_k=True):
     """Minimal HBM bytes of one call: read every logit once, write every output
     once, read p and k (and min_p); the pre-sorted entry also reads at least
-    the k largest sorted values of each row. Without logits the pre-sorted
-    entry writes every output once and reads the survivors' values and
-    indices, at least min(k, V) per row."""
+    the k largest sorted values of each row (every sorted value without k:
+    Z sums the whole row). Without logits the pre-sorted entry writes every
+    output once and reads the survivors' values and indices, at least
+    min(k, V) per row."""
     s = wl.elem_bytes
-    kept = int(np.clip(wl.k, 0, wl.V).sum())
-    params = wl.B * (s + 4 + (s if with_min_p else 0))
+    kept = int(np.clip(wl.k, 0, wl.V).sum()) if with_k else wl.B * wl.V
+    params = wl.B * (s + (4 if with_k else 0) + (s if with_min_p else 0))
     if wl.entry == "with_sorted" and not with_logits:
         return wl.B * wl.V * s + kept * (s + 4) + params
     total = 2 * wl.B * wl.V * s + params
@@ -144,15 +145,16 @@ def _oracle_chunk(lo):
     wl, min_p, sample_q, sample_none, survivors_cap = _CPU_JOB
     r = slice(lo, min(wl.B, lo + 8))
     mp = None if min_p is None else min_p[r]
+    kk = None if wl.k is None else wl.k[r]
     if survivors_cap:
-        sorted_survivors(wl.logits[r], wl.dtype, wl.p[r], wl.k[r], mp, survivors_cap)
+        sorted_survivors(wl.logits[r], wl.dtype, wl.p[r], kk, mp, survivors_cap)
     elif sample_q is not None or sample_none:
-        sample_top_k_top_p(wl.logits[r], wl.dtype, wl.p[r], wl.k[r], mp,
+        sample_top_k_top_p(wl.logits[r], wl.dtype, wl.p[r], kk, mp,
                            None if sample_q is None else sample_q[r], 1e-6)
     elif wl.entry == "apply":
-        apply_top_k_top_p(wl.logits[r], wl.dtype, wl.p[r], wl.k[r], keep_traces=False, min_p_bits=mp)
+        apply_top_k_top_p(wl.logits[r], wl.dtype, wl.p[r], kk, keep_traces=False, min_p_bits=mp)
     else:
-        apply_top_k_top_p_with_sorted(wl.sorted_value[r], wl.sorted_indices[r], wl.dtype, wl.p[r], wl.k[r],
+        apply_top_k_top_p_with_sorted(wl.sorted_value[r], wl.sorted_indices[r], wl.dtype, wl.p[r], kk,
                                       logits_bits=wl.logits[r], keep_traces=False, min_p_bits=mp)
     return r.stop - r.start
 
@@ -234,6 +236,8 @@ def main():
     ap.add_argument("--policy", type=int, default=0, help="plan policy: 0 auto, 1 general, 2 registers")
     ap.add_argument("--min-p", action="store_true", help="add a per-row min_p in [0.01, 0.2] (the min-p stage)")
     ap.add_argument("--no-logits", action="store_true", help="pre-sorted workload without logits (scattered output)")
+    ap.add_argument("--p-only", action="store_true",
+                    help="top-p only: the workload's p with k absent (NULL), e.g. the pre-sorted top-p batch")
     ap.add_argument("--sample", action="store_true", help="filter then sample one index per row (QSample)")
     ap.add_argument("--sample-none", action="store_true", help="filter then take the argmax index per row")
     ap.add_argument("--survivors", action="store_true",
@@ -255,6 +259,8 @@ def main():
 
     wl = make_workload(args.workload)
     dt = wl.dtype
+    if args.p_only:
+        wl.k = None
     mp_bits = min_p_for_workload(args.workload, wl.B, dt) if args.min_p else None
     sampling = args.sample or args.sample_none
     if (sampling or args.survivors) and wl.entry != "apply":
@@ -282,7 +288,7 @@ def main():
     tk.load_library()
     tk.set_plan_policy(args.policy)
     p = dev(wl.p, dt)
-    k = torch.from_numpy(wl.k).cuda()
+    k = None if wl.k is None else torch.from_numpy(wl.k).cuda()
     mp = dev(mp_bits, dt)
     surv_out = None
     if args.survivors:
@@ -375,7 +381,7 @@ def main():
     elif args.survivors:
         nbytes = survivor_bytes(wl, args.min_p, cap)
     else:
-        nbytes = algorithmic_bytes(wl, args.min_p, not args.no_logits)
+        nbytes = algorithmic_bytes(wl, args.min_p, not args.no_logits, not args.p_only)
     achieved = nbytes / (kernel_ms * 1e-3) / 1e9
     rows_per_s = wl.B / (ms_per_step * 1e-3)
 
@@ -395,6 +401,7 @@ def main():
         "config": {
             "workload": WORKLOAD_TEXT[args.workload] + (", min-p U[0.01,0.2] per row" if args.min_p else "")
                         + (", without logits" if args.no_logits and wl.entry == "with_sorted" else "")
+                        + (", top-p only (k absent)" if args.p_only else "")
                         + (", then QSample (q ~ Exp(1), eps 1e-6), one index per row" if args.sample else "")
                         + (", then argmax, one index per row" if args.sample_none else "")
                         + (", sorted survivors (probabilities and indices, capacity 1024 per row)"

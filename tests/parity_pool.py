@@ -17,6 +17,7 @@ A job is a dict:
   logits    "sorted" only: whether logits were passed
   q         "sample" only: path of the saved q matrix, or None (argmax)
   cap       "survivors" only
+  no_k      True: the call passed no k
 """
 
 from __future__ import annotations
@@ -55,6 +56,8 @@ def run_job(job):
     from tests.parity import compare, compare_samples, compare_survivors
 
     wl, mp_bits = _inputs(job)
+    if job.get("no_k"):
+        wl.k = None
     lo, hi = job["lo"], job["hi"]
     res = {}
     if job["kind"] in ("apply", "sorted"):

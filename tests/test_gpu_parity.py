@@ -196,3 +196,30 @@ def test_with_sorted_global_search_full_rows(dtype, V):
                 assert rep.hard_mismatches == 0, (kind, kv, pv, use_logits, rep.details[:2])
                 total.merge(rep)
     say(f"with_sorted global search {dtype} V={V}: {total}")
+
+
+@pytest.mark.parametrize("dtype,V", [("bf16", 65546), ("bf16", 200000), ("f32", 32771), ("f32", 98304),
+                                     ("f16", 131080)])
+def test_with_sorted_without_k_segment_table(dtype, V):
+    """Pre-sorted rows without k, whose top-p boundary comes from the table of
+    segment masses the pre-pass writes into each slice's output region; the
+    last slice of 65546 bf16 or 32771 fp32 values is too short to hold the
+    table and searches the sorted row itself. p from nearly 0 to nearly 1,
+    with and without min-p, ties and distinct values."""
+    need_gpu()
+    total = ParityReport()
+    seed = 1900 + V % 97
+    for kind in ("normal", "ties"):
+        seed += 1
+        B = 6
+        xb = random_rows(seed, B, V, dtype, kind=kind, scale=3.0)
+        idx, sv = stable_ascending_sort(xb, dtype)
+        p = f32_to_bits(np.array([0.02, 0.3, 0.5, 0.9, 0.99, 0.9999], np.float32), dtype)
+        mp = f32_to_bits(np.array([0.0, 0.01, 0.2, 1e-4, 0.5, 1.0], np.float32), dtype)
+        for mm in (None, mp):
+            ref = oracle_sorted(sv, idx, dtype, p, None, logits_bits=xb, min_p_bits=mm)
+            got = gpu_with_sorted(sv, idx, dtype, p, None, xb, min_p=mm)
+            rep = compare(got, xb, ref, dtype)
+            assert rep.hard_mismatches == 0, (kind, mm is None, rep.details[:2])
+            total.merge(rep)
+    say(f"with_sorted without k, segment table {dtype} V={V}: {total}")

@@ -143,6 +143,27 @@ def test_with_sorted_every_row(scratch):
     assert np.array_equal(got["with_logits"], again)
 
 
+def test_with_sorted_p_only_every_row(scratch):
+    """Workload 5 with k absent (top-p alone, the benchmark's --p-only), with
+    and without min-p, every row."""
+    torch = need_gpu()
+    import top_logits_filtering_amd as tk
+
+    wl = make_workload(5)
+    sv, si, x = to_dev(wl.sorted_value, wl.dtype), k_dev(wl.sorted_indices), to_dev(wl.logits, wl.dtype)
+    p = to_dev(wl.p, wl.dtype)
+    mp = to_dev(min_p_for_workload(5, wl.B, wl.dtype), wl.dtype)
+    for name, mm in (("p_only", None), ("p_only_min_p", mp)):
+        out = tk.apply_top_k_top_p_with_sorted(sv, si, p, None, x, min_p=mm)
+        torch.cuda.synchronize()
+        path = _save(scratch, f"sorted5_{name}", from_dev(out, wl.dtype))
+        del out
+        res = run_batch(dict(kind="sorted", config=5, outs={"auto": path}, min_p=mm is not None, no_k=True), wl.B,
+                        ROWS_PER_JOB[5])
+        _record(f"workload5/sorted_{name}/auto", res["auto"])
+        _assert_clean(res["auto"], name)
+
+
 @pytest.mark.parametrize("variant", ["qsample", "qsample_min_p", "argmax"])
 def test_sample_every_row(variant, scratch):
     """Workload 3 followed by sampling (QSample with q ~ Exp(1), eps 1e-6, or

@@ -338,7 +338,167 @@ __device__ __forceinline__ bool boundary_from_copy(const typename DT::raw_t* top
 constexpr int kSortedVecs = 8;  // logits slice held in registers: 8 vectors per thread
 constexpr int kMaxSliceWords = (kThreads * kSortedVecs * 8) / 32;
 
-template <class DT, bool kRegs, bool kNoK>
+// Rows without k whose top-p boundary lies anywhere in the sorted row: Z needs
+// the mass of every position, and every slice's block needs Z. A pre-pass
+// (sorted_segment_mass_kernel) sums the mass of each segment of the sorted
+// row once, and writes the row's table of segment masses into each slice's
+// own region of the output row: the block of slice s reads the copy in its
+// region and only then overwrites that region, so blocks never read what
+// another block writes, and no memory beyond the caller's buffers is used. A
+// slice too short to hold the table (the last one of some rows) searches the
+// sorted row itself, as before. A segment is what one wave of the pre-pass
+// reads: 8 vectors per lane, 4096 fp16/bf16 or 2048 fp32 positions.
+template <class DT>
+constexpr int seg_len() {
+  return kWave * kSortedVecs * DT::kPerVec;
+}
+
+template <class DT>
+__device__ __forceinline__ int segment_count(int V) {
+  return (V + seg_len<DT>() - 1) / seg_len<DT>();  // <= 512 for V <= 2^20
+}
+
+// The table copy of slice s2 of a row, or NULL when the slice cannot hold it.
+template <class DT>
+__device__ __forceinline__ uint64_t* slice_table(typename DT::raw_t* orow, int s2, int V) {
+  constexpr int kCap = RegTile<DT, kSortedVecs>::kCapacity;
+  const int len = min(kCap, V - s2 * kCap);
+  const bool fits = static_cast<int64_t>(len) * static_cast<int64_t>(sizeof(typename DT::raw_t)) >=
+                    static_cast<int64_t>(segment_count<DT>(V)) * 8;
+  return fits ? reinterpret_cast<uint64_t*>(orow + static_cast<size_t>(s2) * kCap) : nullptr;
+}
+
+// The summed mass of one 16-byte vector of sorted values (positions e0.. of a
+// row of V, m the row maximum). A sorted vector is a run of its first value
+// followed by a run of its last one unless it holds three or more distinct
+// values (only in the thin tails of a row): then two masses times their
+// counts give the same integer sum as the elements one by one.
+template <class DT>
+__device__ __forceinline__ uint64_t sorted_vector_mass(const vec_t& q, int e0, int V, float m) {
+  using raw_t = typename DT::raw_t;
+  constexpr int kPV = DT::kPerVec;
+  const raw_t r0 = lane_of<raw_t>(q, 0), rl = lane_of<raw_t>(q, kPV - 1);
+  uint32_t c0 = 0, cl = 0;
+#pragma unroll
+  for (int j = 0; j < kPV; ++j) {
+    const raw_t r = lane_of<raw_t>(q, j);
+    c0 += r == r0 ? 1u : 0u;
+    cl += r == rl ? 1u : 0u;
+  }
+  if (e0 + kPV <= V && c0 + cl >= static_cast<uint32_t>(kPV)) {
+    const uint64_t m0 = mass_fx(DT::value(r0), m);
+    if (r0 == rl) return m0 * kPV;
+    return m0 * c0 + mass_fx(DT::value(rl), m) * cl;
+  }
+  uint64_t sum = 0;
+#pragma unroll
+  for (int j = 0; j < kPV; ++j)
+    if (e0 + j < V) sum += mass_fx(DT::value(lane_of<raw_t>(q, j)), m);
+  return sum;
+}
+
+// Wave g of the grid sums the mass (mass_fx against the row maximum, the top
+// sorted value) of one segment: segment g % nseg of row g / nseg. Its load u
+// reads 64 consecutive vectors (1 KB), one wave sum gives the segment's mass,
+// and lane 0 writes it into every table copy of the row. Waves share nothing,
+// so blocks are small (4 waves) and need no barrier. Rows without a top-p
+// boundary are skipped: the filter kernel reads no table for them.
+constexpr int kSegWavesPerBlock = 4;
+
+template <class DT>
+__global__ __launch_bounds__(kSegWavesPerBlock * kWave) void sorted_segment_mass_kernel(
+    const typename DT::raw_t* __restrict__ sorted_value, const typename DT::raw_t* __restrict__ p,
+    const typename DT::raw_t* __restrict__ min_p, typename DT::raw_t* __restrict__ out, int64_t B, int V, int S,
+    RowStrides ld) {
+  using raw_t = typename DT::raw_t;
+  constexpr int kPV = DT::kPerVec;
+  constexpr int kSegLen = seg_len<DT>();
+  const int nseg = segment_count<DT>(V);
+  // the same in every lane: readfirstlane lets the compiler keep the row's
+  // buffer descriptor in scalar registers
+  const int64_t wg = static_cast<int64_t>(blockIdx.x) * kSegWavesPerBlock +
+                     __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
+  if (wg >= B * nseg) return;  // uniform per wave
+  const int b = static_cast<int>(wg / nseg);
+  const int g = static_cast<int>(wg - static_cast<int64_t>(b) * nseg);
+  const RowParams rp = decode_row_params<DT>(p, nullptr, min_p, b, V);
+  if (rp.pmode != kPBoundary) return;
+  const raw_t* __restrict__ sv = sorted_value + static_cast<size_t>(b) * static_cast<size_t>(ld.sv);
+  raw_t* __restrict__ orow = out + static_cast<size_t>(b) * static_cast<size_t>(ld.o);
+  const int lane = static_cast<int>(threadIdx.x) & (kWave - 1);
+  const int e_seg = g * kSegLen;
+  const __amdgpu_buffer_rsrc_t rs = row_rsrc(sv, V);
+  // the row maximum is requested first: loads complete in order, so the
+  // arithmetic on the first vectors need not wait for the last ones
+  const raw_t top = sv[V - 1];
+  __builtin_amdgcn_sched_barrier(0);
+  vec_t q[kSortedVecs];
+#pragma unroll
+  for (int u = 0; u < kSortedVecs; ++u)
+    q[u] = __builtin_amdgcn_raw_buffer_load_b128(
+        rs, (e_seg + (u * kWave + lane) * kPV) * static_cast<int>(sizeof(raw_t)), 0, 0);
+  const float m = DT::value(top);
+  uint64_t sum = 0;
+#pragma unroll
+  for (int u = 0; u < kSortedVecs; ++u) sum += sorted_vector_mass<DT>(q[u], e_seg + (u * kWave + lane) * kPV, V, m);
+  sum = wave_sum_u64(sum);
+  if (lane < S) {  // lane s2 writes the copy of slice s2
+    uint64_t* tab = slice_table<DT>(orow, lane, V);
+    if (tab != nullptr) tab[g] = sum;
+  }
+}
+
+// The top-p boundary of a row without k from its segment table (start 0):
+// an exclusive scan of the segment masses from the top gives Z and the mass
+// above each segment; F lies in the lowest segment whose mass above is below
+// the threshold, and one block scan over that segment's positions (G
+// consecutive positions per thread, from the top) finds it. The same integer
+// masses as topp_boundary_global, so the same F.
+template <class DT>
+__device__ __forceinline__ int topp_boundary_table(const typename DT::raw_t* __restrict__ sv,
+                                                   const uint64_t* __restrict__ tab, int V, float m, float t,
+                                                   RowSmem& sm) {
+  constexpr int kSegLen = seg_len<DT>();
+  constexpr int G = kSegLen / kThreads;  // 4 or 2
+  const int tid = static_cast<int>(threadIdx.x);
+  const int nseg = segment_count<DT>(V);
+  const int g = nseg - 1 - tid;  // thread tid takes the tid-th segment from the top
+  const uint64_t ms = g >= 0 ? tab[g] : 0ull;
+  uint64_t Z;
+  const uint64_t above = block_exscan_u64(ms, sm, Z);
+  const uint64_t thr = topp_threshold(t, Z);
+  if (thr == 0) return V - 1;
+  const bool hit = g >= 0 && above < thr;
+  uint64_t base;
+  int ts;
+  block_max_u64_i32(hit ? above : 0ull, hit ? tid : -1, sm, base, ts);
+  const int seg = nseg - 1 - ts;
+  const int pbot = seg * kSegLen;
+  const int ptop = min(V - 1, pbot + kSegLen - 1);
+  const int hi = ptop - G * tid;  // this thread: positions hi down to hi - G + 1
+  uint64_t e[G];
+  uint64_t tsum = 0;
+#pragma unroll
+  for (int i = 0; i < G; ++i) {
+    const int j = hi - i;
+    e[i] = j >= pbot ? mass_fx(DT::value(sv[j]), m) : 0ull;
+    tsum += e[i];
+  }
+  uint64_t total;
+  uint64_t acc = base + block_exscan_u64(tsum, sm, total);  // mass strictly above position hi
+  int low = -1;  // this thread's lowest position whose mass strictly above is below thr
+#pragma unroll
+  for (int i = 0; i < G; ++i) {
+    const int j = hi - i;
+    if (j >= pbot && acc < thr) low = j;
+    acc += e[i];
+  }
+  return (V - 1) - block_max_i32(low >= 0 ? (V - 1) - low : -1, sm);
+}
+
+// kTable (with kRegs and kNoK): one block per slice, and rows with a top-p
+// boundary take it from the segment table the pre-pass wrote.
+template <class DT, bool kRegs, bool kNoK, bool kTable = false>
 __global__ __launch_bounds__(kThreads, 8) void sorted_logits_kernel(
     const typename DT::raw_t* __restrict__ sorted_value, const int32_t* __restrict__ sorted_indices,
     const typename DT::raw_t* __restrict__ p, const int32_t* __restrict__ k,
@@ -373,7 +533,7 @@ __global__ __launch_bounds__(kThreads, 8) void sorted_logits_kernel(
   if constexpr (!kNoK) prefetch_top<DT>(sv, V, R, pre);
   __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the slice's
   Tile tile;
-  if constexpr (!kNoK) tile.load(logits + static_cast<size_t>(b) * static_cast<size_t>(ld.x), v0, len);
+  if constexpr (!kNoK || kTable) tile.load(logits + static_cast<size_t>(b) * static_cast<size_t>(ld.x), v0, len);
   const RowParams rp = decode_row_params<DT>(rpr, V);
   if constexpr (!kNoK) {
 #pragma unroll
@@ -384,7 +544,7 @@ __global__ __launch_bounds__(kThreads, 8) void sorted_logits_kernel(
   raw_t* __restrict__ orow = out + static_cast<size_t>(b) * static_cast<size_t>(ld.o);
   const raw_t* __restrict__ xrow = logits + static_cast<size_t>(b) * static_cast<size_t>(ld.x);
   if (!row_filters(rp)) {
-    if constexpr (kNoK) {
+    if constexpr (kNoK && !kTable) {
       for (int ss = s_lo; ss < s_hi; ++ss) {
         v0 = ss * kCap;
         len = min(kCap, V - v0);
@@ -397,7 +557,19 @@ __global__ __launch_bounds__(kThreads, 8) void sorted_logits_kernel(
     return;
   }
   SortedBoundary bd;
-  if constexpr (kNoK) {
+  if constexpr (kTable) {
+    const uint64_t* tab = slice_table<DT>(out + static_cast<size_t>(b) * static_cast<size_t>(ld.o), s, V);
+    if (rp.pmode == kPBoundary && tab != nullptr) {
+      int F = topp_boundary_table<DT>(sv, tab, V, DT::value(sv[V - 1]), rp.t, sm);
+      if (rp.mp_on) F = first_min_p<DT>(SortedSrcGlobal<DT>{sv}, F, V, rp.minp, sm);
+      bd.F = F;
+      bd.KF = DT::key(sv[F]);
+      bd.a = first_at_or_above<DT>(SortedSrcGlobal<DT>{sv}, F, bd.KF, sm);
+    } else {
+      // (fp16 keeps one scan load fewer in flight beside the slice tile, as below)
+      bd = sorted_boundary<DT, std::is_same_v<DT, F16T> ? 3 : 4>(SortedSrcGlobal<DT>{sv}, rp, V, sm);
+    }
+  } else if constexpr (kNoK) {
     bd = sorted_boundary<DT, 8>(SortedSrcGlobal<DT>{sv}, rp, V, sm);
   } else if (boundary_from_copy<DT>(top, R, V, rp)) {
     bd = sorted_boundary_copy<DT>(top, R, V, rp, sm);
@@ -410,7 +582,7 @@ __global__ __launch_bounds__(kThreads, 8) void sorted_logits_kernel(
 
   const int32_t* __restrict__ si = sorted_indices + static_cast<size_t>(b) * static_cast<size_t>(ld.si);
   for (int ss = s_lo; ss < s_hi; ++ss) {
-  if constexpr (kNoK) {
+  if constexpr (kNoK && !kTable) {
     v0 = ss * kCap;
     len = min(kCap, V - v0);
     tile.load(xrow, v0, len);
@@ -579,9 +751,23 @@ static hipError_t launch_sorted_rows(const void* sorted_value, const int32_t* so
                          static_cast<const raw_t*>(min_p), static_cast<const raw_t*>(logits), static_cast<raw_t*>(out),
                          static_cast<int>(V), S, ld, Sb);
     };
-    // without k no row can use the copy of the top values: no copy, and the
-    // slices are read after the scan over the sorted row
-    if (vec_ok && k == nullptr)
+    // without k no row can use the copy of the top values: no copy; with p,
+    // the pre-pass sums the sorted rows' segment masses once (one block per
+    // slice), otherwise the slices are read after each block's own search
+    const bool sv_vec = (reinterpret_cast<uintptr_t>(sorted_value) & 15u) == 0 && (ld.sv * es) % 16 == 0;
+    if (vec_ok && sv_vec && k == nullptr && p != nullptr) {
+      // one wave per segment: seg_len() positions per segment, four waves per block
+      const int64_t seg_waves = B * ((V + seg_len<DT>() - 1) / seg_len<DT>());
+      hipLaunchKernelGGL(sorted_segment_mass_kernel<DT>,
+                         dim3(static_cast<unsigned>((seg_waves + kSegWavesPerBlock - 1) / kSegWavesPerBlock)),
+                         dim3(kSegWavesPerBlock * kWave), 0, stream, static_cast<const raw_t*>(sorted_value),
+                         static_cast<const raw_t*>(p), static_cast<const raw_t*>(min_p), static_cast<raw_t*>(out), B,
+                         static_cast<int>(V), S, ld);
+      hipLaunchKernelGGL((sorted_logits_kernel<DT, true, true, true>), dim3(static_cast<unsigned>(B * S)),
+                         dim3(kThreads), 0, stream, static_cast<const raw_t*>(sorted_value), sorted_indices,
+                         static_cast<const raw_t*>(p), k, static_cast<const raw_t*>(min_p),
+                         static_cast<const raw_t*>(logits), static_cast<raw_t*>(out), static_cast<int>(V), S, ld, S);
+    } else if (vec_ok && k == nullptr)
       go(sorted_logits_kernel<DT, true, true>, B * Sb);
     else if (vec_ok)
       go(sorted_logits_kernel<DT, true, false>, B * S);

@@ -171,6 +171,39 @@ topktopp_status apply_top_k_top_p_ex(const void* logits, int64_t ld_logits, topk
                                      int64_t ld_out, void* stream);
 
 /*
+ * apply_top_k_top_p_strided — apply_top_k_top_p_min_p on arbitrary strided
+ * views (the aclnn entry accepts non-contiguous tensors and makes them
+ * contiguous before filtering, AKP §6.1; this reads and writes the views in
+ * place instead). All strides are in elements:
+ *   logits  element (b, v) at logits[b * logits_row_stride + v * logits_col_stride];
+ *   out     element (b, v) at out[b * out_row_stride + v * out_col_stride];
+ *   p, k, min_p   entry b at p[b * p_stride], k[b * k_stride],
+ *           min_p[b * min_p_stride] (a stride of 0 shares one value among
+ *           all rows; the stride of a NULL operand is ignored).
+ * E.g. a [V, B] buffer filtered as its transpose passes row stride 1 and
+ * column stride B. Input strides must lie in [0, TOPKTOPP_MAX_LD]; out's in
+ * [1, TOPKTOPP_MAX_LD] (ignored along an extent of 1), and out must give
+ * every (b, v) its own element: one of its strides must be at least the
+ * other times that other dimension's extent (out_row_stride >= V *
+ * out_col_stride, or out_col_stride >= B * out_row_stride), else
+ * ERR_INVALID. The byte span of out (from its first to its last element)
+ * must not overlap the span of any input. Elements of the spans that belong
+ * to no (b, v) are neither read nor written. Other arguments, checks and
+ * results as for apply_top_k_top_p_min_p (p, k and min_p may each be NULL,
+ * but not all three).
+ *
+ * When rows are contiguous (logits_col_stride == out_col_stride == 1, row
+ * strides >= V) and p, k and min_p are dense, this is apply_top_k_top_p_ex.
+ * Otherwise every element is accessed on its own by a streamed kernel, which
+ * is several times slower than the vector path of contiguous rows.
+ */
+topktopp_status apply_top_k_top_p_strided(const void* logits, int64_t logits_row_stride, int64_t logits_col_stride,
+                                          topktopp_dtype dtype, int64_t B, int64_t V, const void* p, int64_t p_stride,
+                                          const int32_t* k, int64_t k_stride, const void* min_p,
+                                          int64_t min_p_stride, void* out, int64_t out_row_stride,
+                                          int64_t out_col_stride, void* stream);
+
+/*
  * apply_top_k_top_p_with_sorted_ex — apply_top_k_top_p_min_p_with_sorted on
  * row-strided operands, one row stride (in elements) per [B, V] operand, with
  * the rules of apply_top_k_top_p_ex. ld_logits is ignored when logits is NULL.

@@ -135,6 +135,43 @@ def test_strided_entry_points_check_strides(lib):
     assert g(None, 8, FAKE, 8, 0, 0, 8, None, None, None, None, 0, None, 8, None) == 0
 
 
+def test_element_strided_entry_point_checks(lib):
+    """apply_top_k_top_p_strided: stride ranges, an out layout that gives
+    every position its own element, span overlaps, and the usual order of
+    checks (pointers, dtype, shape)."""
+    f = lib.apply_top_k_top_p_strided
+    out = FAKE + (1 << 36)
+
+    def call(x=FAKE, xr=8, xc=1, dt=0, B=2, V=8, p=FAKE, ps=1, k=None, ks=1, mp=None, ms=1, o=out, orr=8, oc=1):
+        return f(x, xr, xc, dt, B, V, p, ps, k, ks, mp, ms, o, orr, oc, None)
+
+    assert call(x=None) == NULLPTR
+    assert call(o=None) == NULLPTR
+    assert call(p=None) == NULLPTR and "min_p" in tk.last_error()
+    assert call(dt=3) == INVALID and "dtype" in tk.last_error()
+    assert call(V=(1 << 20) + 1) == INVALID
+    assert call(xc=-1) == INVALID and "logits_col_stride" in tk.last_error()
+    assert call(xr=(1 << 31) + 1) == INVALID and "logits_row_stride" in tk.last_error()
+    assert call(ps=-2) == INVALID and "p_stride" in tk.last_error()
+    assert call(k=FAKE + (1 << 34), ks=-1) == INVALID and "k_stride" in tk.last_error()
+    assert call(mp=FAKE + (1 << 35), ms=-1) == INVALID and "min_p_stride" in tk.last_error()
+    assert call(orr=0, oc=1) == INVALID and "out_row_stride" in tk.last_error()
+    assert call(oc=0) == INVALID and "out_col_stride" in tk.last_error()
+    # out strides that map two positions to one element: (b, v) -> 3b + v
+    assert call(orr=3, oc=1) == INVALID and "map two positions" in tk.last_error()
+    assert call(B=3, orr=2, oc=5) == INVALID  # 3 rows in steps of 2 overrun the column stride 5
+    # strides of NULL operands and along extents of 1 are ignored (each call
+    # still fails at a later check, so nothing is launched)
+    assert call(k=None, ks=-5, orr=3) == INVALID and "map two positions" in tk.last_error()
+    assert call(B=1, xr=-3, orr=0, oc=0) == INVALID and "out_col_stride" in tk.last_error()
+    assert call(V=1, xc=-3, oc=0, orr=0) == INVALID and "out_row_stride" in tk.last_error()
+    # the span of out, [out, out + 64), reaches the span of logits
+    assert call(x=out + 32, xr=1, xc=4, orr=1, oc=2) == INVALID and "overlap" in tk.last_error()
+    # p with stride 0 (one value for every row) sitting inside out
+    assert call(p=out + 4, ps=0) == INVALID and "overlap" in tk.last_error()
+    assert call(B=0, x=None, o=None, p=None) == 0  # empty
+
+
 def test_sample_entry_point_checks(lib):
     f = lib.sample_top_k_top_p
     sel = FAKE + (1 << 36)

@@ -72,3 +72,87 @@ def test_with_sorted_strided(use_logits, dtype, V):
         assert rep.hard_mismatches == 0, (dtype, V, use_logits, min_p is None, rep.details[:2])
         assert np.array_equal(got[:, :V], from_dev(dense, dtype))
         assert (got[:, V:] == SENTINEL[dtype]).all()
+
+
+def _filled(shape, dtype):
+    """A device buffer of the given shape holding the sentinel everywhere."""
+    nt = np.uint32 if dtype == "f32" else np.uint16
+    return to_dev(np.full(shape, SENTINEL[dtype], dtype=nt), dtype)
+
+
+def _bits(t, dtype):
+    return from_dev(t.contiguous(), dtype)
+
+
+# (name, dtype, B, V): element-strided layouts of logits and out
+ELEMENT_CASES = [("transposed", "bf16", 8, 70001), ("transposed", "f32", 5, 4099),
+                 ("column_step", "f16", 6, 32000), ("column_step", "bf16", 3, 262144),
+                 ("params_strided", "bf16", 7, 151936), ("rows_overlap", "f32", 6, 65536),
+                 ("column_step", "f16", 1, 5000), ("transposed", "bf16", 9, 2)]
+
+
+@pytest.mark.parametrize("policy", [0, 1])
+@pytest.mark.parametrize("name,dtype,B,V", ELEMENT_CASES)
+def test_apply_element_strided(name, dtype, B, V, policy):
+    """Views with a non-unit element stride (a transposed [V, B] buffer, every
+    second or third column of a wider one, parameters with strides 0, 2 and 3,
+    input rows that share elements) through apply_top_k_top_p_strided: the
+    oracle on the dense values decides, the row-contiguous call must give the
+    same bits, and out's elements outside the view stay untouched."""
+    torch = need_gpu()
+    import top_logits_filtering_amd as tk
+
+    seed = 2300 + V + B
+    xb = random_rows(seed, B, V, dtype, kind="gumbel")
+    k, p = random_params(seed, B, V, dtype, k_lo=1, k_hi=min(V, 3000))
+    mp = random_min_p(seed, B, dtype)
+    if name == "rows_overlap":  # row b starts at element b * V / 2 of one buffer
+        half = V // 2
+        flat = random_rows(seed, 1, half * (B + 1), dtype, kind="gumbel")[0]
+        xb = np.stack([flat[b * half:b * half + V] for b in range(B)])
+    try:
+        tk.set_plan_policy(policy)
+        for min_p in (None, mp):
+            dense = tk.apply_top_k_top_p(to_dev(xb, dtype), to_dev(p, dtype), k_dev(k), min_p=to_dev(min_p, dtype))
+            pd, kd, md = to_dev(p, dtype), k_dev(k), to_dev(min_p, dtype)
+            if name == "transposed":
+                x = to_dev(np.ascontiguousarray(xb.T), dtype).t()
+                obuf = _filled((V, B), dtype)
+                out = obuf.t()
+            elif name == "column_step":
+                wide = np.zeros((B, 2 * V + 1), dtype=xb.dtype)
+                wide[:, 1::2] = xb
+                x = to_dev(wide, dtype)[:, 1::2]
+                obuf = _filled((B, 3 * V), dtype)
+                out = obuf[:, ::3]
+            elif name == "params_strided":
+                x = to_dev(xb, dtype)
+                obuf = _filled((B, V), dtype)
+                out = obuf
+                pb = np.zeros(2 * B, dtype=p.dtype)
+                pb[::2] = p
+                kb = np.zeros(3 * B, dtype=np.int32)
+                kb[::3] = k
+                pd, kd = to_dev(pb, dtype)[::2], k_dev(kb)[::3]
+                if min_p is not None:  # one value shared by every row (stride 0)
+                    md = to_dev(min_p[:1], dtype).expand(B)
+                    min_p = np.repeat(min_p[:1], B)
+                    dense = tk.apply_top_k_top_p(to_dev(xb, dtype), to_dev(p, dtype), k_dev(k),
+                                                 min_p=to_dev(min_p, dtype))
+            else:  # rows_overlap
+                x = to_dev(flat, dtype).as_strided((B, V), (V // 2, 1))
+                obuf = _filled((B, V), dtype)
+                out = obuf
+            torch.cuda.synchronize()
+            tk.apply_top_k_top_p(x, pd, kd, out=out, min_p=md)
+            torch.cuda.synchronize()
+            got = _bits(out, dtype)
+            rep = compare(got, xb, oracle_apply(xb, dtype, p, k, min_p_bits=min_p), dtype)
+            case = (name, dtype, B, V, policy, min_p is not None)
+            assert rep.hard_mismatches == 0, (case, rep.details[:2])
+            assert np.array_equal(got, from_dev(dense, dtype)), case
+            whole = from_dev(obuf.contiguous(), dtype)
+            assert int((whole != SENTINEL[dtype]).sum()) == B * V - int((got == SENTINEL[dtype]).sum()), case
+            say(f"element-strided {case}: {rep}")
+    finally:
+        tk.set_plan_policy(0)

@@ -22,6 +22,7 @@ EXPORTED_SYMBOLS = (
     "apply_top_k_top_p_ex",
     "apply_top_k_top_p_min_p",
     "apply_top_k_top_p_min_p_with_sorted",
+    "apply_top_k_top_p_strided",
     "apply_top_k_top_p_with_sorted",
     "apply_top_k_top_p_with_sorted_ex",
     "sample_top_k_top_p",
@@ -65,6 +66,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.apply_top_k_top_p_ex.restype = i32
     lib.apply_top_k_top_p_with_sorted_ex.argtypes = [vp, i64, vp, i64, i32, i64, i64, vp, vp, vp, vp, i64, vp, i64, vp]
     lib.apply_top_k_top_p_with_sorted_ex.restype = i32
+    lib.apply_top_k_top_p_strided.argtypes = [vp, i64, i64, i32, i64, i64, vp, i64, vp, i64, vp, i64, vp, i64, i64, vp]
+    lib.apply_top_k_top_p_strided.restype = i32
     lib.sample_top_k_top_p.argtypes = [vp, i32, i64, i64, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp]
     lib.sample_top_k_top_p.restype = i32
     lib.top_k_top_p_sorted_survivors.argtypes = [vp, i32, i64, i64, vp, vp, vp, i64, vp, vp, vp, vp]
@@ -131,6 +134,24 @@ def _rows(t):
     return t.data_ptr(), ld
 
 
+def _rows_contiguous(t) -> bool:
+    """Rows contiguous and disjoint: a view the row-strided entry points take."""
+    B, V = t.shape
+    return (V <= 1 or t.stride(1) == 1) and (B <= 1 or t.stride(0) >= V)
+
+
+def _entries(t, B):
+    """(pointer, stride in elements) of a [B] parameter vector of any stride;
+    (None, 0) for None."""
+    if t is None:
+        return None, 0
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    if t.dim() != 1 or t.shape[0] != B:
+        raise ValueError(f"expected a 1-D tensor of {B} entries, got shape {tuple(t.shape)}")
+    return t.data_ptr(), t.stride(0)
+
+
 def _stream(stream, device) -> int:
     """The HIP stream handle to launch on: the given one, else torch's current
     stream of the tensors' device."""
@@ -148,8 +169,10 @@ def _check(status: int):
 
 def apply_top_k_top_p(logits, p=None, k=None, out=None, stream=None, min_p=None):
     """Filter raw logits [B, V]; p [B] (logits dtype), k [B] (int32) and min_p
-    [B] (logits dtype, the min-p stage) are optional. logits and out may be
-    row-strided views (rows contiguous, e.g. a slice of a padded vocabulary)."""
+    [B] (logits dtype, the min-p stage) are optional. Every operand may be a
+    strided view: row-strided ones (rows contiguous, e.g. a slice of a padded
+    vocabulary) take the vector kernels, any other view (a transpose, a
+    column step, parameters with a stride) the element-wise strided kernel."""
     import torch
 
     lib = load_library()
@@ -158,7 +181,19 @@ def apply_top_k_top_p(logits, p=None, k=None, out=None, stream=None, min_p=None)
     B, V = logits.shape
     if out is None:
         out = torch.empty((B, V), dtype=logits.dtype, device=logits.device)
+    if out.dim() != 2 or tuple(out.shape) != (B, V):
+        raise ValueError(f"out must be [{B}, {V}]")
     st = _stream(stream, logits.device)
+    params = [t for t in (p, k, min_p) if t is not None]
+    if not (_rows_contiguous(logits) and _rows_contiguous(out) and all(t.is_contiguous() for t in params)):
+        if not (logits.is_cuda and out.is_cuda):
+            raise ValueError("tensors must live on the GPU")
+        (pp, ps), (kp, ks), (mp, ms) = _entries(p, B), _entries(k, B), _entries(min_p, B)
+        status = lib.apply_top_k_top_p_strided(logits.data_ptr(), logits.stride(0), logits.stride(1),
+                                               _dtype_code(logits), B, V, pp, ps, kp, ks, mp, ms, out.data_ptr(),
+                                               out.stride(0), out.stride(1), st)
+        _check(status)
+        return out
     (xp, ldx), (op, ldo) = _rows(logits), _rows(out)
     if ldx != V or ldo != V:
         status = lib.apply_top_k_top_p_ex(xp, ldx, _dtype_code(logits), B, V, _ptr(p), _ptr(k), _ptr(min_p), op, ldo,

@@ -121,6 +121,76 @@ topktopp_status apply_impl(const void* logits, int64_t ldx, int dtype, int64_t B
                       "filter launch");
 }
 
+// Strides of a strided view: in [lo, TOPKTOPP_MAX_LD].
+topktopp_status check_stride(int64_t s, int64_t lo, const char* name) {
+  if (s < lo || s > TOPKTOPP_MAX_LD)
+    return fail(TOPKTOPP_ERR_INVALID, "stride %s=%lld is outside [%lld, 2^31]", name, (long long)s, (long long)lo);
+  return TOPKTOPP_OK;
+}
+
+// Bytes from the first to one past the last element of a [B, V] view with
+// non-negative strides sr (rows) and sc (elements).
+size_t span2(int64_t B, int64_t V, int64_t sr, int64_t sc, size_t es) {
+  return (static_cast<size_t>(B - 1) * static_cast<size_t>(sr) + static_cast<size_t>(V - 1) * static_cast<size_t>(sc) + 1) *
+         es;
+}
+
+topktopp_status strided_impl(const void* logits, int64_t xr, int64_t xc, int dtype, int64_t B, int64_t V,
+                             const void* p, int64_t ps, const int32_t* k, int64_t ks, const void* min_p, int64_t ms,
+                             void* out, int64_t orr, int64_t oc, void* stream) {
+  g_last_error.clear();
+  if (B >= 0 && V >= 0 && (B == 0 || V == 0)) {  // empty: nothing is read or written, pointers may be NULL
+    if (!valid_dtype(dtype)) return fail(TOPKTOPP_ERR_INVALID, "dtype %d is not one of F32, F16, BF16", dtype);
+    return TOPKTOPP_OK;
+  }
+  if (logits == nullptr) return fail(TOPKTOPP_ERR_NULLPTR, "logits is NULL");
+  if (out == nullptr) return fail(TOPKTOPP_ERR_NULLPTR, "out is NULL");
+  if (topktopp_status s = check_params(p, k, min_p, true)) return s;
+  if (!valid_dtype(dtype)) return fail(TOPKTOPP_ERR_INVALID, "dtype %d is not one of F32, F16, BF16", dtype);
+  if (topktopp_status s = check_shape(B, V)) return s;
+  // a stride along an extent of 1 plays no part: take it as 0 (inputs) or 1 (out)
+  if (B == 1) xr = ps = ks = ms = 0, orr = 1;
+  if (V == 1) xc = 0, oc = 1;
+  if (p == nullptr) ps = 0;
+  if (k == nullptr) ks = 0;
+  if (min_p == nullptr) ms = 0;
+  if (topktopp_status s = check_stride(xr, 0, "logits_row_stride")) return s;
+  if (topktopp_status s = check_stride(xc, 0, "logits_col_stride")) return s;
+  if (topktopp_status s = check_stride(ps, 0, "p_stride")) return s;
+  if (topktopp_status s = check_stride(ks, 0, "k_stride")) return s;
+  if (topktopp_status s = check_stride(ms, 0, "min_p_stride")) return s;
+  if (topktopp_status s = check_stride(orr, 1, "out_row_stride")) return s;
+  if (topktopp_status s = check_stride(oc, 1, "out_col_stride")) return s;
+  if (!(orr >= V * oc || oc >= B * orr))
+    return fail(TOPKTOPP_ERR_INVALID,
+                "out strides (%lld, %lld) may map two positions of [%lld, %lld] to one element", (long long)orr,
+                (long long)oc, (long long)B, (long long)V);
+  const size_t es = elem_size(dtype);
+  const size_t nout = span2(B, V, orr, oc, es);
+  if (overlaps(out, nout, logits, span2(B, V, xr, xc, es)) || overlaps(out, nout, p, span2(B, 1, ps, 0, es)) ||
+      overlaps(out, nout, k, span2(B, 1, ks, 0, 4)) || overlaps(out, nout, min_p, span2(B, 1, ms, 0, es)))
+    return fail(TOPKTOPP_ERR_INVALID, "out overlaps an input buffer");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (V == 1)  // a last dimension of 1 is copied through unfiltered
+    return check_launch(hipMemcpy2DAsync(out, static_cast<size_t>(orr) * es, logits, static_cast<size_t>(xr) * es, es,
+                                         static_cast<size_t>(B), hipMemcpyDeviceToDevice, st),
+                        "hipMemcpy2DAsync");
+  // contiguous rows and dense parameters: the row-strided path
+  const bool dense_params = (p == nullptr || B == 1 || ps == 1) && (k == nullptr || B == 1 || ks == 1) &&
+                            (min_p == nullptr || B == 1 || ms == 1);
+  if (xc == 1 && oc == 1 && dense_params && (B == 1 || (xr >= V && orr >= V)))
+    return apply_impl(logits, B == 1 ? V : xr, dtype, B, V, p, k, min_p, true, out, B == 1 ? V : orr, stream);
+  tkp::RowStrides ld{xr, orr, 0, 0};
+  ld.elementwise = true;
+  ld.xc = xc;
+  ld.oc = oc;
+  ld.pc = ps;
+  ld.kc = ks;
+  ld.mc = ms;
+  return check_launch(tkp::launch_apply(dtype, logits, p, k, min_p, out, B, V, ld, g_policy.load(), st),
+                      "filter launch");
+}
+
 topktopp_status with_sorted_impl(const void* sorted_value, int64_t lds, const int32_t* sorted_indices, int64_t ldi,
                                  int dtype, int64_t B, int64_t V, const void* p, const int32_t* k,
                                  const void* min_p, bool has_min_p, const void* logits, int64_t ldx, void* out,
@@ -269,6 +339,15 @@ topktopp_status apply_top_k_top_p_ex(const void* logits, int64_t ld_logits, topk
                                      const void* p, const int32_t* k, const void* min_p, void* out, int64_t ld_out,
                                      void* stream) {
   return apply_impl(logits, ld_logits, dtype, B, V, p, k, min_p, true, out, ld_out, stream);
+}
+
+topktopp_status apply_top_k_top_p_strided(const void* logits, int64_t logits_row_stride, int64_t logits_col_stride,
+                                          topktopp_dtype dtype, int64_t B, int64_t V, const void* p, int64_t p_stride,
+                                          const int32_t* k, int64_t k_stride, const void* min_p,
+                                          int64_t min_p_stride, void* out, int64_t out_row_stride,
+                                          int64_t out_col_stride, void* stream) {
+  return strided_impl(logits, logits_row_stride, logits_col_stride, dtype, B, V, p, p_stride, k, k_stride, min_p,
+                      min_p_stride, out, out_row_stride, out_col_stride, stream);
 }
 
 topktopp_status apply_top_k_top_p_with_sorted(const void* sorted_value, const int32_t* sorted_indices, topktopp_dtype dtype,

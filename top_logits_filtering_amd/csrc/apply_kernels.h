@@ -314,8 +314,8 @@ __device__ __forceinline__ void select_small(const ApplySmem& S, vec_t* tab, int
 // Returns true when the row fell back to the multi-pass plan over the row in
 // global memory, whose survivors the sampling stage then takes from there;
 // otherwise the plan has done the sampling stage itself. K, I: the result.
-template <class DT, bool kSample, class Tile>
-__device__ __forceinline__ bool candidate_plan(const Tile& tile, const GlobalTile<DT>& gt, int V, const RowParams& rp,
+template <class DT, bool kSample, class Tile, class GT>
+__device__ __forceinline__ bool candidate_plan(const Tile& tile, const GT& gt, int V, const RowParams& rp,
                                                ApplySmem& S, typename DT::raw_t* __restrict__ orow, bool wr,
                                                const SampleArgs& sa, int b, uint32_t& K, uint32_t& I) {
   using raw_t = typename DT::raw_t;
@@ -758,7 +758,7 @@ __device__ __forceinline__ bool candidate_plan(const Tile& tile, const GlobalTil
       __syncthreads();
       cs.for_each([&](auto raw, int idx) {
         const uint32_t key = DT::key(raw);
-        if (key > K || (key == K && static_cast<uint32_t>(idx) >= I)) orow[idx] = raw;
+        if (key > K || (key == K && static_cast<uint32_t>(idx) >= I)) orow[gt.out_at(idx)] = raw;
       });
     }
   } else if constexpr (Tile::kRegisters && Tile::kVecs <= kRegFallbackVecs) {
@@ -775,12 +775,13 @@ __device__ __forceinline__ bool candidate_plan(const Tile& tile, const GlobalTil
 }
 
 
-// `tile` holds the row (registers or global); `irow` is the same row in
-// global memory, re-read by the multi-pass fallback. kSample adds the
-// sampling stage (sample.h) and makes the row's output optional (wr).
-template <class DT, bool kSample, class Tile>
-__device__ __forceinline__ void filter_row(const Tile& tile, const typename DT::raw_t* __restrict__ irow, int V,
-                                           const RowParams& rp, bool use_candidates, ApplySmem& S,
+// `tile` holds the row (registers or global); `gt` is the same row in
+// global memory, re-read by the multi-pass fallback (a GlobalTile, strided
+// for views with a non-unit element stride). kSample adds the sampling stage
+// (sample.h) and makes the row's output optional (wr).
+template <class DT, bool kSample, class Tile, class GT>
+__device__ __forceinline__ void filter_row(const Tile& tile, const GT& gt, int V, const RowParams& rp,
+                                           bool use_candidates, ApplySmem& S,
                                            typename DT::raw_t* __restrict__ orow, bool wr_out,
                                            const SampleArgs& sa, int b) {
   const bool wr = kSample ? wr_out : true;
@@ -788,8 +789,6 @@ __device__ __forceinline__ void filter_row(const Tile& tile, const typename DT::
   constexpr int kPV = DT::kPerVec;
   RowSmem& sm = S.row;
   SelSmem& ss = S.sel;
-  GlobalTile<DT> gt;
-  gt.load(irow, 0, V);
   sel_reset(ss);
 
   if constexpr (kSample) {
@@ -854,7 +853,9 @@ __global__ __launch_bounds__(kThreads) void apply_regs_kernel(const typename DT:
   RegTile<DT, NVEC> tile;
   tile.load(logits + offx, 0, V);
   const RowParams rp = decode_row_params<DT>(rpr, V);
-  filter_row<DT, kSample>(tile, logits + offx, V, rp, use_candidates != 0, S, out + offo, out != nullptr, sa, b);
+  GlobalTile<DT> gt;
+  gt.load(logits + offx, 0, V);
+  filter_row<DT, kSample>(tile, gt, V, rp, use_candidates != 0, S, out + offo, out != nullptr, sa, b);
 }
 
 template <class DT, bool kSample>
@@ -871,7 +872,28 @@ __global__ __launch_bounds__(kThreads) void apply_stream_kernel(const typename D
   const RowParams rp = decode_row_params<DT>(p, k, min_p, b, V);
   GlobalTile<DT> tile;
   tile.load(logits + offx, 0, V);
-  filter_row<DT, kSample>(tile, logits + offx, V, rp, use_candidates != 0, S, out + offo, out != nullptr, sa, b);
+  filter_row<DT, kSample>(tile, tile, V, rp, use_candidates != 0, S, out + offo, out != nullptr, sa, b);
+}
+
+// Views with a non-unit element stride: element (b, v) of logits sits at
+// b * ld.x + v * ld.xc and of out at b * ld.o + v * ld.oc; p, k and min_p
+// step by ld.pc, ld.kc and ld.mc. The streamed plan with element accesses.
+template <class DT>
+__global__ __launch_bounds__(kThreads) void apply_strided_kernel(const typename DT::raw_t* __restrict__ logits,
+                                                                 const typename DT::raw_t* __restrict__ p,
+                                                                 const int32_t* __restrict__ k,
+                                                                 const typename DT::raw_t* __restrict__ min_p,
+                                                                 typename DT::raw_t* __restrict__ out, int V,
+                                                                 RowStrides ld, int use_candidates) {
+  __shared__ ApplySmem S;
+  const int b = blockIdx.x;
+  const RowParams rp = decode_row_params<DT>(
+      fetch_row_params_strided<DT>(p, k, min_p, static_cast<int64_t>(b), ld.pc, ld.kc, ld.mc), V);
+  GlobalTile<DT, true> tile;
+  tile.load_strided(logits + static_cast<size_t>(b) * static_cast<size_t>(ld.x), V, ld.xc, ld.oc);
+  const SampleArgs sa{nullptr, 0, 0.0f, nullptr, nullptr, nullptr, nullptr, 0};
+  filter_row<DT, false>(tile, tile, V, rp, use_candidates != 0, S, out + static_cast<size_t>(b) * static_cast<size_t>(ld.o),
+                        true, sa, b);
 }
 
 template <class DT, int NVEC, bool kSample>
@@ -926,6 +948,15 @@ hipError_t launch_apply_rows(const void* logits, const void* p, const int32_t* k
   constexpr int span = kThreads * DT::kPerVec;
   const int64_t vecs = (V + span - 1) / span;
   const int use_candidates = policy == kPlanGeneral ? 0 : 1;
+  if constexpr (!kSample) {
+    if (ld.elementwise) {
+      hipLaunchKernelGGL((apply_strided_kernel<DT>), dim3(static_cast<unsigned>(B)), dim3(kThreads), 0, stream,
+                         static_cast<const raw_t*>(logits), static_cast<const raw_t*>(p), k,
+                         static_cast<const raw_t*>(min_p), static_cast<raw_t*>(out), static_cast<int>(V), ld,
+                         use_candidates);
+      return hipGetLastError();
+    }
+  }
   // register tiles move whole 16-byte vectors: every row must start 16-byte aligned
   constexpr int64_t es = static_cast<int64_t>(sizeof(raw_t));
   const bool vec_ok = (V % DT::kPerVec) == 0 && (reinterpret_cast<uintptr_t>(logits) & 15u) == 0 &&
@@ -984,8 +1015,10 @@ hipError_t launch_apply_t(const void* logits, const void* p, const int32_t* k, c
     if (s.indices != nullptr) s.indices += r0 * s.cap;
     if (s.counts != nullptr) s.counts += r0;
     const hipError_t e = launch_apply_rows<DT, kSample>(
-        static_cast<const raw_t*>(logits) + r0 * ld.x, p == nullptr ? nullptr : static_cast<const raw_t*>(p) + r0,
-        k == nullptr ? nullptr : k + r0, min_p == nullptr ? nullptr : static_cast<const raw_t*>(min_p) + r0,
+        static_cast<const raw_t*>(logits) + r0 * ld.x,
+        p == nullptr ? nullptr : static_cast<const raw_t*>(p) + r0 * ld.pc,
+        k == nullptr ? nullptr : k + r0 * ld.kc,
+        min_p == nullptr ? nullptr : static_cast<const raw_t*>(min_p) + r0 * ld.mc,
         out == nullptr ? nullptr : static_cast<raw_t*>(out) + r0 * ld.o, nb, V, ld, policy, stream, s);
     if (e != hipSuccess) return e;
   }

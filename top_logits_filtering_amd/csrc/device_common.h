@@ -360,6 +360,21 @@ __device__ __forceinline__ RowParamsRaw<DT> fetch_row_params(const typename DT::
   return r;
 }
 
+// The same for parameter vectors whose entries are pc, kc and mc elements apart.
+template <class DT>
+__device__ __forceinline__ RowParamsRaw<DT> fetch_row_params_strided(const typename DT::raw_t* p, const int32_t* k,
+                                                                     const typename DT::raw_t* min_p, int64_t b,
+                                                                     int64_t pc, int64_t kc, int64_t mc) {
+  RowParamsRaw<DT> r;
+  r.has_k = k != nullptr;
+  r.has_p = p != nullptr;
+  r.has_mp = min_p != nullptr;
+  r.k = r.has_k ? k[b * kc] : 0;
+  r.p = r.has_p ? p[b * pc] : static_cast<typename DT::raw_t>(0);
+  r.mp = r.has_mp ? min_p[b * mc] : static_cast<typename DT::raw_t>(0);
+  return r;
+}
+
 template <class DT>
 __device__ __forceinline__ RowParams decode_row_params(const RowParamsRaw<DT>& r, int V) {
   RowParams rp;

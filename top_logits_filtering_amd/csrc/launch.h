@@ -17,12 +17,18 @@ constexpr int64_t kMaxLaunchBlocks = int64_t{1} << 21;
 enum PlanPolicy : int { kPlanAuto = 0, kPlanGeneral = 1, kPlanStream = 2 };
 
 // Elements between the starts of consecutive rows of each [B, V] operand
-// (each >= V; V when the operand is dense).
+// (each >= V; V when the operand is dense). `elementwise` selects the filter
+// kernel for arbitrary strided views, which also reads the element strides:
+// along a row of logits and out, and between the rows' entries of p, k and
+// min_p (0 shares one entry among all rows).
 struct RowStrides {
   int64_t x;   // logits
   int64_t o;   // out
   int64_t sv;  // sorted_value
   int64_t si;  // sorted_indices
+  bool elementwise = false;
+  int64_t xc = 1, oc = 1;          // element strides of logits and out
+  int64_t pc = 1, kc = 1, mc = 1;  // entry strides of p, k and min_p
 };
 
 hipError_t launch_apply_f32(const void* logits, const void* p, const int32_t* k, const void* min_p, void* out,

@@ -236,8 +236,10 @@ struct RegTile {
 
 // The same interface for rows too long to keep in registers: every traversal
 // reads the row again from global memory, so later traversals mostly hit L2
-// or the Infinity Cache.
-template <class DT>
+// or the Infinity Cache. kStrided: element j of the row sits cs elements after
+// element j - 1 (and of the output row ocs after), for views with a non-unit
+// element stride; every access is then one element at a time.
+template <class DT, bool kStrided = false>
 struct GlobalTile {
   using raw_t = typename DT::raw_t;
   static constexpr bool kRegisters = false;
@@ -250,13 +252,35 @@ struct GlobalTile {
   int len;
   bool aligned;
   bool vec_ok;  // 16-byte aligned and a whole number of vectors: bounded buffer loads
+  int64_t cs = 1;   // element stride of the row (kStrided only)
+  int64_t ocs = 1;  // element stride of the output row (kStrided only)
 
   __device__ __forceinline__ void load(const raw_t* __restrict__ row, int v0, int n) {
     src = row + v0;
     base = v0;
     len = n;
-    aligned = (reinterpret_cast<uintptr_t>(src) & 15u) == 0;
+    aligned = !kStrided && (reinterpret_cast<uintptr_t>(src) & 15u) == 0;
     vec_ok = aligned && (n % kPV) == 0;
+  }
+  // kStrided: the row's element stride and the output row's
+  __device__ __forceinline__ void load_strided(const raw_t* __restrict__ row, int n, int64_t stride,
+                                               int64_t out_stride) {
+    src = row;
+    base = 0;
+    len = n;
+    aligned = false;
+    vec_ok = false;
+    cs = stride;
+    ocs = out_stride;
+  }
+  __device__ __forceinline__ raw_t elem(int e) const {
+    if constexpr (kStrided) return src[static_cast<int64_t>(e) * cs];
+    else return src[e];
+  }
+  // the output element of row index idx, as an offset from the output row's start
+  __device__ __forceinline__ int64_t out_at(int idx) const {
+    if constexpr (kStrided) return static_cast<int64_t>(idx) * ocs;
+    else return idx;
   }
 
   // Vector layers handled per batch by the first traversal: their loads are
@@ -268,7 +292,7 @@ struct GlobalTile {
     if (aligned && e0 + kPV <= len) return *reinterpret_cast<const vec_t*>(src + e0);
     vec_t q = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int j = 0; j < kPV; ++j) set_lane<raw_t>(q, j, (e0 + j < len) ? src[e0 + j] : static_cast<raw_t>(0));
+    for (int j = 0; j < kPV; ++j) set_lane<raw_t>(q, j, (e0 + j < len) ? elem(e0 + j) : static_cast<raw_t>(0));
     return q;
   }
 
@@ -286,6 +310,10 @@ struct GlobalTile {
   __device__ __forceinline__ vec_t vec_at(int, int e0) const { return read(e0); }
 
   __device__ __forceinline__ void store_const(raw_t* __restrict__ row, raw_t c) const {
+    if constexpr (kStrided) {
+      for (int e = static_cast<int>(threadIdx.x); e < len; e += kThreads) row[out_at(base + e)] = c;
+      return;
+    }
     raw_t* dst = row + base;
     const bool dst_aligned = (reinterpret_cast<uintptr_t>(dst) & 15u) == 0;
     vec_t cv = {0u, 0u, 0u, 0u};
@@ -372,6 +400,10 @@ struct GlobalTile {
 
   template <class G>
   __device__ __forceinline__ void store(raw_t* __restrict__ row, G&& g) const {
+    if constexpr (kStrided) {
+      for (int e = static_cast<int>(threadIdx.x); e < len; e += kThreads) row[out_at(base + e)] = g(elem(e), base + e);
+      return;
+    }
     raw_t* dst = row + base;
     const bool dst_aligned = (reinterpret_cast<uintptr_t>(dst) & 15u) == 0;
 #pragma unroll 2

@@ -266,37 +266,58 @@ __device__ __forceinline__ SortedBoundary sorted_boundary_copy(const typename DT
   if (rp.pmode == kPTopOnly) {
     F = R - 1;
   } else if (rp.pmode == kPBoundary) {
+    // Only positions at or above cs hold mass: threads wholly below it (whole
+    // waves, for all but the largest k) skip the exponentials, and only the
+    // thread holding the boundary walks its positions one by one. Every
+    // block of a row repeats this search, and the blocks resident on a
+    // compute unit share its vector ALUs.
     const float m = DT::value(top[R - 1]);
     const int hi = R - G * static_cast<int>(threadIdx.x);  // this thread: positions hi-1 down to hi-G
-    // (the masses are computed twice rather than kept, which keeps two blocks
-    // resident per compute unit)
-    auto mass_at = [&](int c) { return c >= cs ? mass_fx(DT::value(top[c]), m) : 0ull; };
-    uint64_t tsum = 0;
+    const bool live = hi > cs;                              // it holds a position at or above cs
+    auto mass_at = [&](int c) { return mass_fx(DT::value(top[c]), m); };
+    uint64_t tsum = 0, e_lo = 0;  // e_lo: mass of its lowest position at or above cs
+    if (live) {
 #pragma unroll
-    for (int g = 0; g < G; ++g) tsum += mass_at(hi - 1 - g);
+      for (int g = 0; g < G; ++g) {
+        const int c = hi - 1 - g;
+        if (c >= cs) {
+          e_lo = mass_at(c);
+          tsum += e_lo;
+        }
+      }
+    }
     uint64_t Z;
-    uint64_t above = block_exscan_u64(tsum, sm, Z);  // threads run from the top down
+    const uint64_t above = block_exscan_u64(tsum, sm, Z);  // threads run from the top down
     const uint64_t thr = topp_threshold(rp.t, Z);
     if (thr == 0) {
       F = R - 1;
     } else {
       int low = -1;  // this thread's lowest position whose mass strictly above is below thr
+      if (live && above < thr) {
+        if (above + (tsum - e_lo) < thr) {  // even its lowest position qualifies
+          low = max(hi - G, cs);
+        } else {  // the boundary lies among its positions
+          uint64_t acc = above;
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
-        const int c = hi - 1 - g;
-        if (c >= cs && above < thr) low = c;
-        above += mass_at(c);
+          for (int g = 0; g < G; ++g) {
+            const int c = hi - 1 - g;
+            if (c >= cs) {
+              if (acc < thr) low = c;
+              acc += mass_at(c);
+            }
+          }
+        }
       }
       F = R - 1 - block_max_i32(low >= 0 ? R - 1 - low : -1, sm);
     }
   }
-  if (rp.mp_on) {  // min-p survivors are a suffix of the copy (or all of it)
+  if (rp.mp_on) {  // min-p survivors are a suffix of the copy: count them among the positions >= F
     const float m = DT::value(top[R - 1]);
     uint32_t c = 0;
 #pragma unroll
     for (int u = 0; u < G; ++u) {
       const int ci = u * kThreads + static_cast<int>(threadIdx.x);
-      if (ci < R && min_p_keeps(DT::value(top[ci]), m, rp.minp)) ++c;
+      if (ci >= F && ci < R && min_p_keeps(DT::value(top[ci]), m, rp.minp)) ++c;
     }
     F = max(F, R - static_cast<int>(block_sum_u32(c, sm)));
   }

@@ -4,7 +4,11 @@ an MI355X). Row lengths are drawn from three ranges (short rows, rows held in
 registers, streamed rows), so the cases cross every plan's branch points.
 About a third of the filter cases pass row-strided views (each operand in a
 buffer padded by 1-70 elements per row, so most row strides are not a
-multiple of 16 bytes), and the padding must stay untouched."""
+multiple of 16 bytes), and the padding must stay untouched. Of the other
+raw-logits filter cases about a fifth pass element-strided views: logits
+transposed or every second column, out transposed or every third column,
+and p, k and min_p with strides 2, 3 and 2; out's other elements must stay
+untouched."""
 
 import numpy as np
 import pytest
@@ -72,6 +76,45 @@ def strided_sorted(sv, idx, dtype, p, k, logits, mp, pads):
     return np.ascontiguousarray(got[:, :V])
 
 
+def elem_apply(xb, dtype, p, k, mp, mode):
+    """The filter on element-strided views (mode 0-3: logits transposed or
+    every second column, out transposed or every third column); returns the
+    [B, V] result after checking that out's other elements are untouched."""
+    import torch
+    import top_logits_filtering_amd as tk
+
+    B, V = xb.shape
+    nt = np.uint32 if dtype == "f32" else np.uint16
+    if mode % 2 == 0:
+        x = to_dev(np.ascontiguousarray(xb.T), dtype).t()
+    else:
+        wide = np.full((B, 2 * V), SENTINEL[dtype], nt)
+        wide[:, ::2] = xb
+        x = to_dev(wide, dtype)[:, ::2]
+    if mode // 2 == 0:
+        obuf = to_dev(np.full((V, B), SENTINEL[dtype], nt), dtype)
+        out = obuf.t()
+    else:
+        obuf = to_dev(np.full((B, 3 * V), SENTINEL[dtype], nt), dtype)
+        out = obuf[:, ::3]
+
+    def spaced(a, step, conv):
+        if a is None:
+            return None
+        buf = np.zeros(step * len(a), dtype=a.dtype)
+        buf[::step] = a
+        return conv(buf)[::step]
+
+    pd = spaced(p, 2, lambda a: to_dev(a, dtype))
+    kd = spaced(k, 3, k_dev)
+    md = spaced(mp, 2, lambda a: to_dev(a, dtype))
+    tk.apply_top_k_top_p(x, pd, kd, out=out, min_p=md)
+    torch.cuda.synchronize()
+    whole = from_dev(obuf, dtype)
+    assert int((whole != SENTINEL[dtype]).sum()) == B * V, "an element outside the view was written"
+    return from_dev(out.contiguous(), dtype)
+
+
 @pytest.mark.parametrize("sweep_seed", [101, 202])
 def test_random_sweep(sweep_seed):
     need_gpu()
@@ -89,10 +132,13 @@ def test_random_sweep(sweep_seed):
             tag = (entry, dtype, B, V, kind, seed, policy, pp is not None, kk is not None, mp is not None)
             strided = entry in ("apply", "sorted") and rng.random() < 0.35
             pads = [int(v) for v in rng.integers(1, 71, size=4)] if strided else None
-            tag = tag + (pads,)
+            elem = int(rng.integers(0, 4)) if entry == "apply" and not strided and rng.random() < 0.2 else None
+            tag = tag + (pads, elem)
             if entry == "apply":
                 if strided:
                     got = strided_apply(xb, dtype, pp, kk, mp, pads)
+                elif elem is not None:
+                    got = elem_apply(xb, dtype, pp, kk, mp, elem)
                 else:
                     got = gpu_apply(xb, dtype, pp, kk, mp)
                 rep = compare(got, xb, o_apply(xb, dtype, pp, kk, min_p_bits=mp), dtype)

@@ -223,3 +223,32 @@ def test_with_sorted_without_k_segment_table(dtype, V):
             assert rep.hard_mismatches == 0, (kind, mm is None, rep.details[:2])
             total.merge(rep)
     say(f"with_sorted without k, segment table {dtype} V={V}: {total}")
+
+
+NEG_INF_BITS = {"f32": 0xFF800000, "f16": 0xFC00, "bf16": 0xFF80}
+
+
+@pytest.mark.parametrize("dtype,V", [("bf16", 151936), ("f32", 70001), ("f16", 32000), ("bf16", 4099)])
+def test_rows_mostly_neg_inf(dtype, V, policy):
+    """Rows whose entries are largely -inf (a vocabulary masked by an earlier
+    stage, e.g. a grammar constraint): half, 99 %, all but 1000, all but one,
+    with the finite entries at random positions. -inf entries have zero
+    probability; they are masked, and they count in the stable order like any
+    other value below the survivors."""
+    need_gpu()
+    total = ParityReport()
+    rng = np.random.default_rng(V)
+    for i, keep in enumerate((V // 2, V // 100, 1000, 1)):
+        B = 3
+        xb = random_rows(7000 + V + i, B, V, dtype, kind=("normal", "gumbel", "ties", "spikes")[i])
+        for b in range(B):
+            masked = rng.permutation(V)[:V - keep]
+            xb[b, masked] = NEG_INF_BITS[dtype]
+        k, p = random_params(7000 + V + i, B, V, dtype, k_lo=1, k_hi=min(V, 3000))
+        k_big = np.full(B, min(V - 1, keep + 5), np.int32)  # k beyond the finite entries
+        for pp, kk in ((None, k), (p, None), (p, k), (p, k_big), (None, k_big)):
+            got = gpu_apply(xb, dtype, pp, kk)
+            rep = compare(got, xb, oracle_apply(xb, dtype, pp, kk), dtype)
+            assert rep.hard_mismatches == 0, (dtype, V, keep, pp is None, kk is None, rep.details[:2])
+            total.merge(rep)
+    say(f"mostly -inf {dtype} V={V} {policy}: {total}")

@@ -215,3 +215,21 @@ def test_build_rejects_spilling_kernels():
     ])
     assert _spills(report) == [("_ZN3tkp5spillE", 12)]
     assert _spills(report.replace(": 12 ", ": 0 ")) == []
+
+
+def test_binding_view_routing():
+    """Which views the binding passes to the row-strided entry points (rows
+    contiguous and disjoint) and which to the element-strided one; tensor
+    metadata only, so CPU tensors serve."""
+    import torch
+
+    from top_logits_filtering_amd.binding import _rows_contiguous
+
+    base = torch.zeros(6, 40)
+    assert _rows_contiguous(base)
+    assert _rows_contiguous(base[:, :33])  # padded rows
+    assert not _rows_contiguous(torch.zeros(40, 6).t())  # transposed
+    assert not _rows_contiguous(base[:, ::2])  # every second column
+    assert not _rows_contiguous(base.flatten().as_strided((6, 20), (10, 1)))  # rows share elements
+    assert _rows_contiguous(torch.zeros(40, 1).t())  # one row: its stride plays no part
+    assert _rows_contiguous(torch.zeros(6, 1)[:, :1])  # one column

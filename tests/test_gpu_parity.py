@@ -252,3 +252,50 @@ def test_rows_mostly_neg_inf(dtype, V, policy):
             assert rep.hard_mismatches == 0, (dtype, V, keep, pp is None, kk is None, rep.details[:2])
             total.merge(rep)
     say(f"mostly -inf {dtype} V={V} {policy}: {total}")
+
+
+@pytest.mark.parametrize("dtype,V", [("bf16", 151936), ("f32", 70001), ("f16", 4099)])
+def test_mostly_neg_inf_other_entries(dtype, V, policy):
+    """The same kind of rows (-inf except 1000 or one entry, or half) through
+    the pre-sorted entry (with and without logits), min-p, QSample and the
+    sorted survivors."""
+    need_gpu()
+    import torch
+    import top_logits_filtering_amd as tk
+
+    from oracle import sample_top_k_top_p as o_sample
+    from oracle import sorted_survivors as o_surv
+    from tests.gpu_util import k_dev, to_dev
+    from tests.parity import compare_samples, compare_survivors
+    from workloads.synth import random_min_p
+
+    rng = np.random.default_rng(V + 1)
+    for i, keep in enumerate((V // 2, 1000, 1)):
+        B = 3
+        seed = 7100 + V + i
+        xb = random_rows(seed, B, V, dtype, kind=("gumbel", "normal", "ties")[i])
+        for b in range(B):
+            xb[b, rng.permutation(V)[:V - keep]] = NEG_INF_BITS[dtype]
+        k, p = random_params(seed, B, V, dtype, k_lo=1, k_hi=min(V, 3000))
+        mp = random_min_p(seed, B, dtype, specials=False)
+        case = (dtype, V, keep, policy)
+        idx, sv = stable_ascending_sort(xb, dtype)
+        for logits in (xb, None):
+            got = gpu_with_sorted(sv, idx, dtype, p, k, logits)
+            rep = compare(got, xb, oracle_sorted(sv, idx, dtype, p, k, logits_bits=xb), dtype)
+            assert rep.hard_mismatches == 0, (case, "sorted", logits is None, rep.details[:2])
+        got = gpu_apply(xb, dtype, p, None, min_p=mp)
+        rep = compare(got, xb, oracle_apply(xb, dtype, p, None, min_p_bits=mp), dtype)
+        assert rep.hard_mismatches == 0, (case, "min_p", rep.details[:2])
+        q = rng.exponential(1.0, size=(B, V)).astype(np.float32)
+        sel = tk.sample_top_k_top_p(to_dev(xb, dtype), to_dev(p, dtype), k_dev(k), None, torch.from_numpy(q).cuda(),
+                                    1e-6)
+        torch.cuda.synchronize()
+        h, _, det = compare_samples(sel.cpu().numpy(), o_sample(xb, dtype, p, k, None, q.astype(np.float64), 1e-6))
+        assert h == 0, (case, "qsample", det[:2])
+        pr, ix, cn = tk.top_k_top_p_sorted_survivors(to_dev(xb, dtype), to_dev(p, dtype), None, None, cap=64)
+        torch.cuda.synchronize()
+        h, det = compare_survivors(pr.cpu().numpy().astype(np.float64), ix.cpu().numpy(), cn.cpu().numpy(),
+                                   o_surv(xb, dtype, p, None, None, 64))
+        assert h == 0, (case, "survivors", det[:2])
+    say(f"mostly -inf, other entries {dtype} V={V} {policy}: ok")

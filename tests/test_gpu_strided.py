@@ -88,7 +88,8 @@ def _bits(t, dtype):
 ELEMENT_CASES = [("transposed", "bf16", 8, 70001), ("transposed", "f32", 5, 4099),
                  ("column_step", "f16", 6, 32000), ("column_step", "bf16", 3, 262144),
                  ("params_strided", "bf16", 7, 151936), ("rows_overlap", "f32", 6, 65536),
-                 ("column_step", "f16", 1, 5000), ("transposed", "bf16", 9, 2)]
+                 ("column_step", "f16", 1, 5000), ("transposed", "bf16", 9, 2),
+                 ("transposed", "f32", 2, 1 << 20), ("column_step", "bf16", 2, (1 << 20) - 1)]
 
 
 @pytest.mark.parametrize("policy", [0, 1])

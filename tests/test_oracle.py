@@ -199,3 +199,31 @@ def test_t_reading_changes_mask_on_flat_row():
             out = apply_top_k_top_p(x, dtype, p, None, keep_traces=False, t_reading=reading).out[0]
             kept = np.nonzero(out == 0)[0]
             assert np.array_equal(kept, np.arange(1000 - keep, 1000)), (dtype, reading, len(kept))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_neg_inf_entries_are_zero_probability(dtype):
+    """-inf entries have probability zero and sit below every finite value in
+    the stable order, so removing them from a row leaves the decisions on the
+    finite entries unchanged (with k at most the number of finite entries),
+    and the -inf positions come out as -inf."""
+    neg = {"f32": 0xFF800000, "f16": 0xFC00, "bf16": 0xFF80}[dtype]
+    rng = np.random.default_rng(5)
+    for trial in range(12):
+        V = int(rng.integers(3, 400))
+        xb = random_rows(900 + trial, 1, V, dtype, kind=("normal", "ties", "gumbel")[trial % 3])
+        n_fin = int(rng.integers(1, V))
+        fin = np.sort(rng.permutation(V)[:n_fin])
+        full = np.full_like(xb, neg)
+        full[0, fin] = xb[0, fin]
+        comp = np.ascontiguousarray(xb[:, fin])
+        p = xb[:, :1].copy()
+        p[0, 0] = {"f32": np.float32(0.7).view(np.uint32), "f16": np.float16(0.7).view(np.uint16),
+                   "bf16": np.uint16(np.float32(0.7).view(np.uint32) >> 16)}[dtype]
+        p = p[:, 0]
+        for k in (None, np.array([int(rng.integers(1, n_fin + 1))], np.int32)):
+            a = apply_top_k_top_p(full, dtype, p, k).out
+            c = apply_top_k_top_p(comp, dtype, p, k).out
+            assert np.array_equal(a[0, fin], c[0]), (dtype, trial, k)
+            rest = np.setdiff1d(np.arange(V), fin)
+            assert (a[0, rest] == neg).all()

@@ -35,7 +35,8 @@
  * `stream` (a hipStream_t; NULL means the default stream) and the call
  * returns without synchronising. The library allocates no device memory
  * and the entry points never call hipMalloc. `out` must not overlap any input.
- * Rows are dense and row-major: element (b, v) sits at offset b * V + v.
+ * Rows are dense and row-major: element (b, v) sits at offset b * V + v,
+ * except where an entry point takes strides (the _ex and _strided ones).
  *
  * Errors. Arguments are checked on the host before anything is enqueued, in
  * the order of the aclnn checks (AKP §5.3): null pointers first, then dtype,

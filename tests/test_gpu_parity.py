@@ -225,6 +225,36 @@ def test_with_sorted_without_k_segment_table(dtype, V):
     say(f"with_sorted without k, segment table {dtype} V={V}: {total}")
 
 
+@pytest.mark.parametrize("dtype,V", [("bf16", 65546), ("bf16", 262144), ("f32", 32771), ("f16", 131080)])
+def test_with_sorted_disabled_k(dtype, V):
+    """Pre-sorted rows with k given: rows whose k is 0, V or more, or negative
+    have no top-k, and their top-p boundary is searched over the whole sorted
+    row, while the other rows of the batch search the copy of the top values.
+    Mixed batches, with and without min-p and with and without logits; all
+    rows' k disabled too."""
+    need_gpu()
+    total = ParityReport()
+    seed = 2600 + V % 89
+    for kind in ("normal", "ties"):
+        seed += 1
+        B = 8
+        xb = random_rows(seed, B, V, dtype, kind=kind, scale=3.0)
+        idx, sv = stable_ascending_sort(xb, dtype)
+        p = f32_to_bits(np.array([0.02, 0.3, 0.5, 0.9, 0.99, 0.9999, 0.7, 0.95], np.float32), dtype)
+        mp = f32_to_bits(np.array([0.0, 0.01, 0.2, 1e-4, 0.5, 1.0, 0.05, 0.0], np.float32), dtype)
+        mixed = np.array([0, 50, V, 3000, -1, 1, V + 7, 0], np.int32)
+        none_on = np.array([0, V, -5, 0, V + 1, 0, 0, V], np.int32)
+        for k in (mixed, none_on):
+            for mm in (None, mp):
+                for logits in (xb, None):
+                    ref = oracle_sorted(sv, idx, dtype, p, k, logits_bits=xb, min_p_bits=mm)
+                    got = gpu_with_sorted(sv, idx, dtype, p, k, logits, min_p=mm)
+                    rep = compare(got, xb, ref, dtype)
+                    assert rep.hard_mismatches == 0, (kind, k[:3], mm is None, logits is None, rep.details[:2])
+                    total.merge(rep)
+    say(f"with_sorted with disabled k {dtype} V={V}: {total}")
+
+
 NEG_INF_BITS = {"f32": 0xFF800000, "f16": 0xFC00, "bf16": 0xFF80}
 
 

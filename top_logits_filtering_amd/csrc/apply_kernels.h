@@ -646,6 +646,10 @@ __device__ __forceinline__ bool candidate_plan(const Tile& tile, const GT& gt, i
   cs.load(S, fallback ? 0 : ncand);
   K = 0;
   I = 0;
+  // the key of the k-th largest when a selection path below has found it
+  // (the sorted survivors' Z sums the top-k survivors and need not find it again)
+  uint32_t kk_sel = 0;
+  bool kk_found = false;
   if (small) {
     if (threadIdx.x >= kWave) last_stores();
     if (threadIdx.x < kWave) {
@@ -674,6 +678,8 @@ __device__ __forceinline__ bool candidate_plan(const Tile& tile, const GT& gt, i
       sel_pick_count(ss, rp.k);
       if (threadIdx.x < kWave) last_stores();
       K = L + static_cast<uint32_t>(ss.bin);
+      kk_sel = K;
+      kk_found = true;
     } else if (joint_one_pass) {
       // top-k and top-p from one pass: every bin of [L, kmax] holds one key
       cs.for_each([&](auto raw, int) {
@@ -686,6 +692,8 @@ __device__ __forceinline__ bool candidate_plan(const Tile& tile, const GT& gt, i
       sel_pick_joint(ss, rp.k, rp.t);
       if (threadIdx.x < kWave) last_stores();
       const uint64_t thr2 = ss.thr;
+      kk_sel = L + static_cast<uint32_t>(ss.kbin);
+      kk_found = true;
       if (thr2 == 0) {
         top_position<DT>(cs, sm, K, I);
       } else {
@@ -697,6 +705,8 @@ __device__ __forceinline__ bool candidate_plan(const Tile& tile, const GT& gt, i
       if (rp.k_on)
         Kk = kth_largest_key(
             cs, rp.k, L, kmax, [](auto raw, int) { return DT::key(raw); }, [](auto, int) { return true; }, ss);
+      kk_sel = Kk;
+      kk_found = rp.k_on;
       if (rp.pmode == kPNone) {
         K = Kk;
       } else if (rp.pmode == kPTopOnly) {
@@ -734,7 +744,7 @@ __device__ __forceinline__ bool candidate_plan(const Tile& tile, const GT& gt, i
       // (top-p-only rows reuse the row sum of step 3; other rows without k
       // sum the whole row re-read from global memory: keeping the register
       // tile live through the ranking below would spill it)
-      const double Z = ponly ? z_row : survivors_z<DT>(cs, gt, rp, L, kmax, m, ss, sm, S.redd);
+      const double Z = ponly ? z_row : survivors_z<DT>(cs, gt, rp, L, kmax, m, ss, sm, S.redd, kk_found, kk_sel);
       emit_survivors<DT>(cs, K, I, kmax, m, Z, sa, b, ss, reinterpret_cast<uint64_t*>(S.cel.raw));
     } else if (!fallback) {  // every survivor is a candidate
       int32_t pick;

@@ -236,14 +236,18 @@ __device__ __forceinline__ int32_t qsample_pick(const Src& src, uint32_t K, uint
 // the top-k survivors (key >= the k-th largest key), or over the whole row
 // without top-k. `cand` holds every element with key >= lo (all top-k
 // survivors when k is on); `row` is the whole row, read from global memory.
+// kk_known: Kk0 is already the k-th largest key (uniform), not searched again.
 template <class DT, class Cand, class Row>
 __device__ __forceinline__ double survivors_z(const Cand& cand, const Row& row, const RowParams& rp, uint32_t lo,
-                                              uint32_t kmax, float m, SelSmem& ss, RowSmem& sm, double* redd) {
+                                              uint32_t kmax, float m, SelSmem& ss, RowSmem& sm, double* redd,
+                                              bool kk_known = false, uint32_t Kk0 = 0) {
   constexpr float kLog2e = 1.4426950408889634f;
   double z = 0.0;
   if (rp.k_on) {
-    const uint32_t Kk = kth_largest_key(
-        cand, rp.k, lo, kmax, [](auto raw, int) { return DT::key(raw); }, [](auto, int) { return true; }, ss);
+    const uint32_t Kk = kk_known ? Kk0
+                                 : kth_largest_key(
+                                       cand, rp.k, lo, kmax, [](auto raw, int) { return DT::key(raw); },
+                                       [](auto, int) { return true; }, ss);
     cand.for_each([&](auto raw, int) {
       if (DT::key(raw) >= Kk) z += static_cast<double>(__builtin_amdgcn_exp2f((DT::value(raw) - m) * kLog2e));
     });

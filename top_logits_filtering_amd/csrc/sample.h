@@ -40,8 +40,9 @@ __device__ __forceinline__ uint64_t block_max_u64(uint64_t v, RowSmem& sm) {
 // in descending (key, index) order: f(raw, idx, rank) for every survivor,
 // once. `list` holds at least as many u64 entries as there are survivors.
 // Returns the survivor count. Every thread of the block must call it; the
-// histograms are left zeroed.
-template <class DT, class Src, class F>
+// histograms are left zeroed, unless kLast (the block's last use of them:
+// the next row's block clears them when it starts).
+template <class DT, bool kLast = false, class Src, class F>
 __device__ __forceinline__ uint32_t for_each_ranked_survivor(const Src& src, uint32_t K, uint32_t I, uint32_t kmax,
                                                              SelSmem& ss, uint64_t* list, F&& f) {
   const int shift = shift_for_range(kmax - K);
@@ -82,11 +83,13 @@ __device__ __forceinline__ uint32_t for_each_ranked_survivor(const Src& src, uin
     }
   });
   const uint32_t n = ss.bcnt;
-  lds_barrier();
-  // leave the histograms zeroed for later selections
-  ss.cnt[threadIdx.x] = 0;
-  ss.kmx[threadIdx.x] = 0;
-  lds_barrier();
+  if constexpr (!kLast) {
+    lds_barrier();
+    // leave the histograms zeroed for later selections
+    ss.cnt[threadIdx.x] = 0;
+    ss.kmx[threadIdx.x] = 0;
+    lds_barrier();
+  }
   return n;
 }
 
@@ -209,7 +212,9 @@ __device__ __forceinline__ void for_each_ranked_survivor_chunked(const Src& src,
 }
 
 // The QSample pick among the survivors of `src`: the first maximum of
-// exp(x - m) / (q[rank] + eps). Returns the winner's original index (uniform).
+// exp(x - m) / (q[rank] + eps). Returns the winner's original index in
+// thread 0 (the only thread that stores it); the block's last use of the
+// selection histograms and of the reduction slots.
 template <class DT, class Src>
 __device__ __forceinline__ int32_t qsample_pick(const Src& src, uint32_t K, uint32_t I, uint32_t kmax, float m,
                                                 const float* __restrict__ qrow, float eps, SelSmem& ss,
@@ -217,7 +222,7 @@ __device__ __forceinline__ int32_t qsample_pick(const Src& src, uint32_t K, uint
   constexpr float kLog2e = 1.4426950408889634f;
   uint64_t best = 0;  // (monotone key of the score) << 32 | ~rank: the first maximum wins
   uint32_t best_idx = 0;
-  for_each_ranked_survivor<DT>(src, K, I, kmax, ss, list, [&](auto raw, int idx, uint32_t rank) {
+  for_each_ranked_survivor<DT, true>(src, K, I, kmax, ss, list, [&](auto raw, int idx, uint32_t rank) {
     const float e = __builtin_amdgcn_exp2f((DT::value(raw) - m) * kLog2e);
     const float score = e / (qrow[rank] + eps);
     const uint64_t packed = (static_cast<uint64_t>(F32T::key(__float_as_uint(score))) << 32) | (~rank);
@@ -226,10 +231,28 @@ __device__ __forceinline__ int32_t qsample_pick(const Src& src, uint32_t K, uint
       best_idx = static_cast<uint32_t>(idx);
     }
   });
-  const uint64_t win = block_max_u64(best, sm);
-  if (best == win) ss.run_res = best_idx;  // exactly one survivor holds the winning rank
+  // each wave's best and its index through shared memory, one barrier; the
+  // packed values are distinct (one rank each), so one lane holds the wave's
+  const uint64_t wbest = wave_reduce_u64(best, 0ull, [](uint64_t a, uint64_t b) { return a > b ? a : b; });
+  const uint64_t holder = __ballot(best == wbest);
+  const int src_lane = holder != 0 ? __ffsll(static_cast<unsigned long long>(holder)) - 1 : 0;
+  const uint32_t widx = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(best_idx), src_lane));
+  const int l = static_cast<int>(threadIdx.x) & (kWave - 1);
+  if (l == 0) {
+    sm.redu[threadIdx.x / kWave] = wbest;
+    sm.redw[threadIdx.x / kWave] = widx;
+  }
   lds_barrier();
-  return static_cast<int32_t>(ss.run_res);
+  uint32_t pick = 0;
+  if (threadIdx.x == 0) {
+    uint64_t top = 0;
+    for (int w = 0; w < kWaves; ++w)
+      if (sm.redu[w] > top) {
+        top = sm.redu[w];
+        pick = sm.redw[w];
+      }
+  }
+  return static_cast<int32_t>(pick);
 }
 
 // Z of step 4 for the survivors' probabilities: the sum of exp(x - m) over

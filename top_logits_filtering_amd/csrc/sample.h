@@ -294,7 +294,8 @@ __device__ __forceinline__ double survivors_z(const Cand& cand, const Row& row, 
 
 // The sorted-survivors output of one row: probs[r] = exp(x - m) / Z and
 // indices[r] = the original index for descending ranks r < cap, then 0 and
-// -1 up to cap; counts = the survivor count.
+// -1 up to cap; counts = the survivor count. The block's last use of the
+// selection histograms.
 template <class DT, class Src>
 __device__ __forceinline__ void emit_survivors(const Src& src, uint32_t K, uint32_t I, uint32_t kmax, float m,
                                                double Z, const SampleArgs& sa, int b, SelSmem& ss, uint64_t* list) {
@@ -302,7 +303,7 @@ __device__ __forceinline__ void emit_survivors(const Src& src, uint32_t K, uint3
   float* __restrict__ prow = sa.probs == nullptr ? nullptr : sa.probs + static_cast<size_t>(b) * sa.cap;
   int32_t* __restrict__ irow = sa.indices + static_cast<size_t>(b) * sa.cap;
   const float zinv = static_cast<float>(1.0 / Z);
-  const uint32_t n = for_each_ranked_survivor<DT>(src, K, I, kmax, ss, list, [&](auto raw, int idx, uint32_t rank) {
+  const uint32_t n = for_each_ranked_survivor<DT, true>(src, K, I, kmax, ss, list, [&](auto raw, int idx, uint32_t rank) {
     if (rank < sa.cap) {
       irow[rank] = idx;
       if (prow != nullptr) prow[rank] = __builtin_amdgcn_exp2f((DT::value(raw) - m) * kLog2e) * zinv;

@@ -157,3 +157,38 @@ def test_apply_element_strided(name, dtype, B, V, policy):
             say(f"element-strided {case}: {rep}")
     finally:
         tk.set_plan_policy(0)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_element_strided_single_column(dtype):
+    """Rows of one element are copied through whatever the strides: one row,
+    a logits row stride of 0 (one value expanded over the rows), and out as a
+    column of a wider buffer."""
+    torch = need_gpu()
+    import top_logits_filtering_amd as tk
+
+    nt = np.uint32 if dtype == "f32" else np.uint16
+    vals = random_rows(77, 1, 5, dtype, kind="normal")[0]
+    p = to_dev(random_params(77, 5, 1, dtype)[1], dtype)
+    # one row, transposed views of a [1, 1] buffer
+    x1 = to_dev(vals[:1].reshape(1, 1), dtype).t()
+    o1 = _filled((1, 1), dtype).t()
+    tk.apply_top_k_top_p(x1, p[:1], None, out=o1)
+    torch.cuda.synchronize()
+    assert from_dev(o1.contiguous(), dtype)[0, 0] == vals[0]
+    # one value expanded over 5 rows (row stride 0), out every third element of a [5, 3] buffer
+    x = to_dev(vals[:1], dtype).reshape(1, 1).expand(5, 1)
+    obuf = _filled((5, 3), dtype)
+    tk.apply_top_k_top_p(x, p, None, out=obuf[:, 1:2])
+    torch.cuda.synchronize()
+    got = from_dev(obuf, dtype)
+    assert (got[:, 1] == vals[0]).all()
+    assert (got[:, [0, 2]] == nt(SENTINEL[dtype])).all()
+    # rows of one element with a row stride of 2
+    wide = to_dev(np.stack([vals, vals]).T.copy(), dtype)  # [5, 2]
+    obuf = _filled((5, 2), dtype)
+    tk.apply_top_k_top_p(wide[:, :1], p, None, out=obuf[:, 1:])
+    torch.cuda.synchronize()
+    got = from_dev(obuf, dtype)
+    assert np.array_equal(got[:, 1], vals)
+    assert (got[:, 0] == nt(SENTINEL[dtype])).all()

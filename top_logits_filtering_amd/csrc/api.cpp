@@ -171,10 +171,8 @@ topktopp_status strided_impl(const void* logits, int64_t xr, int64_t xc, int dty
       overlaps(out, nout, k, span2(B, 1, ks, 0, 4)) || overlaps(out, nout, min_p, span2(B, 1, ms, 0, es)))
     return fail(TOPKTOPP_ERR_INVALID, "out overlaps an input buffer");
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (V == 1)  // a last dimension of 1 is copied through unfiltered
-    return check_launch(hipMemcpy2DAsync(out, static_cast<size_t>(orr) * es, logits, static_cast<size_t>(xr) * es, es,
-                                         static_cast<size_t>(B), hipMemcpyDeviceToDevice, st),
-                        "hipMemcpy2DAsync");
+  if (V == 1)  // a last dimension of 1 is copied through unfiltered (row strides of any value, 0 included)
+    return check_launch(tkp::launch_copy_column(logits, xr, out, orr, B, static_cast<int>(es), st), "copy launch");
   // contiguous rows and dense parameters: the row-strided path
   const bool dense_params = (p == nullptr || B == 1 || ps == 1) && (k == nullptr || B == 1 || ks == 1) &&
                             (min_p == nullptr || B == 1 || ms == 1);

@@ -89,6 +89,11 @@ inline hipError_t launch_sample(int dtype, const void* logits, const void* p, co
 // caller may capture the call in a graph.
 hipError_t launch_fill_zero_i32(int32_t* dst, int64_t n, hipStream_t stream);
 
+// out[b * dst_stride] = src[b * src_stride] for b < B, elements of es bytes:
+// strided views with rows of one element (any stride, 0 included).
+hipError_t launch_copy_column(const void* src, int64_t src_stride, void* dst, int64_t dst_stride, int64_t B, int es,
+                              hipStream_t stream);
+
 // Sorted survivors of rows of one element.
 hipError_t launch_survivors_single(float* probs, int32_t* indices, int32_t* counts, int64_t B, int64_t cap,
                                    hipStream_t stream);

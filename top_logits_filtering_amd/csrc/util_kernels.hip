@@ -45,4 +45,27 @@ hipError_t launch_survivors_single(float* probs, int32_t* indices, int32_t* coun
   return hipGetLastError();
 }
 
+// Rows of one element of a strided view: out[b * dst_stride] = src[b * src_stride],
+// elements of es bytes (2 or 4); a source stride of 0 repeats one element.
+__global__ void copy_column_kernel(const uint8_t* __restrict__ src, int64_t src_stride, uint8_t* __restrict__ dst,
+                                   int64_t dst_stride, int64_t B, int es) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t b = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; b < B; b += stride) {
+    const uint8_t* s = src + b * src_stride * es;
+    uint8_t* d = dst + b * dst_stride * es;
+    if (es == 4)
+      *reinterpret_cast<uint32_t*>(d) = *reinterpret_cast<const uint32_t*>(s);
+    else
+      *reinterpret_cast<uint16_t*>(d) = *reinterpret_cast<const uint16_t*>(s);
+  }
+}
+
+hipError_t launch_copy_column(const void* src, int64_t src_stride, void* dst, int64_t dst_stride, int64_t B, int es,
+                              hipStream_t stream) {
+  if (B <= 0) return hipSuccess;
+  hipLaunchKernelGGL(copy_column_kernel, dim3(elem_grid(B)), dim3(256), 0, stream, static_cast<const uint8_t*>(src),
+                     src_stride, static_cast<uint8_t*>(dst), dst_stride, B, es);
+  return hipGetLastError();
+}
+
 }  // namespace tkp

@@ -233,3 +233,59 @@ def test_binding_view_routing():
     assert not _rows_contiguous(base.flatten().as_strided((6, 20), (10, 1)))  # rows share elements
     assert _rows_contiguous(torch.zeros(40, 1).t())  # one row: its stride plays no part
     assert _rows_contiguous(torch.zeros(6, 1)[:, :1])  # one column
+
+
+def test_binding_rejects_mismatched_operands():
+    """The binding checks every operand's dtype and shape against the logits
+    before anything reaches the library (a short p or a narrower out would
+    otherwise be read or written past its end), then that all live on the
+    GPU; tensor metadata only, so CPU tensors serve."""
+    import pytest
+    import torch
+
+    import top_logits_filtering_amd as tk
+
+    B, V = 3, 10
+    x = torch.zeros(B, V, dtype=torch.bfloat16)
+    p = torch.full((B,), 0.9, dtype=torch.bfloat16)
+    k = torch.ones(B, dtype=torch.int32)
+    bad = [
+        (TypeError, dict(p=p.float())),
+        (ValueError, dict(p=torch.ones(B + 1, dtype=torch.bfloat16))),
+        (TypeError, dict(k=k.long())),
+        (ValueError, dict(k=torch.ones(B, 1, dtype=torch.int32))),
+        (TypeError, dict(min_p=p.half())),
+        (TypeError, dict(out=torch.zeros(B, V, dtype=torch.float16))),
+        (ValueError, dict(out=torch.zeros(B, V + 1, dtype=torch.bfloat16))),
+    ]
+    for err, kw in bad:
+        args = dict(p=p, k=k)
+        args.update(kw)
+        with pytest.raises(err):
+            tk.apply_top_k_top_p(x, **args)
+    with pytest.raises(ValueError, match="GPU"):
+        tk.apply_top_k_top_p(x, p, k)
+
+    idx = torch.zeros(B, V, dtype=torch.int32)
+    with pytest.raises(TypeError):
+        tk.apply_top_k_top_p_with_sorted(x, idx.long(), p, k)
+    with pytest.raises(TypeError):
+        tk.apply_top_k_top_p_with_sorted(x, idx, p, k, logits=x.half())
+    with pytest.raises(ValueError):
+        tk.apply_top_k_top_p_with_sorted(x, idx[:, :5], p, k)
+
+    with pytest.raises(TypeError):
+        tk.sample_top_k_top_p(x, p, k, selected=torch.zeros(B, dtype=torch.int64))
+    with pytest.raises(TypeError):
+        tk.sample_top_k_top_p(x, p, k, out=torch.zeros(B, V, dtype=torch.float32))
+    with pytest.raises(ValueError):
+        tk.sample_top_k_top_p(x, p[:2], k)
+
+    cap = 4
+    good = (torch.zeros(B, cap), torch.zeros(B, cap, dtype=torch.int32), torch.zeros(B, dtype=torch.int32))
+    with pytest.raises(TypeError):
+        tk.top_k_top_p_sorted_survivors(x, p, k, cap=cap, out=(good[0].double(), good[1], good[2]))
+    with pytest.raises(ValueError):
+        tk.top_k_top_p_sorted_survivors(x, p, k, cap=cap, out=(good[0], good[1], good[2][:2]))
+    with pytest.raises(ValueError, match="GPU"):
+        tk.top_k_top_p_sorted_survivors(x, p, k, cap=cap, out=good)

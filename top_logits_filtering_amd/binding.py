@@ -152,6 +152,46 @@ def _entries(t, B):
     return t.data_ptr(), t.stride(0)
 
 
+def _check_vector(t, B, dtype, name):
+    """A per-row parameter or output: None, or a 1-D tensor of B entries of `dtype`."""
+    if t is None:
+        return
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != 1 or t.shape[0] != B:
+        raise ValueError(f"{name} must be a 1-D tensor of {B} entries, got shape {tuple(t.shape)}")
+
+
+def _check_matrix(t, shape, dtype, name):
+    """None, or a 2-D tensor of `shape` and `dtype`."""
+    if t is None:
+        return
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != 2 or tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must be [{shape[0]}, {shape[1]}], got shape {tuple(t.shape)}")
+
+
+def _check_params(B, dtype, p, k, min_p):
+    """p and min_p [B] in the logits dtype, k [B] int32 (each optional)."""
+    import torch
+
+    _check_vector(p, B, dtype, "p")
+    _check_vector(k, B, torch.int32, "k")
+    _check_vector(min_p, B, dtype, "min_p")
+
+
+def _check_device(device, *tensors):
+    """Every given tensor on the GPU, on `device`."""
+    for t in tensors:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("tensors must live on the GPU")
+        if t.device != device:
+            raise ValueError(f"tensors must share one device: {t.device} and {device}")
+
+
 def _stream(stream, device) -> int:
     """The HIP stream handle to launch on: the given one, else torch's current
     stream of the tensors' device."""
@@ -181,8 +221,9 @@ def apply_top_k_top_p(logits, p=None, k=None, out=None, stream=None, min_p=None)
     B, V = logits.shape
     if out is None:
         out = torch.empty((B, V), dtype=logits.dtype, device=logits.device)
-    if out.dim() != 2 or tuple(out.shape) != (B, V):
-        raise ValueError(f"out must be [{B}, {V}]")
+    _check_matrix(out, (B, V), logits.dtype, "out")
+    _check_params(B, logits.dtype, p, k, min_p)
+    _check_device(logits.device, logits, out, p, k, min_p)
     st = _stream(stream, logits.device)
     params = [t for t in (p, k, min_p) if t is not None]
     if not (_rows_contiguous(logits) and _rows_contiguous(out) and all(t.is_contiguous() for t in params)):
@@ -218,6 +259,11 @@ def apply_top_k_top_p_with_sorted(sorted_value, sorted_indices, p=None, k=None, 
     B, V = sorted_value.shape
     if out is None:
         out = torch.empty((B, V), dtype=sorted_value.dtype, device=sorted_value.device)
+    _check_matrix(sorted_indices, (B, V), torch.int32, "sorted_indices")
+    _check_matrix(logits, (B, V), sorted_value.dtype, "logits")
+    _check_matrix(out, (B, V), sorted_value.dtype, "out")
+    _check_params(B, sorted_value.dtype, p, k, min_p)
+    _check_device(sorted_value.device, sorted_value, sorted_indices, logits, out, p, k, min_p)
     st = _stream(stream, sorted_value.device)
     (sp, lds), (ip, ldi), (xp, ldx), (op, ldo) = _rows(sorted_value), _rows(sorted_indices), _rows(logits), _rows(out)
     if lds != V or ldi != V or ldo != V or (logits is not None and ldx != V):
@@ -254,6 +300,10 @@ def sample_top_k_top_p(logits, p=None, k=None, min_p=None, q=None, eps=0.0, out=
         raise ValueError("q must be float32 [B, V]")
     if selected is None:
         selected = torch.empty((B,), dtype=torch.int32, device=logits.device)
+    _check_matrix(out, (B, V), logits.dtype, "out")
+    _check_vector(selected, B, torch.int32, "selected")
+    _check_params(B, logits.dtype, p, k, min_p)
+    _check_device(logits.device, logits, p, k, min_p, q, out, selected)
     status = lib.sample_top_k_top_p(
         _ptr(logits), _dtype_code(logits), B, V, _ptr(p), _ptr(k), _ptr(min_p), _ptr(q), float(eps), _ptr(out),
         _ptr(selected), _stream(stream, logits.device)
@@ -284,6 +334,11 @@ def top_k_top_p_sorted_survivors(logits, p=None, k=None, min_p=None, cap=1024, w
         probs = torch.empty((B, cap), dtype=torch.float32, device=dev) if with_probs else None
         indices = torch.empty((B, cap), dtype=torch.int32, device=dev)
         counts = torch.empty((B,), dtype=torch.int32, device=dev)
+    _check_matrix(probs, (B, cap), torch.float32, "probs")
+    _check_matrix(indices, (B, cap), torch.int32, "indices")
+    _check_vector(counts, B, torch.int32, "counts")
+    _check_params(B, logits.dtype, p, k, min_p)
+    _check_device(dev, logits, p, k, min_p, probs, indices, counts)
     status = lib.top_k_top_p_sorted_survivors(
         _ptr(logits), _dtype_code(logits), B, V, _ptr(p), _ptr(k), _ptr(min_p), int(cap), _ptr(probs), _ptr(indices),
         _ptr(counts), _stream(stream, dev)

@@ -23,7 +23,9 @@ scattered through sorted_indices). --p-only passes no k (top-p alone).
 and writes one index per row instead of the filtered logits; --sample-none
 uses the argmax mode instead. --survivors returns each row's survivors in
 descending order with their probabilities and original indices (capacity
-1024 per row) instead of the filtered logits.
+1024 per row) instead of the filtered logits. --wide-top-p P replaces the
+rows by N(0,3) rows and runs top-p only with p = P: rows that keep thousands
+of survivors, beyond the candidate list.
 """
 
 import argparse
@@ -79,7 +81,8 @@ def measured_traffic(args):
     """Counter-measured HBM bytes per launch, or None when no counters were
     taken for this workload or the kernel sources changed since."""
     if (args.workload != 3 or args.policy != 0 or args.copy_calibration or args.min_p or args.no_logits
-            or args.sample or args.sample_none or args.survivors or not os.path.exists(TRAFFIC_PROFILE)):
+            or args.p_only or args.wide_top_p is not None or args.sample or args.sample_none or args.survivors
+            or not os.path.exists(TRAFFIC_PROFILE)):
         return None
     text = open(TRAFFIC_PROFILE).read()
     m_bytes = re.search(r"traffic_bytes_per_launch:\s*(\d+)", text)
@@ -238,6 +241,9 @@ def main():
     ap.add_argument("--no-logits", action="store_true", help="pre-sorted workload without logits (scattered output)")
     ap.add_argument("--p-only", action="store_true",
                     help="top-p only: the workload's p with k absent (NULL), e.g. the pre-sorted top-p batch")
+    ap.add_argument("--wide-top-p", type=float, default=None, metavar="P",
+                    help="the workload's rows replaced by N(0,3) rows (thousands of top-p survivors each), top-p "
+                         "only with p = P on every row: the rows that overflow the candidate list")
     ap.add_argument("--sample", action="store_true", help="filter then sample one index per row (QSample)")
     ap.add_argument("--sample-none", action="store_true", help="filter then take the argmax index per row")
     ap.add_argument("--survivors", action="store_true",
@@ -255,10 +261,17 @@ def main():
               "single MI355X; run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
-    from workloads.synth import make_workload, min_p_for_workload
+    from workloads.synth import f32_to_bits, make_workload, min_p_for_workload, random_rows
 
     wl = make_workload(args.workload)
     dt = wl.dtype
+    if args.wide_top_p is not None:
+        if wl.entry != "apply":
+            print("--wide-top-p applies to the raw-logits workloads (1-4)", file=sys.stderr)
+            sys.exit(2)
+        wl.logits = random_rows(0x71DE, wl.B, wl.V, dt, kind="normal", scale=3.0)
+        wl.p = f32_to_bits(np.full(wl.B, args.wide_top_p, np.float32), dt)
+        wl.k = None
     if args.p_only:
         wl.k = None
     mp_bits = min_p_for_workload(args.workload, wl.B, dt) if args.min_p else None
@@ -381,7 +394,7 @@ def main():
     elif args.survivors:
         nbytes = survivor_bytes(wl, args.min_p, cap)
     else:
-        nbytes = algorithmic_bytes(wl, args.min_p, not args.no_logits, not args.p_only)
+        nbytes = algorithmic_bytes(wl, args.min_p, not args.no_logits, wl.k is not None)
     achieved = nbytes / (kernel_ms * 1e-3) / 1e9
     rows_per_s = wl.B / (ms_per_step * 1e-3)
 
@@ -399,9 +412,12 @@ def main():
         "dtype": dt,
         "data": "synthetic",
         "config": {
-            "workload": WORKLOAD_TEXT[args.workload] + (", min-p U[0.01,0.2] per row" if args.min_p else "")
+            "workload": (WORKLOAD_TEXT[args.workload] if args.wide_top_p is None else
+                         f"apply_top_k_top_p, B={wl.B} V={wl.V} {dt} N(0,3) (thousands of top-p survivors per row)")
+                        + (", min-p U[0.01,0.2] per row" if args.min_p else "")
                         + (", without logits" if args.no_logits and wl.entry == "with_sorted" else "")
                         + (", top-p only (k absent)" if args.p_only else "")
+                        + (f", top-p only with p = {args.wide_top_p} on every row" if args.wide_top_p is not None else "")
                         + (", then QSample (q ~ Exp(1), eps 1e-6), one index per row" if args.sample else "")
                         + (", then argmax, one index per row" if args.sample_none else "")
                         + (", sorted survivors (probabilities and indices, capacity 1024 per row)"

@@ -78,6 +78,7 @@ def test_algorithmic_bytes_closed_forms():
 
     w3 = make_workload(3, rows=range(256))
     assert bench.algorithmic_bytes(w3) == 2 * 256 * 151936 * 2 + 256 * (2 + 4)  # 155,584,000 for the bench line
+    assert bench.algorithmic_bytes(w3, with_k=False) == 2 * 256 * 151936 * 2 + 256 * 2  # k absent (top-p only)
     w5 = make_workload(5, rows=range(128))
     kept = int(np.clip(w5.k, 0, w5.V).sum())
     assert bench.algorithmic_bytes(w5) == 2 * 128 * 262144 * 2 + 128 * (2 + 4) + kept * 2

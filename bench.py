@@ -25,7 +25,8 @@ uses the argmax mode instead. --survivors returns each row's survivors in
 descending order with their probabilities and original indices (capacity
 1024 per row) instead of the filtered logits. --wide-top-p P replaces the
 rows by N(0,3) rows and runs top-p only with p = P: rows that keep thousands
-of survivors, beyond the candidate list.
+of survivors, beyond the candidate list. --topk-only K runs top-k only with
+k = K on every row.
 """
 
 import argparse
@@ -81,7 +82,8 @@ def measured_traffic(args):
     """Counter-measured HBM bytes per launch, or None when no counters were
     taken for this workload or the kernel sources changed since."""
     if (args.workload != 3 or args.policy != 0 or args.copy_calibration or args.min_p or args.no_logits
-            or args.p_only or args.wide_top_p is not None or args.sample or args.sample_none or args.survivors
+            or args.p_only or args.wide_top_p is not None or args.topk_only is not None or args.sample
+            or args.sample_none or args.survivors
             or not os.path.exists(TRAFFIC_PROFILE)):
         return None
     text = open(TRAFFIC_PROFILE).read()
@@ -244,6 +246,9 @@ def main():
     ap.add_argument("--wide-top-p", type=float, default=None, metavar="P",
                     help="the workload's rows replaced by N(0,3) rows (thousands of top-p survivors each), top-p "
                          "only with p = P on every row: the rows that overflow the candidate list")
+    ap.add_argument("--topk-only", type=int, default=None, metavar="K",
+                    help="top-k only with k = K on every row (p = 1): large k shows where the candidate bound "
+                         "stops and the multi-pass plan takes over")
     ap.add_argument("--sample", action="store_true", help="filter then sample one index per row (QSample)")
     ap.add_argument("--sample-none", action="store_true", help="filter then take the argmax index per row")
     ap.add_argument("--survivors", action="store_true",
@@ -274,6 +279,9 @@ def main():
         wl.k = None
     if args.p_only:
         wl.k = None
+    if args.topk_only is not None:  # p = 1 on every row: no top-p
+        wl.k = np.full(wl.B, args.topk_only, np.int32)
+        wl.p = f32_to_bits(np.ones(wl.B, np.float32), dt)
     mp_bits = min_p_for_workload(args.workload, wl.B, dt) if args.min_p else None
     sampling = args.sample or args.sample_none
     if (sampling or args.survivors) and wl.entry != "apply":
@@ -418,6 +426,7 @@ def main():
                         + (", without logits" if args.no_logits and wl.entry == "with_sorted" else "")
                         + (", top-p only (k absent)" if args.p_only else "")
                         + (f", top-p only with p = {args.wide_top_p} on every row" if args.wide_top_p is not None else "")
+                        + (f", top-k only with k = {args.topk_only} on every row" if args.topk_only is not None else "")
                         + (", then QSample (q ~ Exp(1), eps 1e-6), one index per row" if args.sample else "")
                         + (", then argmax, one index per row" if args.sample_none else "")
                         + (", sorted survivors (probabilities and indices, capacity 1024 per row)"

@@ -11,29 +11,33 @@
 // Candidate plan (default). Typical decoding rows keep a tiny top set, so:
 //  1. while the row arrives, each thread tracks the two largest maxima of
 //     its 16-byte vectors and, for top-p rows without top-k, an online
-//     (running-max rescaled) sum of exp(x - max);
+//     (running-max rescaled) sum of exp(x - max); rows with k above 1536
+//     (16-bit values in registers) then take the four largest from the
+//     vector maxima kept in shared memory;
 //  2. the whole output row is written as -inf (it does not depend on the
 //     data), in portions issued between the steps below, so these stores
 //     drain while the block works on in registers and shared memory only (a
 //     vector load or a register spill now would wait for them: vector memory
 //     operations complete in order);
-//  3-4. the 2048 per-thread maxima are actual row elements, so the k-th
-//     largest of them bounds the top-k threshold from below; for top-p-only
-//     rows the bound is where the mass of those maxima, walked from the top,
-//     reaches (1 - t) * Z, so every element above it carries at least that
-//     mass and the top-p boundary cannot lie below it. One 1024-bin
-//     histogram pass gives the bound L as a bin edge;
+//  3-4. the 2048 (or 4096) per-thread maxima are actual row elements, so
+//     the k-th largest of them bounds the top-k threshold from below; for
+//     top-p-only rows the bound is where the mass of those maxima, walked
+//     from the top, reaches (1 - t) * Z, so every element above it carries
+//     at least that mass and the top-p boundary cannot lie below it. One
+//     1024-bin histogram pass gives the bound L as a bin edge;
 //  5. every vector whose maximum is >= L is copied into a list in shared
 //     memory (placed by wave ballots, one shared-memory atomic per wave),
 //     then the elements >= L of those vectors into a list of (raw, index)
-//     pairs, at most 5 per thread, which the selection keeps in registers;
+//     pairs, at most 5 per thread, which the selection keeps in registers
+//     (register tiles with more candidate vectors than the vector list
+//     holds list their elements straight from the registers);
 //  6. the exact selection (row_select.h) runs on those candidates only: one
 //     wave ranks them directly when there are at most 64; joint rows whose
 //     candidate keys span fewer than 1024 values take one pass of count and
 //     mass histograms; other rows take range-adaptive radix passes;
 //  7. once every -inf store has completed, the survivors are written over
 //     them.
-// Whenever a bound cannot be formed (k > 2048, top-p mass not reached) or the
+// Whenever a bound cannot be formed (k > 3072, top-p mass not reached) or a
 // list overflows, the block falls back to the multi-pass plan, which
 // rewrites the whole row; the same thread writes the same addresses in the
 // same order, so the earlier -inf stores are overwritten.
@@ -52,7 +56,31 @@
 
 namespace tkp {
 
-constexpr int kTop2 = 2 * kThreads;
+// Largest vector maxima kept per thread for the bound: two, or four for rows
+// with k above kTop4From (taken after the row's arrival from the vector
+// maxima in shared memory, so the arrival of other rows pays nothing). A
+// bound from the k-th largest of them keeps the candidates within the list
+// for k up to about three quarters of the maxima taken; beyond that a row
+// goes to the multi-pass plan.
+constexpr int kTopPerThread = 4;
+constexpr int kTopN = kTopPerThread * kThreads;
+constexpr int kTop2N = 2 * kThreads;
+constexpr uint32_t kTop4From = 3 * kThreads / 2;
+constexpr uint32_t kBoundMaxK2 = kTop2N;     // with two maxima per thread
+constexpr uint32_t kBoundMaxK4 = 3 * kThreads;  // with four
+
+// The first kPer of each thread's kept maxima, as a source for the bound
+// passes (row_select.h); index unused (reads as 0).
+template <class DT, int kPer>
+struct TopMaxima {
+  using raw_t = typename DT::raw_t;
+  const uint32_t* top;
+  template <class F>
+  __device__ __forceinline__ void for_each(F&& f) const {
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) f(static_cast<raw_t>(top[r * kThreads + threadIdx.x]), 0);
+  }
+};
 constexpr int kMaxVecs = 20;
 constexpr int kCandVecCap = 2048;  // candidate vectors kept in shared memory
 constexpr int kStreamVmSlots = 32;  // streamed rows: vector maxima kept for this many layers
@@ -92,7 +120,7 @@ struct ApplySmem {
   RowSmem row;
   SelSmem sel;
   double redd[kWaves];
-  uint32_t top2[kTop2];
+  uint32_t topm[kTopN];  // rank r of thread t's kept vector maxima at r * kThreads + t
   float run[kThreads];  // per-thread running max and rescaled exp sum (top-p-only rows)
   float acc[kThreads];
   union alignas(16) {
@@ -103,6 +131,7 @@ struct ApplySmem {
       uint32_t idx[kCandCap];  // and row indices
     } cel;                     // steps 5-7
   };
+  static_assert(sizeof(cel) <= sizeof(vmh), "the candidate list shares the streamed rows' maxima memory");
   vec_t cvec[kCandVecCap];  // candidate vectors
   uint32_t ce0[kCandVecCap];
   uint32_t nvec;   // candidate vectors reserved so far
@@ -125,8 +154,12 @@ struct CandElems {
 #pragma unroll
     for (int s = 0; s < kCandPerThread; ++s) {
       const int c = s * kThreads + static_cast<int>(threadIdx.x);
-      raw[s] = c < n ? S.cel.raw[c] : 0u;
-      idx[s] = c < n ? S.cel.idx[c] : 0u;
+      raw[s] = 0u;
+      idx[s] = 0u;
+      if (s * kThreads < n && c < n) {  // (the first test is uniform: empty slots cost nothing)
+        raw[s] = S.cel.raw[c];
+        idx[s] = S.cel.idx[c];
+      }
     }
   }
   template <class F>
@@ -326,6 +359,9 @@ __device__ __forceinline__ bool candidate_plan(const Tile& tile, const GT& gt, i
   const bool ponly = rp.pmode == kPBoundary && !rp.k_on;
   constexpr float kLog2e = 1.4426950408889634f;
   float M1 = -INFINITY, M2 = -INFINITY;  // two largest vector maxima of this thread
+  // rows with k above kTop4From take the four largest of the thread's vector
+  // maxima once they are all in shared memory (exact there for 16-bit values)
+  const bool top4 = Tile::kRegisters && sizeof(raw_t) == 2 && rp.k_on && rp.k > kTop4From;
   float run = -INFINITY, acc = 0.0f;     // acc = sum of exp(x - run), top-p-only rows
   // 16-bit upper bounds of each register vector's maximum go to shared
   // memory, two per word, so the compaction below need not revisit the data
@@ -392,8 +428,27 @@ __device__ __forceinline__ bool candidate_plan(const Tile& tile, const GT& gt, i
 
   // The per-thread statistics go to shared memory, so no vector register
   // holds them across the stores below.
-  S.top2[2 * threadIdx.x] = DT::raw_of_value(M1);
-  S.top2[2 * threadIdx.x + 1] = DT::raw_of_value(M2);
+  S.topm[threadIdx.x] = DT::raw_of_value(M1);
+  S.topm[kThreads + threadIdx.x] = DT::raw_of_value(M2);
+  if constexpr (Tile::kRegisters && sizeof(raw_t) == 2) {
+    if (top4) {  // uniform
+      float a[kTopPerThread];
+#pragma unroll
+      for (int r = 0; r < kTopPerThread; ++r) a[r] = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < Tile::kVecs; ++i) {  // this thread's own entries: no barrier needed
+        float v = DT::ub16_value((S.vmw[i >> 1][threadIdx.x] >> ((i & 1) * 16)) & 0xFFFFu);
+#pragma unroll
+        for (int r = 0; r < kTopPerThread; ++r) {
+          const float t = fmaxf(a[r], v);
+          v = fminf(a[r], v);
+          a[r] = t;
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < kTopPerThread; ++r) S.topm[r * kThreads + threadIdx.x] = DT::raw_of_value(a[r]);
+    }
+  }
   S.run[threadIdx.x] = run;
   S.acc[threadIdx.x] = acc;
 
@@ -410,11 +465,15 @@ __device__ __forceinline__ bool candidate_plan(const Tile& tile, const GT& gt, i
   if constexpr (Tile::kRegisters)
     if (wr) tile.template store_const_range<store_upto<Tile::kVecs, 0>(), store_upto<Tile::kVecs, 1>()>(orow, DT::kNegInf);
   // 3. row maximum, smallest finite per-thread maximum, Z for top-p-only rows
-  const float M1s = DT::value(static_cast<raw_t>(S.top2[2 * threadIdx.x]));
-  const float M2s = DT::value(static_cast<raw_t>(S.top2[2 * threadIdx.x + 1]));
-  uint32_t klo = 0xFFFFFFFFu;  // smallest key among finite maxima
-  if (M1s > -INFINITY) klo = DT::key(DT::raw_of_value(M1s));
-  if (M2s > -INFINITY) klo = DT::key(DT::raw_of_value(M2s));
+  const float M1s = DT::value(static_cast<raw_t>(S.topm[threadIdx.x]));
+  uint32_t klo = 0xFFFFFFFFu;  // smallest key among finite maxima (each thread's come in descending order)
+#pragma unroll
+  for (int r = 0; r < kTopPerThread; ++r) {
+    if (r < 2 || top4) {  // uniform
+      const float Mr = DT::value(static_cast<raw_t>(S.topm[r * kThreads + threadIdx.x]));
+      if (Mr > -INFINITY) klo = DT::key(DT::raw_of_value(Mr));
+    }
+  }
   float m;
   block_max_f32_min_u32(M1s, klo, sm, m, klo);
   const uint32_t kmax = DT::key(DT::raw_of_value(m));
@@ -432,15 +491,19 @@ __device__ __forceinline__ bool candidate_plan(const Tile& tile, const GT& gt, i
   if constexpr (Tile::kRegisters)
     if (wr) tile.template store_const_range<store_upto<Tile::kVecs, 1>(), store_upto<Tile::kVecs, 2>()>(orow, DT::kNegInf);
   // 4. candidate bound L
-  const LdsValues<DT> top2{S.top2, kTop2};
+  const TopMaxima<DT, 2> top2{S.topm};
   const bool top_only = rp.pmode == kPTopOnly || (ponly && thr == 0);
   // min-p alone: its survivors lie above m + ln(min_p), so that floor bounds them
   const bool mp_only = rp.mp_on && !rp.k_on && rp.pmode == kPNone;
   uint32_t L = kmax;
   bool fast = klo <= kmax;
+  auto key_of = [](auto raw, int) { return DT::key(raw); };
   if (rp.k_on) {
-    fast = fast && rp.k <= static_cast<uint32_t>(kTop2) &&
-           kth_largest_bound(top2, rp.k, klo, kmax, [](auto raw, int) { return DT::key(raw); }, ss, L);
+    if (top4)
+      fast = fast && rp.k <= kBoundMaxK4 &&
+             kth_largest_bound(TopMaxima<DT, kTopPerThread>{S.topm}, rp.k, klo, kmax, key_of, ss, L);
+    else
+      fast = fast && rp.k <= kBoundMaxK2 && kth_largest_bound(top2, rp.k, klo, kmax, key_of, ss, L);
   } else if (mp_only) {
     L = key_floor<DT>(min_p_floor(m, rp.minp));
   } else if (!top_only) {
@@ -561,7 +624,49 @@ __device__ __forceinline__ bool candidate_plan(const Tile& tile, const GT& gt, i
     lds_barrier();
     nvec = S.nvec;
     fallback = nvec > static_cast<uint32_t>(kCandVecCap);
-    if (!fallback) {
+    bool listed = false;  // the elements are already in the candidate list
+    if constexpr (Tile::kRegisters) {
+      if (fallback) {  // uniform
+        // more candidate vectors than their list holds (large k, wide rows):
+        // each thread counts its elements >= L in its candidate slots, a
+        // block scan places them, and each thread writes its own. The slot
+        // mask is taken first: the element list overwrites the maxima.
+        uint32_t slots = 0;
+        uint32_t mine = 0;
+        tile.for_each_vec([&](int i, const vec_t& q, int e0) {
+          if (is_cand(i, e0)) {
+            slots |= 1u << i;
+#pragma unroll
+            for (int j = 0; j < kPV; ++j)
+              mine += (e0 + j < V && DT::value(lane_of<raw_t>(q, j)) >= Lf) ? 1u : 0u;
+          }
+        });
+        const uint32_t incl = block_incl_scan_u32(mine, ss.wtot32);
+        if (threadIdx.x == kThreads - 1) S.ncand = incl;
+        lds_barrier();  // every slot mask is taken before the list is written
+        uint32_t at = incl - mine;
+        tile.for_each_vec([&](int i, const vec_t& q, int e0) {
+          if ((slots >> i) & 1u) {
+#pragma unroll
+            for (int j = 0; j < kPV; ++j) {
+              const raw_t r = lane_of<raw_t>(q, j);
+              if (e0 + j < V && DT::value(r) >= Lf) {
+                if (at < static_cast<uint32_t>(kCandCap)) {
+                  S.cel.raw[at] = r;
+                  S.cel.idx[at] = static_cast<uint32_t>(e0 + j);
+                }
+                ++at;
+              }
+            }
+          }
+        });
+        lds_barrier();
+        ncand = static_cast<int>(S.ncand);
+        fallback = ncand > kCandCap;
+        listed = true;
+      }
+    }
+    if (!fallback && !listed) {
       // each thread takes listed vectors tid and tid + 1024 (a streamed row
       // requests both from global memory at once); per element lane j of the
       // vectors a wave ballot places the elements >= L
